@@ -1,0 +1,433 @@
+"""CPU oracle for the forward pass of a token-choice Mixture-of-Experts FFN layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import this module.  It is plain NumPy in
+float64, imports neither torch nor the GPU library, and shares no code with
+the GPU path.  It takes exactly the bits the GPU takes (bf16 inputs widened
+exactly to float64) and does not round intermediates.
+
+The pages it follows (cited by title and section):
+  [P1]  wmrh.cn/news/98181, the explainer that opens with "MoE 的核心思想":
+        sections 公式表达重点 (gate scores, softmax, top-K with the other
+        scores sent to minus infinity, renormalised gates), 具体数值示例
+        (worked example), 专家容量限制 (capacity), Router Z-Loss.
+  [P3]  mzlw.cn/news/6844 "MoE 混合专家模型稀疏激活的架构原理与负载均衡挑战":
+        2.1 (h(x) equation and logits = x W_r), 2.2 (L_aux equation),
+        2.3 (capacity equation, token dropping), 三 (the PyTorch MoELayer:
+        SwiGLU Expert, MoERouter top-K then softmax of the top-K logits,
+        load-balance loss from scatter-add counts, per-expert truncation of
+        the ascending token list to capacity, gate-weighted accumulation).
+  [P4]  learnagent.wiki "混合专家模型（Mixture of Experts, MoE）":
+        结构 2 (G(x) = Softmax(W_r x)), 结构 3 (y = sum over top-K of
+        G_i E_i), 结构 4 (selection-only per-expert bias), 运行示例 (softmax,
+        top-K on probabilities, renormalise, GELU experts, compute all
+        experts then gather).
+  [P5]  mstx.cn/posts/467.html "MoE 如何替代 FFN？它解决了什么问题？带来哪些新挑战？":
+        section 1 (FFN(x) = W2 act(W1 x)), section 2 (MoE(x) formula),
+        section 5 (DeepSeek-MoE: fine-grained experts plus a shared expert).
+
+Readings taken where the pages are silent or disagree are listed next to the
+function that takes them.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from fractions import Fraction
+
+import numpy as np
+
+GATE_MODES = ("renorm_all", "softmax_topk", "prob_no_renorm")
+
+
+# ---------------------------------------------------------------- format ---
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 stored as uint16 bits -> float64 (exact): a bf16 is the upper half
+    of an IEEE fp32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+class Bf16Stack:
+    """A stack of bf16 matrices held as uint16 bits; indexing one entry
+    returns it widened to float64, so large expert weights are converted one
+    expert at a time."""
+
+    def __init__(self, bits: np.ndarray):
+        self.bits = np.asarray(bits, dtype=np.uint16)
+        self.shape = self.bits.shape
+
+    def __getitem__(self, e):
+        return bf16_bits_to_f64(self.bits[e])
+
+    def __len__(self):
+        return self.shape[0]
+
+
+# ---------------------------------------------------------------- router ---
+
+def router_logits(x: np.ndarray, w_r: np.ndarray, b_r: np.ndarray | None = None):
+    """logits[t, e] = sum_j x[t, j] * w_r[e, j] (+ b_r[e]).
+
+    [P3] 2.1 writes logits = x . W_r with W_r of shape d x N; the page's
+    MoERouter stores the weight as [N, d] and multiplies by its transpose,
+    which is the same map.  [P4] 结构 2 / 运行示例 uses a linear layer with a
+    bias; the bias (and any fixed per-expert logit offset) is folded in here.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w_r = np.asarray(w_r, dtype=np.float64)
+    out = x @ w_r.T
+    if b_r is not None:
+        out = out + np.asarray(b_r, dtype=np.float64)[None, :]
+    return out
+
+
+def softmax_rows(v: np.ndarray) -> np.ndarray:
+    """Row softmax with the row maximum subtracted ([P4] 结构 2)."""
+    m = v.max(axis=-1, keepdims=True)
+    e = np.exp(v - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def logsumexp_rows(v: np.ndarray) -> np.ndarray:
+    m = v.max(axis=-1, keepdims=True)
+    return (m + np.log(np.exp(v - m).sum(axis=-1, keepdims=True)))[:, 0]
+
+
+def select_topk(scores: np.ndarray, K: int):
+    """The K experts with the largest score for every token.
+
+    Reading (pages silent): equal scores go to the LOWER expert index; the K
+    chosen ids are listed in order of decreasing score.  Implemented as a
+    full stable sort of every row by descending score ([P3] 三 calls topk on
+    the logits, [P4] 运行示例 on the probabilities: softmax is monotone, so
+    the chosen set is the same).
+
+    Returns (idx[T, K] int64, margin[T]) where margin is the score gap
+    between the K-th and (K+1)-th ranked experts (+inf when K == N).
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    if not np.all(np.isfinite(s)):
+        raise ValueError("oracle: non-finite router scores")
+    T, N = s.shape
+    order = np.argsort(-s, axis=1, kind="stable")  # ties keep index order
+    idx = order[:, :K].astype(np.int64)
+    srt = np.take_along_axis(s, order, axis=1)
+    if K < N:
+        margin = srt[:, K - 1] - srt[:, K]
+    else:
+        margin = np.full(T, np.inf)
+    return idx, margin
+
+
+def gate_weights(logits: np.ndarray, idx: np.ndarray, mode: str) -> np.ndarray:
+    """Gate of each chosen expert.
+
+    renorm_all     : P = softmax over all N logits, g = P[idx] / sum P[idx]
+                     ([P4] 运行示例 divides the top-K probabilities by their
+                     sum; [P1] 公式表达重点 says the gates are renormalised).
+    softmax_topk   : g = softmax of the K chosen logits ([P3] 三, MoERouter;
+                     [P3] 2.1 diagram: top-K then softmax).  Equal to
+                     renorm_all in exact arithmetic.
+    prob_no_renorm : g = P[idx] ([P4] 结构 3 and [P3] 2.1 read literally).
+    """
+    if mode == "renorm_all":
+        P = softmax_rows(logits)
+        pk = np.take_along_axis(P, idx, axis=1)
+        return pk / pk.sum(axis=1, keepdims=True)
+    if mode == "softmax_topk":
+        return softmax_rows(np.take_along_axis(logits, idx, axis=1))
+    if mode == "prob_no_renorm":
+        return np.take_along_axis(softmax_rows(logits), idx, axis=1)
+    raise ValueError(mode)
+
+
+# ----------------------------------------------------------------- stats ---
+
+@dataclass
+class RouterStats:
+    count: np.ndarray   # [N] int64: pairs that chose e (before capacity)
+    f: np.ndarray       # [N] count / (T*K)
+    p: np.ndarray       # [N] mean router probability
+    aux: float          # alpha * N * sum f*p
+    z: float            # mean_t sum_e logits^2
+    z_lse: float        # mean_t logsumexp(logits_t)^2  (not from the pages)
+
+
+def router_stats(logits: np.ndarray, idx: np.ndarray, alpha: float) -> RouterStats:
+    """Switch load-balance loss [P3] 2.2: L_aux = alpha * N * sum_i f_i p_i,
+    f_i = share of routed slots that went to expert i, p_i = mean router
+    probability of expert i.  [P3] 三 counts the top-K indices of all T
+    tokens (before any capacity cut) and divides by T*K; that reading is
+    taken, so sum_i f_i = 1.
+
+    Router z-loss, [P1] Router Z-Loss: the page only says the sum of squares
+    of the router logits is penalised.  Read literally as z = mean over
+    tokens of sum_e logits^2, no coefficient.  z_lse (mean squared
+    log-sum-exp) is an extra, common form that the pages do not give.
+    """
+    T, N = logits.shape
+    K = idx.shape[1]
+    count = np.zeros(N, dtype=np.int64)
+    for t in range(T):
+        for k in range(K):
+            count[idx[t, k]] += 1
+    f = count / float(T * K)
+    p = softmax_rows(logits).mean(axis=0)
+    aux = float(alpha * N * np.sum(f * p))
+    z = float(np.mean(np.sum(logits * logits, axis=1)))
+    lse = logsumexp_rows(logits)
+    z_lse = float(np.mean(lse * lse))
+    return RouterStats(count=count, f=f, p=p, aux=aux, z=z, z_lse=z_lse)
+
+
+# -------------------------------------------------------------- capacity ---
+
+def capacity(K: int, N: int, T: int, cf) -> int:
+    """capacity = floor(K / N * CF * S)  [P3] 2.3, with S read as the number
+    of tokens in the batch (the page's MoELayer uses B*S there).  Computed
+    with exact rationals (CF taken from its decimal string), so it never
+    suffers the floating truncation of int(K/N*CF*T).  cf=None: unlimited,
+    returned as T (no expert can receive more than T tokens)."""
+    if cf is None:
+        return int(T)
+    q = Fraction(K, N) * Fraction(str(cf)) * T
+    return int(math.floor(q))
+
+
+@dataclass
+class Assignment:
+    kept: np.ndarray      # [N] rows each expert keeps
+    offset: np.ndarray    # [N+1] exclusive scan of kept
+    pair_row: np.ndarray  # [T, K] row in the expert-contiguous buffer, -1 = dropped
+    row_pair: np.ndarray  # [sum kept] t*K + k of each row
+    dropped: np.ndarray   # [T, K] uint8
+    n_dropped: int
+
+
+def assign_capacity(idx: np.ndarray, N: int, cap: int) -> Assignment:
+    """Token dropping [P3] 2.3 and 三: each expert takes the tokens that chose
+    it in ascending token order and keeps the first `cap`; the rest are
+    dropped (their contribution is 0; the residual outside the layer carries
+    them).  Reading: the cap counts all K slots of an expert together (an
+    expert appears at most once per token), whereas the page's loop caps
+    each k slot separately; the two agree for K=1.
+
+    Kept pairs are laid out expert-contiguously: expert e owns rows
+    [offset[e], offset[e+1]) in ascending token order.
+    """
+    T, K = idx.shape
+    rank = np.full((T, K), -1, dtype=np.int64)
+    seen = np.zeros(N, dtype=np.int64)
+    for t in range(T):
+        for k in range(K):
+            e = int(idx[t, k])
+            rank[t, k] = seen[e]
+            seen[e] += 1
+    kept = np.minimum(seen, cap)
+    offset = np.zeros(N + 1, dtype=np.int64)
+    offset[1:] = np.cumsum(kept)
+    pair_row = np.full((T, K), -1, dtype=np.int64)
+    row_pair = np.full(int(offset[N]), -1, dtype=np.int64)
+    dropped = np.zeros((T, K), dtype=np.uint8)
+    for t in range(T):
+        for k in range(K):
+            e = int(idx[t, k])
+            if rank[t, k] < cap:
+                r = offset[e] + rank[t, k]
+                pair_row[t, k] = r
+                row_pair[r] = t * K + k
+            else:
+                dropped[t, k] = 1
+    return Assignment(kept=kept, offset=offset, pair_row=pair_row,
+                      row_pair=row_pair, dropped=dropped,
+                      n_dropped=int(dropped.sum()))
+
+
+# --------------------------------------------------------------- experts ---
+
+def silu(u):
+    """silu(u) = u * sigmoid(u) = u / (1 + exp(-u))."""
+    return u / (1.0 + np.exp(-u))
+
+
+def gelu_tanh(u):
+    """Tanh approximation of GELU (Hendrycks & Gimpel):
+    0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))."""
+    return 0.5 * u * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)))
+
+
+def expert_swiglu(xr, w1, w3, w2):
+    """[P3] 三, Expert.forward: down( silu(gate(x)) * up(x) ).  Weights in
+    linear-layer layout [out, in]: w1 (gate) [F, d], w3 (up) [F, d],
+    w2 (down) [d, F].  No biases, dropout off (eval mode)."""
+    g = xr @ np.asarray(w1, dtype=np.float64).T
+    u = xr @ np.asarray(w3, dtype=np.float64).T
+    return (silu(g) * u) @ np.asarray(w2, dtype=np.float64).T
+
+
+def expert_gelu(xr, w1, w2, b1=None, b2=None):
+    """[P4] 运行示例 expert: Linear(d, F) -> GELU -> Linear(F, d), biases
+    optional; [P5] section 1 gives the same FFN(x) = W2 act(W1 x)."""
+    h = xr @ np.asarray(w1, dtype=np.float64).T
+    if b1 is not None:
+        h = h + np.asarray(b1, dtype=np.float64)[None, :]
+    o = gelu_tanh(h) @ np.asarray(w2, dtype=np.float64).T
+    if b2 is not None:
+        o = o + np.asarray(b2, dtype=np.float64)[None, :]
+    return o
+
+
+def run_expert(act, xr, e, W):
+    if act == "swiglu":
+        return expert_swiglu(xr, W["w1"][e], W["w3"][e], W["w2"][e])
+    if act == "gelu_tanh":
+        b1 = None if W.get("b1") is None else W["b1"][e]
+        b2 = None if W.get("b2") is None else W["b2"][e]
+        return expert_gelu(xr, W["w1"][e], W["w2"][e], b1, b2)
+    raise ValueError(act)
+
+
+def expert_outputs(act, x, asg: Assignment, W, N, K, experts=None):
+    """y_perm[row] = E_e(x[t]) for every kept row, expert by expert, each as a
+    dense matmul over that expert's rows (the page's per-expert loop, [P3]
+    三).  `experts` limits the work to a subset (rows of others stay NaN)."""
+    d = x.shape[1]
+    y_perm = np.full((int(asg.offset[N]), d), np.nan)
+    for e in range(N) if experts is None else experts:
+        lo, hi = int(asg.offset[e]), int(asg.offset[e + 1])
+        if hi == lo:
+            continue
+        toks = asg.row_pair[lo:hi] // K
+        y_perm[lo:hi] = run_expert(act, x[toks], e, W)
+    return y_perm
+
+
+def combine(y_perm, pair_row, gates, T, d, y_shared=None):
+    """y_t = sum_k [kept] g_tk * E_{idx_tk}(x_t) (+ shared expert), [P1]
+    公式表达重点, [P3] 三 (gate-weighted accumulation), [P4] 结构 3.  A
+    dropped pair adds nothing and the other gates are NOT renormalised."""
+    y = np.zeros((T, d)) if y_shared is None else np.array(y_shared, dtype=np.float64)
+    K = pair_row.shape[1]
+    for t in range(T):
+        for k in range(K):
+            r = pair_row[t, k]
+            if r >= 0:
+                y[t] += gates[t, k] * y_perm[r]
+    return y
+
+
+# ----------------------------------------------------------------- layer ---
+
+@dataclass
+class LayerResult:
+    logits: np.ndarray
+    idx: np.ndarray
+    margin: np.ndarray
+    gates: np.ndarray
+    stats: RouterStats
+    cap: int
+    asg: Assignment
+    y_perm: np.ndarray | None
+    y_shared: np.ndarray | None
+    y: np.ndarray | None
+
+
+def layer_forward(x, W, *, K, act, gate_mode, cf=None, alpha=1.0,
+                  b_r=None, b_sel=None, shared=None, tokens=None,
+                  experts_needed=True):
+    """Whole layer, in the order the pages give it: router logits, selection
+    (scores + optional selection-only bias, [P4] 结构 4), gates (from the raw
+    logits only), statistics, capacity and dispatch, per-expert FFN, shared
+    expert ([P5] section 5), combine.
+
+    W: dict of float64-able arrays w_r [N,d], w1 [N,F,d], w3 [N,F,d] (SwiGLU),
+    w2 [N,d,F], optional b1 [N,F], b2 [N,d].  shared: None or dict
+    (w1 [Fs,d], w3 [Fs,d], w2 [d,Fs]).
+    tokens: optional list of token ids; routing/dispatch/stats are always
+    computed for all T tokens, but the expert FFN and combine only for these
+    tokens (y rows of other tokens are NaN).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T, d = x.shape
+    N = W["w_r"].shape[0]
+    logits = router_logits(x, W["w_r"], b_r)
+    scores = logits if b_sel is None else logits + np.asarray(b_sel, np.float64)[None, :]
+    idx, margin = select_topk(scores, K)
+    gates = gate_weights(logits, idx, gate_mode)
+    stats = router_stats(logits, idx, alpha)
+    cap = capacity(K, N, T, cf)
+    asg = assign_capacity(idx, N, cap)
+    if not experts_needed:
+        return LayerResult(logits, idx, margin, gates, stats, cap, asg, None, None, None)
+    if tokens is None:
+        y_perm = expert_outputs(act, x, asg, W, N, K)
+        y_shared = None if shared is None else expert_swiglu(
+            x, shared["w1"], shared["w3"], shared["w2"])
+        y = combine(y_perm, asg.pair_row, gates, T, d, y_shared)
+    else:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        y_perm = None
+        y = np.full((T, d), np.nan)
+        y_shared = np.full((T, d), np.nan) if shared is not None else None
+        if shared is not None:
+            y_shared[tokens] = expert_swiglu(x[tokens], shared["w1"], shared["w3"], shared["w2"])
+        for t in tokens:
+            acc = np.zeros(d) if shared is None else y_shared[t].copy()
+            for k in range(K):
+                if asg.pair_row[t, k] >= 0:
+                    e = int(idx[t, k])
+                    acc += gates[t, k] * run_expert(act, x[t:t + 1], e, W)[0]
+            y[t] = acc
+    return LayerResult(logits, idx, margin, gates, stats, cap, asg, y_perm, y_shared, y)
+
+
+def brute_force_layer(x, W, *, K, act, gate_mode, cf=None, b_r=None,
+                      b_sel=None, shared=None):
+    """A second, independent route to the same output, following [P4]
+    运行示例: run EVERY expert on EVERY token, then pick each token's chosen
+    outputs and weight them.  Capacity (if any) is applied by listing, for
+    each expert, the tokens that chose it and keeping the first `cap`.
+    Used only on tiny inputs to cross-check layer_forward."""
+    x = np.asarray(x, dtype=np.float64)
+    T, d = x.shape
+    N = W["w_r"].shape[0]
+    logits = x @ np.asarray(W["w_r"], np.float64).T
+    if b_r is not None:
+        logits = logits + b_r
+    scores = logits if b_sel is None else logits + b_sel
+    # selection by exhaustive ranking: expert e outranks e' iff (s_e > s_e')
+    # or (s_e == s_e' and e < e')
+    idx = np.zeros((T, K), dtype=np.int64)
+    for t in range(T):
+        beaten_by = [sum(1 for j in range(N) if scores[t, j] > scores[t, e]
+                         or (scores[t, j] == scores[t, e] and j < e)) for e in range(N)]
+        for e in range(N):
+            if beaten_by[e] < K:
+                idx[t, beaten_by[e]] = e
+    # gates via the masked-softmax form of [P1] 公式表达重点: scores of the
+    # experts not chosen are set to -inf before the softmax
+    masked = np.full_like(logits, -np.inf)
+    np.put_along_axis(masked, idx, np.take_along_axis(logits, idx, axis=1), axis=1)
+    if gate_mode == "prob_no_renorm":
+        full = np.exp(logits - logits.max(axis=1, keepdims=True))
+        full = full / full.sum(axis=1, keepdims=True)
+        gates = np.take_along_axis(full, idx, axis=1)
+    else:
+        m = np.exp(masked - masked.max(axis=1, keepdims=True))
+        gates = np.take_along_axis(m / m.sum(axis=1, keepdims=True), idx, axis=1)
+    all_out = np.stack([run_expert(act, x, e, W) for e in range(N)], axis=1)  # [T,N,d]
+    cap = capacity(K, N, T, cf)
+    keep = np.zeros((T, K), dtype=bool)
+    for e in range(N):
+        chosen = [(t, k) for t in range(T) for k in range(K) if idx[t, k] == e]
+        for (t, k) in chosen[:cap]:
+            keep[t, k] = True
+    y = np.zeros((T, d)) if shared is None else expert_swiglu(
+        x, shared["w1"], shared["w3"], shared["w2"])
+    for t in range(T):
+        for k in range(K):
+            if keep[t, k]:
+                y[t] = y[t] + gates[t, k] * all_out[t, idx[t, k]]
+    return idx, gates, keep, y
