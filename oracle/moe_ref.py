@@ -367,18 +367,29 @@ def layer_forward(x, W, *, K, act, gate_mode, cf=None, alpha=1.0,
             x, shared["w1"], shared["w3"], shared["w2"])
         y = combine(y_perm, asg.pair_row, gates, T, d, y_shared)
     else:
+        # only the listed tokens: each expert runs once over the listed
+        # tokens it kept (so its weights are read once), then every token
+        # sums its K terms in slot order
         tokens = np.asarray(tokens, dtype=np.int64)
         y_perm = None
         y = np.full((T, d), np.nan)
         y_shared = np.full((T, d), np.nan) if shared is not None else None
         if shared is not None:
             y_shared[tokens] = expert_swiglu(x[tokens], shared["w1"], shared["w3"], shared["w2"])
+        term = {}
+        for e in range(N):
+            sel = [(int(t), k) for t in tokens for k in range(K)
+                   if idx[t, k] == e and asg.pair_row[t, k] >= 0]
+            if not sel:
+                continue
+            out = run_expert(act, x[[t for t, _ in sel]], e, W)
+            for (t, k), o in zip(sel, out):
+                term[(t, k)] = o
         for t in tokens:
             acc = np.zeros(d) if shared is None else y_shared[t].copy()
             for k in range(K):
-                if asg.pair_row[t, k] >= 0:
-                    e = int(idx[t, k])
-                    acc += gates[t, k] * run_expert(act, x[t:t + 1], e, W)[0]
+                if (int(t), k) in term:
+                    acc = acc + gates[t, k] * term[(int(t), k)]
             y[t] = acc
     return LayerResult(logits, idx, margin, gates, stats, cap, asg, y_perm, y_shared, y)
 
