@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer forward on one MI355X.
+
+One step = one moe_layer_forward (router, statistics, dispatch, both grouped
+GEMMs with the shared expert when present, combine) over one batch of seeded
+synthetic input already resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-decode]
+
+Default workload: Mixtral-shaped prefill (T=4096, d=4096, N=8, top-2, SwiGLU
+F=14336, bf16).  Unless --no-decode, the line also carries the decode-shaped
+DeepSeek-V3 layer (T=128, d=7168, N=256, top-8, F=2048 + shared expert)
+measured the same way, as HBM GB/s on the expert weights it touches.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/s + active TFLOP/s (prefill); HBM GB/s (decode T=128)"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=256,
+                    help="tokens the oracle runs for the CPU baseline")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.h = C.CDLL("libamdhip64.so.7")
+        self.h.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.h.hipEventDestroy.argtypes = [C.c_void_p]
+        self.h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+
+    def create(self):
+        e = C.c_void_p()
+        if self.h.hipEventCreate(C.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed(self, a, b):
+        ms = C.c_float()
+        if self.h.hipEventElapsedTime(C.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def active_work(w, kept_rows):
+    """Algorithmic flops of the two grouped GEMMs (kept pairs + shared
+    expert) and the expert-weight bytes the step must read."""
+    mats = 3 if w.act == "swiglu" else 2
+    flops_routed = 2.0 * kept_rows * w.d * w.F * mats
+    flops_shared = 2.0 * w.T * w.d * w.F_shared * 3 if w.F_shared else 0.0
+    g1_flops = 2.0 * kept_rows * w.d * w.F * (mats - 1) + (
+        2.0 * w.T * w.d * w.F_shared * 2 if w.F_shared else 0.0)
+    return flops_routed + flops_shared, g1_flops
+
+
+def run_workload(w, steps, warmup, ev):
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_46_amd import _lib as L
+    from sparse_mixture_experts_46_amd import api
+    from sparse_mixture_experts_46_amd.inputs import make_inputs
+
+    inp = make_inputs(w, device="cuda")
+    cfg = api.config_for(w)
+    bufs = api.LayerBuffers(cfg, torch.device("cuda"))
+    wst = api.weights_struct(inp)
+    traces = []
+    for _ in range(steps):
+        t = L.MoeTrace()
+        for i in range(L.MOE_TRACE_EVENTS):
+            t.ev[i] = ev.create()
+        traces.append(t)
+    for _ in range(warmup):
+        api.moe_layer_forward(cfg, inp, inp["x"], bufs=bufs, wstruct=wst)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        api.moe_layer_forward(cfg, inp, inp["x"], bufs=bufs, wstruct=wst, trace=traces[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = np.zeros(5)
+    for t in traces:
+        for j in range(5):
+            stage[j] += ev.elapsed(t.ev[j], t.ev[j + 1])
+    stage /= steps
+    for t in traces:
+        for i in range(L.MOE_TRACE_EVENTS):
+            ev.destroy(t.ev[i])
+    cnt = bufs.counters.cpu().numpy()
+    kept_rows, touched = int(cnt[0]), int(cnt[3])
+    total_flops, g1_flops = active_work(w, kept_rows)
+    mats = 3 if w.act == "swiglu" else 2
+    wbytes = 2.0 * (touched * mats * w.d * w.F + (3 * w.d * w.F_shared if w.F_shared else 0))
+    res = dict(inp=inp, bufs=bufs, wall=wall, stage_ms=stage, kept_rows=kept_rows,
+               touched=touched, total_flops=total_flops, g1_flops=g1_flops, wbytes=wbytes)
+    return res
+
+
+def cpu_baseline(w, inp, sample):
+    """The oracle, as it stands, on the first `sample` tokens of the same
+    workload (routing over those tokens, capacity, experts, combine)."""
+    import numpy as np
+    import torch
+
+    from oracle import moe_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+
+    def bits(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    def f64(t):
+        return None if t is None else t.detach().cpu().double().numpy()
+
+    bf = w.dtype == "bf16"
+    stack = (lambda t: ref.Bf16Stack(bits(t))) if bf else f64
+    W = {"w_r": f64(inp["w_r"]), "w1": stack(inp["w1"]), "w2": stack(inp["w2"])}
+    if inp.get("w3") is not None:
+        W["w3"] = stack(inp["w3"])
+    shared = None
+    if inp.get("ws1") is not None:
+        shared = {"w1": f64(inp["ws1"]), "w3": f64(inp["ws3"]), "w2": f64(inp["ws2"])}
+    x = f64(inp["x"][:sample])
+    t0 = time.perf_counter()
+    ref.layer_forward(x, W, K=w.K, act=w.act, gate_mode=w.gate, cf=w.cf, alpha=w.aux_alpha,
+                      b_r=f64(inp["b_r"]), b_sel=f64(inp["b_sel"]), shared=shared)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {sample} of {w.T} tokens of {w.name} (same weights), full layer "
+                      f"in NumPy float64 incl. per-expert bf16->fp64 weight widening; "
+                      f"{dt:.1f} s"}
+
+
+def traffic_record(name):
+    """HBM bytes per launch of the first grouped GEMM from the committed
+    rocprofv3 counter runs, or None when the kernel source changed since."""
+    import hashlib
+    p = os.path.join(ROOT, "profiles", f"traffic_gemm1_{name}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    src = os.path.join(ROOT, "sparse_mixture_experts_46_amd", "csrc", "gemm_bf16.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("gemm_source_sha256") != h:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); the "
+              "multi-GPU expert-parallel path is not part of it", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from sparse_mixture_experts_46_amd import _lib as L
+    from sparse_mixture_experts_46_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    L.load()
+    ev = HipEvents()
+    w = WL.ALL[a.workload]
+    r = run_workload(w, a.steps, a.warmup, ev)
+    ms = r["wall"] * 1e3 / a.steps
+    tok_s = w.T / (ms / 1e3)
+    g1_ms = float(r["stage_ms"][2])
+    g1_tflops = r["g1_flops"] / (g1_ms * 1e-3) / 1e12
+    traffic = traffic_record(w.name)
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, random init)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "K": w.K, "F": w.F,
+                   "F_shared": w.F_shared, "act": w.act, "capacity_factor": w.cf,
+                   "router": "fp32", "desc": w.desc},
+        "roofline": {"bound": "mfma", "kernel": "grouped GEMM 1 (gate/up + SiLU*mul)",
+                     "achieved": g1_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": g1_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "avg_ms": g1_ms, "flops_per_launch": r["g1_flops"]},
+        "active_tflops": r["total_flops"] / (ms * 1e-3) / 1e12,
+        "active_frac_of_bf16_peak": r["total_flops"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "weight_gbs": r["wbytes"] / (ms * 1e-3) / 1e9,
+        "stage_ms": {k: float(v) for k, v in zip(
+            ["router+stats", "dispatch", "gemm1", "gemm2", "combine"], r["stage_ms"])},
+        "kept_rows": r["kept_rows"],
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, r["inp"], min(a.cpu_sample, w.T))
+    del r
+    torch.cuda.empty_cache()
+    if not a.no_decode:
+        wd = WL.DEEPSEEK_DECODE
+        rd = run_workload(wd, a.steps, a.warmup, ev)
+        msd = rd["wall"] * 1e3 / a.steps
+        gbs = rd["wbytes"] / (msd * 1e-3) / 1e9
+        line["decode"] = {
+            "workload": wd.name, "T": wd.T, "ms_per_step": msd, "tokens_per_s": wd.T / (msd * 1e-3),
+            "touched_experts": rd["touched"], "weight_bytes": rd["wbytes"],
+            "hbm_gbs": gbs, "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
+            "stage_ms": {k: float(v) for k, v in zip(
+                ["router+stats", "dispatch", "gemm1", "gemm2", "combine"], rd["stage_ms"])},
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,244 @@
+/*
+ * moe.h: C ABI of libmoe, the forward pass of a token-choice
+ * Mixture-of-Experts FFN layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pages cited by title and section):
+ *   - router linear layer, logits = x W_r^T (+ b_r): mzlw.cn "MoE 混合专家模型
+ *     稀疏激活的架构原理与负载均衡挑战" 2.1; learnagent.wiki "混合专家模型
+ *     （Mixture of Experts, MoE）" 结构 2.
+ *   - top-K selection and gates renormalised over the chosen K: wmrh.cn
+ *     explainer ("MoE 的核心思想") section 公式表达重点; mzlw.cn section 三
+ *     (MoERouter); learnagent.wiki 运行示例.
+ *   - selection-only per-expert bias: learnagent.wiki 结构 4.
+ *   - Switch auxiliary loss alpha*N*sum f_i p_i: mzlw.cn 2.2; router
+ *     z-loss: wmrh.cn section Router Z-Loss.
+ *   - capacity floor(K/N*CF*S) and token dropping: mzlw.cn 2.3.
+ *   - per-expert FFN (SwiGLU: mzlw.cn section 三, Expert; GELU:
+ *     learnagent.wiki 运行示例), shared expert: mstx.cn "MoE 如何替代
+ *     FFN？…" section 5; grouped GEMM instead of the per-expert loop: the
+ *     comment in mzlw.cn section 三, MoELayer.forward.
+ *   - gate-weighted combine y = sum_k g_k E_k(x): wmrh.cn 公式表达重点;
+ *     learnagent.wiki 结构 3.
+ *
+ * Conventions for every entry point:
+ *   - Every tensor pointer is a DEVICE pointer (HIP device memory of the
+ *     current device), row-major, densely packed, 16-byte aligned.  The
+ *     caller owns every buffer, including the workspace; the library
+ *     allocates nothing and keeps no mutable global state.
+ *   - `stream` is a hipStream_t (may be NULL = default stream).  Work is
+ *     enqueued asynchronously; no entry point synchronises the host.
+ *   - bf16 tensors are IEEE bfloat16 (uint16 storage).  The router weight,
+ *     router biases, logits, gates and statistics are always fp32.
+ *   - Argument errors are detected on the host before anything is enqueued
+ *     and return MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED /
+ *     MOE_ERR_WORKSPACE.  A failed kernel launch returns MOE_ERR_HIP.
+ *     T == 0 is valid and enqueues nothing.
+ *   - Ties between equal router scores go to the lower expert index; the
+ *     K chosen experts of a token are listed by decreasing score.
+ *   - Results are deterministic: repeated calls on the same inputs give
+ *     bitwise-identical outputs (no floating-point atomics).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, K > N, negative size, ...       */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but outside this build's limits        */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required   */
+  MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed   */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+  MOE_ACT_SWIGLU = 0,     /* down( silu(x W1^T) * (x W3^T) )                 */
+  MOE_ACT_GELU_TANH = 1   /* down( gelu_tanh(x W1^T + b1) ) + b2             */
+} moe_act_t;
+
+typedef enum {
+  MOE_GATE_RENORM_ALL = 0,     /* softmax over all N, divided by the top-K sum */
+  MOE_GATE_SOFTMAX_TOPK = 1,   /* softmax of the K chosen logits (same value)  */
+  MOE_GATE_PROB_NO_RENORM = 2  /* softmax over all N, not renormalised         */
+} moe_gate_t;
+
+/* Limits of this build (MOE_ERR_UNSUPPORTED outside them):
+ *   1 <= N <= 1024, 1 <= K <= min(N, 16), d % 64 == 0, F % 64 == 0,
+ *   F_shared % 64 == 0, T <= 2^24, bf16 layers need d, F >= 64.        */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+typedef struct {
+  int64_t T;          /* tokens (rows of x)                                  */
+  int32_t d;          /* model width                                         */
+  int32_t N;          /* routed experts                                      */
+  int32_t K;          /* experts chosen per token                            */
+  int32_t F;          /* routed expert intermediate width                    */
+  int32_t F_shared;   /* shared expert intermediate width, 0 = no shared     */
+  int32_t dtype;      /* moe_dtype_t of x, expert weights, expert biases, y  */
+  int32_t act;        /* moe_act_t                                           */
+  int32_t gate;       /* moe_gate_t                                          */
+  int64_t capacity;   /* rows each expert may keep; < 0 = unlimited          */
+  float aux_alpha;    /* alpha of the Switch auxiliary loss                  */
+  uint32_t flags;     /* reserved, must be 0                                 */
+} moe_config_t;
+
+/* Weights.  Router: w_r [N, d] fp32, b_r [N] fp32 (nullable; also carries any
+ * fixed per-expert logit offset), b_sel [N] fp32 selection-only bias
+ * (nullable).  Experts, in linear-layer layout [out, in], dtype cfg->dtype:
+ * w1 [N, F, d] (SwiGLU gate, or the GELU input projection), w3 [N, F, d]
+ * (SwiGLU up; NULL for GELU), w2 [N, d, F] (down), b1 [N, F] and b2 [N, d]
+ * (GELU only, nullable).  Shared expert (SwiGLU, only when F_shared > 0):
+ * ws1 [F_shared, d], ws3 [F_shared, d], ws2 [d, F_shared].                */
+typedef struct {
+  const float* w_r;
+  const float* b_r;
+  const float* b_sel;
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  const void* b1;
+  const void* b2;
+  const void* ws1;
+  const void* ws3;
+  const void* ws2;
+} moe_weights_t;
+
+/* Router statistics (each pointer nullable):
+ *   count [N] int32: pairs (token, slot) that chose expert e, before capacity
+ *   f     [N] fp32 : count / (T*K)
+ *   p     [N] fp32 : mean over tokens of softmax(logits)_e
+ *   loss  [3] fp32 : { aux = alpha*N*sum_e f_e p_e,
+ *                      z = mean_t sum_e logits_te^2,
+ *                      z_lse = mean_t logsumexp(logits_t)^2 }            */
+typedef struct {
+  int32_t* count;
+  float* f;
+  float* p;
+  float* loss;
+} moe_stats_t;
+
+/* Dispatch outputs.  A "pair" is (token t, slot k), flattened as t*K + k.
+ *   kept     [N]    int32 rows kept by each expert = min(count, capacity)
+ *   offset   [N+1]  int32 exclusive scan of kept; expert e owns rows
+ *                   [offset[e], offset[e+1]) in ascending token order;
+ *                   offset[N] = total kept rows                 (required)
+ *   pair_row [T*K]  int32 row of each pair, -1 if dropped      (required)
+ *   row_pair [T*K]  int32 pair id (t*K+k) of each row; entries at and
+ *                   after offset[N] are left untouched          (required)
+ *   dropped  [T*K]  uint8 1 if the pair was dropped (capacity or bad id)
+ *   counters [4]    int32 { kept rows, dropped pairs, pairs with an
+ *                   out-of-range or repeated expert id, experts with >= 1
+ *                   kept row }
+ *   x_perm   [T*K, d] dtype: x_perm[r] = x[row_pair[r] / K] for r < offset[N]
+ * Each pointer marked nullable in moe_dispatch may be NULL.               */
+typedef struct {
+  int32_t* kept;
+  int32_t* offset;
+  int32_t* pair_row;
+  int32_t* row_pair;
+  uint8_t* dropped;
+  int32_t* counters;
+  void* x_perm;
+} moe_dispatch_t;
+
+/* Outputs of the whole layer.  y [T, d] (dtype) is required; every other
+ * pointer is nullable and, when NULL, the value lives in the workspace.   */
+typedef struct {
+  void* y;
+  int32_t* topk_idx;    /* [T, K] */
+  float* topk_gate;     /* [T, K] */
+  float* logits;        /* [T, N] */
+  moe_stats_t stats;
+  moe_dispatch_t dispatch;  /* x_perm is ignored (rows are gathered in place) */
+} moe_layer_out_t;
+
+/* Optional timing hooks: hipEvent_t handles recorded on `stream` at stage
+ * boundaries of moe_layer_forward (any may be NULL):
+ *   ev[0] before the router, ev[1] after routing + statistics,
+ *   ev[2] after dispatch, right before the first grouped GEMM (gate/up),
+ *   ev[3] after the first grouped GEMM, ev[4] after the second grouped GEMM
+ *   (down), ev[5] after the combine.                                      */
+#define MOE_TRACE_EVENTS 6
+typedef struct {
+  void* ev[MOE_TRACE_EVENTS];
+} moe_trace_t;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status_t s);
+
+/* Capacity floor(K / N * cf * T) (mzlw.cn 2.3, S read as the tokens in the
+ * batch), computed with the factor cf rounded to 1e-9 and exact integer
+ * arithmetic afterwards.  cf < 0 means unlimited and returns T.  Returns -1
+ * on invalid arguments (K < 1, N < 1, T < 0).  Host only.               */
+int64_t moe_capacity(int32_t K, int32_t N, int64_t T, double cf);
+
+/* Bytes of workspace moe_layer_forward needs for `cfg` (host only).     */
+moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes);
+
+/* Bytes of workspace the staged entry points need (host only).          */
+moe_status_t moe_router_workspace_size(const moe_config_t* cfg, size_t* bytes);
+moe_status_t moe_dispatch_workspace_size(const moe_config_t* cfg, size_t* bytes);
+moe_status_t moe_ffn_workspace_size(const moe_config_t* cfg, size_t* bytes);
+
+/* Router: logits, selection, gates and statistics.
+ *   x [T, d] (cfg->dtype), w->w_r, w->b_r, w->b_sel as above.
+ *   topk_idx [T, K] int32, topk_gate [T, K] fp32 (required);
+ *   logits [T, N] fp32 (nullable), stats (nullable, and each member).
+ * Selection key s = logits + b_sel; gates use logits only (cfg->gate).  */
+moe_status_t moe_router_topk(const moe_config_t* cfg, const moe_weights_t* w,
+                             const void* x, int32_t* topk_idx, float* topk_gate,
+                             float* logits, const moe_stats_t* stats,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch: per-expert counts, capacity clamp in token order, layout of the
+ * kept pairs in expert-contiguous rows, and (if out->x_perm) the gathered
+ * rows.  topk_idx [T, K] int32 on the device; ids outside [0, N) and ids
+ * repeated within one token are counted in counters[2] and dropped.
+ * out->kept, out->dropped, out->counters, out->x_perm are nullable; x may
+ * be NULL when out->x_perm is NULL.                                      */
+moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx,
+                          const void* x, const moe_dispatch_t* out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs as grouped GEMMs over the expert-contiguous rows.
+ *   a      : x_perm [rows, d] when a_rows == NULL; otherwise x [T, d] and
+ *            row r reads x[a_rows[r] / K] (a_rows = row_pair).
+ *   offset : [N+1] device row offsets (from moe_dispatch).
+ *   y_perm : [T*K, d] output rows (rows >= offset[N] untouched).
+ *   x_shared / y_shared : [T, d] input / output of the shared expert (both
+ *            required iff F_shared > 0; then every token goes through it). */
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, const moe_weights_t* w,
+                            const void* a, const int32_t* a_rows,
+                            const int32_t* offset, void* y_perm,
+                            const void* x_shared, void* y_shared,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Combine: y[t] = sum_{k=0}^{K-1} [pair_row[t,k] >= 0] gate[t,k] *
+ * y_perm[pair_row[t,k]]  (+ y_shared[t] when y_shared != NULL), summed in
+ * fp32 in that fixed order and rounded once to cfg->dtype.  Dropped pairs
+ * add nothing; the remaining gates are not renormalised.                 */
+moe_status_t moe_combine(const moe_config_t* cfg, const void* y_perm,
+                         const int32_t* pair_row, const float* topk_gate,
+                         const void* y_shared, void* y, void* stream);
+
+/* The whole layer: router, statistics, dispatch, expert FFNs (+ shared
+ * expert), combine.  ws must hold moe_workspace_size(cfg) bytes.  trace
+ * is nullable.                                                           */
+moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
+                               const void* x, const moe_layer_out_t* out,
+                               void* ws, size_t ws_bytes, const moe_trace_t* trace,
+                               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

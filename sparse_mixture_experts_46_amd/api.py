@@ -1,0 +1,221 @@
+"""Python binding of libmoe with the C entry points' names.
+
+Torch tensors supply device memory and the current HIP stream; every step
+of the layer runs in libmoe's HIP kernels.  There is no CPU fallback: the
+functions raise if the library is missing or a tensor is not on the GPU.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as L
+from .workloads import Workload
+
+_ACT = {"swiglu": L.MOE_ACT_SWIGLU, "gelu_tanh": L.MOE_ACT_GELU_TANH}
+_GATE = {"renorm_all": L.MOE_GATE_RENORM_ALL, "softmax_topk": L.MOE_GATE_SOFTMAX_TOPK,
+         "prob_no_renorm": L.MOE_GATE_PROB_NO_RENORM}
+
+
+@dataclass
+class Config:
+    T: int
+    d: int
+    N: int
+    K: int
+    F: int
+    F_shared: int = 0
+    dtype: str = "bf16"
+    act: str = "swiglu"
+    gate: str = "softmax_topk"
+    capacity: int = -1
+    aux_alpha: float = 1.0
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def c(self) -> L.MoeConfig:
+        return L.MoeConfig(T=self.T, d=self.d, N=self.N, K=self.K, F=self.F,
+                           F_shared=self.F_shared,
+                           dtype=L.MOE_BF16 if self.dtype == "bf16" else L.MOE_F32,
+                           act=_ACT[self.act], gate=_GATE[self.gate], capacity=self.capacity,
+                           aux_alpha=self.aux_alpha, flags=0)
+
+
+def config_for(w: Workload) -> Config:
+    cap = -1 if w.cf is None else moe_capacity(w.K, w.N, w.T, w.cf)
+    return Config(T=w.T, d=w.d, N=w.N, K=w.K, F=w.F, F_shared=w.F_shared, dtype=w.dtype,
+                  act=w.act, gate=w.gate, capacity=cap, aux_alpha=w.aux_alpha)
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors only")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _size(fn, cfg: Config) -> int:
+    n = C.c_size_t(0)
+    L.check(fn(C.byref(cfg.c()), C.byref(n)), fn.__name__)
+    return n.value
+
+
+def moe_capacity(K: int, N: int, T: int, cf) -> int:
+    """floor(K/N * cf * T); cf None/negative = unlimited (returns T)."""
+    return int(L.load().moe_capacity(K, N, T, -1.0 if cf is None else float(cf)))
+
+
+def moe_workspace_size(cfg: Config) -> int:
+    return _size(L.load().moe_workspace_size, cfg)
+
+
+def weights_struct(t: dict) -> L.MoeWeights:
+    w = L.MoeWeights()
+    for k in ("w_r", "b_r", "b_sel", "w1", "w3", "w2", "b1", "b2", "ws1", "ws3", "ws2"):
+        v = t.get(k)
+        setattr(w, k, None if v is None else _p(v).value)
+    return w
+
+
+def moe_router_topk(cfg: Config, w: dict, x: torch.Tensor, want_logits=False,
+                    want_stats=True) -> dict:
+    lib = L.load()
+    dev = x.device
+    T, N, K = cfg.T, cfg.N, cfg.K
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, N), dtype=torch.float32, device=dev) if want_logits else None
+    out = {"idx": idx, "gate": gate, "logits": logits}
+    st = None
+    if want_stats:
+        out["count"] = torch.empty(N, dtype=torch.int32, device=dev)
+        out["f"] = torch.empty(N, dtype=torch.float32, device=dev)
+        out["p"] = torch.empty(N, dtype=torch.float32, device=dev)
+        out["loss"] = torch.empty(3, dtype=torch.float32, device=dev)
+        st = L.MoeStats(count=_p(out["count"]).value, f=_p(out["f"]).value,
+                        p=_p(out["p"]).value, loss=_p(out["loss"]).value)
+    ws = _ws(_size(lib.moe_router_workspace_size, cfg), dev)
+    L.check(lib.moe_router_topk(C.byref(cfg.c()), C.byref(weights_struct(w)), _p(x), _p(idx),
+                                _p(gate), _p(logits), C.byref(st) if st else None, _p(ws),
+                                ws.numel(), _stream()), "moe_router_topk")
+    out["_ws"] = ws
+    return out
+
+
+def moe_dispatch(cfg: Config, idx: torch.Tensor, x: torch.Tensor | None = None,
+                 want_x_perm=False) -> dict:
+    lib = L.load()
+    dev = idx.device
+    T, N, K = cfg.T, cfg.N, cfg.K
+    o = {"kept": torch.empty(N, dtype=torch.int32, device=dev),
+         "offset": torch.empty(N + 1, dtype=torch.int32, device=dev),
+         "pair_row": torch.empty(T * K, dtype=torch.int32, device=dev),
+         "row_pair": torch.full((T * K,), -1, dtype=torch.int32, device=dev),
+         "dropped": torch.empty(T * K, dtype=torch.uint8, device=dev),
+         "counters": torch.empty(4, dtype=torch.int32, device=dev),
+         "x_perm": (torch.empty((T * K, cfg.d), dtype=cfg.torch_dtype, device=dev)
+                    if want_x_perm else None)}
+    d = L.MoeDispatch(**{k: (None if o[k] is None else _p(o[k]).value)
+                         for k in ("kept", "offset", "pair_row", "row_pair", "dropped",
+                                   "counters", "x_perm")})
+    ws = _ws(_size(lib.moe_dispatch_workspace_size, cfg), dev)
+    L.check(lib.moe_dispatch(C.byref(cfg.c()), _p(idx), _p(x), C.byref(d), _p(ws), ws.numel(),
+                             _stream()), "moe_dispatch")
+    o["_ws"] = ws
+    return o
+
+
+def moe_expert_ffn(cfg: Config, w: dict, a: torch.Tensor, offset: torch.Tensor,
+                   a_rows: torch.Tensor | None = None, x_shared: torch.Tensor | None = None,
+                   y_perm: torch.Tensor | None = None) -> dict:
+    lib = L.load()
+    dev = a.device
+    if y_perm is None:
+        y_perm = torch.empty((cfg.T * cfg.K, cfg.d), dtype=cfg.torch_dtype, device=dev)
+    y_shared = (torch.empty((cfg.T, cfg.d), dtype=cfg.torch_dtype, device=dev)
+                if cfg.F_shared else None)
+    ws = _ws(_size(lib.moe_ffn_workspace_size, cfg), dev)
+    L.check(lib.moe_expert_ffn(C.byref(cfg.c()), C.byref(weights_struct(w)), _p(a), _p(a_rows),
+                               _p(offset), _p(y_perm), _p(x_shared), _p(y_shared), _p(ws),
+                               ws.numel(), _stream()), "moe_expert_ffn")
+    return {"y_perm": y_perm, "y_shared": y_shared, "_ws": ws}
+
+
+def moe_combine(cfg: Config, y_perm: torch.Tensor, pair_row: torch.Tensor, gate: torch.Tensor,
+                y_shared: torch.Tensor | None = None) -> torch.Tensor:
+    lib = L.load()
+    y = torch.empty((cfg.T, cfg.d), dtype=cfg.torch_dtype, device=y_perm.device)
+    L.check(lib.moe_combine(C.byref(cfg.c()), _p(y_perm), _p(pair_row), _p(gate), _p(y_shared),
+                            _p(y), _stream()), "moe_combine")
+    return y
+
+
+class LayerBuffers:
+    """Preallocated outputs and workspace for repeated moe_layer_forward calls."""
+
+    def __init__(self, cfg: Config, device, want_logits=False):
+        T, N, K = cfg.T, cfg.N, cfg.K
+        self.cfg = cfg
+        self.y = torch.empty((T, cfg.d), dtype=cfg.torch_dtype, device=device)
+        self.idx = torch.empty((T, K), dtype=torch.int32, device=device)
+        self.gate = torch.empty((T, K), dtype=torch.float32, device=device)
+        self.logits = (torch.empty((T, N), dtype=torch.float32, device=device)
+                       if want_logits else None)
+        self.count = torch.empty(N, dtype=torch.int32, device=device)
+        self.f = torch.empty(N, dtype=torch.float32, device=device)
+        self.p = torch.empty(N, dtype=torch.float32, device=device)
+        self.loss = torch.empty(3, dtype=torch.float32, device=device)
+        self.kept = torch.empty(N, dtype=torch.int32, device=device)
+        self.offset = torch.empty(N + 1, dtype=torch.int32, device=device)
+        self.pair_row = torch.empty(T * K, dtype=torch.int32, device=device)
+        self.row_pair = torch.empty(T * K, dtype=torch.int32, device=device)
+        self.dropped = torch.empty(T * K, dtype=torch.uint8, device=device)
+        self.counters = torch.empty(4, dtype=torch.int32, device=device)
+        self.ws = _ws(moe_workspace_size(cfg), device)
+        self.out = L.MoeLayerOut()
+        self.out.y = _p(self.y).value
+        self.out.topk_idx = _p(self.idx).value
+        self.out.topk_gate = _p(self.gate).value
+        self.out.logits = None if self.logits is None else _p(self.logits).value
+        self.out.stats = L.MoeStats(count=_p(self.count).value, f=_p(self.f).value,
+                                    p=_p(self.p).value, loss=_p(self.loss).value)
+        self.out.dispatch = L.MoeDispatch(
+            kept=_p(self.kept).value, offset=_p(self.offset).value,
+            pair_row=_p(self.pair_row).value, row_pair=_p(self.row_pair).value,
+            dropped=_p(self.dropped).value, counters=_p(self.counters).value, x_perm=None)
+        self.ccfg = cfg.c()
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k in ("y", "idx", "gate", "logits", "count", "f", "p",
+                                               "loss", "kept", "offset", "pair_row", "row_pair",
+                                               "dropped", "counters")}
+
+
+def moe_layer_forward(cfg: Config, w: dict, x: torch.Tensor, bufs: LayerBuffers | None = None,
+                      wstruct: L.MoeWeights | None = None, trace: L.MoeTrace | None = None,
+                      want_logits=False) -> LayerBuffers:
+    lib = L.load()
+    if bufs is None:
+        bufs = LayerBuffers(cfg, x.device, want_logits=want_logits)
+    if wstruct is None:
+        wstruct = weights_struct(w)
+    L.check(lib.moe_layer_forward(C.byref(bufs.ccfg), C.byref(wstruct), _p(x), C.byref(bufs.out),
+                                  _p(bufs.ws), bufs.ws.numel(),
+                                  C.byref(trace) if trace is not None else None, _stream()),
+            "moe_layer_forward")
+    return bufs

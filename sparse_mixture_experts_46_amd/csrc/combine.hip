@@ -1,0 +1,108 @@
+// Gate-weighted combine: y_t = sum_k [kept] g_tk * E_{e_tk}(x_t) (+ shared).
+//
+// Pages (by title and section): wmrh.cn explainer ("MoE 的核心思想")
+// 公式表达重点 (output = gate-weighted sum of the chosen experts' outputs);
+// learnagent.wiki "混合专家模型（Mixture of Experts, MoE）" 结构 3 (same sum);
+// mzlw.cn "MoE 混合专家模型稀疏激活的架构原理与负载均衡挑战" 2.3 (a dropped
+// token skips the expert computation and is carried by the residual, so it
+// contributes nothing here).
+//
+// Deterministic gather-reduce: each output element sums its K terms in slot
+// order in fp32, then adds the shared expert, then rounds once.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// bf16: each thread owns 8 consecutive columns (16 bytes).
+__global__ __launch_bounds__(256) void combine_bf16_kernel(
+    const uint16_t* __restrict__ y_perm, const int32_t* __restrict__ pair_row,
+    const float* __restrict__ gate, const uint16_t* __restrict__ y_shared,
+    uint16_t* __restrict__ y, int64_t T, int d, int K) {
+  const int chunks = d / 8;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    int32_t rows[kMaxTopK];
+    float gs[kMaxTopK];
+    for (int k = 0; k < K; ++k) {
+      rows[k] = pair_row[t * K + k];
+      gs[k] = gate[t * K + k];
+    }
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+      float acc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+      for (int k = 0; k < K; ++k) {
+        if (rows[k] < 0) continue;
+        const uint4 v = *(const uint4*)(y_perm + (int64_t)rows[k] * d + c * 8);
+        float f[8];
+        unpack_bf16x8(v, f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(gs[k], f[j], acc[j]);
+      }
+      if (y_shared) {
+        const uint4 v = *(const uint4*)(y_shared + t * d + c * 8);
+        float f[8];
+        unpack_bf16x8(v, f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += f[j];
+      }
+      uint4 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+      *(uint4*)(y + t * d + c * 8) = o;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(
+    const float* __restrict__ y_perm, const int32_t* __restrict__ pair_row,
+    const float* __restrict__ gate, const float* __restrict__ y_shared,
+    float* __restrict__ y, int64_t T, int d, int K) {
+  const int chunks = d / 4;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    int32_t rows[kMaxTopK];
+    float gs[kMaxTopK];
+    for (int k = 0; k < K; ++k) {
+      rows[k] = pair_row[t * K + k];
+      gs[k] = gate[t * K + k];
+    }
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < K; ++k) {
+        if (rows[k] < 0) continue;
+        const float4 v = *(const float4*)(y_perm + (int64_t)rows[k] * d + c * 4);
+        acc.x = fmaf(gs[k], v.x, acc.x);
+        acc.y = fmaf(gs[k], v.y, acc.y);
+        acc.z = fmaf(gs[k], v.z, acc.z);
+        acc.w = fmaf(gs[k], v.w, acc.w);
+      }
+      if (y_shared) {
+        const float4 v = *(const float4*)(y_shared + t * d + c * 4);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      *(float4*)(y + t * d + c * 4) = acc;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y_perm, const int32_t* pair_row,
+                          const float* gate, const void* y_shared, void* y,
+                          int64_t T, int d, int K, bool bf16,
+                          hipStream_t stream) {
+  int64_t grid = T < 8192 ? T : 8192;
+  if (grid < 1) grid = 1;
+  if (bf16)
+    combine_bf16_kernel<<<(unsigned)grid, 256, 0, stream>>>(
+        (const uint16_t*)y_perm, pair_row, gate, (const uint16_t*)y_shared, (uint16_t*)y, T, d, K);
+  else
+    combine_f32_kernel<<<(unsigned)grid, 256, 0, stream>>>(
+        (const float*)y_perm, pair_row, gate, (const float*)y_shared, (float*)y, T, d, K);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,207 @@
+// Dispatch: per-expert counts, capacity clamp in token order, the layout of
+// the kept (token, slot) pairs in expert-contiguous rows, and the gather of
+// the kept tokens into those rows.
+//
+// Pages (by title and section):
+//   mzlw.cn "MoE 混合专家模型稀疏激活的架构原理与负载均衡挑战": 2.3 (capacity
+//     floor(K/N * CF * S); tokens over an expert's capacity are dropped and
+//     reach the next layer through the residual path), section 三 (MoELayer:
+//     for each expert, the ascending list of tokens that chose it is cut to
+//     `capacity` and those rows are gathered; the per-expert loop is to be
+//     replaced by grouped matrix multiplication).
+//
+// Token order without atomics on the ranks: every block of 256 tokens
+// builds, in LDS, one bit per (expert, token) for the tokens that chose the
+// expert.  The in-block rank of a pair is the popcount of the expert's bits
+// below its token; the rank across blocks adds an exclusive scan of the
+// per-block counts.  Everything is integer and deterministic.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int DT = kDispatchTokens;   // tokens per block
+constexpr int DW = DT / 32;           // 32-bit words per expert bitmap
+
+// Fills the block's bitmap; returns in bad[] per pair whether the id is out
+// of range or repeats an earlier slot of the same token.
+__device__ __forceinline__ void build_bitmap(const int32_t* __restrict__ idx,
+                                             int64_t T, int N, int K,
+                                             uint32_t* bm, int64_t t,
+                                             int local) {
+  for (int i = threadIdx.x; i < N * DW; i += DT) bm[i] = 0u;
+  __syncthreads();
+  if (t < T) {
+    for (int k = 0; k < K; ++k) {
+      int e = idx[t * K + k];
+      bool bad = (e < 0) || (e >= N);
+      for (int k2 = 0; k2 < k && !bad; ++k2) bad = (idx[t * K + k2] == e);
+      if (!bad) atomicOr(&bm[e * DW + (local >> 5)], 1u << (local & 31));
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(DT) void dispatch_hist_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int N, int K,
+    int32_t* __restrict__ blk_count, int32_t* __restrict__ blk_bad) {
+  extern __shared__ uint32_t bm[];
+  __shared__ int nbad;
+  const int local = threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * DT + local;
+  if (local == 0) nbad = 0;
+  build_bitmap(idx, T, N, K, bm, t, local);
+  if (t < T) {
+    int mybad = 0;
+    for (int k = 0; k < K; ++k) {
+      int e = idx[t * K + k];
+      bool bad = (e < 0) || (e >= N);
+      for (int k2 = 0; k2 < k && !bad; ++k2) bad = (idx[t * K + k2] == e);
+      mybad += bad ? 1 : 0;
+    }
+    if (mybad) atomicAdd(&nbad, mybad);  // integer: order-independent
+  }
+  for (int e = local; e < N; e += DT) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < DW; ++w) c += __popc(bm[e * DW + w]);
+    blk_count[(int64_t)blockIdx.x * N + e] = c;
+  }
+  __syncthreads();
+  if (local == 0) blk_bad[blockIdx.x] = nbad;
+}
+
+// One block of 1024 threads: per-expert exclusive scan over blocks (token
+// order), capacity clamp, exclusive scan of kept rows over experts.
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
+    const int32_t* __restrict__ blk_count, const int32_t* __restrict__ blk_bad,
+    int64_t nblk, int64_t T, int N, int K, int64_t cap,
+    int32_t* __restrict__ blk_base, int32_t* __restrict__ kept_out,
+    int32_t* __restrict__ offset, int32_t* __restrict__ counters) {
+  __shared__ int32_t skept[kMaxExperts];
+  __shared__ int32_t scan[1024];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < N; e += 1024) {
+    int32_t run = 0;
+    for (int64_t b = 0; b < nblk; ++b) {
+      int32_t c = blk_count[b * N + e];
+      blk_base[b * N + e] = run;
+      run += c;
+    }
+    int32_t kp = (int64_t)run < cap ? run : (int32_t)cap;
+    skept[e] = kp;
+    if (kept_out) kept_out[e] = kp;
+  }
+  __syncthreads();
+  // exclusive scan of skept[0..N) ; N <= 1024 so one element per thread
+  int32_t v = tid < N ? skept[tid] : 0;
+  scan[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int32_t add = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  if (tid < N) offset[tid] = scan[tid] - v;
+  if (tid == 0) {
+    int32_t total = scan[1023];
+    offset[N] = total;
+    if (counters) {
+      int64_t bad = 0;
+      for (int64_t b = 0; b < nblk; ++b) bad += blk_bad[b];
+      int touched = 0;
+      for (int e = 0; e < N; ++e) touched += skept[e] > 0 ? 1 : 0;
+      counters[0] = total;
+      counters[1] = (int32_t)(T * K - total);
+      counters[2] = (int32_t)bad;
+      counters[3] = touched;
+    }
+  }
+}
+
+__global__ __launch_bounds__(DT) void dispatch_assign_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int N, int K, int64_t cap,
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ offset,
+    int32_t* __restrict__ pair_row, int32_t* __restrict__ row_pair,
+    uint8_t* __restrict__ dropped) {
+  extern __shared__ uint32_t bm[];
+  const int local = threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * DT + local;
+  build_bitmap(idx, T, N, K, bm, t, local);
+  if (t >= T) return;
+  const int w = local >> 5;
+  const uint32_t below = (1u << (local & 31)) - 1u;
+  for (int k = 0; k < K; ++k) {
+    const int64_t pr = t * K + k;
+    int e = idx[pr];
+    bool bad = (e < 0) || (e >= N);
+    for (int k2 = 0; k2 < k && !bad; ++k2) bad = (idx[t * K + k2] == e);
+    int32_t row = -1;
+    if (!bad) {
+      int r = 0;
+      for (int w2 = 0; w2 < w; ++w2) r += __popc(bm[e * DW + w2]);
+      r += __popc(bm[e * DW + w] & below);
+      int64_t rank = (int64_t)blk_base[(int64_t)blockIdx.x * N + e] + r;
+      if (rank < cap) {
+        row = offset[e] + (int32_t)rank;
+        row_pair[row] = (int32_t)pr;
+      }
+    }
+    pair_row[pr] = row;
+    if (dropped) dropped[pr] = row < 0 ? 1 : 0;
+  }
+}
+
+// x_perm[r] = x[row_pair[r] / K] for r < offset[N]; 16-byte chunks.
+__global__ __launch_bounds__(256) void permute_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ row_pair,
+    const int32_t* __restrict__ offset, int N, int K, int chunks,
+    uint4* __restrict__ x_perm) {
+  const int total = offset[N];
+  for (int r = blockIdx.x; r < total; r += gridDim.x) {
+    const int64_t src = row_pair[r] / K;
+    const uint4* s = x + src * chunks;
+    uint4* dst = x_perm + (int64_t)r * chunks;
+    for (int c = threadIdx.x; c < chunks; c += 256) dst[c] = s[c];
+  }
+}
+
+}  // namespace
+
+int64_t dispatch_num_blocks(int64_t T) { return (T + DT - 1) / DT; }
+
+hipError_t launch_dispatch(const int32_t* idx, int64_t T, int N, int K,
+                           int64_t capacity, int32_t* blk_count,
+                           int32_t* blk_base, int32_t* blk_bad,
+                           int32_t* kept, int32_t* offset, int32_t* pair_row,
+                           int32_t* row_pair, uint8_t* dropped,
+                           int32_t* counters, hipStream_t stream) {
+  const int64_t nblk = dispatch_num_blocks(T);
+  const size_t smem = (size_t)N * DW * sizeof(uint32_t);
+  const int64_t cap = capacity < 0 ? T : capacity;
+  dispatch_hist_kernel<<<(unsigned)nblk, DT, smem, stream>>>(idx, T, N, K, blk_count, blk_bad);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dispatch_scan_kernel<<<1, 1024, 0, stream>>>(blk_count, blk_bad, nblk, T, N, K, cap,
+                                               blk_base, kept, offset, counters);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dispatch_assign_kernel<<<(unsigned)nblk, DT, smem, stream>>>(
+      idx, T, N, K, cap, blk_base, offset, pair_row, row_pair, dropped);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* row_pair,
+                          const int32_t* offset, int N, int K, int d,
+                          int64_t max_rows, void* x_perm, hipStream_t stream) {
+  const int chunks = d * elem_bytes / 16;
+  int64_t grid = max_rows < 4096 ? max_rows : 4096;
+  if (grid < 1) grid = 1;
+  permute_kernel<<<(unsigned)grid, 256, 0, stream>>>((const uint4*)x, row_pair, offset, N, K,
+                                                     chunks, (uint4*)x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

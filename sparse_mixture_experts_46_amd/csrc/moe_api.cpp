@@ -1,0 +1,346 @@
+// libmoe C ABI: argument checks, workspace layout and the launch sequence
+// of the MoE layer forward.  Host code only; kernels live in the .hip files.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+moe_status_t check_config(const moe_config_t* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->d <= 0 || c->N <= 0 || c->K <= 0 || c->F <= 0 || c->F_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->K > c->N) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->act != MOE_ACT_SWIGLU && c->act != MOE_ACT_GELU_TANH) return MOE_ERR_INVALID_ARG;
+  if (c->gate < MOE_GATE_RENORM_ALL || c->gate > MOE_GATE_PROB_NO_RENORM) return MOE_ERR_INVALID_ARG;
+  if (c->flags != 0) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->aux_alpha)) return MOE_ERR_INVALID_ARG;
+  if (c->N > MOE_MAX_EXPERTS || c->K > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (c->d % 64 || c->F % 64 || c->F_shared % 64) return MOE_ERR_UNSUPPORTED;
+  if (c->F_shared != 0 && (c->F_shared != c->F || c->act != MOE_ACT_SWIGLU)) return MOE_ERR_UNSUPPORTED;
+  if (c->T > (int64_t(1) << 24)) return MOE_ERR_UNSUPPORTED;
+  if (c->T * c->K > (int64_t)INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t elem_bytes(const moe_config_t* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+
+// ---- workspace layouts -----------------------------------------------------
+struct RouterWs {
+  size_t logits, part_p, part_cnt, part_z, total;
+};
+RouterWs router_ws(const moe_config_t* c) {
+  RouterWs w;
+  const int64_t nb = router_num_blocks(c->T);
+  size_t o = 0;
+  w.logits = o; o = align_up(o + (size_t)c->T * c->N * 4);
+  w.part_p = o; o = align_up(o + (size_t)nb * c->N * 4);
+  w.part_cnt = o; o = align_up(o + (size_t)nb * c->N * 4);
+  w.part_z = o; o = align_up(o + (size_t)nb * 2 * 4);
+  w.total = o;
+  return w;
+}
+
+struct DispatchWs {
+  size_t blk_count, blk_base, blk_bad, total;
+};
+DispatchWs dispatch_ws(const moe_config_t* c) {
+  DispatchWs w;
+  const int64_t nb = dispatch_num_blocks(c->T);
+  size_t o = 0;
+  w.blk_count = o; o = align_up(o + (size_t)nb * c->N * 4);
+  w.blk_base = o; o = align_up(o + (size_t)nb * c->N * 4);
+  w.blk_bad = o; o = align_up(o + (size_t)nb * 4);
+  w.total = o;
+  return w;
+}
+
+struct FfnWs {
+  size_t tile_base, h, total;
+};
+FfnWs ffn_ws(const moe_config_t* c) {
+  FfnWs w;
+  size_t o = 0;
+  w.tile_base = o; o = align_up(o + (size_t)2 * (c->N + 2) * 4);
+  w.h = o; o = align_up(o + ffn_workspace_bytes(c->T, c->d, c->N, c->K, c->F, c->F_shared,
+                                                c->dtype == MOE_BF16));
+  w.total = o;
+  return w;
+}
+
+struct LayerWs {
+  RouterWs r;
+  DispatchWs dsp;
+  FfnWs f;
+  size_t router, dispatch, ffn;
+  size_t idx, gate, kept, offset, pair_row, row_pair, counters, y_perm, y_shared;
+  size_t total;
+};
+LayerWs layer_ws(const moe_config_t* c) {
+  LayerWs w;
+  w.r = router_ws(c);
+  w.dsp = dispatch_ws(c);
+  w.f = ffn_ws(c);
+  const size_t pairs = (size_t)c->T * c->K;
+  const size_t eb = elem_bytes(c);
+  size_t o = 0;
+  w.router = o; o = align_up(o + w.r.total);
+  w.dispatch = o; o = align_up(o + w.dsp.total);
+  w.ffn = o; o = align_up(o + w.f.total);
+  w.idx = o; o = align_up(o + pairs * 4);
+  w.gate = o; o = align_up(o + pairs * 4);
+  w.kept = o; o = align_up(o + (size_t)c->N * 4);
+  w.offset = o; o = align_up(o + (size_t)(c->N + 1) * 4);
+  w.pair_row = o; o = align_up(o + pairs * 4);
+  w.row_pair = o; o = align_up(o + pairs * 4);
+  w.counters = o; o = align_up(o + 4 * 4);
+  w.y_perm = o; o = align_up(o + pairs * (size_t)c->d * eb);
+  w.y_shared = o; o = align_up(o + (c->F_shared > 0 ? (size_t)c->T * c->d * eb : 0));
+  w.total = o;
+  return w;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<unsigned char*>(ws) + off);
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status_t check_weights_router(const moe_weights_t* w) {
+  if (!w || !w->w_r) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status_t check_weights_ffn(const moe_config_t* c, const moe_weights_t* w) {
+  if (!w || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
+  if (c->act == MOE_ACT_SWIGLU && !w->w3) return MOE_ERR_INVALID_ARG;
+  if (c->act == MOE_ACT_SWIGLU && (w->b1 || w->b2)) return MOE_ERR_UNSUPPORTED;
+  if (c->F_shared > 0 && (!w->ws1 || !w->ws3 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// ---- stages ----------------------------------------------------------------
+moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void* x,
+                       int32_t* idx, float* gate, float* logits, const moe_stats_t* st,
+                       void* ws, hipStream_t s) {
+  const RouterWs L = router_ws(c);
+  float* lg = logits ? logits : at<float>(ws, L.logits);
+  hipError_t e = launch_router_logits(x, c->dtype == MOE_BF16, w->w_r, w->b_r, lg, c->T, c->d,
+                                      c->N, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_router_topk(lg, w->b_sel, idx, gate, at<float>(ws, L.part_p),
+                         at<int32_t>(ws, L.part_cnt), at<float>(ws, L.part_z), c->T, c->N, c->K,
+                         c->gate, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (st && (st->count || st->f || st->p || st->loss)) {
+    e = launch_router_stats(at<float>(ws, L.part_p), at<int32_t>(ws, L.part_cnt),
+                            at<float>(ws, L.part_z), router_num_blocks(c->T), c->T, c->N, c->K,
+                            c->aux_alpha, st->count, st->f, st->p, st->loss, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status_t do_dispatch(const moe_config_t* c, const int32_t* idx, const moe_dispatch_t* o,
+                         void* ws, hipStream_t s) {
+  const DispatchWs L = dispatch_ws(c);
+  hipError_t e = launch_dispatch(idx, c->T, c->N, c->K, c->capacity, at<int32_t>(ws, L.blk_count),
+                                 at<int32_t>(ws, L.blk_base), at<int32_t>(ws, L.blk_bad), o->kept,
+                                 o->offset, o->pair_row, o->row_pair, o->dropped, o->counters, s);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+int64_t moe_capacity(int32_t K, int32_t N, int64_t T, double cf) {
+  if (K < 1 || N < 1 || T < 0 || std::isnan(cf)) return -1;
+  if (cf < 0) return T;
+  const double scaled = cf * 1e9;
+  if (scaled > 9.0e18) return -1;
+  const __int128 num = (__int128)std::llround(scaled);
+  const __int128 q = ((__int128)K * num * (__int128)T) / ((__int128)N * (__int128)1000000000);
+  return (int64_t)q;
+}
+
+moe_status_t moe_router_workspace_size(const moe_config_t* cfg, size_t* bytes) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = router_ws(cfg).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_dispatch_workspace_size(const moe_config_t* cfg, size_t* bytes) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = dispatch_ws(cfg).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_ffn_workspace_size(const moe_config_t* cfg, size_t* bytes) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = ffn_ws(cfg).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = layer_ws(cfg).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_router_topk(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                             int32_t* topk_idx, float* topk_gate, float* logits,
+                             const moe_stats_t* stats, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights_router(w)) != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < router_ws(cfg).total) return MOE_ERR_WORKSPACE;
+  return do_router(cfg, w, x, topk_idx, topk_gate, logits, stats, ws, (hipStream_t)stream);
+}
+
+moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, const void* x,
+                          const moe_dispatch_t* out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!out) return MOE_ERR_INVALID_ARG;
+  if (cfg->T == 0) return MOE_OK;
+  if (!topk_idx || !out->offset || !out->pair_row || !out->row_pair) return MOE_ERR_INVALID_ARG;
+  if (out->x_perm && !x) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < dispatch_ws(cfg).total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  st = do_dispatch(cfg, topk_idx, out, ws, s);
+  if (st != MOE_OK) return st;
+  if (out->x_perm) {
+    hipError_t e = launch_permute(x, (int)elem_bytes(cfg), out->row_pair, out->offset, cfg->N,
+                                  cfg->K, cfg->d, cfg->T * cfg->K, out->x_perm, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, const moe_weights_t* w, const void* a,
+                            const int32_t* a_rows, const int32_t* offset, void* y_perm,
+                            const void* x_shared, void* y_shared, void* ws, size_t ws_bytes,
+                            void* stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights_ffn(cfg, w)) != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!a || !offset || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (cfg->F_shared > 0 && (!x_shared || !y_shared)) return MOE_ERR_INVALID_ARG;
+  const FfnWs L = ffn_ws(cfg);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  FfnProblem p = {};
+  p.T = cfg->T; p.d = cfg->d; p.N = cfg->N; p.K = cfg->K; p.F = cfg->F;
+  p.F_shared = cfg->F_shared; p.act = cfg->act; p.bf16 = cfg->dtype == MOE_BF16;
+  p.a = a; p.a_rows = a_rows; p.offset = offset;
+  p.w1 = w->w1; p.w3 = w->w3; p.w2 = w->w2; p.b1 = w->b1; p.b2 = w->b2;
+  p.ws1 = w->ws1; p.ws3 = w->ws3; p.ws2 = w->ws2;
+  p.x_shared = x_shared; p.y_perm = y_perm; p.y_shared = y_shared;
+  p.h = at<void>(ws, L.h);
+  p.tile_base = at<int32_t>(ws, L.tile_base);
+  return hip_status(launch_expert_ffn(p, (hipStream_t)stream, nullptr, nullptr));
+}
+
+moe_status_t moe_combine(const moe_config_t* cfg, const void* y_perm, const int32_t* pair_row,
+                         const float* topk_gate, const void* y_shared, void* y, void* stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!y_perm || !pair_row || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(y_perm, pair_row, topk_gate, y_shared, y, cfg->T, cfg->d,
+                                   cfg->K, cfg->dtype == MOE_BF16, (hipStream_t)stream));
+}
+
+moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                               const moe_layer_out_t* out, void* ws, size_t ws_bytes,
+                               const moe_trace_t* trace, void* stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights_router(w)) != MOE_OK) return st;
+  if ((st = check_weights_ffn(cfg, w)) != MOE_OK) return st;
+  if (!out) return MOE_ERR_INVALID_ARG;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !out->y) return MOE_ERR_INVALID_ARG;
+  const LayerWs L = layer_ws(cfg);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  auto mark = [&](int i) -> moe_status_t {
+    if (trace && trace->ev[i]) return hip_status(hipEventRecord((hipEvent_t)trace->ev[i], s));
+    return MOE_OK;
+  };
+
+  int32_t* idx = out->topk_idx ? out->topk_idx : at<int32_t>(ws, L.idx);
+  float* gate = out->topk_gate ? out->topk_gate : at<float>(ws, L.gate);
+  moe_dispatch_t d = out->dispatch;
+  d.x_perm = nullptr;
+  if (!d.kept) d.kept = at<int32_t>(ws, L.kept);
+  if (!d.offset) d.offset = at<int32_t>(ws, L.offset);
+  if (!d.pair_row) d.pair_row = at<int32_t>(ws, L.pair_row);
+  if (!d.row_pair) d.row_pair = at<int32_t>(ws, L.row_pair);
+  if (!d.counters) d.counters = at<int32_t>(ws, L.counters);
+
+  if ((st = mark(0)) != MOE_OK) return st;
+  st = do_router(cfg, w, x, idx, gate, out->logits, &out->stats, at<void>(ws, L.router), s);
+  if (st != MOE_OK) return st;
+  if ((st = mark(1)) != MOE_OK) return st;
+  st = do_dispatch(cfg, idx, &d, at<void>(ws, L.dispatch), s);
+  if (st != MOE_OK) return st;
+
+  const FfnWs FL = ffn_ws(cfg);
+  unsigned char* fws = at<unsigned char>(ws, L.ffn);
+  FfnProblem p = {};
+  p.T = cfg->T; p.d = cfg->d; p.N = cfg->N; p.K = cfg->K; p.F = cfg->F;
+  p.F_shared = cfg->F_shared; p.act = cfg->act; p.bf16 = cfg->dtype == MOE_BF16;
+  p.a = x; p.a_rows = d.row_pair; p.offset = d.offset;  // rows gathered in the GEMM
+  p.w1 = w->w1; p.w3 = w->w3; p.w2 = w->w2; p.b1 = w->b1; p.b2 = w->b2;
+  p.ws1 = w->ws1; p.ws3 = w->ws3; p.ws2 = w->ws2;
+  p.x_shared = x;
+  p.y_perm = at<void>(ws, L.y_perm);
+  p.y_shared = cfg->F_shared > 0 ? at<void>(ws, L.y_shared) : nullptr;
+  p.h = fws + FL.h;
+  p.tile_base = (int32_t*)(fws + FL.tile_base);
+  hipEvent_t pre = (trace && trace->ev[2]) ? (hipEvent_t)trace->ev[2] : nullptr;
+  hipEvent_t mid = (trace && trace->ev[3]) ? (hipEvent_t)trace->ev[3] : nullptr;
+  if (launch_expert_ffn(p, s, pre, mid) != hipSuccess) return MOE_ERR_HIP;
+  if ((st = mark(4)) != MOE_OK) return st;
+  if (launch_combine(p.y_perm, d.pair_row, gate, p.y_shared, out->y, cfg->T, cfg->d, cfg->K,
+                     p.bf16, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return mark(5);
+}
+
+}  // extern "C"

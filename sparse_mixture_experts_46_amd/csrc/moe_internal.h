@@ -1,0 +1,82 @@
+// Internal launch interface between the C-ABI host layer (moe_api.cpp) and
+// the kernel translation units.  Every launcher enqueues on `stream`, never
+// synchronises, and returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- router --
+// Tokens handled by one block of the top-K kernel (multiple of 4).
+int router_tokens_per_block(int64_t T);
+int64_t router_num_blocks(int64_t T);
+
+hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r,
+                                const float* b_r, float* logits, int64_t T,
+                                int d, int N, hipStream_t stream);
+
+// Selection, gates and per-block partial statistics.
+//   part_p [nblk, N] fp32, part_cnt [nblk, N] int32, part_z [nblk, 2] fp32
+hipError_t launch_router_topk(const float* logits, const float* b_sel,
+                              int32_t* idx, float* gate, float* part_p,
+                              int32_t* part_cnt, float* part_z, int64_t T,
+                              int N, int K, int gate_mode, hipStream_t stream);
+
+hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
+                               const float* part_z, int64_t nblk, int64_t T,
+                               int N, int K, float alpha, int32_t* count,
+                               float* f, float* p, float* loss,
+                               hipStream_t stream);
+
+// -------------------------------------------------------------- dispatch --
+constexpr int kDispatchTokens = 256;  // tokens per dispatch block
+int64_t dispatch_num_blocks(int64_t T);
+
+hipError_t launch_dispatch(const int32_t* idx, int64_t T, int N, int K,
+                           int64_t capacity, int32_t* blk_count,
+                           int32_t* blk_base, int32_t* blk_bad,
+                           int32_t* kept, int32_t* offset, int32_t* pair_row,
+                           int32_t* row_pair, uint8_t* dropped,
+                           int32_t* counters, hipStream_t stream);
+
+hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* row_pair,
+                          const int32_t* offset, int N, int K, int d,
+                          int64_t max_rows, void* x_perm, hipStream_t stream);
+
+// ------------------------------------------------------------ expert FFN --
+// One group of the grouped GEMMs: rows [row0, row0 + M) of the A operand,
+// weights of `Nout x Kdim` (row-major, K contiguous).
+struct FfnProblem {
+  int64_t T;
+  int d, N, K, F, F_shared;
+  int act;          // moe_act_t
+  bool bf16;
+  const void* a;    // x_perm, or x when a_rows != nullptr
+  const int32_t* a_rows;
+  const int32_t* offset;  // [N+1] device
+  const void *w1, *w3, *w2, *b1, *b2;
+  const void *ws1, *ws3, *ws2;
+  const void* x_shared;
+  void* h;          // [(T*K + T_shared), max(F, F_shared)] intermediate
+  void* y_perm;     // [T*K, d]
+  void* y_shared;   // [T, d]
+  int32_t* tile_base;  // [2 * (N + 2)] scratch
+};
+
+size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared,
+                           bool bf16);
+// ev_pre / ev_mid (nullable) are recorded right before and right after the
+// first grouped GEMM.
+hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream,
+                             hipEvent_t ev_pre, hipEvent_t ev_mid);
+
+// --------------------------------------------------------------- combine --
+hipError_t launch_combine(const void* y_perm, const int32_t* pair_row,
+                          const float* gate, const void* y_shared, void* y,
+                          int64_t T, int d, int K, bool bf16,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,357 @@
+// Router: logits = x W_r^T (+ b_r), top-K selection, gates and the
+// per-block partial sums of the load-balance and z-loss statistics.
+//
+// Pages (by title and section):
+//   mzlw.cn "MoE 混合专家模型稀疏激活的架构原理与负载均衡挑战": 2.1 (router as
+//     a light linear map of the token to one score per expert, top-K then
+//     softmax), 2.2 (L_aux = alpha N sum f_i p_i), section 三 (MoERouter:
+//     weight [N, d], logits = x W^T, topk on logits, softmax of the top-K
+//     logits, counts of the flattened indices divided by T*K).
+//   learnagent.wiki "混合专家模型（Mixture of Experts, MoE）": 结构 2
+//     (G(x) = Softmax(W_r x)), 结构 4 (per-expert bias that only steers the
+//     choice), 运行示例 (softmax, top-K on probabilities, divide by their sum).
+//   wmrh.cn explainer ("MoE 的核心思想"): 公式表达重点 (renormalised gates),
+//     Router Z-Loss (penalty on the squares of the router logits).
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// ------------------------------------------------------------ logits GEMM --
+// fp32 MFMA (v_mfma_f32_32x32x2_f32) tile of 64 tokens x 64 experts, four
+// waves in a 2x2 grid, K staged through LDS in chunks of 32.  x may be bf16
+// (widened exactly to fp32 when staged) or fp32.
+namespace {
+
+constexpr int RT_M = 64, RT_N = 64, RT_K = 32, RT_PAD = 1;
+
+template <bool XBF16>
+__global__ __launch_bounds__(256) void router_logits_kernel(
+    const void* __restrict__ xv, const float* __restrict__ w_r,
+    const float* __restrict__ b_r, float* __restrict__ logits, int64_t T,
+    int d, int N) {
+  __shared__ float xs[2][RT_M][RT_K + RT_PAD];
+  __shared__ float ws[2][RT_N][RT_K + RT_PAD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t t0 = (int64_t)blockIdx.x * RT_M;
+  const int e0 = blockIdx.y * RT_N;
+
+  // staging assignment: x tile 64 x 32 -> bf16: one 8-element chunk per
+  // thread; fp32: two 4-element chunks.  W tile 64 x 32 fp32: two chunks.
+  float xr[8];
+  float4 wr[2];
+  auto load_tile = [&](int k0) {
+    if (XBF16) {
+      int r = tid >> 2, c = (tid & 3) * 8;
+      int64_t t = t0 + r; if (t >= T) t = T - 1;
+      const uint16_t* x = (const uint16_t*)xv;
+      uint4 v = *(const uint4*)(x + t * d + k0 + c);
+      unpack_bf16x8(v, xr);
+    } else {
+      const float* x = (const float*)xv;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;
+        int64_t t = t0 + r; if (t >= T) t = T - 1;
+        float4 v = *(const float4*)(x + t * d + k0 + c);
+        xr[i * 4 + 0] = v.x; xr[i * 4 + 1] = v.y; xr[i * 4 + 2] = v.z; xr[i * 4 + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;
+      int e = e0 + r;
+      if (e < N) wr[i] = *(const float4*)(w_r + (int64_t)e * d + k0 + c);
+      else wr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    if (XBF16) {
+      int r = tid >> 2, c = (tid & 3) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xs[buf][r][c + j] = xr[j];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xs[buf][r][c + j] = xr[i * 4 + j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;
+      ws[buf][r][c + 0] = wr[i].x; ws[buf][r][c + 1] = wr[i].y;
+      ws[buf][r][c + 2] = wr[i].z; ws[buf][r][c + 3] = wr[i].w;
+    }
+  };
+
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+
+  const int nk = d / RT_K;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_tile((kt + 1) * RT_K);
+    const int ar = wm * 32 + (lane & 31), br = wn * 32 + (lane & 31), kk = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < RT_K / 2; ++s) {
+      float a = xs[buf][ar][2 * s + kk];
+      float b = ws[buf][br][2 * s + kk];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  // D layout: column = lane % 32, row = 8*(v/4) + 4*(lane/32) + v%4
+  const int col = e0 + wn * 32 + (lane & 31);
+  if (col < N) {
+    const float bias = b_r ? b_r[col] : 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      int row = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      int64_t t = t0 + row;
+      if (t < T) logits[t * N + col] = acc[v] + bias;
+    }
+  }
+}
+
+// --------------------------------------------------------------- top-K ----
+// One wave per token.  Lane l holds experts l, l+64, ... (up to 16 each).
+// Selection key s = logit + b_sel, turned into an unsigned key that orders
+// like the float (NaN below -inf); ties go to the lower expert index by
+// packing (key, ~index) into 64 bits and taking the maximum.
+__device__ __forceinline__ uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN: lowest
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int NJ>
+__global__ __launch_bounds__(256) void router_topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ b_sel,
+    int32_t* __restrict__ idx, float* __restrict__ gate,
+    float* __restrict__ part_p, int32_t* __restrict__ part_cnt,
+    float* __restrict__ part_z, int64_t T, int N, int K, int gate_mode,
+    int tpb) {
+  extern __shared__ unsigned char smem_raw[];
+  float* sp = (float*)smem_raw;                  // [4][N] per-wave prob sums
+  int32_t* scnt = (int32_t*)(sp + 4 * N);        // [N] block counts
+  float* sz = (float*)(scnt + N);                // [4][2]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < N; e += 256) scnt[e] = 0;
+  __syncthreads();
+
+  float pacc[NJ];
+  float bsel[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    pacc[j] = 0.f;
+    int e = lane + 64 * j;
+    bsel[j] = (b_sel && e < N) ? b_sel[e] : 0.f;
+  }
+  float zsum = 0.f, lsum = 0.f;
+
+  const int64_t tb0 = (int64_t)blockIdx.x * tpb;
+  const int per_wave = tpb / 4;
+  for (int i = 0; i < per_wave; ++i) {
+    const int64_t t = tb0 + (int64_t)wave * per_wave + i;
+    if (t >= T) break;
+    float l[NJ];
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      int e = lane + 64 * j;
+      l[j] = (e < N) ? logits[t * N + e] : -INFINITY;
+      m = fmaxf(m, l[j]);
+    }
+    m = wave_max(m);
+    float ssum = 0.f, sq = 0.f;
+    float ex[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      int e = lane + 64 * j;
+      ex[j] = (e < N) ? expf(l[j] - m) : 0.f;
+      ssum += ex[j];
+      sq += (e < N) ? l[j] * l[j] : 0.f;
+    }
+    ssum = wave_sum(ssum);
+    sq = wave_sum(sq);
+    const float inv = 1.0f / ssum;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) pacc[j] += ex[j] * inv;
+    const float lse = m + logf(ssum);
+    zsum += sq;
+    lsum += lse * lse;
+
+    // K rounds of arg-max over the not-yet-taken experts
+    uint32_t taken = 0;
+    float my_l = 0.f;  // lane k keeps the logit of its chosen expert
+    int my_e = 0;
+    float lmax_sel = -INFINITY;
+    for (int r = 0; r < K; ++r) {
+      unsigned long long best = 0ull;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        int e = lane + 64 * j;
+        if (e < N && !((taken >> j) & 1u)) {
+          unsigned long long key =
+              ((unsigned long long)order_key(l[j] + bsel[j]) << 32) |
+              (unsigned long long)(0xffffffffu - (uint32_t)e);
+          best = key > best ? key : best;
+        }
+      }
+      best = wave_max_u64(best);
+      const int ew = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+      const int jw = ew >> 6;
+      float cand = 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) cand = (j == jw) ? l[j] : cand;
+      const float lw = __shfl(cand, ew & 63, MOE_WAVE);
+      if (lane == (ew & 63)) taken |= 1u << jw;
+      if (lane == r) { my_l = lw; my_e = ew; }
+      lmax_sel = fmaxf(lmax_sel, lw);
+      if (lane == 0) atomicAdd(&scnt[ew], 1);  // integer: order-independent
+    }
+    // gates
+    float g;
+    if (gate_mode == 2) {  // softmax over all N, not renormalised
+      g = expf(my_l - m) * inv;
+    } else {  // renormalised over the chosen K (both forms are equal)
+      float ek = (lane < K) ? expf(my_l - lmax_sel) : 0.f;
+      float den = wave_sum(ek);
+      g = ek / den;
+    }
+    if (lane < K) {
+      idx[t * K + lane] = my_e;
+      gate[t * K + lane] = g;
+    }
+  }
+  // fixed-order reduction of the block's partial sums
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    int e = lane + 64 * j;
+    if (e < N) sp[wave * N + e] = pacc[j];
+  }
+  if (lane == 0) { sz[wave * 2] = zsum; sz[wave * 2 + 1] = lsum; }
+  __syncthreads();
+  for (int e = tid; e < N; e += 256) {
+    float s = sp[e];
+    s += sp[N + e];
+    s += sp[2 * N + e];
+    s += sp[3 * N + e];
+    part_p[(int64_t)blockIdx.x * N + e] = s;
+    part_cnt[(int64_t)blockIdx.x * N + e] = scnt[e];
+  }
+  if (tid == 0) {
+    part_z[blockIdx.x * 2] = ((sz[0] + sz[2]) + sz[4]) + sz[6];
+    part_z[blockIdx.x * 2 + 1] = ((sz[1] + sz[3]) + sz[5]) + sz[7];
+  }
+}
+
+// --------------------------------------------------------------- stats ----
+// One block of 1024 threads; every sum runs in a fixed order.
+__global__ __launch_bounds__(1024) void router_stats_kernel(
+    const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt,
+    const float* __restrict__ part_z, int64_t nblk, int64_t T, int N, int K,
+    float alpha, int32_t* __restrict__ count, float* __restrict__ f,
+    float* __restrict__ p, float* __restrict__ loss) {
+  __shared__ float red[1024];
+  const int tid = threadIdx.x;
+  const float invT = 1.0f / (float)T;
+  const float invTK = 1.0f / ((float)T * (float)K);
+  float fp = 0.f;
+  for (int e = tid; e < N; e += 1024) {
+    float s = 0.f;
+    int64_t c = 0;
+    for (int64_t b = 0; b < nblk; ++b) {
+      s += part_p[b * N + e];
+      c += part_cnt[b * N + e];
+    }
+    float pe = s * invT;
+    float fe = (float)c * invTK;
+    if (count) count[e] = (int32_t)c;
+    if (f) f[e] = fe;
+    if (p) p[e] = pe;
+    fp += fe * pe;
+  }
+  red[tid] = fp;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0 && loss) {
+    float z = 0.f, zl = 0.f;
+    for (int64_t b = 0; b < nblk; ++b) { z += part_z[2 * b]; zl += part_z[2 * b + 1]; }
+    loss[0] = alpha * (float)N * red[0];
+    loss[1] = z * invT;
+    loss[2] = zl * invT;
+  }
+}
+
+}  // namespace
+
+int router_tokens_per_block(int64_t T) {
+  // 64 tokens per block; more when T is huge, so at most 4096 blocks.
+  int64_t tpb = 64;
+  while ((T + tpb - 1) / tpb > 4096) tpb *= 2;
+  return (int)tpb;
+}
+
+int64_t router_num_blocks(int64_t T) {
+  int tpb = router_tokens_per_block(T);
+  return (T + tpb - 1) / tpb;
+}
+
+hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r,
+                                const float* b_r, float* logits, int64_t T,
+                                int d, int N, hipStream_t stream) {
+  dim3 grid((unsigned)((T + RT_M - 1) / RT_M), (unsigned)((N + RT_N - 1) / RT_N));
+  if (x_bf16)
+    router_logits_kernel<true><<<grid, 256, 0, stream>>>(x, w_r, b_r, logits, T, d, N);
+  else
+    router_logits_kernel<false><<<grid, 256, 0, stream>>>(x, w_r, b_r, logits, T, d, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_topk(const float* logits, const float* b_sel,
+                              int32_t* idx, float* gate, float* part_p,
+                              int32_t* part_cnt, float* part_z, int64_t T,
+                              int N, int K, int gate_mode, hipStream_t stream) {
+  const int tpb = router_tokens_per_block(T);
+  const unsigned nblk = (unsigned)((T + tpb - 1) / tpb);
+  const size_t smem = (size_t)4 * N * sizeof(float) + (size_t)N * sizeof(int32_t) + 8 * sizeof(float);
+  const int nj = (N + 63) / 64;
+#define MOE_TOPK_CASE(NJV)                                                          \
+  case NJV:                                                                         \
+    router_topk_kernel<NJV><<<nblk, 256, smem, stream>>>(logits, b_sel, idx, gate,  \
+        part_p, part_cnt, part_z, T, N, K, gate_mode, tpb);                        \
+    break;
+  switch (nj) {
+    MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
+    MOE_TOPK_CASE(5) MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8)
+    MOE_TOPK_CASE(9) MOE_TOPK_CASE(10) MOE_TOPK_CASE(11) MOE_TOPK_CASE(12)
+    MOE_TOPK_CASE(13) MOE_TOPK_CASE(14) MOE_TOPK_CASE(15) MOE_TOPK_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_TOPK_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
+                               const float* part_z, int64_t nblk, int64_t T,
+                               int N, int K, float alpha, int32_t* count,
+                               float* f, float* p, float* loss,
+                               hipStream_t stream) {
+  router_stats_kernel<<<1, 1024, 0, stream>>>(part_p, part_cnt, part_z, nblk, T,
+                                              N, K, alpha, count, f, p, loss);
+  return hipGetLastError();
+}
+
+}  // namespace moe
