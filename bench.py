@@ -41,7 +41,23 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=256,
                     help="tokens the oracle runs for the CPU baseline")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, run one elementwise fp32 kernel that reads and "
+                         "writes this many MiB (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    """One plain streaming kernel of known size: dst = -src over `mib` MiB of
+    fp32, i.e. mib MiB read and mib MiB written."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 class HipEvents:
@@ -196,6 +212,8 @@ def main():
         sys.exit(1)
     L.load()
     ev = HipEvents()
+    if a.copy_probe_mib:
+        copy_probe(a.copy_probe_mib)
     w = WL.ALL[a.workload]
     r = run_workload(w, a.steps, a.warmup, ev)
     ms = r["wall"] * 1e3 / a.steps

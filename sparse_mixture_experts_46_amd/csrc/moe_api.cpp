@@ -38,12 +38,15 @@ size_t elem_bytes(const moe_config_t* c) { return c->dtype == MOE_BF16 ? 2 : 4; 
 
 // ---- workspace layouts -----------------------------------------------------
 struct RouterWs {
-  size_t logits, part_p, part_cnt, part_z, total;
+  size_t split, logits, part_p, part_cnt, part_z, total;
 };
 RouterWs router_ws(const moe_config_t* c) {
   RouterWs w;
   const int64_t nb = router_num_blocks(c->T);
   size_t o = 0;
+  const int ns = router_num_splits(c->T, c->d, c->N);
+  w.split = o;  // logit partials, one [T, N] slab per K split (only if > 1 split)
+  o = align_up(o + (ns > 1 ? (size_t)ns * c->T * c->N * 4 : 0));
   w.logits = o; o = align_up(o + (size_t)c->T * c->N * 4);
   w.part_p = o; o = align_up(o + (size_t)nb * c->N * 4);
   w.part_cnt = o; o = align_up(o + (size_t)nb * c->N * 4);
@@ -137,8 +140,8 @@ moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void
                        void* ws, hipStream_t s) {
   const RouterWs L = router_ws(c);
   float* lg = logits ? logits : at<float>(ws, L.logits);
-  hipError_t e = launch_router_logits(x, c->dtype == MOE_BF16, w->w_r, w->b_r, lg, c->T, c->d,
-                                      c->N, s);
+  hipError_t e = launch_router_logits(x, c->dtype == MOE_BF16, w->w_r, w->b_r,
+                                      at<float>(ws, L.split), lg, c->T, c->d, c->N, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_router_topk(lg, w->b_sel, idx, gate, at<float>(ws, L.part_p),
                          at<int32_t>(ws, L.part_cnt), at<float>(ws, L.part_z), c->T, c->N, c->K,

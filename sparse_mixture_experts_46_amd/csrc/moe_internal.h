@@ -14,16 +14,21 @@ namespace moe {
 int router_tokens_per_block(int64_t T);
 int64_t router_num_blocks(int64_t T);
 
-hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r,
-                                const float* b_r, float* logits, int64_t T,
-                                int d, int N, hipStream_t stream);
+// K splits of the logits GEMM for this shape (partials [splits, T, N]).
+int router_num_splits(int64_t T, int d, int N);
 
-// Selection, gates and per-block partial statistics.
+// logits = x W_r^T + b_r.  With several K splits the partial products go to
+// part [splits, T, N] and a reduction writes logits; with one split the
+// logits are written directly (part unused).
+hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, const float* b_r,
+                                float* part, float* logits, int64_t T, int d, int N,
+                                hipStream_t stream);
+
+// Selection, gates and per-block partial statistics:
 //   part_p [nblk, N] fp32, part_cnt [nblk, N] int32, part_z [nblk, 2] fp32
-hipError_t launch_router_topk(const float* logits, const float* b_sel,
-                              int32_t* idx, float* gate, float* part_p,
-                              int32_t* part_cnt, float* part_z, int64_t T,
-                              int N, int K, int gate_mode, hipStream_t stream);
+hipError_t launch_router_topk(const float* logits, const float* b_sel, int32_t* idx, float* gate,
+                              float* part_p, int32_t* part_cnt, float* part_z, int64_t T, int N,
+                              int K, int gate_mode, hipStream_t stream);
 
 hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
                                const float* part_z, int64_t nblk, int64_t T,

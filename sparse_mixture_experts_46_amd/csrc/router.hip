@@ -20,7 +20,10 @@ namespace moe {
 // ------------------------------------------------------------ logits GEMM --
 // fp32 MFMA (v_mfma_f32_32x32x2_f32) tile of 64 tokens x 64 experts, four
 // waves in a 2x2 grid, K staged through LDS in chunks of 32.  x may be bf16
-// (widened exactly to fp32 when staged) or fp32.
+// (widened exactly to fp32 when staged) or fp32.  Few token or expert tiles
+// (small N, or decode-sized T) split K over gridDim.z: split z writes its
+// partial dot products to part[z]; the top-K kernel sums the splits in
+// order z = 0, 1, ... and adds the bias, so the result is deterministic.
 namespace {
 
 constexpr int RT_M = 64, RT_N = 64, RT_K = 32, RT_PAD = 1;
@@ -28,8 +31,7 @@ constexpr int RT_M = 64, RT_N = 64, RT_K = 32, RT_PAD = 1;
 template <bool XBF16>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const void* __restrict__ xv, const float* __restrict__ w_r,
-    const float* __restrict__ b_r, float* __restrict__ logits, int64_t T,
-    int d, int N) {
+    const float* __restrict__ b_r, float* __restrict__ part, int64_t T, int d, int N) {
   __shared__ float xs[2][RT_M][RT_K + RT_PAD];
   __shared__ float ws[2][RT_N][RT_K + RT_PAD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -91,13 +93,16 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 
-  const int nk = d / RT_K;
-  load_tile(0);
+  const int nks = d / RT_K;  // K steps in total; this split owns [k_lo, k_hi)
+  const int k_lo = (int)(((int64_t)blockIdx.z * nks) / gridDim.z);
+  const int k_hi = (int)(((int64_t)(blockIdx.z + 1) * nks) / gridDim.z);
+  const int nk = k_hi - k_lo;
+  load_tile(k_lo * RT_K);
   store_tile(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile((kt + 1) * RT_K);
+    if (kt + 1 < nk) load_tile((k_lo + kt + 1) * RT_K);
     const int ar = wm * 32 + (lane & 31), br = wn * 32 + (lane & 31), kk = lane >> 5;
 #pragma unroll
     for (int s = 0; s < RT_K / 2; ++s) {
@@ -110,14 +115,28 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   }
   // D layout: column = lane % 32, row = 8*(v/4) + 4*(lane/32) + v%4
   const int col = e0 + wn * 32 + (lane & 31);
+  float* out = part + (int64_t)blockIdx.z * T * N;
   if (col < N) {
-    const float bias = b_r ? b_r[col] : 0.f;
+    // one split: this is the final logit, bias included
+    const float bias = (gridDim.z == 1 && b_r) ? b_r[col] : 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       int row = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       int64_t t = t0 + row;
-      if (t < T) logits[t * N + col] = acc[v] + bias;
+      if (t < T) out[t * N + col] = acc[v] + bias;
     }
+  }
+}
+
+// logits[t, e] = sum_{z = 0, 1, ...} part[z, t, e] + b_r[e] (fixed order).
+__global__ __launch_bounds__(256) void router_split_reduce_kernel(
+    const float* __restrict__ part, int nsplit, const float* __restrict__ b_r,
+    float* __restrict__ logits, int64_t T, int N) {
+  const int64_t n = T * (int64_t)N;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float acc = part[i];
+    for (int z = 1; z < nsplit; ++z) acc += part[(int64_t)z * n + i];
+    logits[i] = acc + (b_r ? b_r[i % N] : 0.f);
   }
 }
 
@@ -255,51 +274,77 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 }
 
 // --------------------------------------------------------------- stats ----
-// One block of 1024 threads; every sum runs in a fixed order.
+// One block of 1024 threads.  Thread t sums, for expert e = t % N, the block
+// partials b = c, c + C, c + 2C, ... (c = t / N, C = 1024 / N chunks) in
+// increasing b; then the first N threads add the C chunk sums in order.
+// Every sum runs in a fixed order, so the result is deterministic.
 __global__ __launch_bounds__(1024) void router_stats_kernel(
     const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt,
     const float* __restrict__ part_z, int64_t nblk, int64_t T, int N, int K,
     float alpha, int32_t* __restrict__ count, float* __restrict__ f,
     float* __restrict__ p, float* __restrict__ loss) {
+  __shared__ float sp[1024];
+  __shared__ int64_t sc[1024];
   __shared__ float red[1024];
+  __shared__ float rz[1024], rl[1024];
   const int tid = threadIdx.x;
+  const int C = 1024 / N;  // N <= 1024
+  const int e = tid % N, c = tid / N;
+  float s = 0.f;
+  int64_t cnt = 0;
+  if (c < C) {
+    for (int64_t b = c; b < nblk; b += C) {
+      s += part_p[b * N + e];
+      cnt += part_cnt[b * N + e];
+    }
+  }
+  sp[tid] = s;
+  sc[tid] = cnt;
+  float z = 0.f, zl = 0.f;
+  for (int64_t b = tid; b < nblk; b += 1024) { z += part_z[2 * b]; zl += part_z[2 * b + 1]; }
+  rz[tid] = z;
+  rl[tid] = zl;
+  __syncthreads();
   const float invT = 1.0f / (float)T;
   const float invTK = 1.0f / ((float)T * (float)K);
   float fp = 0.f;
-  for (int e = tid; e < N; e += 1024) {
-    float s = 0.f;
-    int64_t c = 0;
-    for (int64_t b = 0; b < nblk; ++b) {
-      s += part_p[b * N + e];
-      c += part_cnt[b * N + e];
-    }
-    float pe = s * invT;
-    float fe = (float)c * invTK;
-    if (count) count[e] = (int32_t)c;
-    if (f) f[e] = fe;
-    if (p) p[e] = pe;
-    fp += fe * pe;
+  if (tid < N) {
+    float st = 0.f;
+    int64_t ct = 0;
+    for (int q = 0; q < C; ++q) { st += sp[q * N + tid]; ct += sc[q * N + tid]; }
+    const float pe = st * invT;
+    const float fe = (float)ct * invTK;
+    if (count) count[tid] = (int32_t)ct;
+    if (f) f[tid] = fe;
+    if (p) p[tid] = pe;
+    fp = fe * pe;
   }
+  __syncthreads();
   red[tid] = fp;
   __syncthreads();
   for (int o = 512; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
+    if (tid < o) {
+      red[tid] += red[tid + o];
+      rz[tid] += rz[tid + o];
+      rl[tid] += rl[tid + o];
+    }
     __syncthreads();
   }
   if (tid == 0 && loss) {
-    float z = 0.f, zl = 0.f;
-    for (int64_t b = 0; b < nblk; ++b) { z += part_z[2 * b]; zl += part_z[2 * b + 1]; }
     loss[0] = alpha * (float)N * red[0];
-    loss[1] = z * invT;
-    loss[2] = zl * invT;
+    loss[1] = rz[0] * invT;
+    loss[2] = rl[0] * invT;
   }
 }
 
 }  // namespace
 
 int router_tokens_per_block(int64_t T) {
-  // 64 tokens per block; more when T is huge, so at most 4096 blocks.
-  int64_t tpb = 64;
+  // one wave per token; blocks of 4 waves.  Enough blocks to cover the CUs
+  // for small T (>= 4 tokens per block), 64 tokens per block for large T and
+  // more when T is huge, so at most 4096 blocks.
+  int64_t tpb = 4;
+  while (tpb < 64 && (T + tpb - 1) / tpb > 512) tpb *= 2;
   while ((T + tpb - 1) / tpb > 4096) tpb *= 2;
   return (int)tpb;
 }
@@ -309,29 +354,47 @@ int64_t router_num_blocks(int64_t T) {
   return (T + tpb - 1) / tpb;
 }
 
-hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r,
-                                const float* b_r, float* logits, int64_t T,
-                                int d, int N, hipStream_t stream) {
-  dim3 grid((unsigned)((T + RT_M - 1) / RT_M), (unsigned)((N + RT_N - 1) / RT_N));
+int router_num_splits(int64_t T, int d, int N) {
+  // aim for >= 512 workgroups, with at least 4 K steps (128 elements) per split
+  const int64_t tiles = ((T + RT_M - 1) / RT_M) * ((N + RT_N - 1) / RT_N);
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t max_s = d / (4 * RT_K);
+  if (s > max_s) s = max_s;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, const float* b_r,
+                                float* part, float* logits, int64_t T, int d, int N,
+                                hipStream_t stream) {
+  const int ns = router_num_splits(T, d, N);
+  dim3 grid((unsigned)((T + RT_M - 1) / RT_M), (unsigned)((N + RT_N - 1) / RT_N), (unsigned)ns);
+  float* out = ns == 1 ? logits : part;
   if (x_bf16)
-    router_logits_kernel<true><<<grid, 256, 0, stream>>>(x, w_r, b_r, logits, T, d, N);
+    router_logits_kernel<true><<<grid, 256, 0, stream>>>(x, w_r, b_r, out, T, d, N);
   else
-    router_logits_kernel<false><<<grid, 256, 0, stream>>>(x, w_r, b_r, logits, T, d, N);
+    router_logits_kernel<false><<<grid, 256, 0, stream>>>(x, w_r, b_r, out, T, d, N);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  int64_t n = T * (int64_t)N;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  router_split_reduce_kernel<<<(unsigned)blocks, 256, 0, stream>>>(part, ns, b_r, logits, T, N);
   return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const float* logits, const float* b_sel,
-                              int32_t* idx, float* gate, float* part_p,
-                              int32_t* part_cnt, float* part_z, int64_t T,
-                              int N, int K, int gate_mode, hipStream_t stream) {
+hipError_t launch_router_topk(const float* logits, const float* b_sel, int32_t* idx, float* gate,
+                              float* part_p, int32_t* part_cnt, float* part_z, int64_t T, int N,
+                              int K, int gate_mode, hipStream_t stream) {
   const int tpb = router_tokens_per_block(T);
   const unsigned nblk = (unsigned)((T + tpb - 1) / tpb);
   const size_t smem = (size_t)4 * N * sizeof(float) + (size_t)N * sizeof(int32_t) + 8 * sizeof(float);
   const int nj = (N + 63) / 64;
-#define MOE_TOPK_CASE(NJV)                                                          \
-  case NJV:                                                                         \
-    router_topk_kernel<NJV><<<nblk, 256, smem, stream>>>(logits, b_sel, idx, gate,  \
-        part_p, part_cnt, part_z, T, N, K, gate_mode, tpb);                        \
+#define MOE_TOPK_CASE(NJV)                                                              \
+  case NJV:                                                                             \
+    router_topk_kernel<NJV><<<nblk, 256, smem, stream>>>(logits, b_sel, idx, gate,      \
+        part_p, part_cnt, part_z, T, N, K, gate_mode, tpb);                            \
     break;
   switch (nj) {
     MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)

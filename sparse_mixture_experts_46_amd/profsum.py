@@ -1,0 +1,121 @@
+"""Summarise rocprofv3 output of bench.py into short text files.
+
+    python -m sparse_mixture_experts_46_amd.profsum --trace DIR [--fetch DIR --write DIR]
+        --workload NAME --out profiles/ --cmd "<the rocprofv3 command lines>"
+
+--trace : directory of a `rocprofv3 --kernel-trace --stats --output-format csv` run
+--fetch / --write : directories of `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`
+          runs of `bench.py --copy-probe-mib M ...`.  The probe kernel (one fp32
+          negation reading M MiB and writing M MiB) gives the factor that turns
+          each counter (KiB per dispatch) into bytes.
+Writes <out>/kernels_<workload>.md and, with counters, <out>/traffic_gemm1_<workload>.json
+(HBM bytes per launch of the first grouped GEMM, tied to the SHA-256 of its source).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+GEMM_SRC = os.path.join(PKG, "csrc", "gemm_bf16.hip")
+
+
+def short(name: str) -> str:
+    n = name
+    if "moe::" in n:
+        n = re.sub(r"\(.*\)$", "", n.replace("(anonymous namespace)::", ""))
+        n = n.replace("void ", "")
+        return n
+    m = re.search(r"at::native::[^<(]*?(\w+_kernel\w*)", n)
+    if "neg_kernel" in n:
+        return "torch neg (copy probe)"
+    return ("torch " + m.group(1)) if m else n[:60]
+
+
+def one(pattern):
+    f = glob.glob(pattern, recursive=True)
+    if not f:
+        raise FileNotFoundError(pattern)
+    return f[0]
+
+
+def stats_table(trace_dir):
+    rows = list(csv.DictReader(open(one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
+    out = []
+    for r in rows:
+        out.append((short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                    float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    out.sort(key=lambda x: -x[3])
+    return out
+
+
+def counters(pmc_dir, counter):
+    rows = list(csv.DictReader(open(one(os.path.join(pmc_dir, "**", "*counter_collection.csv")))))
+    by = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        by.setdefault(short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return by
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--cmd", required=True)
+    ap.add_argument("--probe-mib", type=int, default=1024)
+    ap.add_argument("--gemm1", default="gemm_tile_kernel<256, 256, 2, 2, true, 0>")
+    a = ap.parse_args()
+    os.makedirs(a.out, exist_ok=True)
+    tab = stats_table(a.trace)
+    lines = [f"# rocprofv3 kernel statistics: bench.py, workload {a.workload}", "",
+             "Command(s):", "", "```", a.cmd.strip(), "```", "",
+             "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
+    for n, c, avg, tot, pct in tab[:25]:
+        lines.append(f"| `{n}` | {c} | {avg:.1f} | {tot:.3f} | {pct:.2f} |")
+    if a.fetch and a.write:
+        f = counters(a.fetch, "FETCH_SIZE")
+        w = counters(a.write, "WRITE_SIZE")
+        probe_bytes = a.probe_mib * (1 << 20)
+        fk = f["torch neg (copy probe)"][0]
+        wk = w["torch neg (copy probe)"][0]
+        fscale = probe_bytes / (fk * 1024.0)
+        wscale = probe_bytes / (wk * 1024.0)
+        lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+                  f"Copy probe: {a.probe_mib} MiB read + {a.probe_mib} MiB written; "
+                  f"FETCH_SIZE read {fk:.0f} KiB (scale x{fscale:.3f}), "
+                  f"WRITE_SIZE read {wk:.0f} KiB (scale x{wscale:.3f}).", "",
+                  "| kernel | fetch MB/launch (scaled) | write MB/launch (scaled) |",
+                  "|---|---|---|"]
+        rec = {}
+        for k in sorted(set(f) & set(w)):
+            if "moe::" not in k and not k.startswith("gemm") and "moe" not in k:
+                if not any(s in k for s in ("gemm", "router", "dispatch", "combine", "tile_setup")):
+                    continue
+            fb = sum(f[k]) / len(f[k]) * 1024 * fscale
+            wb = sum(w[k]) / len(w[k]) * 1024 * wscale
+            rec[k] = (fb, wb)
+            lines.append(f"| `{k}` | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+        g1 = [k for k in rec if a.gemm1 in k]
+        if g1:
+            fb, wb = rec[g1[0]]
+            sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+            json.dump({"workload": a.workload, "kernel": g1[0], "fetch_bytes": fb,
+                       "write_bytes": wb, "bytes_per_launch": fb + wb,
+                       "fetch_scale": fscale, "write_scale": wscale,
+                       "gemm_source_sha256": sha, "cmd": a.cmd.strip()},
+                      open(os.path.join(a.out, f"traffic_gemm1_{a.workload}.json"), "w"), indent=1)
+    open(os.path.join(a.out, f"kernels_{a.workload}.md"), "w").write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    main()
