@@ -81,7 +81,7 @@ hipError_t run_pingpong(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
 template <bool DUAL, int EPI>
 hipError_t run_skinny(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   int64_t grid = (max_tiles + 3) / 4;
-  const int64_t cap = (int64_t)num_cus() * 8;
+  const int64_t cap = (int64_t)num_cus() * 16;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   gemm_skinny_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);

@@ -8,13 +8,14 @@
 
 namespace moe {
 
-// One wave computes a 16-row x 16-column output block.  Over a 128-wide K
-// chunk, lane l (row l%16, quarter q = l/16) holds K elements
-// [q*32, q*32+32) of its row in four 8-element slots; step j of the four
-// MFMAs consumes slot j of A and of B, so both operands see the same K
-// permutation and the product is unchanged.
+// One wave computes a 16-row x 16-column output block.  Lane l holds row
+// l % 16 and, for each 32-wide K step, the 8 elements at offset 8 * (l / 16):
+// the MFMA operand layout, which also makes the four lanes of a row read 64
+// contiguous bytes per load instruction.  Loads for UNR K steps are issued
+// before their MFMAs so every wave keeps many bytes in flight.
 template <bool DUAL, int EPI>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p) {
+  constexpr int UNR = 16;
   const int lane = threadIdx.x & 63;
   const int wave_g = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * 4;
@@ -38,59 +39,37 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p) {
     const uint16_t* pb0 = (ti.shared ? p.bs0 : p.b0 + (int64_t)ti.g * p.b_stride) + (int64_t)n * Kd;
     const uint16_t* pb1 = DUAL ? (ti.shared ? p.bs1 : p.b1 + (int64_t)ti.g * p.b_stride) + (int64_t)n * Kd
                                : nullptr;
-    pa += q * 32; pb0 += q * 32;
-    if (DUAL) pb1 += q * 32;
+    pa += q * 8; pb0 += q * 8;
+    if (DUAL) pb1 += q * 8;
 
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    const int nk = (int)(Kd / 128);
+    const int nk32 = (int)(Kd / 32);  // MFMA K steps
     int kc = 0;
-    for (; kc + 1 < nk; kc += 2) {
-      uint4 a[8], b[8], c[8];
+    for (; kc + UNR <= nk32; kc += UNR) {
+      uint4 a[UNR], b[UNR], c[UNR];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int off = (j >> 2) * 128 + (j & 3) * 8;
-        a[j] = *(const uint4*)(pa + kc * 128 + off);
-        b[j] = *(const uint4*)(pb0 + kc * 128 + off);
-        if (DUAL) c[j] = *(const uint4*)(pb1 + kc * 128 + off);
+      for (int j = 0; j < UNR; ++j) {
+        const int off = (kc + j) * 32;
+        a[j] = *(const uint4*)(pa + off);
+        b[j] = *(const uint4*)(pb0 + off);
+        if (DUAL) c[j] = *(const uint4*)(pb1 + off);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < UNR; ++j) {
         bf16x8_t fa = __builtin_bit_cast(bf16x8_t, a[j]);
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, __builtin_bit_cast(bf16x8_t, b[j]), acc0, 0, 0, 0);
         if (DUAL)
           acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, __builtin_bit_cast(bf16x8_t, c[j]), acc1, 0, 0, 0);
       }
     }
-    for (; kc < nk; ++kc) {
-      uint4 a[4], b[4], c[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a[j] = *(const uint4*)(pa + kc * 128 + j * 8);
-        b[j] = *(const uint4*)(pb0 + kc * 128 + j * 8);
-        if (DUAL) c[j] = *(const uint4*)(pb1 + kc * 128 + j * 8);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8_t fa = __builtin_bit_cast(bf16x8_t, a[j]);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, __builtin_bit_cast(bf16x8_t, b[j]), acc0, 0, 0, 0);
-        if (DUAL)
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, __builtin_bit_cast(bf16x8_t, c[j]), acc1, 0, 0, 0);
-      }
-    }
-    if (Kd % 128) {  // a final 64-wide chunk: lane quarter q holds [q*16, q*16+16)
-      const int64_t k0 = (int64_t)nk * 128 - q * 32 + q * 16;
-      const uint16_t* qa = pa + k0;
-      const uint16_t* qb = pb0 + k0;
-      const uint16_t* qc = DUAL ? pb1 + k0 : nullptr;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bf16x8_t fa = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qa + j * 8));
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            fa, __builtin_bit_cast(bf16x8_t, *(const uint4*)(qb + j * 8)), acc0, 0, 0, 0);
-        if (DUAL)
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              fa, __builtin_bit_cast(bf16x8_t, *(const uint4*)(qc + j * 8)), acc1, 0, 0, 0);
-      }
+    for (; kc < nk32; ++kc) {
+      const int off = kc * 32;
+      bf16x8_t fa = __builtin_bit_cast(bf16x8_t, *(const uint4*)(pa + off));
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          fa, __builtin_bit_cast(bf16x8_t, *(const uint4*)(pb0 + off)), acc0, 0, 0, 0);
+      if (DUAL)
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            fa, __builtin_bit_cast(bf16x8_t, *(const uint4*)(pb1 + off)), acc1, 0, 0, 0);
     }
     // D layout (16x16): col = lane % 16, row = 4*(lane/16) + v
     const int col = ti.nt * 16 + (lane & 15);
