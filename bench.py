@@ -184,14 +184,12 @@ def cpu_baseline(w, inp, sample):
 def traffic_record(name):
     """HBM bytes per launch of the first grouped GEMM from the committed
     rocprofv3 counter runs, or None when the kernel source changed since."""
-    import hashlib
     p = os.path.join(ROOT, "profiles", f"traffic_gemm1_{name}.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    src = os.path.join(ROOT, "sparse_mixture_experts_46_amd", "csrc", "gemm_bf16.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("gemm_source_sha256") != h:
+    from sparse_mixture_experts_46_amd.profsum import gemm_source_sha256
+    if rec.get("gemm_source_sha256") != gemm_source_sha256():
         return None
     return rec.get("bytes_per_launch")
 

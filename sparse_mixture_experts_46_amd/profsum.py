@@ -22,7 +22,16 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-GEMM_SRC = os.path.join(PKG, "csrc", "gemm_bf16.hip")
+GEMM_SRCS = ["gemm_bf16.hip", "gemm_common.h", "gemm_pingpong.h", "gemm_tile.h", "gemm_skinny.h"]
+
+
+def gemm_source_sha256() -> str:
+    """SHA-256 over the grouped-GEMM sources (traffic figures go stale when
+    any of them changes)."""
+    h = hashlib.sha256()
+    for f in GEMM_SRCS:
+        h.update(open(os.path.join(PKG, "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def short(name: str) -> str:
@@ -73,7 +82,7 @@ def main():
     ap.add_argument("--out", required=True)
     ap.add_argument("--cmd", required=True)
     ap.add_argument("--probe-mib", type=int, default=1024)
-    ap.add_argument("--gemm1", default="gemm_tile_kernel<256, 256, 2, 2, true, 0>")
+    ap.add_argument("--gemm1", default="gemm_pingpong_kernel<256, 256, 32, 4, 2, 4, 2, true, 0>")
     a = ap.parse_args()
     os.makedirs(a.out, exist_ok=True)
     tab = stats_table(a.trace)
@@ -108,7 +117,7 @@ def main():
         g1 = [k for k in rec if a.gemm1 in k]
         if g1:
             fb, wb = rec[g1[0]]
-            sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+            sha = gemm_source_sha256()
             json.dump({"workload": a.workload, "kernel": g1[0], "fetch_bytes": fb,
                        "write_bytes": wb, "bytes_per_launch": fb + wb,
                        "fetch_scale": fscale, "write_scale": wscale,
