@@ -87,15 +87,38 @@ class HipEvents:
         self.h.hipEventDestroy(e)
 
 
-def active_work(w, kept_rows):
+STAGES = ["router+stats", "dispatch", "gemm1_main", "gemm1_tail", "gemm2_main", "gemm2_tail",
+          "combine"]
+
+
+def split_rows(w):
+    """Row-tile height at which the library splits each expert's rows into a
+    main and a tail launch, or 0 when one launch covers every row (the tile
+    is picked by the mean rows per expert, T*K/N)."""
+    return 256 if w.dtype == "bf16" and w.T * w.K / w.N > 640.0 else 0
+
+
+def main_rows(m, split):
+    """Rows of a group that the main launch computes: whole tiles of `split`
+    rows, the last one at least half full; the rest go to the tail launch."""
+    if split <= 0:
+        return m
+    full, rem = divmod(m, split)
+    return min((full + (1 if 2 * rem >= split else 0)) * split, m)
+
+
+def active_work(w, group_rows):
     """Algorithmic flops of the two grouped GEMMs (kept pairs + shared
-    expert) and the expert-weight bytes the step must read."""
+    expert) and of the main launch of the first one (gate/up)."""
     mats = 3 if w.act == "swiglu" else 2
+    kept_rows = sum(group_rows)
     flops_routed = 2.0 * kept_rows * w.d * w.F * mats
     flops_shared = 2.0 * w.T * w.d * w.F_shared * 3 if w.F_shared else 0.0
-    g1_flops = 2.0 * kept_rows * w.d * w.F * (mats - 1) + (
-        2.0 * w.T * w.d * w.F_shared * 2 if w.F_shared else 0.0)
-    return flops_routed + flops_shared, g1_flops
+    sp = split_rows(w)
+    main = sum(main_rows(m, sp) for m in group_rows)
+    g1_main = 2.0 * main * w.d * w.F * (mats - 1) + (
+        2.0 * main_rows(w.T, sp) * w.d * w.F_shared * 2 if w.F_shared else 0.0)
+    return flops_routed + flops_shared, g1_main
 
 
 def run_workload(w, steps, warmup, ev):
@@ -124,9 +147,9 @@ def run_workload(w, steps, warmup, ev):
         api.moe_layer_forward(cfg, inp, inp["x"], bufs=bufs, wstruct=wst, trace=traces[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage = np.zeros(5)
+    stage = np.zeros(len(STAGES))
     for t in traces:
-        for j in range(5):
+        for j in range(len(STAGES)):
             stage[j] += ev.elapsed(t.ev[j], t.ev[j + 1])
     stage /= steps
     for t in traces:
@@ -134,7 +157,9 @@ def run_workload(w, steps, warmup, ev):
             ev.destroy(t.ev[i])
     cnt = bufs.counters.cpu().numpy()
     kept_rows, touched = int(cnt[0]), int(cnt[3])
-    total_flops, g1_flops = active_work(w, kept_rows)
+    group_rows = [int(v) for v in np.diff(bufs.offset.cpu().numpy().astype(np.int64))]
+    assert sum(group_rows) == kept_rows
+    total_flops, g1_flops = active_work(w, group_rows)
     mats = 3 if w.act == "swiglu" else 2
     wbytes = 2.0 * (touched * mats * w.d * w.F + (3 * w.d * w.F_shared if w.F_shared else 0))
     res = dict(inp=inp, bufs=bufs, wall=wall, stage_ms=stage, kept_rows=kept_rows,
@@ -235,15 +260,16 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "K": w.K, "F": w.F,
                    "F_shared": w.F_shared, "act": w.act, "capacity_factor": w.cf,
                    "router": "fp32", "desc": w.desc},
-        "roofline": {"bound": "mfma", "kernel": "grouped GEMM 1 (gate/up + SiLU*mul)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "grouped GEMM 1, main launch (gate/up + SiLU*mul"
+                               + (f", whole {split_rows(w)}-row tiles)" if split_rows(w) else ")"),
                      "achieved": g1_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": g1_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "avg_ms": g1_ms, "flops_per_launch": r["g1_flops"]},
         "active_tflops": r["total_flops"] / (ms * 1e-3) / 1e12,
         "active_frac_of_bf16_peak": r["total_flops"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "weight_gbs": r["wbytes"] / (ms * 1e-3) / 1e9,
-        "stage_ms": {k: float(v) for k, v in zip(
-            ["router+stats", "dispatch", "gemm1", "gemm2", "combine"], r["stage_ms"])},
+        "stage_ms": {k: float(v) for k, v in zip(STAGES, r["stage_ms"])},
         "kept_rows": r["kept_rows"],
     }
     if not a.no_cpu_baseline:
@@ -260,8 +286,7 @@ def main():
             "touched_experts": rd["touched"], "weight_bytes": rd["wbytes"],
             "hbm_gbs": gbs, "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
-            "stage_ms": {k: float(v) for k, v in zip(
-                ["router+stats", "dispatch", "gemm1", "gemm2", "combine"], rd["stage_ms"])},
+            "stage_ms": {k: float(v) for k, v in zip(STAGES, rd["stage_ms"])},
         }
     print(json.dumps(line), flush=True)
 

@@ -42,8 +42,9 @@ struct TileCfg {
   int bm, bn, wm, wn;
 };
 
+// wg_per_cu: resident workgroups per CU the grid is sized for
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SW, bool DUAL, int EPI>
-hipError_t run_tile(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
+hipError_t run_tile(const GemmArgs& a, int64_t max_tiles, hipStream_t s, int wg_per_cu = 1) {
   auto kern = gemm_tile_kernel<BM, BN, BK, WM, WN, ST, SW, DUAL, EPI>;
   const size_t smem = (size_t)ST * (BM + BN) * BK * 2;
   static bool attr_set = false;
@@ -53,7 +54,7 @@ hipError_t run_tile(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  int64_t grid = num_cus();
+  int64_t grid = (int64_t)num_cus() * wg_per_cu;
   if (max_tiles < grid) grid = ((max_tiles + 7) / 8) * 8;
   if (grid < 8) grid = 8;
   kern<<<(unsigned)grid, WM * WN * 64, smem, s>>>(a);
@@ -89,7 +90,7 @@ hipError_t run_skinny(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
 }
 
 // Tile shapes by the expected rows per expert.
-enum Kind { K_SKINNY = 0, K_SMALL = 1, K_MID = 2, K_BIG = 3 };
+enum Kind { K_SKINNY = 0, K_SMALL = 1, K_MID = 2, K_BIG = 3, K_TAIL = 4 };
 
 Kind pick_kind(double rows_per_expert) {
   if (rows_per_expert <= 24.0) return K_SKINNY;
@@ -104,6 +105,7 @@ void kind_dims(Kind k, bool dual, int* bm, int* bno) {
     case K_SKINNY: *bm = 16; *bno = 16; return;
     case K_SMALL:  *bm = 64; *bno = dual ? 128 : 256; return;
     case K_MID:    *bm = 128; *bno = dual ? 128 : 256; return;
+    case K_TAIL:   *bm = 64; *bno = dual ? 32 : 64; return;
     default:       *bm = 256; *bno = dual ? 128 : 256; return;
   }
 }
@@ -116,6 +118,9 @@ hipError_t run_kind(Kind k, const GemmArgs& a, int64_t max_tiles, hipStream_t s)
     // rows: conflict-free fragment reads on the 64-bank LDS
     case K_SMALL:  return run_tile<64, 256, 64, 1, 4, 2, 1, DUAL, EPI>(a, max_tiles, s);
     case K_MID:    return run_pingpong<128, 256, 32, 2, 4, 4, 2, DUAL, EPI>(a, max_tiles, s);
+    // narrow tiles for the few leftover rows of each group: many workgroups
+    // share the weight stream of the touched experts
+    case K_TAIL:   return run_tile<64, 64, 64, 2, DUAL ? 1 : 2, 2, 1, DUAL, EPI>(a, max_tiles, s, 1);
     // 8 waves, 64 x 128 each, ping-pong between the two waves of each SIMD
     default:       return run_pingpong<256, 256, 32, 4, 2, 4, 2, DUAL, EPI>(a, max_tiles, s);
   }
@@ -138,28 +143,47 @@ size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared, 
   return (h + 255) / 256 * 256;
 }
 
-hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, hipEvent_t ev_pre,
-                             hipEvent_t ev_mid) {
+hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipEvent_t* ev) {
+  auto mark = [&](int i) -> hipError_t {
+    return (ev && ev[i]) ? hipEventRecord(ev[i], stream) : hipSuccess;
+  };
+  hipError_t err;
   if (!p.bf16) {
-    hipError_t e = ev_pre ? hipEventRecord(ev_pre, stream) : hipSuccess;
-    if (e == hipSuccess) e = launch_ffn_f32(p, stream);
-    if (e == hipSuccess && ev_mid) e = hipEventRecord(ev_mid, stream);
-    return e;
+    if ((err = mark(0)) != hipSuccess) return err;
+    if ((err = launch_ffn_f32(p, stream)) != hipSuccess) return err;
+    for (int i = 1; i < 5; ++i)
+      if ((err = mark(i)) != hipSuccess) return err;
+    return hipSuccess;
   }
   const bool swiglu = (p.act == 0);
   const int64_t rows = p.T * p.K;
   const int64_t srows = p.F_shared > 0 ? p.T : 0;
   const int G = p.N + (srows > 0 ? 1 : 0);
   const double rpe = (double)rows / (double)p.N;
-  Kind k1 = pick_kind(rpe), k2 = k1;
-  int bm1, bno1, bm2, bno2;
-  kind_dims(k1, swiglu, &bm1, &bno1);
-  kind_dims(k2, false, &bm2, &bno2);
-  int32_t* base1 = p.tile_base;
-  int32_t* base2 = p.tile_base + (p.N + 2);
-  tile_setup_kernel<<<1, 1024, 0, stream>>>(p.offset, p.N, srows, bm1, bno1, p.F, p.F_shared,
-                                            bm2, bno2, p.d, p.d, base1, base2);
-  hipError_t err = hipGetLastError();
+  const Kind k = pick_kind(rpe);
+  // With the largest tiles a partial last row tile per expert wastes most of
+  // a 256-row tile (and, in the second GEMM with its few column tiles, can
+  // add a whole round of workgroups).  There each group's rows are split:
+  // the main launch covers whole 256-row tiles (the last one at least half
+  // full) and a tail launch of 64 x 64 tiles the remainder (< 128 rows).
+  const bool split1 = false;
+  const bool split2 = (k == K_BIG);
+  int bm1, bno1, bm2, bno2, tbm1, tbno1, tbm2, tbno2;
+  kind_dims(k, swiglu, &bm1, &bno1);
+  kind_dims(k, false, &bm2, &bno2);
+  kind_dims(K_TAIL, swiglu, &tbm1, &tbno1);
+  kind_dims(K_TAIL, false, &tbm2, &tbno2);
+  const int sbm1 = split1 ? bm1 : 0, sbm2 = split2 ? bm2 : 0;
+  int32_t* base[4];
+  for (int i = 0; i < 4; ++i) base[i] = p.tile_base + i * (p.N + 2);
+  TileSpecs specs = {};
+  specs.s[0] = {bm1, bno1, p.F, p.F_shared, sbm1, 0};
+  specs.s[1] = {bm2, bno2, p.d, p.d, sbm2, 0};
+  specs.s[2] = {tbm1, tbno1, p.F, p.F_shared, sbm1, 1};
+  specs.s[3] = {tbm2, tbno2, p.d, p.d, sbm2, 1};
+  tile_setup_kernel<<<1, 1024, 0, stream>>>(p.offset, p.N, srows, specs,
+                                            (split1 || split2) ? 4 : 2, p.tile_base);
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
 
   const int Fm = p.F > p.F_shared ? p.F : p.F_shared;
@@ -187,20 +211,27 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, hipEvent_t
   g1.bias = (const uint16_t*)p.b1;
   g1.c = h;
   g1.c_shared = h_shared;
-  g1.tile_base = base1;
+  g1.tile_base = base[0];
   g1.G = G;
+  g1.split_bm = sbm1;
+  g1.region = 0;
+  if ((err = mark(0)) != hipSuccess) return err;
   const int64_t mt1 = max_tiles_for(rows + srows, G, bm1, Fm, bno1);
-  if (ev_pre) {
-    err = hipEventRecord(ev_pre, stream);
-    if (err != hipSuccess) return err;
-  }
-  err = swiglu ? run_kind<true, EPI_SILU_MUL>(k1, g1, mt1, stream)
-               : run_kind<false, EPI_GELU>(k1, g1, mt1, stream);
+  err = swiglu ? run_kind<true, EPI_SILU_MUL>(k, g1, mt1, stream)
+               : run_kind<false, EPI_GELU>(k, g1, mt1, stream);
   if (err != hipSuccess) return err;
-  if (ev_mid) {
-    err = hipEventRecord(ev_mid, stream);
+  if ((err = mark(1)) != hipSuccess) return err;
+  if (split1) {
+    GemmArgs t1 = g1;
+    t1.tile_base = base[2];
+    t1.region = 1;
+    // a tail is shorter than half a main tile
+    const int64_t tt1 = (int64_t)G * ((sbm1 / 2 + tbm1 - 1) / tbm1) * ((Fm + tbno1 - 1) / tbno1);
+    err = swiglu ? run_kind<true, EPI_SILU_MUL>(K_TAIL, t1, tt1, stream)
+                 : run_kind<false, EPI_GELU>(K_TAIL, t1, tt1, stream);
     if (err != hipSuccess) return err;
   }
+  if ((err = mark(2)) != hipSuccess) return err;
 
   // ---- GEMM 2: y = h W2^T [+ b2]
   GemmArgs g2 = {};
@@ -219,16 +250,27 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, hipEvent_t
   g2.bs1 = nullptr;
   g2.Nout = p.d;
   g2.Nout_shared = p.d;
-  g2.Kdim = p.F;
+  g2.Kdim = p.F;  // (F_shared is either 0 or F: checked on the host)
   g2.bias = (const uint16_t*)p.b2;
   g2.c = (uint16_t*)p.y_perm;
   g2.c_shared = (uint16_t*)p.y_shared;
-  g2.tile_base = base2;
+  g2.tile_base = base[1];
   g2.G = G;
-  // (F_shared is either 0 or F: checked on the host)
+  g2.split_bm = sbm2;
+  g2.region = 0;
   const int64_t mt2 = max_tiles_for(rows + srows, G, bm2, p.d, bno2);
-  err = run_kind<false, EPI_BIAS>(k2, g2, mt2, stream);
-  return err;
+  err = run_kind<false, EPI_BIAS>(k, g2, mt2, stream);
+  if (err != hipSuccess) return err;
+  if ((err = mark(3)) != hipSuccess) return err;
+  if (split2) {
+    GemmArgs t2 = g2;
+    t2.tile_base = base[3];
+    t2.region = 1;
+    const int64_t tt2 = (int64_t)G * ((sbm2 / 2 + tbm2 - 1) / tbm2) * ((p.d + tbno2 - 1) / tbno2);
+    err = run_kind<false, EPI_BIAS>(K_TAIL, t2, tt2, stream);
+    if (err != hipSuccess) return err;
+  }
+  return mark(4);
 }
 
 }  // namespace moe

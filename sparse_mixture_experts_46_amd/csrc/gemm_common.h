@@ -33,7 +33,27 @@ struct GemmArgs {
   uint16_t* c_shared;       // shared output [shared_rows, Nout_shared]
   const int32_t* tile_base; // [G + 1]
   int G;
+  int split_bm;             // 0: one launch covers every row; else see main_rows()
+  int region;               // 0: main rows of each group, 1: the tail rows
 };
+
+// Rows [0, main_rows) of a group go to the main launch, in tiles of split_bm
+// rows whose last one is at least half full; the remaining rows (fewer than
+// split_bm / 2) go to the tail launch, which uses small tiles.  Without a
+// split the main launch covers every row.
+__host__ __device__ __forceinline__ int main_rows(int M, int split_bm) {
+  if (split_bm <= 0) return M;
+  const int full = M / split_bm, rem = M % split_bm;
+  const int cov = (full + (2 * rem >= split_bm ? 1 : 0)) * split_bm;
+  return cov < M ? cov : M;
+}
+
+__host__ __device__ __forceinline__ void region_rows(int M, int split_bm, int region, int* first,
+                                                     int* count) {
+  const int cov = main_rows(M, split_bm);
+  *first = region == 0 ? 0 : cov;
+  *count = region == 0 ? cov : M - cov;
+}
 
 template <int EPI>
 __device__ __forceinline__ float epi1(float acc, float bias) {
@@ -53,8 +73,12 @@ __device__ __forceinline__ TileInfo resolve_tile(const GemmArgs& p, int tile, in
   ti.g = find_group(p.tile_base, p.G, tile);
   const int local = tile - p.tile_base[ti.g];
   ti.shared = (ti.g == p.n_routed);
-  ti.row0 = ti.shared ? 0 : p.offset[ti.g];
-  ti.M = ti.shared ? (int)p.shared_rows : (int)(p.offset[ti.g + 1] - ti.row0);
+  const int64_t g0 = ti.shared ? 0 : p.offset[ti.g];
+  const int Mg = ti.shared ? (int)p.shared_rows : (int)(p.offset[ti.g + 1] - g0);
+  int first, count;
+  region_rows(Mg, p.split_bm, p.region, &first, &count);
+  ti.row0 = g0 + first;
+  ti.M = count;
   ti.Nout = ti.shared ? p.Nout_shared : p.Nout;
   const int mtiles = (ti.M + BM - 1) / BM;
   ti.mt = local % mtiles;
@@ -63,36 +87,45 @@ __device__ __forceinline__ TileInfo resolve_tile(const GemmArgs& p, int tile, in
   return ti;
 }
 
-
 // ------------------------------------------------------------ tile setup --
-// tile_base[g] = sum_{g' < g} ceil(M_g'/BM) * ceil(Nout_g'/BNo), for two
-// tilings at once (first and second GEMM).  One block of 1024 threads.
+// One tiling of the groups: tile height bm, bno output columns per tile,
+// output widths of the routed / shared groups, and the row region.
+struct TileSpec {
+  int bm, bno, nout, nout_s, split_bm, region;
+};
+
+struct TileSpecs {
+  TileSpec s[4];
+};
+
+// base[k][g] = sum_{g' < g} tiles of group g' under spec k (k < nspec);
+// tables are (n_routed + 2) apart.  One block of 1024 threads.
 __global__ __launch_bounds__(1024) void tile_setup_kernel(
-    const int32_t* __restrict__ offset, int n_routed, int64_t shared_rows,
-    int bm1, int bno1, int nout1, int nout1_s, int bm2, int bno2, int nout2,
-    int nout2_s, int32_t* __restrict__ base1, int32_t* __restrict__ base2) {
-  __shared__ int32_t s1[2048], s2[2048];
+    const int32_t* __restrict__ offset, int n_routed, int64_t shared_rows, TileSpecs specs,
+    int nspec, int32_t* __restrict__ base) {
+  __shared__ int32_t cnt[4][1040];
   const int G = n_routed + (shared_rows > 0 ? 1 : 0);
-  for (int g = threadIdx.x; g < 2048; g += 1024) {
-    int32_t t1 = 0, t2 = 0;
-    if (g < G) {
-      int64_t M = g < n_routed ? (int64_t)(offset[g + 1] - offset[g]) : shared_rows;
-      int n1 = g < n_routed ? nout1 : nout1_s, n2 = g < n_routed ? nout2 : nout2_s;
-      t1 = (int32_t)(((M + bm1 - 1) / bm1) * ((n1 + bno1 - 1) / bno1));
-      t2 = (int32_t)(((M + bm2 - 1) / bm2) * ((n2 + bno2 - 1) / bno2));
+  for (int g = threadIdx.x; g < G; g += 1024) {
+    const int M = g < n_routed ? (int)(offset[g + 1] - offset[g]) : (int)shared_rows;
+    for (int k = 0; k < nspec; ++k) {
+      const TileSpec& sp = specs.s[k];
+      int first, count;
+      region_rows(M, sp.split_bm, sp.region, &first, &count);
+      const int n = g < n_routed ? sp.nout : sp.nout_s;
+      cnt[k][g] = ((count + sp.bm - 1) / sp.bm) * ((n + sp.bno - 1) / sp.bno);
     }
-    s1[g] = t1; s2[g] = t2;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {  // G <= 1025: a short serial scan is enough
-    int32_t r1 = 0, r2 = 0;
+  if (threadIdx.x < nspec) {  // G <= 1025: a short serial scan per table
+    const int k = threadIdx.x;
+    int32_t* b = base + (int64_t)k * (n_routed + 2);
+    int32_t r = 0;
     for (int g = 0; g < G; ++g) {
-      base1[g] = r1; base2[g] = r2;
-      r1 += s1[g]; r2 += s2[g];
+      b[g] = r;
+      r += cnt[k][g];
     }
-    base1[G] = r1; base2[G] = r2;
+    b[G] = r;
   }
 }
-
 
 }  // namespace moe

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
       int lr = ti.mt * BM + r;
       if (lr >= ti.M) lr = ti.M - 1;
       int64_t ar;
-      if (ti.shared) ar = lr;
+      if (ti.shared) ar = ti.row0 + lr;
       else {
         const int64_t gr = ti.row0 + lr;
         ar = p.a_rows ? (int64_t)(p.a_rows[gr] / p.a_div) : gr;

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p) {
     if (lr >= ti.M) lr = ti.M - 1;
     const uint16_t* pa;
     if (ti.shared) {
-      pa = p.a_shared + (int64_t)lr * p.lda;
+      pa = p.a_shared + (ti.row0 + lr) * p.lda;
     } else {
       const int64_t gr = ti.row0 + lr;
       const int64_t ar = p.a_rows ? (int64_t)(p.a_rows[gr] / p.a_div) : gr;

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs p) 
       if (lr >= ti.M) lr = ti.M - 1;
       int64_t ar;
       if (ti.shared) {
-        ar = lr;
+        ar = ti.row0 + lr;
       } else {
         const int64_t gr = ti.row0 + lr;
         ar = p.a_rows ? (int64_t)(p.a_rows[gr] / p.a_div) : gr;

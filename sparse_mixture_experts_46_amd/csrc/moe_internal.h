@@ -68,15 +68,15 @@ struct FfnProblem {
   void* h;          // [(T*K + T_shared), max(F, F_shared)] intermediate
   void* y_perm;     // [T*K, d]
   void* y_shared;   // [T, d]
-  int32_t* tile_base;  // [2 * (N + 2)] scratch
+  int32_t* tile_base;  // [4 * (N + 2)] scratch: four tile tables
 };
 
 size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared,
                            bool bf16);
-// ev_pre / ev_mid (nullable) are recorded right before and right after the
-// first grouped GEMM.
-hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream,
-                             hipEvent_t ev_pre, hipEvent_t ev_mid);
+// ev (nullable, else 5 nullable events): recorded before the first grouped
+// GEMM, after its main launch, after its tail launch, after the main launch
+// of the second grouped GEMM and after its tail launch.
+hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipEvent_t* ev);
 
 // --------------------------------------------------------------- combine --
 hipError_t launch_combine(const void* y_perm, const int32_t* pair_row,

@@ -204,6 +204,10 @@ FFN_CASES = [
     ("mid_gelu_bias", "gelu_tanh", "bf16", [200, 150, 128, 300], 128, 256, 0),
     ("big_swiglu", "swiglu", "bf16", [700, 1024, 513, 800], 128, 256, 0),
     ("big_shared", "swiglu", "bf16", [900, 700, 650, 800], 256, 128, 128),
+    # large tiles with tails: 76, 127 (the whole group), 0 and 4 leftover
+    # rows, and 104 leftover rows in the shared group (T = 1384)
+    ("big_tails", "swiglu", "bf16", [1100, 127, 0, 1540], 128, 128, 128),
+    ("big_tails_gelu", "gelu_tanh", "bf16", [300, 1500, 1025, 120], 128, 256, 0),
     ("f32_gelu_bias", "gelu_tanh", "f32", [5, 0, 7, 4], 64, 128, 0),
     ("f32_swiglu_shared", "swiglu", "f32", [3, 9, 1, 3], 64, 64, 64),
 ]
