@@ -44,7 +44,7 @@ RouterWs router_ws(const moe_config_t* c) {
   RouterWs w;
   const int64_t nb = router_num_blocks(c->T);
   size_t o = 0;
-  const int ns = router_num_splits(c->T, c->d, c->N);
+  const int ns = router_num_splits(c->T, c->d, c->N, c->dtype == MOE_BF16);
   w.split = o;  // logit partials, one [T, N] slab per K split (only if > 1 split)
   o = align_up(o + (ns > 1 ? (size_t)ns * c->T * c->N * 4 : 0));
   w.logits = o; o = align_up(o + (size_t)c->T * c->N * 4);

@@ -15,7 +15,7 @@ int router_tokens_per_block(int64_t T);
 int64_t router_num_blocks(int64_t T);
 
 // K splits of the logits GEMM for this shape (partials [splits, T, N]).
-int router_num_splits(int64_t T, int d, int N);
+int router_num_splits(int64_t T, int d, int N, bool x_bf16);
 
 // logits = x W_r^T + b_r.  With several K splits the partial products go to
 // part [splits, T, N] and a reduction writes logits; with one split the

@@ -18,19 +18,18 @@
 namespace moe {
 
 // ------------------------------------------------------------ logits GEMM --
-// fp32 MFMA (v_mfma_f32_32x32x2_f32) tile of 64 tokens x 64 experts, four
-// waves in a 2x2 grid, K staged through LDS in chunks of 32.  x may be bf16
-// (widened exactly to fp32 when staged) or fp32.  Few token or expert tiles
-// (small N, or decode-sized T) split K over gridDim.z: split z writes its
-// partial dot products to part[z]; the top-K kernel sums the splits in
-// order z = 0, 1, ... and adds the bias, so the result is deterministic.
+// fp32 activations: fp32 MFMA (v_mfma_f32_32x32x2_f32) tile of 64 tokens x
+// 64 experts, four waves in a 2x2 grid, K staged through LDS in chunks of
+// 32.  Few token or expert tiles (small N, or decode-sized T) split K over
+// gridDim.z: split z writes its partial dot products to part[z]; a reduce
+// kernel sums the splits in order z = 0, 1, ... and adds the bias, so the
+// result is deterministic.
 namespace {
 
 constexpr int RT_M = 64, RT_N = 64, RT_K = 32, RT_PAD = 1;
 
-template <bool XBF16>
 __global__ __launch_bounds__(256) void router_logits_kernel(
-    const void* __restrict__ xv, const float* __restrict__ w_r,
+    const float* __restrict__ x, const float* __restrict__ w_r,
     const float* __restrict__ b_r, float* __restrict__ part, int64_t T, int d, int N) {
   __shared__ float xs[2][RT_M][RT_K + RT_PAD];
   __shared__ float ws[2][RT_N][RT_K + RT_PAD];
@@ -39,51 +38,26 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   const int64_t t0 = (int64_t)blockIdx.x * RT_M;
   const int e0 = blockIdx.y * RT_N;
 
-  // staging assignment: x tile 64 x 32 -> bf16: one 8-element chunk per
-  // thread; fp32: two 4-element chunks.  W tile 64 x 32 fp32: two chunks.
-  float xr[8];
-  float4 wr[2];
+  // staging assignment: x and W tiles 64 x 32 fp32, two 4-element chunks
+  // per thread each
+  float4 xr[2], wr[2];
   auto load_tile = [&](int k0) {
-    if (XBF16) {
-      int r = tid >> 2, c = (tid & 3) * 8;
-      int64_t t = t0 + r; if (t >= T) t = T - 1;
-      const uint16_t* x = (const uint16_t*)xv;
-      uint4 v = *(const uint4*)(x + t * d + k0 + c);
-      unpack_bf16x8(v, xr);
-    } else {
-      const float* x = (const float*)xv;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;
-        int64_t t = t0 + r; if (t >= T) t = T - 1;
-        float4 v = *(const float4*)(x + t * d + k0 + c);
-        xr[i * 4 + 0] = v.x; xr[i * 4 + 1] = v.y; xr[i * 4 + 2] = v.z; xr[i * 4 + 3] = v.w;
-      }
-    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;
+      int64_t t = t0 + r; if (t >= T) t = T - 1;
+      xr[i] = *(const float4*)(x + t * d + k0 + c);
       int e = e0 + r;
       if (e < N) wr[i] = *(const float4*)(w_r + (int64_t)e * d + k0 + c);
       else wr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   auto store_tile = [&](int buf) {
-    if (XBF16) {
-      int r = tid >> 2, c = (tid & 3) * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xs[buf][r][c + j] = xr[j];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xs[buf][r][c + j] = xr[i * 4 + j];
-      }
-    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;
+      xs[buf][r][c + 0] = xr[i].x; xs[buf][r][c + 1] = xr[i].y;
+      xs[buf][r][c + 2] = xr[i].z; xs[buf][r][c + 3] = xr[i].w;
       ws[buf][r][c + 0] = wr[i].x; ws[buf][r][c + 1] = wr[i].y;
       ws[buf][r][c + 2] = wr[i].z; ws[buf][r][c + 3] = wr[i].w;
     }
@@ -125,6 +99,134 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
       int64_t t = t0 + row;
       if (t < T) out[t * N + col] = acc[v] + bias;
     }
+  }
+}
+
+// bf16 activations: each fp32 router weight is split exactly into three
+// bf16 parts, w = hi + mid + lo (hi the round-to-nearest bf16 of w, mid of
+// w - hi, lo of what is left: 3 x 8 significand bits hold all 24).  Every
+// product of a bf16 x with a part is exact in fp32 and the MFMA accumulates
+// in fp32, so v_mfma_f32_32x32x16_bf16 gives fp32-accurate logits at bf16
+// matrix-core rate.  The split is done while the weight tile is staged, so
+// the fp32 weight is read once per tile and nothing is precomputed.
+// Tile: 64*FM tokens x 64 experts, four waves in a 2x2 grid (wave tile
+// 32*FM x 32), K staged through LDS in chunks of 32; K splits over
+// gridDim.z as in the fp32 kernel.
+constexpr int RB_N = 64, RB_K = 32, RB_LD = RB_K + 8;  // LDS row: 80 bytes
+
+__device__ __forceinline__ void split3_bf16(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = f32_to_bf16(w);
+  const float r1 = w - bf16_to_f32(hi);  // exact
+  mid = f32_to_bf16(r1);
+  const float r2 = r1 - bf16_to_f32(mid);  // exact
+  lo = f32_to_bf16(r2);
+}
+
+template <int FM>
+__global__ __launch_bounds__(256) void router_logits_bf16x3_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_r,
+    const float* __restrict__ b_r, float* __restrict__ part, int64_t T, int d, int N) {
+  constexpr int BM = 64 * FM;
+  constexpr int XL = BM * RB_K / 8 / 256;  // 16-byte x chunks per thread per stage
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][RB_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][3][RB_N][RB_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t t0 = (int64_t)blockIdx.x * BM;
+  const int e0 = blockIdx.y * RB_N;
+
+  uint4 xr0, xr1;  // x chunks of rows r and r + 64 (the second only when XL == 2)
+  float4 wr[2];
+  static_assert(XL == 1 || XL == 2, "x chunks per thread");
+#define MOE_RB_LOAD(K0)                                                              \
+  do {                                                                               \
+    {                                                                                \
+      const int r = tid >> 2, c = (tid & 3) * 8;                                     \
+      const int64_t ta = t0 + r < T ? t0 + r : T - 1;                                \
+      xr0 = *(const uint4*)(x + ta * d + (K0) + c);                                  \
+      if (XL == 2) {                                                                 \
+        const int64_t tb = t0 + r + 64 < T ? t0 + r + 64 : T - 1;                    \
+        xr1 = *(const uint4*)(x + tb * d + (K0) + c);                                \
+      }                                                                              \
+    }                                                                                \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                  \
+      const int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;                      \
+      const int e = e0 + r;                                                          \
+      wr[i] = e < N ? *(const float4*)(w_r + (int64_t)e * d + (K0) + c)              \
+                    : make_float4(0.f, 0.f, 0.f, 0.f);                               \
+    }                                                                                \
+  } while (0)
+#define MOE_RB_STORE(BUF)                                                            \
+  do {                                                                               \
+    {                                                                                \
+      const int r = tid >> 2, c = (tid & 3) * 8;                                     \
+      *(uint4*)&xs[BUF][r][c] = xr0;                                                 \
+      if (XL == 2) *(uint4*)&xs[BUF][r + 64][c] = xr1;                               \
+    }                                                                                \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                  \
+      const int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;                      \
+      uint16_t h0, h1, h2, h3, m0, m1, m2, m3, l0, l1, l2, l3;                       \
+      split3_bf16(wr[i].x, h0, m0, l0);                                              \
+      split3_bf16(wr[i].y, h1, m1, l1);                                              \
+      split3_bf16(wr[i].z, h2, m2, l2);                                              \
+      split3_bf16(wr[i].w, h3, m3, l3);                                              \
+      *(uint2*)&ws[BUF][0][r][c] = make_uint2(h0 | ((uint32_t)h1 << 16), h2 | ((uint32_t)h3 << 16)); \
+      *(uint2*)&ws[BUF][1][r][c] = make_uint2(m0 | ((uint32_t)m1 << 16), m2 | ((uint32_t)m3 << 16)); \
+      *(uint2*)&ws[BUF][2][r][c] = make_uint2(l0 | ((uint32_t)l1 << 16), l2 | ((uint32_t)l3 << 16)); \
+    }                                                                                \
+  } while (0)
+
+  f32x16_t acc[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+
+  const int nks = d / RB_K;
+  const int k_lo = (int)(((int64_t)blockIdx.z * nks) / gridDim.z);
+  const int k_hi = (int)(((int64_t)(blockIdx.z + 1) * nks) / gridDim.z);
+  const int nk = k_hi - k_lo;
+  MOE_RB_LOAD(k_lo * RB_K);
+  MOE_RB_STORE(0);
+  __syncthreads();
+  const int kq = (lane >> 5) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) MOE_RB_LOAD((k_lo + kt + 1) * RB_K);
+#pragma unroll
+    for (int ks = 0; ks < RB_K / 16; ++ks) {
+      const int kk = ks * 16 + kq;
+      bf16x8_t fb[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        fb[p] = __builtin_bit_cast(bf16x8_t, *(const uint4*)&ws[buf][p][wn * 32 + (lane & 31)][kk]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const bf16x8_t fa =
+            __builtin_bit_cast(bf16x8_t, *(const uint4*)&xs[buf][wm * 32 * FM + i * 32 + (lane & 31)][kk]);
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[p], acc[i], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) MOE_RB_STORE(buf ^ 1);
+    __syncthreads();
+  }
+#undef MOE_RB_LOAD
+#undef MOE_RB_STORE
+  // D layout: column (expert) = lane % 32, row (token) = 8*(v/4) + 4*(lane/32) + v%4
+  const int col = e0 + wn * 32 + (lane & 31);
+  float* out = part + (int64_t)blockIdx.z * T * N;
+  if (col < N) {
+    const float bias = (gridDim.z == 1 && b_r) ? b_r[col] : 0.f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * 32 * FM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int64_t t = t0 + row;
+        if (t < T) out[t * N + col] = acc[i][v] + bias;
+      }
   }
 }
 
@@ -354,9 +456,14 @@ int64_t router_num_blocks(int64_t T) {
   return (T + tpb - 1) / tpb;
 }
 
-int router_num_splits(int64_t T, int d, int N) {
+int router_tile_m(int64_t T, bool x_bf16) {
+  return (x_bf16 && T >= 1024) ? 128 : 64;
+}
+
+int router_num_splits(int64_t T, int d, int N, bool x_bf16) {
   // aim for >= 512 workgroups, with at least 4 K steps (128 elements) per split
-  const int64_t tiles = ((T + RT_M - 1) / RT_M) * ((N + RT_N - 1) / RT_N);
+  const int tm = router_tile_m(T, x_bf16);
+  const int64_t tiles = ((T + tm - 1) / tm) * ((N + RT_N - 1) / RT_N);
   int64_t s = (512 + tiles - 1) / tiles;
   const int64_t max_s = d / (4 * RT_K);
   if (s > max_s) s = max_s;
@@ -368,13 +475,17 @@ int router_num_splits(int64_t T, int d, int N) {
 hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, const float* b_r,
                                 float* part, float* logits, int64_t T, int d, int N,
                                 hipStream_t stream) {
-  const int ns = router_num_splits(T, d, N);
-  dim3 grid((unsigned)((T + RT_M - 1) / RT_M), (unsigned)((N + RT_N - 1) / RT_N), (unsigned)ns);
+  static_assert(RB_N == RT_N && RB_K == RT_K, "both logit kernels tile experts and K alike");
+  const int ns = router_num_splits(T, d, N, x_bf16);
+  const int tm = router_tile_m(T, x_bf16);
+  dim3 grid((unsigned)((T + tm - 1) / tm), (unsigned)((N + RT_N - 1) / RT_N), (unsigned)ns);
   float* out = ns == 1 ? logits : part;
-  if (x_bf16)
-    router_logits_kernel<true><<<grid, 256, 0, stream>>>(x, w_r, b_r, out, T, d, N);
+  if (x_bf16 && tm == 128)
+    router_logits_bf16x3_kernel<2><<<grid, 256, 0, stream>>>((const uint16_t*)x, w_r, b_r, out, T, d, N);
+  else if (x_bf16)
+    router_logits_bf16x3_kernel<1><<<grid, 256, 0, stream>>>((const uint16_t*)x, w_r, b_r, out, T, d, N);
   else
-    router_logits_kernel<false><<<grid, 256, 0, stream>>>(x, w_r, b_r, out, T, d, N);
+    router_logits_kernel<<<grid, 256, 0, stream>>>((const float*)x, w_r, b_r, out, T, d, N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   int64_t n = T * (int64_t)N;

@@ -77,6 +77,9 @@ ROUTER_CASES = [
     WL.Workload(name="noren", T=90, d=64, N=16, K=3, F=64, gate="prob_no_renorm", seed=11,
                 sel_bias=True),
     WL.Workload(name="n1_k1", T=33, d=64, N=1, K=1, F=64, seed=12),
+    # 128-token logit tiles (T >= 1024) with a ragged last token tile and a
+    # ragged expert tile
+    WL.Workload(name="t1100_n40", T=1100, d=320, N=40, K=3, F=64, seed=14),
 ]
 
 
