@@ -87,38 +87,18 @@ class HipEvents:
         self.h.hipEventDestroy(e)
 
 
-STAGES = ["router+stats", "dispatch", "gemm1_main", "gemm1_tail", "gemm2_main", "gemm2_tail",
-          "combine"]
+STAGES = ["router+stats", "dispatch", "gemm1", "gemm2_main", "gemm2_tail", "combine"]
 
 
-def split_rows(w):
-    """Row-tile height at which the library splits each expert's rows into a
-    main and a tail launch, or 0 when one launch covers every row (the tile
-    is picked by the mean rows per expert, T*K/N)."""
-    return 256 if w.dtype == "bf16" and w.T * w.K / w.N > 640.0 else 0
-
-
-def main_rows(m, split):
-    """Rows of a group that the main launch computes: whole tiles of `split`
-    rows, the last one at least half full; the rest go to the tail launch."""
-    if split <= 0:
-        return m
-    full, rem = divmod(m, split)
-    return min((full + (1 if 2 * rem >= split else 0)) * split, m)
-
-
-def active_work(w, group_rows):
+def active_work(w, kept_rows):
     """Algorithmic flops of the two grouped GEMMs (kept pairs + shared
-    expert) and of the main launch of the first one (gate/up)."""
+    expert) and of the first one alone (gate/up, one launch)."""
     mats = 3 if w.act == "swiglu" else 2
-    kept_rows = sum(group_rows)
     flops_routed = 2.0 * kept_rows * w.d * w.F * mats
     flops_shared = 2.0 * w.T * w.d * w.F_shared * 3 if w.F_shared else 0.0
-    sp = split_rows(w)
-    main = sum(main_rows(m, sp) for m in group_rows)
-    g1_main = 2.0 * main * w.d * w.F * (mats - 1) + (
-        2.0 * main_rows(w.T, sp) * w.d * w.F_shared * 2 if w.F_shared else 0.0)
-    return flops_routed + flops_shared, g1_main
+    g1_flops = 2.0 * kept_rows * w.d * w.F * (mats - 1) + (
+        2.0 * w.T * w.d * w.F_shared * 2 if w.F_shared else 0.0)
+    return flops_routed + flops_shared, g1_flops
 
 
 def run_workload(w, steps, warmup, ev):
@@ -157,9 +137,7 @@ def run_workload(w, steps, warmup, ev):
             ev.destroy(t.ev[i])
     cnt = bufs.counters.cpu().numpy()
     kept_rows, touched = int(cnt[0]), int(cnt[3])
-    group_rows = [int(v) for v in np.diff(bufs.offset.cpu().numpy().astype(np.int64))]
-    assert sum(group_rows) == kept_rows
-    total_flops, g1_flops = active_work(w, group_rows)
+    total_flops, g1_flops = active_work(w, kept_rows)
     mats = 3 if w.act == "swiglu" else 2
     wbytes = 2.0 * (touched * mats * w.d * w.F + (3 * w.d * w.F_shared if w.F_shared else 0))
     res = dict(inp=inp, bufs=bufs, wall=wall, stage_ms=stage, kept_rows=kept_rows,
@@ -260,9 +238,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "K": w.K, "F": w.F,
                    "F_shared": w.F_shared, "act": w.act, "capacity_factor": w.cf,
                    "router": "fp32", "desc": w.desc},
-        "roofline": {"bound": "mfma",
-                     "kernel": "grouped GEMM 1, main launch (gate/up + SiLU*mul"
-                               + (f", whole {split_rows(w)}-row tiles)" if split_rows(w) else ")"),
+        "roofline": {"bound": "mfma", "kernel": "grouped GEMM 1 (gate/up + SiLU*mul)",
                      "achieved": g1_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": g1_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "avg_ms": g1_ms, "flops_per_launch": r["g1_flops"]},

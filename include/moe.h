@@ -164,13 +164,12 @@ typedef struct {
  * boundaries of moe_layer_forward (any may be NULL):
  *   ev[0] before the router, ev[1] after routing + statistics,
  *   ev[2] after dispatch, right before the first grouped GEMM (gate/up),
- *   ev[3] after its main launch, ev[4] after its tail launch, ev[5] after
- *   the main launch of the second grouped GEMM (down), ev[6] after its tail
- *   launch, ev[7] after the combine.  With the largest tiles (more than 640
- *   rows per expert on average) the main launches cover each expert's rows
- *   in whole 256-row tiles, the last at least half full, and the tail
- *   launches the remainder; otherwise the tail launches are empty.       */
-#define MOE_TRACE_EVENTS 8
+ *   ev[3] after it, ev[4] after the main launch of the second grouped GEMM
+ *   (down), ev[5] after its tail launch, ev[6] after the combine.  With the
+ *   largest tiles (more than 640 rows per expert on average) the main launch
+ *   covers each expert's rows in whole 256-row tiles, the last at least half
+ *   full, and the tail launch the remainder; otherwise there is no tail.  */
+#define MOE_TRACE_EVENTS 7
 typedef struct {
   void* ev[MOE_TRACE_EVENTS];
 } moe_trace_t;

@@ -11,7 +11,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_GELU_TANH = 0, 1
 MOE_GATE_RENORM_ALL, MOE_GATE_SOFTMAX_TOPK, MOE_GATE_PROB_NO_RENORM = 0, 1, 2
-MOE_TRACE_EVENTS = 8
+MOE_TRACE_EVENTS = 7
 
 EXPORTED = ("moe_status_string", "moe_capacity", "moe_workspace_size",
             "moe_router_workspace_size", "moe_dispatch_workspace_size",

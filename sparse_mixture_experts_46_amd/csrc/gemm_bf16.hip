@@ -151,7 +151,7 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   if (!p.bf16) {
     if ((err = mark(0)) != hipSuccess) return err;
     if ((err = launch_ffn_f32(p, stream)) != hipSuccess) return err;
-    for (int i = 1; i < 5; ++i)
+    for (int i = 1; i < 4; ++i)
       if ((err = mark(i)) != hipSuccess) return err;
     return hipSuccess;
   }
@@ -161,28 +161,28 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   const int G = p.N + (srows > 0 ? 1 : 0);
   const double rpe = (double)rows / (double)p.N;
   const Kind k = pick_kind(rpe);
-  // With the largest tiles a partial last row tile per expert wastes most of
-  // a 256-row tile (and, in the second GEMM with its few column tiles, can
-  // add a whole round of workgroups).  There each group's rows are split:
-  // the main launch covers whole 256-row tiles (the last one at least half
-  // full) and a tail launch of 64 x 64 tiles the remainder (< 128 rows).
-  const bool split1 = false;
+  // With the largest tiles the second GEMM has only d / 256 column tiles
+  // per row tile, so a partial last row tile per expert can add a whole
+  // round of workgroups.  There each group's rows are split: the main launch
+  // covers whole 256-row tiles (the last one at least half full) and a tail
+  // launch of 64 x 64 tiles the remainder (< 128 rows).  The first GEMM, with
+  // its many column tiles, runs in one launch: a separate tail launch would
+  // stream the touched experts' gate/up weights a second time, which costs
+  // more than the partial tiles it saves.
   const bool split2 = (k == K_BIG);
-  int bm1, bno1, bm2, bno2, tbm1, tbno1, tbm2, tbno2;
+  int bm1, bno1, bm2, bno2, tbm, tbno;
   kind_dims(k, swiglu, &bm1, &bno1);
   kind_dims(k, false, &bm2, &bno2);
-  kind_dims(K_TAIL, swiglu, &tbm1, &tbno1);
-  kind_dims(K_TAIL, false, &tbm2, &tbno2);
-  const int sbm1 = split1 ? bm1 : 0, sbm2 = split2 ? bm2 : 0;
-  int32_t* base[4];
-  for (int i = 0; i < 4; ++i) base[i] = p.tile_base + i * (p.N + 2);
+  kind_dims(K_TAIL, false, &tbm, &tbno);
+  const int sbm2 = split2 ? bm2 : 0;
+  int32_t* base[3];
+  for (int i = 0; i < 3; ++i) base[i] = p.tile_base + i * (p.N + 2);
   TileSpecs specs = {};
-  specs.s[0] = {bm1, bno1, p.F, p.F_shared, sbm1, 0};
+  specs.s[0] = {bm1, bno1, p.F, p.F_shared, 0, 0};
   specs.s[1] = {bm2, bno2, p.d, p.d, sbm2, 0};
-  specs.s[2] = {tbm1, tbno1, p.F, p.F_shared, sbm1, 1};
-  specs.s[3] = {tbm2, tbno2, p.d, p.d, sbm2, 1};
-  tile_setup_kernel<<<1, 1024, 0, stream>>>(p.offset, p.N, srows, specs,
-                                            (split1 || split2) ? 4 : 2, p.tile_base);
+  specs.s[2] = {tbm, tbno, p.d, p.d, sbm2, 1};
+  tile_setup_kernel<<<1, 1024, 0, stream>>>(p.offset, p.N, srows, specs, split2 ? 3 : 2,
+                                            p.tile_base);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
@@ -213,7 +213,7 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   g1.c_shared = h_shared;
   g1.tile_base = base[0];
   g1.G = G;
-  g1.split_bm = sbm1;
+  g1.split_bm = 0;
   g1.region = 0;
   if ((err = mark(0)) != hipSuccess) return err;
   const int64_t mt1 = max_tiles_for(rows + srows, G, bm1, Fm, bno1);
@@ -221,17 +221,6 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
                : run_kind<false, EPI_GELU>(k, g1, mt1, stream);
   if (err != hipSuccess) return err;
   if ((err = mark(1)) != hipSuccess) return err;
-  if (split1) {
-    GemmArgs t1 = g1;
-    t1.tile_base = base[2];
-    t1.region = 1;
-    // a tail is shorter than half a main tile
-    const int64_t tt1 = (int64_t)G * ((sbm1 / 2 + tbm1 - 1) / tbm1) * ((Fm + tbno1 - 1) / tbno1);
-    err = swiglu ? run_kind<true, EPI_SILU_MUL>(K_TAIL, t1, tt1, stream)
-                 : run_kind<false, EPI_GELU>(K_TAIL, t1, tt1, stream);
-    if (err != hipSuccess) return err;
-  }
-  if ((err = mark(2)) != hipSuccess) return err;
 
   // ---- GEMM 2: y = h W2^T [+ b2]
   GemmArgs g2 = {};
@@ -261,16 +250,17 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   const int64_t mt2 = max_tiles_for(rows + srows, G, bm2, p.d, bno2);
   err = run_kind<false, EPI_BIAS>(k, g2, mt2, stream);
   if (err != hipSuccess) return err;
-  if ((err = mark(3)) != hipSuccess) return err;
+  if ((err = mark(2)) != hipSuccess) return err;
   if (split2) {
     GemmArgs t2 = g2;
-    t2.tile_base = base[3];
+    t2.tile_base = base[2];
     t2.region = 1;
-    const int64_t tt2 = (int64_t)G * ((sbm2 / 2 + tbm2 - 1) / tbm2) * ((p.d + tbno2 - 1) / tbno2);
+    // a tail is shorter than half a main tile
+    const int64_t tt2 = (int64_t)G * ((sbm2 / 2 + tbm - 1) / tbm) * ((p.d + tbno - 1) / tbno);
     err = run_kind<false, EPI_BIAS>(K_TAIL, t2, tt2, stream);
     if (err != hipSuccess) return err;
   }
-  return mark(4);
+  return mark(3);
 }
 
 }  // namespace moe

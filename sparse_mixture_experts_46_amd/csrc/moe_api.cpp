@@ -75,7 +75,7 @@ struct FfnWs {
 FfnWs ffn_ws(const moe_config_t* c) {
   FfnWs w;
   size_t o = 0;
-  w.tile_base = o; o = align_up(o + (size_t)4 * (c->N + 2) * 4);
+  w.tile_base = o; o = align_up(o + (size_t)3 * (c->N + 2) * 4);
   w.h = o; o = align_up(o + ffn_workspace_bytes(c->T, c->d, c->N, c->K, c->F, c->F_shared,
                                                 c->dtype == MOE_BF16));
   w.total = o;
@@ -336,14 +336,14 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   p.y_shared = cfg->F_shared > 0 ? at<void>(ws, L.y_shared) : nullptr;
   p.h = fws + FL.h;
   p.tile_base = (int32_t*)(fws + FL.tile_base);
-  hipEvent_t fev[5] = {};
+  hipEvent_t fev[4] = {};
   if (trace)
-    for (int i = 0; i < 5; ++i) fev[i] = (hipEvent_t)trace->ev[2 + i];
+    for (int i = 0; i < 4; ++i) fev[i] = (hipEvent_t)trace->ev[2 + i];
   if (launch_expert_ffn(p, s, fev) != hipSuccess) return MOE_ERR_HIP;
   if (launch_combine(p.y_perm, d.pair_row, gate, p.y_shared, out->y, cfg->T, cfg->d, cfg->K,
                      p.bf16, s) != hipSuccess)
     return MOE_ERR_HIP;
-  return mark(7);
+  return mark(6);
 }
 
 }  // extern "C"

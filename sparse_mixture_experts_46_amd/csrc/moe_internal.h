@@ -68,14 +68,14 @@ struct FfnProblem {
   void* h;          // [(T*K + T_shared), max(F, F_shared)] intermediate
   void* y_perm;     // [T*K, d]
   void* y_shared;   // [T, d]
-  int32_t* tile_base;  // [4 * (N + 2)] scratch: four tile tables
+  int32_t* tile_base;  // [3 * (N + 2)] scratch: three tile tables
 };
 
 size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared,
                            bool bf16);
-// ev (nullable, else 5 nullable events): recorded before the first grouped
-// GEMM, after its main launch, after its tail launch, after the main launch
-// of the second grouped GEMM and after its tail launch.
+// ev (nullable, else 4 nullable events): recorded before the first grouped
+// GEMM, after it, after the main launch of the second grouped GEMM and after
+// its tail launch.
 hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipEvent_t* ev);
 
 // --------------------------------------------------------------- combine --

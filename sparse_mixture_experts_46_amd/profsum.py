@@ -83,6 +83,7 @@ def main():
     ap.add_argument("--cmd", required=True)
     ap.add_argument("--probe-mib", type=int, default=1024)
     ap.add_argument("--gemm1", default="gemm_pingpong_kernel<256, 256, 32, 4, 2, 4, 2, true, 0>")
+    ap.add_argument("--bench-log", help="stdout of the traced bench.py run (its JSON line)")
     a = ap.parse_args()
     os.makedirs(a.out, exist_ok=True)
     tab = stats_table(a.trace)
@@ -91,6 +92,23 @@ def main():
              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
     for n, c, avg, tot, pct in tab[:25]:
         lines.append(f"| `{n}` | {c} | {avg:.1f} | {tot:.3f} | {pct:.2f} |")
+    if a.bench_log:
+        js = [json.loads(l) for l in open(a.bench_log) if l.startswith("{")]
+        if js:
+            b = js[-1]
+            lines += ["", "## bench.py's own HIP-event timings in the traced run", "",
+                      f"Prefill ({b['config']['workload']}): ms_per_step {b['ms_per_step']:.3f}; "
+                      f"roofline kernel `{b['roofline']['kernel']}` avg "
+                      f"{b['roofline']['avg_ms'] * 1e3:.1f} us, "
+                      f"{b['roofline']['achieved']:.0f} TFLOP/s.", "",
+                      "| stage | ms |", "|---|---|"]
+            lines += [f"| {k} | {v:.3f} |" for k, v in b["stage_ms"].items()]
+            if "decode" in b:
+                dd = b["decode"]
+                lines += ["", f"Decode ({dd['workload']}): ms_per_step {dd['ms_per_step']:.3f}, "
+                              f"{dd['hbm_gbs']:.0f} GB/s of expert weights.", "",
+                          "| stage | ms |", "|---|---|"]
+                lines += [f"| {k} | {v:.3f} |" for k, v in dd["stage_ms"].items()]
     if a.fetch and a.write:
         f = counters(a.fetch, "FETCH_SIZE")
         w = counters(a.write, "WRITE_SIZE")
