@@ -56,7 +56,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
   extern __shared__ uint4 smem[];
   char* sbase = (char*)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform, so per-wave buffer resources and LDS bases live in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
   const int wm = wave / WN, wn = wave % WN;
   const int total = p.tile_base[p.G];
