@@ -90,7 +90,7 @@ hipError_t run_skinny(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
 }
 
 // Tile shapes by the expected rows per expert.
-enum Kind { K_SKINNY = 0, K_SMALL = 1, K_MID = 2, K_BIG = 3, K_TAIL = 4 };
+enum Kind { K_SKINNY = 0, K_SMALL = 1, K_MID = 2, K_BIG = 3, K_TAIL = 4, K_TAIL64 = 5 };
 
 Kind pick_kind(double rows_per_expert) {
   if (rows_per_expert <= 24.0) return K_SKINNY;
@@ -105,7 +105,8 @@ void kind_dims(Kind k, bool dual, int* bm, int* bno) {
     case K_SKINNY: *bm = 16; *bno = 16; return;
     case K_SMALL:  *bm = 64; *bno = dual ? 128 : 256; return;
     case K_MID:    *bm = 128; *bno = dual ? 128 : 256; return;
-    case K_TAIL:   *bm = 64; *bno = dual ? 32 : 64; return;
+    case K_TAIL:   *bm = 32; *bno = dual ? 32 : 64; return;
+    case K_TAIL64: *bm = 64; *bno = dual ? 32 : 64; return;
     default:       *bm = 256; *bno = dual ? 128 : 256; return;
   }
 }
@@ -118,9 +119,13 @@ hipError_t run_kind(Kind k, const GemmArgs& a, int64_t max_tiles, hipStream_t s)
     // rows: conflict-free fragment reads on the 64-bank LDS
     case K_SMALL:  return run_tile<64, 256, 64, 1, 4, 2, 1, DUAL, EPI>(a, max_tiles, s);
     case K_MID:    return run_pingpong<128, 256, 32, 2, 4, 4, 2, DUAL, EPI>(a, max_tiles, s);
-    // narrow tiles for the few leftover rows of each group: many workgroups
-    // share the weight stream of the touched experts
-    case K_TAIL:   return run_tile<64, 64, 64, 2, DUAL ? 1 : 2, 2, 1, DUAL, EPI>(a, max_tiles, s, 1);
+    // small tiles for the few leftover rows of each group, two workgroups per
+    // CU, K in slices of 128 (256 contiguous bytes per weight row): many
+    // workgroups share the weight stream of the touched experts
+    // (256-byte LDS rows: swizzle row & 15)
+    case K_TAIL:   return run_tile<32, 64, 128, 1, DUAL ? 1 : 2, 3, 0, DUAL, EPI>(a, max_tiles, s, 2);
+    // the same for K not a multiple of 128
+    case K_TAIL64: return run_tile<64, 64, 64, 2, DUAL ? 1 : 2, 2, 1, DUAL, EPI>(a, max_tiles, s, 1);
     // 8 waves, 64 x 128 each, ping-pong between the two waves of each SIMD
     default:       return run_pingpong<256, 256, 32, 4, 2, 4, 2, DUAL, EPI>(a, max_tiles, s);
   }
@@ -173,7 +178,8 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   int bm1, bno1, bm2, bno2, tbm, tbno;
   kind_dims(k, swiglu, &bm1, &bno1);
   kind_dims(k, false, &bm2, &bno2);
-  kind_dims(K_TAIL, false, &tbm, &tbno);
+  const Kind tk = (p.F % 128 == 0) ? K_TAIL : K_TAIL64;  // K of GEMM 2 is F
+  kind_dims(tk, false, &tbm, &tbno);
   const int sbm2 = split2 ? bm2 : 0;
   int32_t* base[3];
   for (int i = 0; i < 3; ++i) base[i] = p.tile_base + i * (p.N + 2);
@@ -257,7 +263,7 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
     t2.region = 1;
     // a tail is shorter than half a main tile
     const int64_t tt2 = (int64_t)G * ((sbm2 / 2 + tbm - 1) / tbm) * ((p.d + tbno - 1) / tbno);
-    err = run_kind<false, EPI_BIAS>(K_TAIL, t2, tt2, stream);
+    err = run_kind<false, EPI_BIAS>(tk, t2, tt2, stream);
     if (err != hipSuccess) return err;
   }
   return mark(3);

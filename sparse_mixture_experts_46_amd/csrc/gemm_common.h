@@ -61,6 +61,33 @@ __device__ __forceinline__ float epi1(float acc, float bias) {
   return acc + bias;
 }
 
+// Order in which a persistent workgroup visits the tile table.  Workgroups
+// are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8).
+// With at least as many tiles as workgroups, each round of nb tiles is cut
+// into 8 contiguous runs, one per XCD, so an XCD works on neighbouring tiles
+// (same expert, adjacent columns) that share its L2 while all XCDs stay on
+// the same stretch of the table.  With fewer tiles than workgroups the tiles
+// are cut into 8 contiguous ranges of ceil(total / 8), so every XCD has work.
+struct TileWalk {
+  int tile, step, end;
+};
+__device__ __forceinline__ TileWalk tile_walk(int total) {
+  const int nb = gridDim.x, bid = blockIdx.x;
+  TileWalk w;
+  w.step = nb;
+  w.end = total;
+  if ((nb & 7) != 0) {
+    w.tile = bid;
+  } else if (total >= nb) {
+    w.tile = (bid & 7) * (nb >> 3) + (bid >> 3);
+  } else {  // one round: at most one tile per workgroup
+    const int per = (total + 7) >> 3, x = bid & 7;
+    w.tile = x * per + (bid >> 3);
+    w.end = (x + 1) * per < total ? (x + 1) * per : total;
+  }
+  return w;
+}
+
 // Resolve tile -> (group, first row, rows, output columns, A/B/C pointers).
 struct TileInfo {
   int g, M, Nout, mt, nt;

@@ -18,8 +18,8 @@
 //    and waited for STAGES-2 stages later, past the end of K the last slice is
 //    re-loaded into the unused slot (drained before the epilogue).
 //  * Persistent: one workgroup per CU walks the device-side tile table in a
-//    fixed round-robin; tile ids are remapped so each XCD gets a contiguous
-//    run (same expert, neighbouring column tiles) that shares its L2.
+//    fixed order; each XCD walks its own contiguous range of tiles (same
+//    expert, neighbouring column tiles) that shares its L2.
 //  * SwiGLU (DUAL): the B tile holds BN/2 gate rows and the same BN/2 up
 //    rows; silu(gate) * up is formed in registers.
 #pragma once
@@ -62,9 +62,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
   const int grp = wave >> 2;
   const int wm = wave / WN, wn = wave % WN;
   const int total = p.tile_base[p.G];
-  const int nb = gridDim.x;
-  const int bid = blockIdx.x;
-  const int first = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
+  const TileWalk walk = tile_walk(total);
   const int lrow = lane / CH, pch = lane % CH;
 
   int arow[FM], brow[FN];
@@ -83,7 +81,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
   }
   const int khalf = lane >> 5;
 
-  for (int tile = first; tile < total; tile += nb) {
+  for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
     const TileInfo ti = resolve_tile(p, tile, BM, BNo);
     const int64_t Kd = p.Kdim;
     const char* abase = (const char*)(ti.shared ? p.a_shared : p.a);

@@ -2,8 +2,8 @@
 // gfx950 matrix cores, bf16 operands, fp32 accumulation.
 //
 //  * Persistent: one workgroup per CU walks the device-side tile table in a
-//    fixed round-robin; tile ids are remapped so each XCD gets a contiguous
-//    run (same expert, neighbouring column tiles) that shares its L2.
+//    fixed order; each XCD walks its own contiguous range of tiles (same
+//    expert, neighbouring column tiles) that shares its L2.
 //  * A BK-wide K slice of every A and B row of the tile goes straight from
 //    global memory into LDS (global_load_lds_dwordx4, 16 bytes per lane, no
 //    staging registers).  One wave instruction fills 1 KB of LDS: rows of
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs p) 
   constexpr int LA = BM / (NW * RPI), LB = BN / (NW * RPI);
   constexpr int ROWS = BM + BN;
   constexpr int STAGE = ROWS * RB;       // bytes per stage
-  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(BK == 32 || BK == 64 || BK == 128, "BK");
   static_assert(BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "tile/wave mismatch");
   static_assert(!DUAL || (FN % 2 == 0), "dual tile needs an even fragment count");
   static_assert(STAGES >= 2, "stages");
@@ -65,9 +65,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs p) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int total = p.tile_base[p.G];
-  const int nb = gridDim.x;
-  const int bid = blockIdx.x;
-  const int first = (nb % 8 == 0) ? (bid % 8) * (nb / 8) + bid / 8 : bid;
+  const TileWalk walk = tile_walk(total);
   const int lrow = lane / CH, pch = lane % CH;
 
   // LDS rows (within a stage) whose fragments this lane reads
@@ -87,7 +85,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile_kernel(GemmArgs p) 
   }
   const int khalf = lane >> 5;
 
-  for (int tile = first; tile < total; tile += nb) {
+  for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
     const TileInfo ti = resolve_tile(p, tile, BM, BNo);
     const int64_t Kd = p.Kdim;
     // ---- this lane's DMA sources: uniform base + per-lane byte offset

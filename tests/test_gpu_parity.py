@@ -211,6 +211,8 @@ FFN_CASES = [
     # rows, and 104 leftover rows in the shared group (T = 1384)
     ("big_tails", "swiglu", "bf16", [1100, 127, 0, 1540], 128, 128, 128),
     ("big_tails_gelu", "gelu_tanh", "bf16", [300, 1500, 1025, 120], 128, 256, 0),
+    # F = 192 (not a multiple of 128): the tail launch takes 64-wide K slices
+    ("big_tails_f192", "gelu_tanh", "bf16", [1000, 900, 100, 800], 128, 192, 0),
     ("f32_gelu_bias", "gelu_tanh", "f32", [5, 0, 7, 4], 64, 128, 0),
     ("f32_swiglu_shared", "swiglu", "f32", [3, 9, 1, 3], 64, 64, 64),
 ]
