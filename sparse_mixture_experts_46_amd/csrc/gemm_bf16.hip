@@ -95,7 +95,11 @@ enum Kind { K_SKINNY = 0, K_SMALL = 1, K_MID = 2, K_BIG = 3, K_TAIL = 4, K_TAIL6
 Kind pick_kind(double rows_per_expert) {
   if (rows_per_expert <= 24.0) return K_SKINNY;
   if (rows_per_expert <= 96.0) return K_SMALL;
-  if (rows_per_expert <= 640.0) return K_MID;
+  // 256-row tiles move fewer operand bytes per flop than 128-row ones; they
+  // pay off from ~160 rows per expert on (DeepSeek-shaped prefill, ~256 rows
+  // per expert: 9.6 ms with them against 10.5 ms with 128-row tiles, padding
+  // included)
+  if (rows_per_expert <= 160.0) return K_MID;
   return K_BIG;
 }
 
@@ -166,15 +170,17 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   const int G = p.N + (srows > 0 ? 1 : 0);
   const double rpe = (double)rows / (double)p.N;
   const Kind k = pick_kind(rpe);
-  // With the largest tiles the second GEMM has only d / 256 column tiles
-  // per row tile, so a partial last row tile per expert can add a whole
-  // round of workgroups.  There each group's rows are split: the main launch
-  // covers whole 256-row tiles (the last one at least half full) and a tail
-  // launch of 64 x 64 tiles the remainder (< 128 rows).  The first GEMM, with
-  // its many column tiles, runs in one launch: a separate tail launch would
-  // stream the touched experts' gate/up weights a second time, which costs
-  // more than the partial tiles it saves.
-  const bool split2 = (k == K_BIG);
+  // With the largest tiles and many rows per expert (> 640) the second GEMM
+  // has only d / 256 column tiles per row tile, so a partial last row tile
+  // per expert can add a whole round of workgroups.  There each group's rows
+  // are split: the main launch covers whole 256-row tiles (the last one at
+  // least half full) and a tail launch of small tiles the remainder (< 128
+  // rows).  With fewer rows per expert most experts would have a tail, each
+  // streaming that expert's weights a second time.  The first GEMM, with its
+  // many column tiles, always runs in one launch: a tail launch would stream
+  // the touched experts' gate/up weights a second time, which costs more
+  // than the partial tiles it saves.
+  const bool split2 = (k == K_BIG) && rpe > 640.0;
   int bm1, bno1, bm2, bno2, tbm, tbno;
   kind_dims(k, swiglu, &bm1, &bno1);
   kind_dims(k, false, &bm2, &bno2);

@@ -205,6 +205,9 @@ FFN_CASES = [
     ("small_swiglu", "swiglu", "bf16", [50, 70, 3, 64, 65, 90, 11, 60], 256, 320, 0),
     ("mid_swiglu", "swiglu", "bf16", [300, 129, 1, 0, 257, 400, 128, 250], 192, 384, 0),
     ("mid_gelu_bias", "gelu_tanh", "bf16", [200, 150, 128, 300], 128, 256, 0),
+    # 97-160 rows per expert: the 128-row ping-pong tiles
+    ("mid128_swiglu", "swiglu", "bf16", [150, 97, 0, 260, 129, 130, 200, 100], 192, 384, 0),
+    ("mid128_gelu_bias", "gelu_tanh", "bf16", [120, 140, 100, 170], 128, 256, 0),
     ("big_swiglu", "swiglu", "bf16", [700, 1024, 513, 800], 128, 256, 0),
     ("big_shared", "swiglu", "bf16", [900, 700, 650, 800], 256, 128, 128),
     # large tiles with tails: 76, 127 (the whole group), 0 and 4 leftover
