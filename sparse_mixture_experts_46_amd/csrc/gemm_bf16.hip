@@ -131,9 +131,9 @@ hipError_t run_kind(Kind k, const GemmArgs& a, int64_t max_tiles, hipStream_t s)
     // the same for K not a multiple of 128
     case K_TAIL64: return run_tile<64, 64, 64, 2, DUAL ? 1 : 2, 2, 1, DUAL, EPI>(a, max_tiles, s, 1);
     // 8 waves, 64 x 128 each, ping-pong between the two waves of each SIMD.
-    // Three 32 KB stages: with 32 CUs per XCD a deeper ring (4 stages = 4 MB
-    // in flight) fills the XCD's L2 and evicts the tiles that neighbouring
-    // CUs share (DeepSeek-shaped GEMM 1: 5.5 ms with 3 stages, 6.0 with 4)
+    // Three 32 KB stages measured faster than four or five (DeepSeek-shaped
+    // GEMM 1: 5.5 ms with 3, 6.0 with 4); the deeper rings keep up to 4-5 MB
+    // of loads in flight per XCD, which likely crowds its 4 MB L2
     default:       return run_pingpong<256, 256, 32, 4, 2, 3, 2, DUAL, EPI>(a, max_tiles, s);
   }
 }
