@@ -24,6 +24,8 @@
 //    rows; silu(gate) * up is formed in registers.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_common.h"
 #include "gemm_tile.h"
 
@@ -48,7 +50,6 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int BNo = DUAL ? BN / 2 : BN;
   constexpr int LA = BM / (NW * RPI), LB = BN / (NW * RPI);
-  constexpr int NL = LA + LB;
   constexpr int ROWS = BM + BN;
   constexpr int STAGE = ROWS * RB;
   constexpr int KS = BK / 16;
@@ -65,9 +66,12 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
   const TileWalk walk = tile_walk(total);
   const int lrow = lane / CH, pch = lane % CH;
 
+  // A fragment i of wave-row wm holds tile rows i * (32 * WM) + 32 * wm + ...:
+  // the first half of the fragments covers rows [0, BM / 2) on every wave,
+  // so a half-height tile keeps all SIMDs equally busy
   int arow[FM], brow[FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) arow[i] = wm * TM + i * 32 + (lane & 31);
+  for (int i = 0; i < FM; ++i) arow[i] = i * (32 * WM) + wm * 32 + (lane & 31);
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     int r;
@@ -111,117 +115,129 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
       boff[i] = (uint32_t)(((int64_t)n * Kd + (pch ^ swz<CH, SWZ>(BM + r)) * 8) * 2);
     }
     const int nk = (int)(Kd / BK);
-    auto issue = [&](int stage_k, int buf) {
-      const int kk = stage_k < nk ? stage_k : nk - 1;
-      char* st = sbase + buf * STAGE;
-      const uint32_t kb = (uint32_t)(kk * BK) * 2;
+    // The tile body, for a full tile or (HALF) a last tile of at most BM / 2
+    // rows: then only the first half of the A loads and of the fragments run.
+    auto run = [&](auto half_c) {
+      constexpr bool HALF = decltype(half_c)::value;
+      constexpr int FMA = HALF ? FM / 2 : FM;  // A fragments computed
+      constexpr int LAA = HALF ? LA / 2 : LA;  // A loads issued per stage
+      constexpr int NLA = LAA + LB;
+      auto issue = [&](int stage_k, int buf) {
+        const int kk = stage_k < nk ? stage_k : nk - 1;
+        char* st = sbase + buf * STAGE;
+        const uint32_t kb = (uint32_t)(kk * BK) * 2;
 #pragma unroll
-      for (int i = 0; i < LA; ++i) buf_dma16(abase, aoff[i] + kb, st + (i * NW + wave) * RPI * RB);
+        for (int i = 0; i < LAA; ++i) buf_dma16(abase, aoff[i] + kb, st + (i * NW + wave) * RPI * RB);
 #pragma unroll
-      for (int i = 0; i < LB; ++i) {
-        const int r_ = (i * NW + wave) * RPI;
-        const char* bb = (DUAL && r_ >= BN / 2) ? bbase1 : bbase0;
-        buf_dma16(bb, boff[i] + kb, st + (BM + r_) * RB);
+        for (int i = 0; i < LB; ++i) {
+          const int r_ = (i * NW + wave) * RPI;
+          const char* bb = (DUAL && r_ >= BN / 2) ? bbase1 : bbase0;
+          buf_dma16(bb, boff[i] + kb, st + (BM + r_) * RB);
+        }
+      };
+
+      f32x16_t acc[FN][FMA];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FMA; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
+
+      // prologue: stages 0 .. STAGES-2
+#pragma unroll
+      for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
+      wait_vmcnt<(STAGES - 2) * NLA>();  // stage 0 landed (own share)
+      __syncthreads();
+      if (grp == 1) __builtin_amdgcn_s_barrier();  // B runs one phase behind
+
+      bf16x8_t fa[KS][FMA], fb[KS][FN];
+      int buf = 0;
+      for (int kt = 0; kt < nk; ++kt) {
+        // ---- M phase: DMA share for stage kt+STAGES-1, fragments of stage kt
+        int pbuf = buf + STAGES - 1;
+        if (pbuf >= STAGES) pbuf -= STAGES;
+        const uint4* s = (const uint4*)(sbase + buf * STAGE);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int ch = ks * 2 + khalf;
+#pragma unroll
+          for (int i = 0; i < FMA; ++i)
+            fa[ks][i] = __builtin_bit_cast(bf16x8_t, s[arow[i] * CH + (ch ^ swz<CH, SWZ>(arow[i]))]);
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            fb[ks][j] = __builtin_bit_cast(bf16x8_t, s[brow[j] * CH + (ch ^ swz<CH, SWZ>(brow[j]))]);
+        }
+        // this wave's share of stage kt+STAGES-1, issued after its fragment
+        // reads have completed
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kt + STAGES - 1, pbuf);
+        // stage kt+1 (issued STAGES-2 phases ago) must have landed before the
+        // next memory phase of either group
+        wait_vmcnt<(STAGES - 2) * NLA>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- C phase
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int i = 0; i < FMA; ++i)
+              acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[j][i], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        buf = (buf + 1 == STAGES) ? 0 : buf + 1;
       }
-    };
+      if (grp == 0) __builtin_amdgcn_s_barrier();  // realign with B
+      wait_vmcnt<0>();
+      __syncthreads();
 
-    f32x16_t acc[FN][FM];
+      // ---- epilogue: 4 consecutive output columns per lane, 8-byte stores
+      uint16_t* cbase = ti.shared ? p.c_shared : p.c;
+      const int64_t ldc = ti.Nout;
+      constexpr int FO = DUAL ? FN / 2 : FN;
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int i = 0; i < FMA; ++i) {
+        const int lr = ti.mt * BM + i * (32 * WM) + wm * 32 + (lane & 31);
+        if (lr >= ti.M) continue;
+        uint16_t* crow = cbase + (ti.row0 + lr) * ldc;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FO; ++j) {
+          const int cbase_col = ti.nt * BNo + (DUAL ? wn * (TN / 2) : wn * TN) + j * 32 + 4 * khalf;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
-
-    // prologue: stages 0 .. STAGES-2
+          for (int q = 0; q < 4; ++q) {
+            const int col = cbase_col + 8 * q;
+            if (col >= ti.Nout) continue;
+            float o[4];
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
-    wait_vmcnt<(STAGES - 2) * NL>();  // stage 0 landed (own share)
-    __syncthreads();
-    if (grp == 1) __builtin_amdgcn_s_barrier();  // B runs one phase behind
-
-    bf16x8_t fa[KS][FM], fb[KS][FN];
-    int buf = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-      // ---- M phase: DMA share for stage kt+STAGES-1, fragments of stage kt
-      int pbuf = buf + STAGES - 1;
-      if (pbuf >= STAGES) pbuf -= STAGES;
-      const uint4* s = (const uint4*)(sbase + buf * STAGE);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch = ks * 2 + khalf;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          fa[ks][i] = __builtin_bit_cast(bf16x8_t, s[arow[i] * CH + (ch ^ swz<CH, SWZ>(arow[i]))]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          fb[ks][j] = __builtin_bit_cast(bf16x8_t, s[brow[j] * CH + (ch ^ swz<CH, SWZ>(brow[j]))]);
-      }
-      // this wave's share of stage kt+STAGES-1, issued after its fragment
-      // reads have completed
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      __builtin_amdgcn_sched_barrier(0);
-      issue(kt + STAGES - 1, pbuf);
-      // stage kt+1 (issued STAGES-2 phases ago) must have landed before the
-      // next memory phase of either group
-      wait_vmcnt<(STAGES - 2) * NL>();
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- C phase
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[j][i], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      buf = (buf + 1 == STAGES) ? 0 : buf + 1;
-    }
-    if (grp == 0) __builtin_amdgcn_s_barrier();  // realign with B
-    wait_vmcnt<0>();
-    __syncthreads();
-
-    // ---- epilogue: 4 consecutive output columns per lane, 8-byte stores
-    uint16_t* cbase = ti.shared ? p.c_shared : p.c;
-    const int64_t ldc = ti.Nout;
-    constexpr int FO = DUAL ? FN / 2 : FN;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int lr = ti.mt * BM + wm * TM + i * 32 + (lane & 31);
-      if (lr >= ti.M) continue;
-      uint16_t* crow = cbase + (ti.row0 + lr) * ldc;
-#pragma unroll
-      for (int j = 0; j < FO; ++j) {
-        const int cbase_col = ti.nt * BNo + (DUAL ? wn * (TN / 2) : wn * TN) + j * 32 + 4 * khalf;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = cbase_col + 8 * q;
-          if (col >= ti.Nout) continue;
-          float o[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int v = 4 * q + u;
-            if (DUAL) {
-              o[u] = silu_f(acc[j][i][v]) * acc[j + FN / 2][i][v];
-            } else {
-              float bias = 0.f;
-              if (EPI != EPI_SILU_MUL && p.bias && !ti.shared)
-                bias = bf16_to_f32(p.bias[(int64_t)ti.g * p.Nout + col + u]);
-              o[u] = epi1<EPI>(acc[j][i][v], bias);
+            for (int u = 0; u < 4; ++u) {
+              const int v = 4 * q + u;
+              if (DUAL) {
+                o[u] = silu_f(acc[j][i][v]) * acc[j + FN / 2][i][v];
+              } else {
+                float bias = 0.f;
+                if (EPI != EPI_SILU_MUL && p.bias && !ti.shared)
+                  bias = bf16_to_f32(p.bias[(int64_t)ti.g * p.Nout + col + u]);
+                o[u] = epi1<EPI>(acc[j][i][v], bias);
+              }
             }
+            uint2 pk;
+            pk.x = pack_bf16x2(o[0], o[1]);
+            pk.y = pack_bf16x2(o[2], o[3]);
+            *(uint2*)(crow + col) = pk;
           }
-          uint2 pk;
-          pk.x = pack_bf16x2(o[0], o[1]);
-          pk.y = pack_bf16x2(o[2], o[3]);
-          *(uint2*)(crow + col) = pk;
         }
       }
-    }
+    };
+    // half-height mode needs an even split of the A loads and fragments
+    constexpr bool kHalfOk = (FM % 2 == 0) && (LA % 2 == 0);
+    if (kHalfOk && ti.M - ti.mt * BM <= BM / 2) run(std::true_type{});
+    else run(std::false_type{});
   }
 }
 
