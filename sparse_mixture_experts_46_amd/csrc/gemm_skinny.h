@@ -25,6 +25,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p) {
     const TileInfo ti = resolve_tile(p, tile, 16, 16);
     const int64_t Kd = p.Kdim;
     int lr = ti.mt * 16 + row;
+    // lanes of rows past the group's end load nothing (their accumulator
+    // rows are never stored); their A operand is zero
+    const bool arow_ok = lr < ti.M;
     if (lr >= ti.M) lr = ti.M - 1;
     const uint16_t* pa;
     if (ti.shared) {
@@ -50,7 +53,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < UNR; ++j) {
         const int off = (kc + j) * 32;
-        a[j] = *(const uint4*)(pa + off);
+        a[j] = arow_ok ? *(const uint4*)(pa + off) : make_uint4(0, 0, 0, 0);
         b[j] = *(const uint4*)(pb0 + off);
         if (DUAL) c[j] = *(const uint4*)(pb1 + off);
       }
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p) {
     }
     for (; kc < nk32; ++kc) {
       const int off = kc * 32;
-      bf16x8_t fa = __builtin_bit_cast(bf16x8_t, *(const uint4*)(pa + off));
+      bf16x8_t fa = __builtin_bit_cast(bf16x8_t, arow_ok ? *(const uint4*)(pa + off) : make_uint4(0, 0, 0, 0));
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
           fa, __builtin_bit_cast(bf16x8_t, *(const uint4*)(pb0 + off)), acc0, 0, 0, 0);
       if (DUAL)
