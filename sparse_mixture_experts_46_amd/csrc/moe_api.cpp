@@ -38,7 +38,7 @@ size_t elem_bytes(const moe_config_t* c) { return c->dtype == MOE_BF16 ? 2 : 4; 
 
 // ---- workspace layouts -----------------------------------------------------
 struct RouterWs {
-  size_t split, logits, part_p, part_cnt, part_z, total;
+  size_t split, logits, part_p, part_cnt, part_z, part_fp, total;
 };
 RouterWs router_ws(const moe_config_t* c) {
   RouterWs w;
@@ -51,6 +51,7 @@ RouterWs router_ws(const moe_config_t* c) {
   w.part_p = o; o = align_up(o + (size_t)nb * c->N * 4);
   w.part_cnt = o; o = align_up(o + (size_t)nb * c->N * 4);
   w.part_z = o; o = align_up(o + (size_t)nb * 2 * 4);
+  w.part_fp = o; o = align_up(o + (size_t)((c->N + 63) / 64) * 4);
   w.total = o;
   return w;
 }
@@ -149,7 +150,8 @@ moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (st && (st->count || st->f || st->p || st->loss)) {
     e = launch_router_stats(at<float>(ws, L.part_p), at<int32_t>(ws, L.part_cnt),
-                            at<float>(ws, L.part_z), router_num_blocks(c->T), c->T, c->N, c->K,
+                            at<float>(ws, L.part_z), at<float>(ws, L.part_fp),
+                            router_num_blocks(c->T), c->T, c->N, c->K,
                             c->aux_alpha, st->count, st->f, st->p, st->loss, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }

@@ -30,8 +30,9 @@ hipError_t launch_router_topk(const float* logits, const float* b_sel, int32_t* 
                               float* part_p, int32_t* part_cnt, float* part_z, int64_t T, int N,
                               int K, int gate_mode, hipStream_t stream);
 
+// part_fp: [ceil(N / 64)] fp32 scratch (per-expert-block sums of f_e * p_e)
 hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
-                               const float* part_z, int64_t nblk, int64_t T,
+                               const float* part_z, float* part_fp, int64_t nblk, int64_t T,
                                int N, int K, float alpha, int32_t* count,
                                float* f, float* p, float* loss,
                                hipStream_t stream);

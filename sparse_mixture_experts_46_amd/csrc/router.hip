@@ -110,9 +110,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 // matrix-core rate.  The split is done while the weight tile is staged, so
 // the fp32 weight is read once per tile and nothing is precomputed.
 // Tile: 64*FM tokens x 64 experts, four waves in a 2x2 grid (wave tile
-// 32*FM x 32), K staged through LDS in chunks of 32; K splits over
-// gridDim.z as in the fp32 kernel.
-constexpr int RB_N = 64, RB_K = 32, RB_LD = RB_K + 8;  // LDS row: 80 bytes
+// 32*FM x 32).  K is staged RBK = 64 wide (d is a multiple of 64); the next
+// slice is loaded into registers while the MFMAs of the current one run
+// from LDS, and about 46 KB of LDS per workgroup lets three share a CU.  K
+// splits over gridDim.z as in the fp32 kernel.
+constexpr int RB_N = 64;
 
 __device__ __forceinline__ void split3_bf16(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
   hi = f32_to_bf16(w);
@@ -122,58 +124,72 @@ __device__ __forceinline__ void split3_bf16(float w, uint16_t& hi, uint16_t& mid
   lo = f32_to_bf16(r2);
 }
 
-template <int FM>
+__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) {
+  return (uint32_t)a | ((uint32_t)b << 16);
+}
+
+template <int FM, int RBK>
 __global__ __launch_bounds__(256) void router_logits_bf16x3_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ w_r,
     const float* __restrict__ b_r, float* __restrict__ part, int64_t T, int d, int N) {
   constexpr int BM = 64 * FM;
-  constexpr int XL = BM * RB_K / 8 / 256;  // 16-byte x chunks per thread per stage
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][RB_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][3][RB_N][RB_LD];
+  constexpr int LD = RBK + 8;                 // LDS row, bf16 elements (16-byte aligned rows)
+  constexpr int XC = RBK / 8;                 // 16-byte x chunks per row
+  constexpr int XL = BM * XC / 256;           // x chunks per thread
+  constexpr int WC = RBK / 4;                 // float4 w chunks per row
+  constexpr int WL = RB_N * WC / 256;         // w chunks per thread
+  static_assert(XL >= 1 && WL >= 1 && (BM * XC) % 256 == 0 && (RB_N * WC) % 256 == 0, "staging");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[BM][LD];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[3][RB_N][LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t t0 = (int64_t)blockIdx.x * BM;
   const int e0 = blockIdx.y * RB_N;
 
-  uint4 xr0, xr1;  // x chunks of rows r and r + 64 (the second only when XL == 2)
-  float4 wr[2];
-  static_assert(XL == 1 || XL == 2, "x chunks per thread");
+  // staging registers as named variables (an indexed array ended up in
+  // scratch memory)
+  static_assert(XL <= 4 && WL <= 4, "staging registers");
+  uint4 xr0, xr1, xr2, xr3;
+  float4 wr0, wr1, wr2, wr3;
+#define MOE_RB_LDX(I, K0)                                                            \
+  if (XL > I) {                                                                      \
+    const int q = tid + I * 256, r = q / XC, c = (q % XC) * 8;                       \
+    const int64_t t = t0 + r < T ? t0 + r : T - 1;                                   \
+    xr##I = *(const uint4*)(x + t * d + (K0) + c);                                   \
+  }
+#define MOE_RB_LDW(I, K0)                                                            \
+  if (WL > I) {                                                                      \
+    const int q = tid + I * 256, r = q / WC, c = (q % WC) * 4;                       \
+    const int e = e0 + r;                                                            \
+    wr##I = e < N ? *(const float4*)(w_r + (int64_t)e * d + (K0) + c)                \
+                  : make_float4(0.f, 0.f, 0.f, 0.f);                                 \
+  }
+#define MOE_RB_STX(I)                                                                \
+  if (XL > I) {                                                                      \
+    const int q = tid + I * 256, r = q / XC, c = (q % XC) * 8;                       \
+    *(uint4*)&xs[r][c] = xr##I;                                                      \
+  }
+#define MOE_RB_STW(I)                                                                \
+  if (WL > I) {                                                                      \
+    const int q = tid + I * 256, r = q / WC, c = (q % WC) * 4;                       \
+    uint16_t h0, h1, h2, h3, m0, m1, m2, m3, l0, l1, l2, l3;                         \
+    split3_bf16(wr##I.x, h0, m0, l0);                                                \
+    split3_bf16(wr##I.y, h1, m1, l1);                                                \
+    split3_bf16(wr##I.z, h2, m2, l2);                                                \
+    split3_bf16(wr##I.w, h3, m3, l3);                                                \
+    *(uint2*)&ws[0][r][c] = make_uint2(pack2(h0, h1), pack2(h2, h3));                \
+    *(uint2*)&ws[1][r][c] = make_uint2(pack2(m0, m1), pack2(m2, m3));                \
+    *(uint2*)&ws[2][r][c] = make_uint2(pack2(l0, l1), pack2(l2, l3));                \
+  }
 #define MOE_RB_LOAD(K0)                                                              \
   do {                                                                               \
-    {                                                                                \
-      const int r = tid >> 2, c = (tid & 3) * 8;                                     \
-      const int64_t ta = t0 + r < T ? t0 + r : T - 1;                                \
-      xr0 = *(const uint4*)(x + ta * d + (K0) + c);                                  \
-      if (XL == 2) {                                                                 \
-        const int64_t tb = t0 + r + 64 < T ? t0 + r + 64 : T - 1;                    \
-        xr1 = *(const uint4*)(x + tb * d + (K0) + c);                                \
-      }                                                                              \
-    }                                                                                \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                  \
-      const int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;                      \
-      const int e = e0 + r;                                                          \
-      wr[i] = e < N ? *(const float4*)(w_r + (int64_t)e * d + (K0) + c)              \
-                    : make_float4(0.f, 0.f, 0.f, 0.f);                               \
-    }                                                                                \
+    MOE_RB_LDX(0, K0) MOE_RB_LDX(1, K0) MOE_RB_LDX(2, K0) MOE_RB_LDX(3, K0)          \
+    MOE_RB_LDW(0, K0) MOE_RB_LDW(1, K0) MOE_RB_LDW(2, K0) MOE_RB_LDW(3, K0)          \
   } while (0)
-#define MOE_RB_STORE(BUF)                                                            \
+#define MOE_RB_STORE()                                                               \
   do {                                                                               \
-    {                                                                                \
-      const int r = tid >> 2, c = (tid & 3) * 8;                                     \
-      *(uint4*)&xs[BUF][r][c] = xr0;                                                 \
-      if (XL == 2) *(uint4*)&xs[BUF][r + 64][c] = xr1;                               \
-    }                                                                                \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                  \
-      const int q = tid + i * 256, r = q >> 3, c = (q & 7) * 4;                      \
-      uint16_t h0, h1, h2, h3, m0, m1, m2, m3, l0, l1, l2, l3;                       \
-      split3_bf16(wr[i].x, h0, m0, l0);                                              \
-      split3_bf16(wr[i].y, h1, m1, l1);                                              \
-      split3_bf16(wr[i].z, h2, m2, l2);                                              \
-      split3_bf16(wr[i].w, h3, m3, l3);                                              \
-      *(uint2*)&ws[BUF][0][r][c] = make_uint2(h0 | ((uint32_t)h1 << 16), h2 | ((uint32_t)h3 << 16)); \
-      *(uint2*)&ws[BUF][1][r][c] = make_uint2(m0 | ((uint32_t)m1 << 16), m2 | ((uint32_t)m3 << 16)); \
-      *(uint2*)&ws[BUF][2][r][c] = make_uint2(l0 | ((uint32_t)l1 << 16), l2 | ((uint32_t)l3 << 16)); \
-    }                                                                                \
+    MOE_RB_STX(0) MOE_RB_STX(1) MOE_RB_STX(2) MOE_RB_STX(3)                          \
+    MOE_RB_STW(0) MOE_RB_STW(1) MOE_RB_STW(2) MOE_RB_STW(3)                          \
   } while (0)
 
   f32x16_t acc[FM];
@@ -182,36 +198,44 @@ __global__ __launch_bounds__(256) void router_logits_bf16x3_kernel(
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
 
-  const int nks = d / RB_K;
+  const int nks = d / RBK;
   const int k_lo = (int)(((int64_t)blockIdx.z * nks) / gridDim.z);
   const int k_hi = (int)(((int64_t)(blockIdx.z + 1) * nks) / gridDim.z);
   const int nk = k_hi - k_lo;
-  MOE_RB_LOAD(k_lo * RB_K);
-  MOE_RB_STORE(0);
-  __syncthreads();
   const int kq = (lane >> 5) * 8;
+  const int k_last = k_hi > k_lo ? k_hi - 1 : k_lo;
+  MOE_RB_LOAD((k_lo < k_last ? k_lo : k_last) * RBK);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) MOE_RB_LOAD((k_lo + kt + 1) * RB_K);
+    __syncthreads();  // the previous slice's fragments have been read
+    MOE_RB_STORE();
+    __syncthreads();
+    // next slice in flight during the MFMAs (the last step re-loads its own
+    // slice: the loads stay unconditional and the registers are not used)
+    {
+      const int kn = k_lo + kt + 1 < k_last ? k_lo + kt + 1 : k_last;
+      MOE_RB_LOAD(kn * RBK);
+    }
 #pragma unroll
-    for (int ks = 0; ks < RB_K / 16; ++ks) {
+    for (int ks = 0; ks < RBK / 16; ++ks) {
       const int kk = ks * 16 + kq;
       bf16x8_t fb[3];
 #pragma unroll
       for (int p = 0; p < 3; ++p)
-        fb[p] = __builtin_bit_cast(bf16x8_t, *(const uint4*)&ws[buf][p][wn * 32 + (lane & 31)][kk]);
+        fb[p] = __builtin_bit_cast(bf16x8_t, *(const uint4*)&ws[p][wn * 32 + (lane & 31)][kk]);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const bf16x8_t fa =
-            __builtin_bit_cast(bf16x8_t, *(const uint4*)&xs[buf][wm * 32 * FM + i * 32 + (lane & 31)][kk]);
+            __builtin_bit_cast(bf16x8_t, *(const uint4*)&xs[wm * 32 * FM + i * 32 + (lane & 31)][kk]);
 #pragma unroll
         for (int p = 0; p < 3; ++p)
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[p], acc[i], 0, 0, 0);
       }
     }
-    if (kt + 1 < nk) MOE_RB_STORE(buf ^ 1);
-    __syncthreads();
   }
+#undef MOE_RB_LDX
+#undef MOE_RB_LDW
+#undef MOE_RB_STX
+#undef MOE_RB_STW
 #undef MOE_RB_LOAD
 #undef MOE_RB_STORE
   // D layout: column (expert) = lane % 32, row (token) = 8*(v/4) + 4*(lane/32) + v%4
@@ -376,64 +400,84 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 }
 
 // --------------------------------------------------------------- stats ----
-// One block of 1024 threads.  Thread t sums, for expert e = t % N, the block
-// partials b = c, c + C, c + 2C, ... (c = t / N, C = 1024 / N chunks) in
-// increasing b; then the first N threads add the C chunk sums in order.
-// Every sum runs in a fixed order, so the result is deterministic.
-__global__ __launch_bounds__(1024) void router_stats_kernel(
-    const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt,
-    const float* __restrict__ part_z, int64_t nblk, int64_t T, int N, int K,
-    float alpha, int32_t* __restrict__ count, float* __restrict__ f,
-    float* __restrict__ p, float* __restrict__ loss) {
+// Per-expert statistics.  Block b owns experts [64 b, 64 b + 64).  Thread t
+// sums, for expert 64 b + t % 64, the block partials j = c, c + 16, ...
+// (c = t / 64) in increasing j; the first 64 threads add the 16 chunk sums
+// in order and write count, f and p; thread 0 adds the block's f_e * p_e in
+// expert order into part_fp[b].  Every sum runs in a fixed order.
+__global__ __launch_bounds__(1024) void router_stats_expert_kernel(
+    const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt, int64_t nblk,
+    int64_t T, int N, int K, int32_t* __restrict__ count, float* __restrict__ f,
+    float* __restrict__ p, float* __restrict__ part_fp) {
   __shared__ float sp[1024];
   __shared__ int64_t sc[1024];
-  __shared__ float red[1024];
-  __shared__ float rz[1024], rl[1024];
-  const int tid = threadIdx.x;
-  const int C = 1024 / N;  // N <= 1024
-  const int e = tid % N, c = tid / N;
+  __shared__ float red[64];
+  const int tid = threadIdx.x, el = tid & 63, c = tid >> 6;
+  const int e = blockIdx.x * 64 + el;
   float s = 0.f;
   int64_t cnt = 0;
-  if (c < C) {
-    for (int64_t b = c; b < nblk; b += C) {
-      s += part_p[b * N + e];
-      cnt += part_cnt[b * N + e];
+  if (e < N) {
+    for (int64_t j = c; j < nblk; j += 16) {
+      s += part_p[j * N + e];
+      cnt += part_cnt[j * N + e];
     }
   }
   sp[tid] = s;
   sc[tid] = cnt;
+  __syncthreads();
+  if (tid < 64) {
+    float st = 0.f;
+    int64_t ct = 0;
+    for (int q = 0; q < 16; ++q) {
+      st += sp[q * 64 + tid];
+      ct += sc[q * 64 + tid];
+    }
+    float fp = 0.f;
+    if (e < N) {
+      const float pe = st * (1.0f / (float)T);
+      const float fe = (float)ct * (1.0f / ((float)T * (float)K));
+      if (count) count[e] = (int32_t)ct;
+      if (f) f[e] = fe;
+      if (p) p[e] = pe;
+      fp = fe * pe;
+    }
+    red[tid] = fp;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.f;
+    for (int i = 0; i < 64; ++i) acc += red[i];
+    part_fp[blockIdx.x] = acc;
+  }
+}
+
+// Loss terms: aux = alpha * N * (sum of part_fp in block order); z and z_lse
+// from the per-token-block partials (strided sums, then a fixed tree).
+__global__ __launch_bounds__(1024) void router_stats_final_kernel(
+    const float* __restrict__ part_fp, int nfp, const float* __restrict__ part_z, int64_t nblk,
+    int64_t T, int N, float alpha, float* __restrict__ loss) {
+  __shared__ float rz[1024], rl[1024];
+  const int tid = threadIdx.x;
   float z = 0.f, zl = 0.f;
-  for (int64_t b = tid; b < nblk; b += 1024) { z += part_z[2 * b]; zl += part_z[2 * b + 1]; }
+  for (int64_t b = tid; b < nblk; b += 1024) {
+    z += part_z[2 * b];
+    zl += part_z[2 * b + 1];
+  }
   rz[tid] = z;
   rl[tid] = zl;
   __syncthreads();
-  const float invT = 1.0f / (float)T;
-  const float invTK = 1.0f / ((float)T * (float)K);
-  float fp = 0.f;
-  if (tid < N) {
-    float st = 0.f;
-    int64_t ct = 0;
-    for (int q = 0; q < C; ++q) { st += sp[q * N + tid]; ct += sc[q * N + tid]; }
-    const float pe = st * invT;
-    const float fe = (float)ct * invTK;
-    if (count) count[tid] = (int32_t)ct;
-    if (f) f[tid] = fe;
-    if (p) p[tid] = pe;
-    fp = fe * pe;
-  }
-  __syncthreads();
-  red[tid] = fp;
-  __syncthreads();
   for (int o = 512; o > 0; o >>= 1) {
     if (tid < o) {
-      red[tid] += red[tid + o];
       rz[tid] += rz[tid + o];
       rl[tid] += rl[tid + o];
     }
     __syncthreads();
   }
-  if (tid == 0 && loss) {
-    loss[0] = alpha * (float)N * red[0];
+  if (tid == 0) {
+    float aux = 0.f;
+    for (int i = 0; i < nfp; ++i) aux += part_fp[i];
+    const float invT = 1.0f / (float)T;
+    loss[0] = alpha * (float)N * aux;
     loss[1] = rz[0] * invT;
     loss[2] = rl[0] * invT;
   }
@@ -461,11 +505,11 @@ int router_tile_m(int64_t T, bool x_bf16) {
 }
 
 int router_num_splits(int64_t T, int d, int N, bool x_bf16) {
-  // aim for >= 512 workgroups, with at least 4 K steps (128 elements) per split
+  // aim for >= 512 workgroups, with at least 128 K elements per split
   const int tm = router_tile_m(T, x_bf16);
   const int64_t tiles = ((T + tm - 1) / tm) * ((N + RT_N - 1) / RT_N);
   int64_t s = (512 + tiles - 1) / tiles;
-  const int64_t max_s = d / (4 * RT_K);
+  const int64_t max_s = d / 128 > 0 ? d / 128 : 1;
   if (s > max_s) s = max_s;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
@@ -475,15 +519,16 @@ int router_num_splits(int64_t T, int d, int N, bool x_bf16) {
 hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, const float* b_r,
                                 float* part, float* logits, int64_t T, int d, int N,
                                 hipStream_t stream) {
-  static_assert(RB_N == RT_N && RB_K == RT_K, "both logit kernels tile experts and K alike");
+  static_assert(RB_N == RT_N, "both logit kernels tile experts alike");
   const int ns = router_num_splits(T, d, N, x_bf16);
   const int tm = router_tile_m(T, x_bf16);
   dim3 grid((unsigned)((T + tm - 1) / tm), (unsigned)((N + RT_N - 1) / RT_N), (unsigned)ns);
   float* out = ns == 1 ? logits : part;
+  const uint16_t* xb = (const uint16_t*)x;
   if (x_bf16 && tm == 128)
-    router_logits_bf16x3_kernel<2><<<grid, 256, 0, stream>>>((const uint16_t*)x, w_r, b_r, out, T, d, N);
+    router_logits_bf16x3_kernel<2, 64><<<grid, 256, 0, stream>>>(xb, w_r, b_r, out, T, d, N);
   else if (x_bf16)
-    router_logits_bf16x3_kernel<1><<<grid, 256, 0, stream>>>((const uint16_t*)x, w_r, b_r, out, T, d, N);
+    router_logits_bf16x3_kernel<1, 64><<<grid, 256, 0, stream>>>(xb, w_r, b_r, out, T, d, N);
   else
     router_logits_kernel<<<grid, 256, 0, stream>>>((const float*)x, w_r, b_r, out, T, d, N);
   hipError_t e = hipGetLastError();
@@ -519,12 +564,16 @@ hipError_t launch_router_topk(const float* logits, const float* b_sel, int32_t* 
 }
 
 hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
-                               const float* part_z, int64_t nblk, int64_t T,
+                               const float* part_z, float* part_fp, int64_t nblk, int64_t T,
                                int N, int K, float alpha, int32_t* count,
                                float* f, float* p, float* loss,
                                hipStream_t stream) {
-  router_stats_kernel<<<1, 1024, 0, stream>>>(part_p, part_cnt, part_z, nblk, T,
-                                              N, K, alpha, count, f, p, loss);
+  const int nfp = (N + 63) / 64;
+  router_stats_expert_kernel<<<nfp, 1024, 0, stream>>>(part_p, part_cnt, nblk, T, N, K, count,
+                                                       f, p, part_fp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !loss) return e;
+  router_stats_final_kernel<<<1, 1024, 0, stream>>>(part_fp, nfp, part_z, nblk, T, N, alpha, loss);
   return hipGetLastError();
 }
 
