@@ -377,6 +377,55 @@ def test_layer_deterministic_and_reusable():
             assert torch.equal(v.view(torch.uint8), first[k].view(torch.uint8)), k
 
 
+GRAPH_CASES = [
+    WL.scaled(WL.MIXTRAL_PREFILL, T=1200, d=128, F=256, N=4, name="mixtral_bigtile_graph"),
+    WL.scaled(WL.DEEPSEEK_DECODE, T=20, d=256, F=128, F_shared=128, N=64,
+              name="deepseek_decode_graph"),
+    WL.scaled(WL.SWITCH_TOP1, T=1500, d=256, F=512, name="switch_graph"),
+]
+
+
+@pytest.mark.parametrize("w", GRAPH_CASES, ids=lambda w: w.name)
+def test_layer_graph_replay(w):
+    """moe_layer_forward captured into a HIP graph: every replay, with eager
+    work of the program (another layer call, torch ops, synchronisations) in
+    between, matches the eager result bit for bit."""
+    say("graph", w.name)
+    inp = gpu_inputs(w)
+    cfg = api.config_for(w)
+    wst = api.weights_struct(inp)
+    eager = api.moe_layer_forward(cfg, inp, inp["x"], wstruct=wst)
+    torch.cuda.synchronize()
+    ref_out = {k: v.clone() for k, v in eager.as_dict().items() if v is not None}
+    bufs = api.LayerBuffers(cfg, torch.device(DEV))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        api.moe_layer_forward(cfg, inp, inp["x"], bufs=bufs, wstruct=wst)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.moe_layer_forward(cfg, inp, inp["x"], bufs=bufs, wstruct=wst)
+    other_x = inp["x"].flip(0).contiguous()
+    other = api.LayerBuffers(cfg, torch.device(DEV))
+    for rep in range(4):
+        for v in bufs.as_dict().values():  # poison the graph's outputs
+            if v is not None:
+                v.view(torch.uint8).fill_(0xFF)
+        g.replay()
+        api.moe_layer_forward(cfg, inp, other_x, bufs=other, wstruct=wst)  # eager work between
+        torch.cuda.synchronize()
+        for k, v in bufs.as_dict().items():
+            if v is None or k not in ref_out:
+                continue
+            if k == "row_pair":
+                tot = int(ref_out["offset"][-1])
+                assert torch.equal(v[:tot], ref_out[k][:tot]), (w.name, rep, k)
+            else:
+                assert torch.equal(v.view(torch.uint8), ref_out[k].view(torch.uint8)), (w.name, rep, k)
+
+
 FULL = [
     (WL.MIXTRAL_PREFILL, 48),
     (WL.SWITCH_TOP1, 256),
