@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=256,
+    ap.add_argument("--cpu-sample", type=int, default=2048,
                     help="tokens the oracle runs for the CPU baseline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, run one elementwise fp32 kernel that reads and "
