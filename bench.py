@@ -39,8 +39,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=2048,
-                    help="tokens the oracle runs for the CPU baseline")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="tokens the oracle runs for the CPU baseline (0: all T tokens)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, run one elementwise fp32 kernel that reads and "
                          "writes this many MiB (reference for the HBM byte counters)")
@@ -272,7 +272,7 @@ def main():
         "kept_rows": r["kept_rows"],
     }
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, r["inp"], min(a.cpu_sample, w.T))
+        line["cpu_baseline"] = cpu_baseline(w, r["inp"], min(a.cpu_sample or w.T, w.T))
     del r
     torch.cuda.empty_cache()
     if not a.no_decode:
