@@ -71,7 +71,12 @@ typedef enum {
 
 /* Limits of this build (MOE_ERR_UNSUPPORTED outside them):
  *   1 <= N <= 1024, 1 <= K <= min(N, 16), d % 64 == 0, F % 64 == 0,
- *   F_shared % 64 == 0, T <= 2^24, bf16 layers need d, F >= 64.        */
+ *   F_shared % 64 == 0, T <= 2^24, bf16 layers need d, F >= 64.
+ *   bf16 layers also need every grouped-GEMM operand addressed from one
+ *   base to fit in 4 GiB (the kernels use 32-bit byte offsets):
+ *   2*T*d < 2^32 (x) and 2*(T*K + T_shared)*max(F, F_shared) < 2^32 (the
+ *   intermediate h; T_shared = T with a shared expert), and one expert's
+ *   weight matrix 2*F*d < 2^32.                                          */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 

@@ -31,6 +31,17 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->F_shared != 0 && (c->F_shared != c->F || c->act != MOE_ACT_SWIGLU)) return MOE_ERR_UNSUPPORTED;
   if (c->T > (int64_t(1) << 24)) return MOE_ERR_UNSUPPORTED;
   if (c->T * c->K > (int64_t)INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if (c->dtype == MOE_BF16) {
+    // the grouped GEMMs address x, h and one expert's weights with 32-bit
+    // byte offsets from a single base
+    const int64_t lim = int64_t(1) << 32;
+    const int64_t fm = c->F > c->F_shared ? c->F : c->F_shared;
+    const int64_t h_rows = c->T * c->K + (c->F_shared > 0 ? c->T : 0);
+    if (2 * c->T * (int64_t)c->d >= lim) return MOE_ERR_UNSUPPORTED;
+    if (2 * h_rows * fm >= lim) return MOE_ERR_UNSUPPORTED;
+    if (2 * (int64_t)c->F * c->d >= lim || 2 * (int64_t)c->F_shared * c->d >= lim)
+      return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 

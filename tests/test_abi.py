@@ -113,6 +113,22 @@ def test_config_validation(lib, bad, code):
     assert ws_size(lib, c)[0] == code
 
 
+@pytest.mark.parametrize("shape,T_ok", [
+    (dict(d=7168, N=64, K=1, F=64), 299593),      # x: 2*T*d just under 2^32
+    (dict(d=64, N=16, K=16, F=4096), 32767),      # h: 2*T*K*F just under 2^32
+])
+def test_bf16_operand_offsets_fit_32_bits(lib, shape, T_ok):
+    """bf16 layers whose x or h would need byte offsets of 2^32 or more from
+    one base are refused; one token fewer is accepted."""
+    c = cfg_of(WL.MIXTRAL_PREFILL)
+    for k, v in shape.items():
+        setattr(c, k, v)
+    c.T = T_ok
+    assert ws_size(lib, c)[0] == L.MOE_OK
+    c.T = T_ok + 1
+    assert ws_size(lib, c)[0] == L.MOE_ERR_UNSUPPORTED
+
+
 def test_entry_points_reject_before_launch(lib):
     """Null pointers, short workspaces and bad configs return an error code
     from the host checks, so nothing is ever enqueued."""
