@@ -38,10 +38,6 @@ int num_cus() {
   return g_num_cus;
 }
 
-struct TileCfg {
-  int bm, bn, wm, wn;
-};
-
 // wg_per_cu: resident workgroups per CU the grid is sized for
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SW, bool DUAL, int EPI>
 hipError_t run_tile(const GemmArgs& a, int64_t max_tiles, hipStream_t s, int wg_per_cu = 1) {

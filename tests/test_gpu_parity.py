@@ -352,6 +352,35 @@ def test_layer_small(w):
     check_layer(w, inp, bufs)
 
 
+EXTREME = [
+    # every token to experts 3 and 11 (two groups of 1500 rows, 14 empty)
+    (WL.scaled(WL.MIXTRAL_PREFILL, T=1500, d=128, F=256, N=16, name="all_to_two"), [3, 11]),
+    # every token to expert 5 under a capacity of 78: 922 of 1000 dropped
+    (WL.scaled(WL.SWITCH_TOP1, T=1000, d=128, F=256, N=16, name="all_to_one_capped"), [5]),
+]
+
+
+@pytest.mark.parametrize("w,hot", EXTREME, ids=lambda v: getattr(v, "name", str(v)))
+def test_layer_extreme_routing(w, hot):
+    """A router bias that sends every token to the same experts: one or two
+    huge groups beside empty ones (and, with a capacity, mostly dropped
+    pairs) through routing, dispatch, the tile tables and both GEMMs."""
+    say("extreme", w.name)
+    inp = gpu_inputs(w)
+    b_r = torch.zeros(w.N, dtype=torch.float32, device=DEV)
+    if inp.get("b_r") is not None:
+        b_r += inp["b_r"]
+    for e in hot:
+        b_r[e] += 50.0
+    inp["b_r"] = b_r
+    cfg = api.config_for(w)
+    bufs = api.moe_layer_forward(cfg, inp, inp["x"], want_logits=True)
+    torch.cuda.synchronize()
+    idx = np.sort(bufs.idx.cpu().numpy(), axis=1)
+    assert (idx == np.array(sorted(hot))[None, :]).all()
+    check_layer(w, inp, bufs)
+
+
 def test_layer_deterministic_and_reusable():
     """Two launches give bitwise-identical outputs, also after the buffers
     were poisoned with NaN/garbage in between."""
