@@ -168,9 +168,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
           for (int j = 0; j < FN; ++j)
             fb[ks][j] = __builtin_bit_cast(bf16x8_t, s[brow[j] * CH + (ch ^ swz<CH, SWZ>(brow[j]))]);
         }
-        // this wave's share of stage kt+STAGES-1, issued after its fragment
-        // reads have completed
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        // this wave's share of stage kt+STAGES-1 (into the slot of stage
+        // kt-1, which every wave finished reading before the last barrier),
+        // issued while the fragment reads are still in flight
         __builtin_amdgcn_sched_barrier(0);
         issue(kt + STAGES - 1, pbuf);
         // stage kt+1 (issued STAGES-2 phases ago) must have landed before the
