@@ -57,10 +57,11 @@ hipError_t run_tile(const GemmArgs& a, int64_t max_tiles, hipStream_t s, int wg_
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int SW, bool DUAL, int EPI>
+template <int BM, int BN, int WM, int WN, int DA, int DB, bool DUAL, int EPI>
 hipError_t run_pingpong(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
-  auto kern = gemm_pingpong_kernel<BM, BN, BK, WM, WN, ST, SW, DUAL, EPI>;
-  const size_t smem = (size_t)ST * (BM + BN) * BK * 2;
+  auto kern = gemm_pingpong_kernel<BM, BN, WM, WN, DA, DB, DUAL, EPI>;
+  // DA blocks of A and DB blocks of B, 64 K-columns (128 bytes) per row
+  const size_t smem = (size_t)DA * BM * 128 + (size_t)DB * BN * 128;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -118,7 +119,8 @@ hipError_t run_kind(Kind k, const GemmArgs& a, int64_t max_tiles, hipStream_t s)
     // swizzles: (row >> 1) & 7 for 128-byte rows, (row >> 2) & 3 for 64-byte
     // rows: conflict-free fragment reads on the 64-bank LDS
     case K_SMALL:  return run_tile<64, 256, 64, 1, 4, 2, 1, DUAL, EPI>(a, max_tiles, s);
-    case K_MID:    return run_pingpong<128, 256, 32, 2, 4, 4, 2, DUAL, EPI>(a, max_tiles, s);
+    // 8 waves, 64 x 64 each (128 KB of LDS)
+    case K_MID:    return run_pingpong<128, 256, 2, 4, 2, 3, DUAL, EPI>(a, max_tiles, s);
     // small tiles for the few leftover rows of each group, two workgroups per
     // CU, K in slices of 128 (256 contiguous bytes per weight row): many
     // workgroups share the weight stream of the touched experts
@@ -126,11 +128,9 @@ hipError_t run_kind(Kind k, const GemmArgs& a, int64_t max_tiles, hipStream_t s)
     case K_TAIL:   return run_tile<32, 64, 128, 1, DUAL ? 1 : 2, 3, 0, DUAL, EPI>(a, max_tiles, s, 2);
     // the same for K not a multiple of 128
     case K_TAIL64: return run_tile<64, 64, 64, 2, DUAL ? 1 : 2, 2, 1, DUAL, EPI>(a, max_tiles, s, 1);
-    // 8 waves, 64 x 128 each, ping-pong between the two waves of each SIMD.
-    // Three 32 KB stages measured faster than four or five (DeepSeek-shaped
-    // GEMM 1: 5.5 ms with 3, 6.0 with 4); the deeper rings keep up to 4-5 MB
-    // of loads in flight per XCD, which likely crowds its 4 MB L2
-    default:       return run_pingpong<256, 256, 32, 4, 2, 3, 2, DUAL, EPI>(a, max_tiles, s);
+    // 8 waves, 64 x 128 each, ping-pong between the two waves of each SIMD;
+    // two 32 KB A blocks and three 32 KB B blocks fill the 160 KB of LDS
+    default:       return run_pingpong<256, 256, 4, 2, 2, 3, DUAL, EPI>(a, max_tiles, s);
   }
 }
 

@@ -5,18 +5,27 @@
 // (so each lane ends with runs of 4 consecutive output columns).
 //
 //  * 8 waves in two groups: waves 0-3 and waves 4-7 (one of each per SIMD).
-//    Every k-step (one BK-wide LDS stage) a wave runs a memory phase M (read
-//    the stage's MFMA fragments from LDS into registers, then issue its share
-//    of the DMA for stage kt+STAGES-1) and a compute phase C (the MFMAs on
-//    those registers).  The second group starts one s_barrier late, so on
-//    every SIMD one wave computes while the other moves data.
+//    K advances in 32-wide sub-steps.  Every sub-step a wave runs a memory
+//    phase M (read the sub-step's MFMA fragments from LDS into registers,
+//    issue its share of a DMA) and a compute phase C (the MFMAs on those
+//    registers).  The second group starts one s_barrier late, so on every
+//    SIMD one wave computes while the other moves data.
 //  * Global -> LDS with buffer_load ... lds (MUBUF, 16 bytes per lane, no
-//    staging registers); one wave instruction fills 1 KB of a stage: rows of
-//    2*BK bytes, lane l -> row l / CH, physical chunk l % CH, fetching logical
-//    chunk (l % CH) ^ swz(row) (XOR swizzle, conflict-free fragment reads).
-//  * STAGES-deep ring; loads for stage kt+STAGES-1 are issued during stage kt
-//    and waited for STAGES-2 stages later, past the end of K the last slice is
-//    re-loaded into the unused slot (drained before the epilogue).
+//    staging registers), in 64-wide K blocks: each wave instruction fetches
+//    8 rows x 128 bytes, i.e. whole 128-byte lines.  Fetching half lines (a
+//    32-wide block, 64 bytes per row) measured about half the per-CU load
+//    throughput, which the 256 x 256 tile needs in full at the MFMA rate.
+//    Lanes 0-31 take K 0..31 of the block and lanes 32-63 K 32..63, so one
+//    instruction's 1 KB of LDS is [half][8 rows][64 B] and each 32-wide
+//    sub-step reads one half.  Physical 16-byte chunk c of a row holds
+//    logical chunk c ^ ((row >> 2) & 3), which spreads the fragment reads
+//    over the banks.
+//  * A and B have separate rings of DA and DB blocks.  Sub-step 2j issues
+//    A(j+1) into the slot of A(j+1-DA); sub-step 2j+1 issues B(j+2) into the
+//    slot of B(j+2-DB) and then waits for A(j+1) and B(j+1).  With DA >= 2
+//    and DB >= 3 every overwritten slot was last read before the previous
+//    barrier, and the weights get three sub-steps of lead.  Past the end of
+//    K the last block is re-loaded (drained before the epilogue).
 //  * Persistent: one workgroup per CU walks the device-side tile table in a
 //    fixed order; each XCD walks its own contiguous range of tiles (same
 //    expert, neighbouring column tiles) that shares its L2.
@@ -39,23 +48,25 @@ __device__ __forceinline__ void buf_dma16(const void* base, uint32_t voff, void*
 #endif
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int SWZ, bool DUAL, int EPI>
+// Physical chunk of logical 16-byte chunk c in tile row r (an involution).
+__device__ __forceinline__ int pp_swz(int r) { return (r >> 2) & 3; }
+
+template <int BM, int BN, int WM, int WN, int DA, int DB, bool DUAL, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
   static_assert(WM * WN == 8, "8 waves");
+  static_assert(DA >= 2 && DB >= 3, "ring depths the slot reuse relies on");
   constexpr int NW = 8;
-  constexpr int CH = BK / 8;
-  constexpr int RB = BK * 2;
-  constexpr int RPI = 1024 / RB;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int BNo = DUAL ? BN / 2 : BN;
-  constexpr int LA = BM / (NW * RPI), LB = BN / (NW * RPI);
-  constexpr int ROWS = BM + BN;
-  constexpr int STAGE = ROWS * RB;
-  constexpr int KS = BK / 16;
-  static_assert(STAGES >= 3, "stages");
+  constexpr int LA = BM / (NW * 8), LB = BN / (NW * 8);  // DMA instructions per wave per block
+  static_assert(LA >= 1 && LB >= 1 && LA * NW * 8 == BM && LB * NW * 8 == BN, "tile rows");
+  constexpr int ASLOT = BM * 128, BSLOT = BN * 128;  // bytes of one 64-wide K block
   extern __shared__ uint4 smem[];
-  char* sbase = (char*)smem;
+  char* abuf = (char*)smem;
+  char* bbuf = abuf + DA * ASLOT;
+  const uint4* abuf4 = (const uint4*)abuf;
+  const uint4* bbuf4 = (const uint4*)bbuf;
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform, so per-wave buffer resources and LDS bases live in SGPRs
@@ -64,14 +75,21 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
   const int wm = wave / WN, wn = wave % WN;
   const int total = p.tile_base[p.G];
   const TileWalk walk = tile_walk(total);
-  const int lrow = lane / CH, pch = lane % CH;
+  // DMA lane map: K half, row within the instruction's 8, physical chunk
+  const int dh = lane >> 5, drow = (lane & 31) >> 2, dch = lane & 3;
+  const int khalf = lane >> 5;
 
-  // A fragment i of wave-row wm holds tile rows i * (32 * WM) + 32 * wm + ...:
-  // the first half of the fragments covers rows [0, BM / 2) on every wave,
-  // so a half-height tile keeps all SIMDs equally busy
-  int arow[FM], brow[FN];
+  // Fragment rows, as uint4 indices inside a slot (half 0).  A fragment i of
+  // wave-row wm holds tile rows i * (32 * WM) + 32 * wm + ...: the first half
+  // of the fragments covers rows [0, BM / 2) on every wave, so a half-height
+  // tile keeps all SIMDs equally busy.
+  int aidx[FM], asw[FM], bidx[FN], bsw[FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) arow[i] = i * (32 * WM) + wm * 32 + (lane & 31);
+  for (int i = 0; i < FM; ++i) {
+    const int r = i * (32 * WM) + wm * 32 + (lane & 31);
+    aidx[i] = (r >> 3) * 64 + (r & 7) * 4;
+    asw[i] = pp_swz(r);
+  }
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     int r;
@@ -81,9 +99,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
     } else {
       r = wn * TN + j * 32;
     }
-    brow[j] = BM + r + (lane & 31);
+    r += lane & 31;
+    bidx[j] = (r >> 3) * 64 + (r & 7) * 4;
+    bsw[j] = pp_swz(r);
   }
-  const int khalf = lane >> 5;
 
   for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
     const TileInfo ti = resolve_tile(p, tile, BM, BNo);
@@ -92,7 +111,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
     uint32_t aoff[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int r = (i * NW + wave) * RPI + lrow;
+      const int r = (i * NW + wave) * 8 + drow;
       int lr = ti.mt * BM + r;
       if (lr >= ti.M) lr = ti.M - 1;
       int64_t ar;
@@ -101,7 +120,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
         const int64_t gr = ti.row0 + lr;
         ar = p.a_rows ? (int64_t)(p.a_rows[gr] / p.a_div) : gr;
       }
-      aoff[i] = (uint32_t)((ar * p.lda + (pch ^ swz<CH, SWZ>(r)) * 8) * 2);
+      aoff[i] = (uint32_t)((ar * p.lda + dh * 32 + (dch ^ pp_swz(r)) * 8) * 2);
     }
     const char* bbase0 = (const char*)(ti.shared ? p.bs0 : p.b0 + (int64_t)ti.g * p.b_stride);
     const char* bbase1 = DUAL ? (const char*)(ti.shared ? p.bs1 : p.b1 + (int64_t)ti.g * p.b_stride)
@@ -109,30 +128,31 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
     uint32_t boff[LB];
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
-      const int r = (i * NW + wave) * RPI + lrow;
+      const int r = (i * NW + wave) * 8 + drow;
       int n = ti.nt * BNo + ((DUAL && r >= BN / 2) ? r - BN / 2 : r);
       if (n >= ti.Nout) n = ti.Nout - 1;
-      boff[i] = (uint32_t)(((int64_t)n * Kd + (pch ^ swz<CH, SWZ>(BM + r)) * 8) * 2);
+      boff[i] = (uint32_t)(((int64_t)n * Kd + dh * 32 + (dch ^ pp_swz(r)) * 8) * 2);
     }
-    const int nk = (int)(Kd / BK);
+    const int nk = (int)(Kd / 64);
     // The tile body, for a full tile or (HALF) a last tile of at most BM / 2
     // rows: then only the first half of the A loads and of the fragments run.
     auto run = [&](auto half_c) {
       constexpr bool HALF = decltype(half_c)::value;
       constexpr int FMA = HALF ? FM / 2 : FM;  // A fragments computed
-      constexpr int LAA = HALF ? LA / 2 : LA;  // A loads issued per stage
-      constexpr int NLA = LAA + LB;
-      auto issue = [&](int stage_k, int buf) {
-        const int kk = stage_k < nk ? stage_k : nk - 1;
-        char* st = sbase + buf * STAGE;
-        const uint32_t kb = (uint32_t)(kk * BK) * 2;
+      constexpr int LAA = HALF ? LA / 2 : LA;  // A loads issued per block
+      auto issue_a = [&](int blk, int slot) {
+        const uint32_t kb = (uint32_t)(blk < nk ? blk : nk - 1) * 128u;
+        char* st = abuf + slot * ASLOT;
 #pragma unroll
-        for (int i = 0; i < LAA; ++i) buf_dma16(abase, aoff[i] + kb, st + (i * NW + wave) * RPI * RB);
+        for (int i = 0; i < LAA; ++i) buf_dma16(abase, aoff[i] + kb, st + (i * NW + wave) * 1024);
+      };
+      auto issue_b = [&](int blk, int slot) {
+        const uint32_t kb = (uint32_t)(blk < nk ? blk : nk - 1) * 128u;
+        char* st = bbuf + slot * BSLOT;
 #pragma unroll
         for (int i = 0; i < LB; ++i) {
-          const int r_ = (i * NW + wave) * RPI;
-          const char* bb = (DUAL && r_ >= BN / 2) ? bbase1 : bbase0;
-          buf_dma16(bb, boff[i] + kb, st + (BM + r_) * RB);
+          const char* bb = (DUAL && (i * NW + wave) * 8 >= BN / 2) ? bbase1 : bbase0;
+          buf_dma16(bb, boff[i] + kb, st + (i * NW + wave) * 1024);
         }
       };
 
@@ -144,45 +164,28 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
 
-      // prologue: stages 0 .. STAGES-2
+      bf16x8_t fa[2][FMA], fb[2][FN];
+      auto read_fragments = [&](int sa, int sb, int h) {
+        const uint4* sA = abuf4 + sa * (ASLOT / 16) + h * 32;
+        const uint4* sB = bbuf4 + sb * (BSLOT / 16) + h * 32;
 #pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
-      wait_vmcnt<(STAGES - 2) * NLA>();  // stage 0 landed (own share)
-      __syncthreads();
-      if (grp == 1) __builtin_amdgcn_s_barrier();  // B runs one phase behind
-
-      bf16x8_t fa[KS][FMA], fb[KS][FN];
-      int buf = 0;
-      for (int kt = 0; kt < nk; ++kt) {
-        // ---- M phase: DMA share for stage kt+STAGES-1, fragments of stage kt
-        int pbuf = buf + STAGES - 1;
-        if (pbuf >= STAGES) pbuf -= STAGES;
-        const uint4* s = (const uint4*)(sbase + buf * STAGE);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < 2; ++ks) {
           const int ch = ks * 2 + khalf;
 #pragma unroll
-          for (int i = 0; i < FMA; ++i)
-            fa[ks][i] = __builtin_bit_cast(bf16x8_t, s[arow[i] * CH + (ch ^ swz<CH, SWZ>(arow[i]))]);
+          for (int i = 0; i < FMA; ++i) fa[ks][i] = __builtin_bit_cast(bf16x8_t, sA[aidx[i] + (ch ^ asw[i])]);
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            fb[ks][j] = __builtin_bit_cast(bf16x8_t, s[brow[j] * CH + (ch ^ swz<CH, SWZ>(brow[j]))]);
+          for (int j = 0; j < FN; ++j) fb[ks][j] = __builtin_bit_cast(bf16x8_t, sB[bidx[j] + (ch ^ bsw[j])]);
         }
-        // this wave's share of stage kt+STAGES-1 (into the slot of stage
-        // kt-1, which every wave finished reading before the last barrier),
-        // issued while the fragment reads are still in flight
-        __builtin_amdgcn_sched_barrier(0);
-        issue(kt + STAGES - 1, pbuf);
-        // stage kt+1 (issued STAGES-2 phases ago) must have landed before the
-        // next memory phase of either group
-        wait_vmcnt<(STAGES - 2) * NLA>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
+      };
+      // end of an M phase: fragments in registers, then the group barrier;
+      // the C phase; its closing barrier
+      auto finish_m_then_compute = [&]() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // ---- C phase
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -191,7 +194,35 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        buf = (buf + 1 == STAGES) ? 0 : buf + 1;
+      };
+
+      // prologue: B(0), A(0), B(1); block 0 landed everywhere before the loop
+      issue_b(0, 0);
+      issue_a(0, 0);
+      issue_b(1, 1);
+      wait_vmcnt<LB>();
+      __syncthreads();
+      if (grp == 1) __builtin_amdgcn_s_barrier();  // B runs one phase behind
+
+      int sa = 0, sb = 0;  // slots of block j
+      for (int j = 0; j < nk; ++j) {
+        const int sa1 = sa + 1 == DA ? 0 : sa + 1;
+        const int sb1 = sb + 1 == DB ? 0 : sb + 1;
+        const int sb2 = sb1 + 1 == DB ? 0 : sb1 + 1;
+        // ---- sub-step 2j: K 0..31 of block j; DMA share of A(j+1), issued
+        // while the fragment reads are in flight
+        read_fragments(sa, sb, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a(j + 1, sa1);
+        finish_m_then_compute();
+        // ---- sub-step 2j+1: K 32..63 of block j; DMA share of B(j+2)
+        read_fragments(sa, sb, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(j + 2, sb2);
+        wait_vmcnt<LB>();  // this wave's shares of A(j+1) and B(j+1) landed
+        finish_m_then_compute();
+        sa = sa1;
+        sb = sb1;
       }
       if (grp == 0) __builtin_amdgcn_s_barrier();  // realign with B
       wait_vmcnt<0>();

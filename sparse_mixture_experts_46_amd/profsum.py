@@ -82,7 +82,7 @@ def main():
     ap.add_argument("--out", required=True)
     ap.add_argument("--cmd", required=True)
     ap.add_argument("--probe-mib", type=int, default=1024)
-    ap.add_argument("--gemm1", default="gemm_pingpong_kernel<256, 256, 32, 4, 2, 3, 2, true, 0>")
+    ap.add_argument("--gemm1", default="gemm_pingpong_kernel<256, 256, 4, 2, 2, 3, true, 0>")
     ap.add_argument("--bench-log", help="stdout of the traced bench.py run (its JSON line)")
     a = ap.parse_args()
     os.makedirs(a.out, exist_ok=True)
