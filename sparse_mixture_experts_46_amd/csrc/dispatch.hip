@@ -29,8 +29,8 @@ constexpr int DW = DT / 32;           // 32-bit words per expert bitmap
 __device__ __forceinline__ void build_bitmap(const int32_t* __restrict__ idx,
                                              int64_t T, int N, int K,
                                              uint32_t* bm, int64_t t,
-                                             int local) {
-  for (int i = threadIdx.x; i < N * DW; i += DT) bm[i] = 0u;
+                                             int local, int nthreads) {
+  for (int i = threadIdx.x; i < N * DW; i += nthreads) bm[i] = 0u;
   __syncthreads();
   if (t < T) {
     for (int k = 0; k < K; ++k) {
@@ -43,6 +43,18 @@ __device__ __forceinline__ void build_bitmap(const int32_t* __restrict__ idx,
   __syncthreads();
 }
 
+// Slots of token t whose id is out of range or repeats an earlier slot.
+__device__ __forceinline__ int count_bad(const int32_t* __restrict__ idx, int64_t t, int N, int K) {
+  int nb = 0;
+  for (int k = 0; k < K; ++k) {
+    int e = idx[t * K + k];
+    bool bad = (e < 0) || (e >= N);
+    for (int k2 = 0; k2 < k && !bad; ++k2) bad = (idx[t * K + k2] == e);
+    nb += bad ? 1 : 0;
+  }
+  return nb;
+}
+
 __global__ __launch_bounds__(DT) void dispatch_hist_kernel(
     const int32_t* __restrict__ idx, int64_t T, int N, int K,
     int32_t* __restrict__ blk_count, int32_t* __restrict__ blk_bad) {
@@ -51,15 +63,9 @@ __global__ __launch_bounds__(DT) void dispatch_hist_kernel(
   const int local = threadIdx.x;
   const int64_t t = (int64_t)blockIdx.x * DT + local;
   if (local == 0) nbad = 0;
-  build_bitmap(idx, T, N, K, bm, t, local);
+  build_bitmap(idx, T, N, K, bm, t, local, DT);
   if (t < T) {
-    int mybad = 0;
-    for (int k = 0; k < K; ++k) {
-      int e = idx[t * K + k];
-      bool bad = (e < 0) || (e >= N);
-      for (int k2 = 0; k2 < k && !bad; ++k2) bad = (idx[t * K + k2] == e);
-      mybad += bad ? 1 : 0;
-    }
+    const int mybad = count_bad(idx, t, N, K);
     if (mybad) atomicAdd(&nbad, mybad);  // integer: order-independent
   }
   for (int e = local; e < N; e += DT) {
@@ -70,6 +76,43 @@ __global__ __launch_bounds__(DT) void dispatch_hist_kernel(
   }
   __syncthreads();
   if (local == 0) blk_bad[blockIdx.x] = nbad;
+}
+
+// Exclusive scan of skept[0..N) (N <= 1024) by a block of 1024 threads, with
+// scan[] as LDS scratch: offset[e] (global) and, if soff is given, the same
+// in LDS; offset[N] = the total, which every thread gets back.
+__device__ __forceinline__ int32_t scan_kept(const int32_t* skept, int32_t* scan, int N,
+                                             int32_t* __restrict__ offset, int32_t* soff) {
+  const int tid = threadIdx.x;
+  const int32_t v = tid < N ? skept[tid] : 0;
+  scan[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int32_t add = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  if (tid < N) {
+    offset[tid] = scan[tid] - v;
+    if (soff) soff[tid] = scan[tid] - v;
+  }
+  const int32_t total = scan[1023];
+  if (tid == 0) offset[N] = total;
+  __syncthreads();
+  return total;
+}
+
+// counters = {kept rows, dropped pairs, bad ids, touched experts}
+__device__ __forceinline__ void write_counters(int32_t* __restrict__ counters, int32_t total,
+                                               int64_t T, int K, int64_t bad,
+                                               const int32_t* skept, int N) {
+  int touched = 0;
+  for (int e = 0; e < N; ++e) touched += skept[e] > 0 ? 1 : 0;
+  counters[0] = total;
+  counters[1] = (int32_t)(T * K - total);
+  counters[2] = (int32_t)bad;
+  counters[3] = touched;
 }
 
 // One block of 1024 threads: per-expert exclusive scan over blocks (token
@@ -94,43 +137,23 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     if (kept_out) kept_out[e] = kp;
   }
   __syncthreads();
-  // exclusive scan of skept[0..N) ; N <= 1024 so one element per thread
-  int32_t v = tid < N ? skept[tid] : 0;
-  scan[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int32_t add = tid >= o ? scan[tid - o] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  if (tid < N) offset[tid] = scan[tid] - v;
-  if (tid == 0) {
-    int32_t total = scan[1023];
-    offset[N] = total;
-    if (counters) {
-      int64_t bad = 0;
-      for (int64_t b = 0; b < nblk; ++b) bad += blk_bad[b];
-      int touched = 0;
-      for (int e = 0; e < N; ++e) touched += skept[e] > 0 ? 1 : 0;
-      counters[0] = total;
-      counters[1] = (int32_t)(T * K - total);
-      counters[2] = (int32_t)bad;
-      counters[3] = touched;
-    }
+  const int32_t total = scan_kept(skept, scan, N, offset, nullptr);
+  if (tid == 0 && counters) {
+    int64_t bad = 0;
+    for (int64_t b = 0; b < nblk; ++b) bad += blk_bad[b];
+    write_counters(counters, total, T, K, bad, skept, N);
   }
 }
 
-__global__ __launch_bounds__(DT) void dispatch_assign_kernel(
-    const int32_t* __restrict__ idx, int64_t T, int N, int K, int64_t cap,
-    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ offset,
-    int32_t* __restrict__ pair_row, int32_t* __restrict__ row_pair,
-    uint8_t* __restrict__ dropped) {
-  extern __shared__ uint32_t bm[];
-  const int local = threadIdx.x;
-  const int64_t t = (int64_t)blockIdx.x * DT + local;
-  build_bitmap(idx, T, N, K, bm, t, local);
-  if (t >= T) return;
+// Rows of token t's slots: rank among the tokens that chose the expert =
+// base[e] (earlier blocks; 0 if base is null) + the bits of this block's
+// bitmap below the token; kept iff rank < cap, at row off[e] + rank.
+__device__ __forceinline__ void assign_token(const int32_t* __restrict__ idx, int64_t t,
+                                             int local, int N, int K, int64_t cap,
+                                             const uint32_t* bm, const int32_t* base,
+                                             const int32_t* off, int32_t* __restrict__ pair_row,
+                                             int32_t* __restrict__ row_pair,
+                                             uint8_t* __restrict__ dropped) {
   const int w = local >> 5;
   const uint32_t below = (1u << (local & 31)) - 1u;
   for (int k = 0; k < K; ++k) {
@@ -143,15 +166,65 @@ __global__ __launch_bounds__(DT) void dispatch_assign_kernel(
       int r = 0;
       for (int w2 = 0; w2 < w; ++w2) r += __popc(bm[e * DW + w2]);
       r += __popc(bm[e * DW + w] & below);
-      int64_t rank = (int64_t)blk_base[(int64_t)blockIdx.x * N + e] + r;
+      int64_t rank = (int64_t)(base ? base[e] : 0) + r;
       if (rank < cap) {
-        row = offset[e] + (int32_t)rank;
+        row = off[e] + (int32_t)rank;
         row_pair[row] = (int32_t)pr;
       }
     }
     pair_row[pr] = row;
     if (dropped) dropped[pr] = row < 0 ? 1 : 0;
   }
+}
+
+__global__ __launch_bounds__(DT) void dispatch_assign_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int N, int K, int64_t cap,
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ offset,
+    int32_t* __restrict__ pair_row, int32_t* __restrict__ row_pair,
+    uint8_t* __restrict__ dropped) {
+  extern __shared__ uint32_t bm[];
+  const int local = threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * DT + local;
+  build_bitmap(idx, T, N, K, bm, t, local, DT);
+  if (t >= T) return;
+  assign_token(idx, t, local, N, K, cap, bm, blk_base + (int64_t)blockIdx.x * N, offset, pair_row,
+               row_pair, dropped);
+}
+
+// All of the above in one block of 1024 threads when every token fits one
+// dispatch block (T <= DT): the bitmap is built once, block bases are zero,
+// and the offsets stay in LDS for the assignment.  Saves two launches on
+// decode-sized batches.
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int N, int K, int64_t cap,
+    int32_t* __restrict__ kept_out, int32_t* __restrict__ offset,
+    int32_t* __restrict__ counters, int32_t* __restrict__ pair_row,
+    int32_t* __restrict__ row_pair, uint8_t* __restrict__ dropped) {
+  extern __shared__ uint32_t bm[];
+  __shared__ int32_t skept[kMaxExperts];
+  __shared__ int32_t soff[kMaxExperts];
+  __shared__ int32_t scan[1024];
+  __shared__ int nbad;
+  const int local = threadIdx.x;
+  const int64_t t = local < DT ? (int64_t)local : T;  // threads past DT: no token
+  if (local == 0) nbad = 0;
+  build_bitmap(idx, T, N, K, bm, t, local, 1024);
+  if (t < T) {
+    const int mybad = count_bad(idx, t, N, K);
+    if (mybad) atomicAdd(&nbad, mybad);  // integer: order-independent
+  }
+  for (int e = local; e < N; e += 1024) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < DW; ++w) c += __popc(bm[e * DW + w]);
+    const int32_t kp = (int64_t)c < cap ? c : (int32_t)cap;
+    skept[e] = kp;
+    if (kept_out) kept_out[e] = kp;
+  }
+  __syncthreads();
+  const int32_t total = scan_kept(skept, scan, N, offset, soff);
+  if (local == 0 && counters) write_counters(counters, total, T, K, nbad, skept, N);
+  if (t < T) assign_token(idx, t, local, N, K, cap, bm, nullptr, soff, pair_row, row_pair, dropped);
 }
 
 // x_perm[r] = x[row_pair[r] / K] for r < offset[N]; 16-byte chunks.
@@ -181,6 +254,11 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int N, int K,
   const int64_t nblk = dispatch_num_blocks(T);
   const size_t smem = (size_t)N * DW * sizeof(uint32_t);
   const int64_t cap = capacity < 0 ? T : capacity;
+  if (nblk == 1) {
+    dispatch_small_kernel<<<1, 1024, smem, stream>>>(idx, T, N, K, cap, kept, offset, counters,
+                                                     pair_row, row_pair, dropped);
+    return hipGetLastError();
+  }
   dispatch_hist_kernel<<<(unsigned)nblk, DT, smem, stream>>>(idx, T, N, K, blk_count, blk_bad);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -152,8 +152,19 @@ moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void
                        void* ws, hipStream_t s) {
   const RouterWs L = router_ws(c);
   float* lg = logits ? logits : at<float>(ws, L.logits);
-  hipError_t e = launch_router_logits(x, c->dtype == MOE_BF16, w->w_r, w->b_r,
-                                      at<float>(ws, L.split), lg, c->T, c->d, c->N, s);
+  const bool bf16 = c->dtype == MOE_BF16;
+  if (router_small_path(c->T, c->N)) {
+    hipError_t e = launch_router_logits(x, bf16, w->w_r, w->b_r, at<float>(ws, L.split), lg, c->T,
+                                        c->d, c->N, s, /*reduce_splits=*/false);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = launch_router_small(at<float>(ws, L.split), router_num_splits(c->T, c->d, c->N, bf16),
+                            w->b_r, w->b_sel, lg, idx, gate, c->T, c->N, c->K, c->gate,
+                            c->aux_alpha, st ? st->count : nullptr, st ? st->f : nullptr,
+                            st ? st->p : nullptr, st ? st->loss : nullptr, s);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
+  hipError_t e = launch_router_logits(x, bf16, w->w_r, w->b_r, at<float>(ws, L.split), lg, c->T,
+                                      c->d, c->N, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_router_topk(lg, w->b_sel, idx, gate, at<float>(ws, L.part_p),
                          at<int32_t>(ws, L.part_cnt), at<float>(ws, L.part_z), c->T, c->N, c->K,

@@ -18,17 +18,28 @@ int64_t router_num_blocks(int64_t T);
 int router_num_splits(int64_t T, int d, int N, bool x_bf16);
 
 // logits = x W_r^T + b_r.  With several K splits the partial products go to
-// part [splits, T, N] and a reduction writes logits; with one split the
-// logits are written directly (part unused).
+// part [splits, T, N] and (reduce_splits) a reduction writes logits; with one
+// split the logits are written directly (part unused).
 hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, const float* b_r,
                                 float* part, float* logits, int64_t T, int d, int N,
-                                hipStream_t stream);
+                                hipStream_t stream, bool reduce_splits = true);
 
 // Selection, gates and per-block partial statistics:
 //   part_p [nblk, N] fp32, part_cnt [nblk, N] int32, part_z [nblk, 2] fp32
 hipError_t launch_router_topk(const float* logits, const float* b_sel, int32_t* idx, float* gate,
                               float* part_p, int32_t* part_cnt, float* part_z, int64_t T, int N,
                               int K, int gate_mode, hipStream_t stream);
+
+// Small batches (router_small_path): one workgroup reduces the logit splits
+// (part from launch_router_logits without its reduction; nsplit =
+// router_num_splits), selects, gates and writes the statistics.  Null
+// count / f / p / loss are skipped.
+constexpr int64_t kRouterSmallT = 64;
+bool router_small_path(int64_t T, int N);
+hipError_t launch_router_small(const float* part, int nsplit, const float* b_r, const float* b_sel,
+                               float* logits, int32_t* idx, float* gate, int64_t T, int N, int K,
+                               int gate_mode, float alpha, int32_t* count, float* f, float* p,
+                               float* loss, hipStream_t stream);
 
 // part_fp: [ceil(N / 64)] fp32 scratch (per-expert-block sums of f_e * p_e)
 hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,

@@ -277,6 +277,83 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// One token's softmax statistics, top-K selection and gates, computed by
+// one wave: lane l holds the logits of experts l, l + 64, ... in l[].  Adds
+// the token's probabilities to pacc, its sum of squared logits to zsum and
+// its squared log-sum-exp to lsum; writes K ids and gates; counts each
+// chosen expert in scnt (LDS, integer atomics).
+template <int NJ>
+__device__ __forceinline__ void topk_one_token(const float (&l)[NJ], const float (&bsel)[NJ],
+                                               int lane, int N, int K, int gate_mode,
+                                               float (&pacc)[NJ], float& zsum, float& lsum,
+                                               int32_t* __restrict__ idx_t,
+                                               float* __restrict__ gate_t, int32_t* scnt) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) m = fmaxf(m, l[j]);
+  m = wave_max(m);
+  float ssum = 0.f, sq = 0.f;
+  float ex[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    int e = lane + 64 * j;
+    ex[j] = (e < N) ? expf(l[j] - m) : 0.f;
+    ssum += ex[j];
+    sq += (e < N) ? l[j] * l[j] : 0.f;
+  }
+  ssum = wave_sum(ssum);
+  sq = wave_sum(sq);
+  const float inv = 1.0f / ssum;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) pacc[j] += ex[j] * inv;
+  const float lse = m + logf(ssum);
+  zsum += sq;
+  lsum += lse * lse;
+
+  // K rounds of arg-max over the not-yet-taken experts
+  uint32_t taken = 0;
+  float my_l = 0.f;  // lane k keeps the logit of its chosen expert
+  int my_e = 0;
+  float lmax_sel = -INFINITY;
+  for (int r = 0; r < K; ++r) {
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      int e = lane + 64 * j;
+      if (e < N && !((taken >> j) & 1u)) {
+        unsigned long long key =
+            ((unsigned long long)order_key(l[j] + bsel[j]) << 32) |
+            (unsigned long long)(0xffffffffu - (uint32_t)e);
+        best = key > best ? key : best;
+      }
+    }
+    best = wave_max_u64(best);
+    const int ew = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+    const int jw = ew >> 6;
+    float cand = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) cand = (j == jw) ? l[j] : cand;
+    const float lw = __shfl(cand, ew & 63, MOE_WAVE);
+    if (lane == (ew & 63)) taken |= 1u << jw;
+    if (lane == r) { my_l = lw; my_e = ew; }
+    lmax_sel = fmaxf(lmax_sel, lw);
+    if (lane == 0) atomicAdd(&scnt[ew], 1);  // integer: order-independent
+  }
+  // gates
+  float g;
+  if (gate_mode == 2) {  // softmax over all N, not renormalised
+    g = expf(my_l - m) * inv;
+  } else {  // renormalised over the chosen K (both forms are equal)
+    float ek = (lane < K) ? expf(my_l - lmax_sel) : 0.f;
+    float den = wave_sum(ek);
+    g = ek / den;
+  }
+  if (lane < K) {
+    idx_t[lane] = my_e;
+    gate_t[lane] = g;
+  }
+}
+
 template <int NJ>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ logits, const float* __restrict__ b_sel,
@@ -308,74 +385,13 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     const int64_t t = tb0 + (int64_t)wave * per_wave + i;
     if (t >= T) break;
     float l[NJ];
-    float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       int e = lane + 64 * j;
       l[j] = (e < N) ? logits[t * N + e] : -INFINITY;
-      m = fmaxf(m, l[j]);
     }
-    m = wave_max(m);
-    float ssum = 0.f, sq = 0.f;
-    float ex[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      int e = lane + 64 * j;
-      ex[j] = (e < N) ? expf(l[j] - m) : 0.f;
-      ssum += ex[j];
-      sq += (e < N) ? l[j] * l[j] : 0.f;
-    }
-    ssum = wave_sum(ssum);
-    sq = wave_sum(sq);
-    const float inv = 1.0f / ssum;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) pacc[j] += ex[j] * inv;
-    const float lse = m + logf(ssum);
-    zsum += sq;
-    lsum += lse * lse;
-
-    // K rounds of arg-max over the not-yet-taken experts
-    uint32_t taken = 0;
-    float my_l = 0.f;  // lane k keeps the logit of its chosen expert
-    int my_e = 0;
-    float lmax_sel = -INFINITY;
-    for (int r = 0; r < K; ++r) {
-      unsigned long long best = 0ull;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        int e = lane + 64 * j;
-        if (e < N && !((taken >> j) & 1u)) {
-          unsigned long long key =
-              ((unsigned long long)order_key(l[j] + bsel[j]) << 32) |
-              (unsigned long long)(0xffffffffu - (uint32_t)e);
-          best = key > best ? key : best;
-        }
-      }
-      best = wave_max_u64(best);
-      const int ew = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-      const int jw = ew >> 6;
-      float cand = 0.f;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) cand = (j == jw) ? l[j] : cand;
-      const float lw = __shfl(cand, ew & 63, MOE_WAVE);
-      if (lane == (ew & 63)) taken |= 1u << jw;
-      if (lane == r) { my_l = lw; my_e = ew; }
-      lmax_sel = fmaxf(lmax_sel, lw);
-      if (lane == 0) atomicAdd(&scnt[ew], 1);  // integer: order-independent
-    }
-    // gates
-    float g;
-    if (gate_mode == 2) {  // softmax over all N, not renormalised
-      g = expf(my_l - m) * inv;
-    } else {  // renormalised over the chosen K (both forms are equal)
-      float ek = (lane < K) ? expf(my_l - lmax_sel) : 0.f;
-      float den = wave_sum(ek);
-      g = ek / den;
-    }
-    if (lane < K) {
-      idx[t * K + lane] = my_e;
-      gate[t * K + lane] = g;
-    }
+    topk_one_token<NJ>(l, bsel, lane, N, K, gate_mode, pacc, zsum, lsum, idx + t * K, gate + t * K,
+                       scnt);
   }
   // fixed-order reduction of the block's partial sums
 #pragma unroll
@@ -483,6 +499,94 @@ __global__ __launch_bounds__(1024) void router_stats_final_kernel(
   }
 }
 
+
+// ------------------------------------------------------- small batches ----
+// Everything after the logit GEMM in one workgroup of 16 waves, for small T:
+// the sum of the logit splits (same order as router_split_reduce_kernel),
+// top-K and gates (topk_one_token), and the statistics.  Wave w takes tokens
+// w, w + 16, ...; the per-expert probability sums and the z terms are then
+// added over the waves in wave order, f_e * p_e over experts in expert
+// order.  Saves four launches on decode-sized batches.
+template <int NJ>
+__global__ __launch_bounds__(1024) void router_small_kernel(
+    const float* __restrict__ part, int nsplit, const float* __restrict__ b_r,
+    const float* __restrict__ b_sel, float* __restrict__ logits, int32_t* __restrict__ idx,
+    float* __restrict__ gate, int64_t T, int N, int K, int gate_mode, float alpha,
+    int32_t* __restrict__ count, float* __restrict__ f, float* __restrict__ p,
+    float* __restrict__ loss) {
+  extern __shared__ unsigned char smem_raw[];
+  float* sp = (float*)smem_raw;                  // [16][N] per-wave prob sums
+  int32_t* scnt = (int32_t*)(sp + 16 * N);       // [N] counts
+  float* sfp = (float*)(scnt + N);               // [N] f_e * p_e
+  float* sz = sfp + N;                           // [16][2]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < N; e += 1024) scnt[e] = 0;
+  __syncthreads();
+
+  float pacc[NJ], bsel[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    pacc[j] = 0.f;
+    const int e = lane + 64 * j;
+    bsel[j] = (b_sel && e < N) ? b_sel[e] : 0.f;
+  }
+  float zsum = 0.f, lsum = 0.f;
+  const int64_t n = T * (int64_t)N;
+  for (int64_t t = wave; t < T; t += 16) {
+    float l[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      if (e < N) {
+        const int64_t i = t * N + e;
+        if (nsplit > 1) {
+          float acc = part[i];
+          for (int z = 1; z < nsplit; ++z) acc += part[(int64_t)z * n + i];
+          l[j] = acc + (b_r ? b_r[e] : 0.f);
+          logits[i] = l[j];
+        } else {
+          l[j] = logits[i];
+        }
+      } else {
+        l[j] = -INFINITY;
+      }
+    }
+    topk_one_token<NJ>(l, bsel, lane, N, K, gate_mode, pacc, zsum, lsum, idx + t * K, gate + t * K,
+                       scnt);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    if (e < N) sp[wave * N + e] = pacc[j];
+  }
+  if (lane == 0) { sz[wave * 2] = zsum; sz[wave * 2 + 1] = lsum; }
+  __syncthreads();
+  for (int e = tid; e < N; e += 1024) {
+    float st = 0.f;
+    for (int w = 0; w < 16; ++w) st += sp[w * N + e];
+    const int32_t ct = scnt[e];
+    const float pe = st * (1.0f / (float)T);
+    const float fe = (float)ct * (1.0f / ((float)T * (float)K));
+    if (count) count[e] = ct;
+    if (f) f[e] = fe;
+    if (p) p[e] = pe;
+    sfp[e] = fe * pe;
+  }
+  __syncthreads();
+  if (tid == 0 && loss) {
+    float aux = 0.f;
+    for (int e = 0; e < N; ++e) aux += sfp[e];
+    float z = 0.f, zl = 0.f;
+    for (int w = 0; w < 16; ++w) {
+      z += sz[2 * w];
+      zl += sz[2 * w + 1];
+    }
+    const float invT = 1.0f / (float)T;
+    loss[0] = alpha * (float)N * aux;
+    loss[1] = z * invT;
+    loss[2] = zl * invT;
+  }
+}
 }  // namespace
 
 int router_tokens_per_block(int64_t T) {
@@ -518,7 +622,7 @@ int router_num_splits(int64_t T, int d, int N, bool x_bf16) {
 
 hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, const float* b_r,
                                 float* part, float* logits, int64_t T, int d, int N,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool reduce_splits) {
   static_assert(RB_N == RT_N, "both logit kernels tile experts alike");
   const int ns = router_num_splits(T, d, N, x_bf16);
   const int tm = router_tile_m(T, x_bf16);
@@ -532,7 +636,7 @@ hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, co
   else
     router_logits_kernel<<<grid, 256, 0, stream>>>((const float*)x, w_r, b_r, out, T, d, N);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ns == 1) return e;
+  if (e != hipSuccess || ns == 1 || !reduce_splits) return e;
   int64_t n = T * (int64_t)N;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
@@ -574,6 +678,27 @@ hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !loss) return e;
   router_stats_final_kernel<<<1, 1024, 0, stream>>>(part_fp, nfp, part_z, nblk, T, N, alpha, loss);
+  return hipGetLastError();
+}
+
+bool router_small_path(int64_t T, int N) { return T <= kRouterSmallT && N <= 256; }
+
+hipError_t launch_router_small(const float* part, int nsplit, const float* b_r, const float* b_sel,
+                               float* logits, int32_t* idx, float* gate, int64_t T, int N, int K,
+                               int gate_mode, float alpha, int32_t* count, float* f, float* p,
+                               float* loss, hipStream_t stream) {
+  const size_t smem = (size_t)18 * N * sizeof(float) + 32 * sizeof(float);
+  const int nj = (N + 63) / 64;
+#define MOE_SMALL_CASE(NJV)                                                                    \
+  case NJV:                                                                                    \
+    router_small_kernel<NJV><<<1, 1024, smem, stream>>>(part, nsplit, b_r, b_sel, logits, idx, \
+        gate, T, N, K, gate_mode, alpha, count, f, p, loss);                                  \
+    break;
+  switch (nj) {
+    MOE_SMALL_CASE(1) MOE_SMALL_CASE(2) MOE_SMALL_CASE(3) MOE_SMALL_CASE(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_SMALL_CASE
   return hipGetLastError();
 }
 
