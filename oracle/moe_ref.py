@@ -19,12 +19,15 @@ The pages it follows (cited by title and section):
         the ascending token list to capacity, gate-weighted accumulation).
   [P4]  learnagent.wiki "混合专家模型（Mixture of Experts, MoE）":
         结构 2 (G(x) = Softmax(W_r x)), 结构 3 (y = sum over top-K of
-        G_i E_i), 结构 4 (selection-only per-expert bias), 运行示例 (softmax,
-        top-K on probabilities, renormalise, GELU experts, compute all
-        experts then gather).
+        G_i E_i), 结构 4 (selection-only per-expert bias; the auxiliary-loss-
+        free method adjusts that bias by how often each expert is chosen),
+        运行示例 (softmax, top-K on probabilities, renormalise, GELU experts,
+        compute all experts then gather).
   [P5]  mstx.cn/posts/467.html "MoE 如何替代 FFN？它解决了什么问题？带来哪些新挑战？":
         section 1 (FFN(x) = W2 act(W1 x)), section 2 (MoE(x) formula),
-        section 5 (DeepSeek-MoE: fine-grained experts plus a shared expert).
+        section 5 (DeepSeek-MoE: fine-grained experts plus a shared expert),
+        the challenges list (expert usage and routing entropy are what a
+        training run monitors).
 
 Readings taken where the pages are silent or disagree are listed next to the
 function that takes them.
@@ -153,6 +156,7 @@ class RouterStats:
     aux: float          # alpha * N * sum f*p
     z: float            # mean_t sum_e logits^2
     z_lse: float        # mean_t logsumexp(logits_t)^2  (not from the pages)
+    entropy: float      # mean_t of the entropy of softmax(logits_t)
 
 
 def router_stats(logits: np.ndarray, idx: np.ndarray, alpha: float) -> RouterStats:
@@ -179,7 +183,54 @@ def router_stats(logits: np.ndarray, idx: np.ndarray, alpha: float) -> RouterSta
     z = float(np.mean(np.sum(logits * logits, axis=1)))
     lse = logsumexp_rows(logits)
     z_lse = float(np.mean(lse * lse))
-    return RouterStats(count=count, f=f, p=p, aux=aux, z=z, z_lse=z_lse)
+    entropy = routing_entropy(logits)
+    return RouterStats(count=count, f=f, p=p, aux=aux, z=z, z_lse=z_lse, entropy=entropy)
+
+
+def routing_entropy(logits: np.ndarray) -> float:
+    """Mean over tokens of the entropy of the token's routing distribution,
+    H_t = -sum_e P_te log P_te with P_t = softmax(logits_t).  [P5] lists
+    routing entropy among what a training run monitors and gives no formula;
+    this per-token mean is the plain reading (0 = every token certain of one
+    expert, log N = uniform).  Terms with P = 0 contribute 0."""
+    P = softmax_rows(np.asarray(logits, dtype=np.float64))
+    T = P.shape[0]
+    total = 0.0
+    for t in range(T):
+        row = P[t]
+        nz = row[row > 0]
+        total += float(-np.sum(nz * np.log(nz)))
+    return total / T
+
+
+def noisy_logits(logits: np.ndarray, noise: np.ndarray, noise_std: float) -> np.ndarray:
+    """Training-time router noise, [P3] 三 (MoERouter.forward): a standard
+    normal draw per (token, expert), scaled by noise_std, is added to the
+    logits; top-K, the gates and the load-balance loss then all use the noisy
+    logits.  The draws are an input here (the caller's generator), so both
+    sides see the same numbers."""
+    return np.asarray(logits, np.float64) + float(noise_std) * np.asarray(noise, np.float64)
+
+
+def bias_update(b_sel, count: np.ndarray, T: int, K: int, rate: float) -> np.ndarray:
+    """Auxiliary-loss-free balancing, [P4] 结构 4: the selection-only bias is
+    not trained by gradients but moved after each step by how often its
+    expert was chosen; an expert chosen too little gets a larger bias.
+
+    Reading (the page gives neither the comparison nor the step): "too
+    little" and "too much" are measured against the mean load T*K/N, and the
+    bias moves by a fixed step `rate` up or down (the sign rule of the
+    DeepSeek-V3 report the page cites); an expert exactly at the mean keeps
+    its bias.  count = pairs that chose the expert, before capacity."""
+    count = np.asarray(count, dtype=np.int64)
+    N = count.shape[0]
+    b = np.zeros(N) if b_sel is None else np.asarray(b_sel, np.float64).copy()
+    for e in range(N):
+        # compare count_e with T*K/N without rounding: count_e*N vs T*K
+        diff = T * K - int(count[e]) * N
+        step = 1.0 if diff > 0 else (-1.0 if diff < 0 else 0.0)
+        b[e] = b[e] + rate * step
+    return b
 
 
 # -------------------------------------------------------------- capacity ---
@@ -322,7 +373,8 @@ def combine(y_perm, pair_row, gates, T, d, y_shared=None):
 
 @dataclass
 class LayerResult:
-    logits: np.ndarray
+    logits: np.ndarray        # router output x W_r^T + b_r (before any noise)
+    logits_used: np.ndarray   # what selection, gates and statistics see
     idx: np.ndarray
     margin: np.ndarray
     gates: np.ndarray
@@ -336,7 +388,7 @@ class LayerResult:
 
 def layer_forward(x, W, *, K, act, gate_mode, cf=None, alpha=1.0,
                   b_r=None, b_sel=None, shared=None, tokens=None,
-                  experts_needed=True):
+                  experts_needed=True, noise=None, noise_std=0.0):
     """Whole layer, in the order the pages give it: router logits, selection
     (scores + optional selection-only bias, [P4] 结构 4), gates (from the raw
     logits only), statistics, capacity and dispatch, per-expert FFN, shared
@@ -348,19 +400,22 @@ def layer_forward(x, W, *, K, act, gate_mode, cf=None, alpha=1.0,
     tokens: optional list of token ids; routing/dispatch/stats are always
     computed for all T tokens, but the expert FFN and combine only for these
     tokens (y rows of other tokens are NaN).
+    noise: optional [T, N] standard-normal draws; with it the router works on
+    noisy_logits(logits, noise, noise_std) from selection on.
     """
     x = np.asarray(x, dtype=np.float64)
     T, d = x.shape
     N = W["w_r"].shape[0]
     logits = router_logits(x, W["w_r"], b_r)
-    scores = logits if b_sel is None else logits + np.asarray(b_sel, np.float64)[None, :]
+    used = logits if noise is None else noisy_logits(logits, noise, noise_std)
+    scores = used if b_sel is None else used + np.asarray(b_sel, np.float64)[None, :]
     idx, margin = select_topk(scores, K)
-    gates = gate_weights(logits, idx, gate_mode)
-    stats = router_stats(logits, idx, alpha)
+    gates = gate_weights(used, idx, gate_mode)
+    stats = router_stats(used, idx, alpha)
     cap = capacity(K, N, T, cf)
     asg = assign_capacity(idx, N, cap)
     if not experts_needed:
-        return LayerResult(logits, idx, margin, gates, stats, cap, asg, None, None, None)
+        return LayerResult(logits, used, idx, margin, gates, stats, cap, asg, None, None, None)
     if tokens is None:
         y_perm = expert_outputs(act, x, asg, W, N, K)
         y_shared = None if shared is None else expert_swiglu(
@@ -391,7 +446,7 @@ def layer_forward(x, W, *, K, act, gate_mode, cf=None, alpha=1.0,
                 if (int(t), k) in term:
                     acc = acc + gates[t, k] * term[(int(t), k)]
             y[t] = acc
-    return LayerResult(logits, idx, margin, gates, stats, cap, asg, y_perm, y_shared, y)
+    return LayerResult(logits, used, idx, margin, gates, stats, cap, asg, y_perm, y_shared, y)
 
 
 def brute_force_layer(x, W, *, K, act, gate_mode, cf=None, b_r=None,

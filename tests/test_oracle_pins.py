@@ -385,3 +385,109 @@ def test_bf16_decoding():
     assert abs(v[2] - 3.140625) == 0.0
     assert v[5] == float.fromhex("0x1.fep127")
     assert v[6] == 2.0 ** -133
+
+
+# ------------------------------------------- router training variants pins
+
+def test_entropy_closed_forms():
+    """Uniform logits: H = ln N.  Two experts with P = (1/4, 3/4):
+    H = -(1/4 ln 1/4 + 3/4 ln 3/4).  One dominant expert: H -> 0."""
+    for N in (2, 8, 256):
+        lg = np.full((3, N), 0.7)
+        assert abs(ref.routing_entropy(lg) - math.log(N)) < 1e-13
+    lg = np.array([[0.2, 0.2 + math.log(3.0)]])
+    want = -(0.25 * math.log(0.25) + 0.75 * math.log(0.75))
+    assert abs(ref.routing_entropy(lg) - want) < 1e-15
+    lg = np.array([[0.0, -60.0, -60.0, -60.0]])
+    assert ref.routing_entropy(lg) < 1e-23
+
+
+def test_entropy_matches_scipy():
+    """Against scipy.stats.entropy of scipy.special.softmax rows (an
+    independent library route: different softmax, different entropy sum)."""
+    import scipy.special
+    import scipy.stats
+    r = rng(41)
+    lg = r.normal(size=(50, 37)) * 3.0
+    want = float(np.mean(scipy.stats.entropy(scipy.special.softmax(lg, axis=1), axis=1)))
+    assert abs(ref.routing_entropy(lg) - want) < 1e-12
+    st = ref.router_stats(lg, ref.select_topk(lg, 4)[0], 1.0)
+    assert st.entropy == ref.routing_entropy(lg)
+
+
+def test_noise_zero_is_the_clean_router():
+    r = rng(42)
+    T, N, d, K = 40, 16, 32, 3
+    x = r.normal(size=(T, d))
+    W, _ = rand_weights(r, N, d, 64, "swiglu")
+    clean = ref.layer_forward(x, W, K=K, act="swiglu", gate_mode="softmax_topk",
+                              experts_needed=False)
+    for noise, std in [(np.zeros((T, N)), 0.1), (r.normal(size=(T, N)), 0.0)]:
+        res = ref.layer_forward(x, W, K=K, act="swiglu", gate_mode="softmax_topk",
+                                experts_needed=False, noise=noise, noise_std=std)
+        assert np.array_equal(res.idx, clean.idx)
+        assert np.array_equal(res.gates, clean.gates)
+        assert np.array_equal(res.logits, clean.logits)
+        assert res.stats.z == clean.stats.z and res.stats.entropy == clean.stats.entropy
+
+
+def test_noise_constant_per_token_closed_forms():
+    """Noise c_t shared by every expert of a token shifts the token's logits:
+    softmax, top-K and gates do not change (shift invariance), and the
+    z-loss gains exactly 2 s mean_t(c_t sum_e l_te) + N s^2 mean_t(c_t^2)."""
+    r = rng(43)
+    T, N, d, K, s = 30, 12, 16, 2, 0.25
+    x = r.normal(size=(T, d))
+    W, _ = rand_weights(r, N, d, 64, "swiglu")
+    c = r.normal(size=T)
+    noise = np.repeat(c[:, None], N, axis=1)
+    clean = ref.layer_forward(x, W, K=K, act="swiglu", gate_mode="renorm_all",
+                              experts_needed=False)
+    res = ref.layer_forward(x, W, K=K, act="swiglu", gate_mode="renorm_all",
+                            experts_needed=False, noise=noise, noise_std=s)
+    assert np.array_equal(res.idx, clean.idx)
+    assert np.allclose(res.gates, clean.gates, rtol=0, atol=1e-14)
+    assert np.allclose(res.stats.p, clean.stats.p, rtol=0, atol=1e-14)
+    assert abs(res.stats.entropy - clean.stats.entropy) < 1e-12
+    lg = clean.logits
+    dz = 2 * s * np.mean(c * lg.sum(axis=1)) + N * s * s * np.mean(c * c)
+    assert abs(res.stats.z - (clean.stats.z + dz)) < 1e-10
+    assert np.array_equal(res.logits, clean.logits)  # the router output itself is clean
+
+
+def test_noise_spike_forces_the_choice():
+    """A noise spike on one expert of each token puts it first, and the
+    statistics follow the noisy logits (p_e is the mean noisy probability)."""
+    r = rng(44)
+    T, N, d, K = 25, 10, 16, 2
+    x = r.normal(size=(T, d))
+    W, _ = rand_weights(r, N, d, 64, "swiglu")
+    forced = r.integers(0, N, size=T)
+    noise = np.zeros((T, N))
+    noise[np.arange(T), forced] = 1000.0
+    res = ref.layer_forward(x, W, K=K, act="swiglu", gate_mode="softmax_topk",
+                            experts_needed=False, noise=noise, noise_std=0.1)
+    assert np.array_equal(res.idx[:, 0], forced)
+    assert np.allclose(res.gates[:, 0], 1.0, atol=1e-12)
+    want_p = np.bincount(forced, minlength=N) / T
+    assert np.allclose(res.stats.p, want_p, atol=1e-12)
+
+
+def test_bias_update_rules():
+    """Hand-worked: N=4, K=1, T=8, counts (4,2,2,0): mean load 2, so the
+    over-loaded expert 0 loses `rate`, expert 3 gains it, 1 and 2 keep theirs.
+    Balanced counts leave the bias alone; a missing bias counts as zero."""
+    b = np.array([0.5, -0.25, 0.0, 1.0])
+    out = ref.bias_update(b, np.array([4, 2, 2, 0]), T=8, K=1, rate=0.125)
+    assert np.array_equal(out, [0.375, -0.25, 0.0, 1.125])
+    assert np.array_equal(b, [0.5, -0.25, 0.0, 1.0])  # input untouched
+    assert np.array_equal(ref.bias_update(b, np.array([3, 3, 3, 3]), T=6, K=2, rate=1.0), b)
+    assert np.array_equal(ref.bias_update(None, np.array([5, 1, 0]), T=3, K=2, rate=0.5),
+                          [-0.5, 0.5, 0.5])  # mean load 2: 5 above it, 1 and 0 below
+
+
+def test_bias_update_uses_exact_mean():
+    """T*K/N = 7/3 is not an integer: counts 2 (below) and 3 (above) move
+    in opposite directions; no rounding of the mean may merge them."""
+    out = ref.bias_update(None, np.array([2, 3, 2]), T=7, K=1, rate=1.0)
+    assert np.array_equal(out, [1.0, -1.0, 1.0])
