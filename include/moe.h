@@ -12,6 +12,11 @@
  *   - selection-only per-expert bias: learnagent.wiki 结构 4.
  *   - Switch auxiliary loss alpha*N*sum f_i p_i: mzlw.cn 2.2; router
  *     z-loss: wmrh.cn section Router Z-Loss.
+ *   - training-time router noise (noise_std times a standard-normal draw
+ *     added to every logit before top-K, gates and the balance loss):
+ *     mzlw.cn section 三 (MoERouter.forward); the auxiliary-loss-free bias
+ *     update: learnagent.wiki 结构 4; routing entropy as a monitored
+ *     quantity: mstx.cn, the list of new challenges.
  *   - capacity floor(K/N*CF*S) and token dropping: mzlw.cn 2.3.
  *   - per-expert FFN (SwiGLU: mzlw.cn section 三, Expert; GELU:
  *     learnagent.wiki 运行示例), shared expert: mstx.cn "MoE 如何替代
@@ -93,6 +98,9 @@ typedef struct {
   int64_t capacity;   /* rows each expert may keep; < 0 = unlimited          */
   float aux_alpha;    /* alpha of the Switch auxiliary loss                  */
   uint32_t flags;     /* reserved, must be 0                                 */
+  float noise_std;    /* scale of moe_weights_t.noise (used only with it)    */
+  float bias_rate;    /* step of the selection-bias update written to
+                         moe_stats_t.b_sel_out (used only with it)           */
 } moe_config_t;
 
 /* Weights.  Router: w_r [N, d] fp32, b_r [N] fp32 (nullable; also carries any
@@ -101,7 +109,11 @@ typedef struct {
  * w1 [N, F, d] (SwiGLU gate, or the GELU input projection), w3 [N, F, d]
  * (SwiGLU up; NULL for GELU), w2 [N, d, F] (down), b1 [N, F] and b2 [N, d]
  * (GELU only, nullable).  Shared expert (SwiGLU, only when F_shared > 0):
- * ws1 [F_shared, d], ws3 [F_shared, d], ws2 [d, F_shared].                */
+ * ws1 [F_shared, d], ws3 [F_shared, d], ws2 [d, F_shared].
+ * noise [T, N] fp32 (nullable): this step's standard-normal draws, from
+ * the caller's generator.  With it the router works on
+ * logits + noise_std * noise from selection on (top-K, gates and every
+ * statistic); the logits output still holds the noise-free logits.        */
 typedef struct {
   const float* w_r;
   const float* b_r;
@@ -114,6 +126,7 @@ typedef struct {
   const void* ws1;
   const void* ws3;
   const void* ws2;
+  const float* noise;
 } moe_weights_t;
 
 /* Router statistics (each pointer nullable):
@@ -122,12 +135,20 @@ typedef struct {
  *   p     [N] fp32 : mean over tokens of softmax(logits)_e
  *   loss  [3] fp32 : { aux = alpha*N*sum_e f_e p_e,
  *                      z = mean_t sum_e logits_te^2,
- *                      z_lse = mean_t logsumexp(logits_t)^2 }            */
+ *                      z_lse = mean_t logsumexp(logits_t)^2 }
+ *   entropy [1] fp32 : mean_t of -sum_e P_te log P_te, P_t = softmax(logits_t)
+ *   b_sel_out [N] fp32 : the selection bias after one auxiliary-loss-free
+ *                      step: b_sel[e] + bias_rate * sign(T*K/N - count[e])
+ *                      (b_sel NULL counts as 0).  May alias weights.b_sel:
+ *                      it is written after selection has read it.
+ * "logits" here are the ones the router works on (with noise if given).  */
 typedef struct {
   int32_t* count;
   float* f;
   float* p;
   float* loss;
+  float* entropy;
+  float* b_sel_out;
 } moe_stats_t;
 
 /* Dispatch outputs.  A "pair" is (token t, slot k), flattened as t*K + k.

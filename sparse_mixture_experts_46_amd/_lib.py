@@ -23,16 +23,17 @@ class MoeConfig(C.Structure):
     _fields_ = [("T", C.c_int64), ("d", C.c_int32), ("N", C.c_int32), ("K", C.c_int32),
                 ("F", C.c_int32), ("F_shared", C.c_int32), ("dtype", C.c_int32),
                 ("act", C.c_int32), ("gate", C.c_int32), ("capacity", C.c_int64),
-                ("aux_alpha", C.c_float), ("flags", C.c_uint32)]
+                ("aux_alpha", C.c_float), ("flags", C.c_uint32), ("noise_std", C.c_float),
+                ("bias_rate", C.c_float)]
 
 
 class MoeWeights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("w_r", "b_r", "b_sel", "w1", "w3", "w2", "b1", "b2",
-                                          "ws1", "ws3", "ws2")]
+                                          "ws1", "ws3", "ws2", "noise")]
 
 
 class MoeStats(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in ("count", "f", "p", "loss")]
+    _fields_ = [(n, C.c_void_p) for n in ("count", "f", "p", "loss", "entropy", "b_sel_out")]
 
 
 class MoeDispatch(C.Structure):

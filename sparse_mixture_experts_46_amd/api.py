@@ -32,6 +32,8 @@ class Config:
     gate: str = "softmax_topk"
     capacity: int = -1
     aux_alpha: float = 1.0
+    noise_std: float = 0.0   # scale of the router noise (used with w["noise"])
+    bias_rate: float = 0.0   # step of the selection-bias update (used with b_sel_out)
 
     @property
     def torch_dtype(self):
@@ -42,7 +44,8 @@ class Config:
                            F_shared=self.F_shared,
                            dtype=L.MOE_BF16 if self.dtype == "bf16" else L.MOE_F32,
                            act=_ACT[self.act], gate=_GATE[self.gate], capacity=self.capacity,
-                           aux_alpha=self.aux_alpha, flags=0)
+                           aux_alpha=self.aux_alpha, flags=0, noise_std=self.noise_std,
+                           bias_rate=self.bias_rate)
 
 
 def config_for(w: Workload) -> Config:
@@ -86,14 +89,17 @@ def moe_workspace_size(cfg: Config) -> int:
 
 def weights_struct(t: dict) -> L.MoeWeights:
     w = L.MoeWeights()
-    for k in ("w_r", "b_r", "b_sel", "w1", "w3", "w2", "b1", "b2", "ws1", "ws3", "ws2"):
+    for k in ("w_r", "b_r", "b_sel", "w1", "w3", "w2", "b1", "b2", "ws1", "ws3", "ws2", "noise"):
         v = t.get(k)
         setattr(w, k, None if v is None else _p(v).value)
     return w
 
 
 def moe_router_topk(cfg: Config, w: dict, x: torch.Tensor, want_logits=False,
-                    want_stats=True) -> dict:
+                    want_stats=True, b_sel_out: torch.Tensor | None = None) -> dict:
+    """Router entry point.  w may carry "noise" [T, N] fp32 (with
+    cfg.noise_std); b_sel_out [N] fp32 receives one bias-update step (with
+    cfg.bias_rate) and may be w["b_sel"] itself."""
     lib = L.load()
     dev = x.device
     T, N, K = cfg.T, cfg.N, cfg.K
@@ -102,13 +108,17 @@ def moe_router_topk(cfg: Config, w: dict, x: torch.Tensor, want_logits=False,
     logits = torch.empty((T, N), dtype=torch.float32, device=dev) if want_logits else None
     out = {"idx": idx, "gate": gate, "logits": logits}
     st = None
-    if want_stats:
+    if want_stats or b_sel_out is not None:
         out["count"] = torch.empty(N, dtype=torch.int32, device=dev)
         out["f"] = torch.empty(N, dtype=torch.float32, device=dev)
         out["p"] = torch.empty(N, dtype=torch.float32, device=dev)
         out["loss"] = torch.empty(3, dtype=torch.float32, device=dev)
+        out["entropy"] = torch.empty(1, dtype=torch.float32, device=dev)
+        out["b_sel_out"] = b_sel_out
         st = L.MoeStats(count=_p(out["count"]).value, f=_p(out["f"]).value,
-                        p=_p(out["p"]).value, loss=_p(out["loss"]).value)
+                        p=_p(out["p"]).value, loss=_p(out["loss"]).value,
+                        entropy=_p(out["entropy"]).value,
+                        b_sel_out=None if b_sel_out is None else _p(b_sel_out).value)
     ws = _ws(_size(lib.moe_router_workspace_size, cfg), dev)
     L.check(lib.moe_router_topk(C.byref(cfg.c()), C.byref(weights_struct(w)), _p(x), _p(idx),
                                 _p(gate), _p(logits), C.byref(st) if st else None, _p(ws),
@@ -180,6 +190,7 @@ class LayerBuffers:
         self.f = torch.empty(N, dtype=torch.float32, device=device)
         self.p = torch.empty(N, dtype=torch.float32, device=device)
         self.loss = torch.empty(3, dtype=torch.float32, device=device)
+        self.entropy = torch.empty(1, dtype=torch.float32, device=device)
         self.kept = torch.empty(N, dtype=torch.int32, device=device)
         self.offset = torch.empty(N + 1, dtype=torch.int32, device=device)
         self.pair_row = torch.empty(T * K, dtype=torch.int32, device=device)
@@ -193,7 +204,8 @@ class LayerBuffers:
         self.out.topk_gate = _p(self.gate).value
         self.out.logits = None if self.logits is None else _p(self.logits).value
         self.out.stats = L.MoeStats(count=_p(self.count).value, f=_p(self.f).value,
-                                    p=_p(self.p).value, loss=_p(self.loss).value)
+                                    p=_p(self.p).value, loss=_p(self.loss).value,
+                                    entropy=_p(self.entropy).value, b_sel_out=None)
         self.out.dispatch = L.MoeDispatch(
             kept=_p(self.kept).value, offset=_p(self.offset).value,
             pair_row=_p(self.pair_row).value, row_pair=_p(self.row_pair).value,
@@ -202,8 +214,8 @@ class LayerBuffers:
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k in ("y", "idx", "gate", "logits", "count", "f", "p",
-                                               "loss", "kept", "offset", "pair_row", "row_pair",
-                                               "dropped", "counters")}
+                                               "loss", "entropy", "kept", "offset", "pair_row",
+                                               "row_pair", "dropped", "counters")}
 
 
 def moe_layer_forward(cfg: Config, w: dict, x: torch.Tensor, bufs: LayerBuffers | None = None,

@@ -26,6 +26,7 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->gate < MOE_GATE_RENORM_ALL || c->gate > MOE_GATE_PROB_NO_RENORM) return MOE_ERR_INVALID_ARG;
   if (c->flags != 0) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->aux_alpha)) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->noise_std) || !std::isfinite(c->bias_rate)) return MOE_ERR_INVALID_ARG;
   if (c->N > MOE_MAX_EXPERTS || c->K > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (c->d % 64 || c->F % 64 || c->F_shared % 64) return MOE_ERR_UNSUPPORTED;
   if (c->F_shared != 0 && (c->F_shared != c->F || c->act != MOE_ACT_SWIGLU)) return MOE_ERR_UNSUPPORTED;
@@ -61,7 +62,7 @@ RouterWs router_ws(const moe_config_t* c) {
   w.logits = o; o = align_up(o + (size_t)c->T * c->N * 4);
   w.part_p = o; o = align_up(o + (size_t)nb * c->N * 4);
   w.part_cnt = o; o = align_up(o + (size_t)nb * c->N * 4);
-  w.part_z = o; o = align_up(o + (size_t)nb * 2 * 4);
+  w.part_z = o; o = align_up(o + (size_t)nb * 3 * 4);
   w.part_fp = o; o = align_up(o + (size_t)((c->N + 63) / 64) * 4);
   w.total = o;
   return w;
@@ -153,28 +154,34 @@ moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void
   const RouterWs L = router_ws(c);
   float* lg = logits ? logits : at<float>(ws, L.logits);
   const bool bf16 = c->dtype == MOE_BF16;
+  int32_t* count = st ? st->count : nullptr;
+  float* f = st ? st->f : nullptr;
+  float* p = st ? st->p : nullptr;
+  float* loss = st ? st->loss : nullptr;
+  float* entropy = st ? st->entropy : nullptr;
+  float* b_out = st ? st->b_sel_out : nullptr;
   if (router_small_path(c->T, c->N)) {
     hipError_t e = launch_router_logits(x, bf16, w->w_r, w->b_r, at<float>(ws, L.split), lg, c->T,
                                         c->d, c->N, s, /*reduce_splits=*/false);
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = launch_router_small(at<float>(ws, L.split), router_num_splits(c->T, c->d, c->N, bf16),
-                            w->b_r, w->b_sel, lg, idx, gate, c->T, c->N, c->K, c->gate,
-                            c->aux_alpha, st ? st->count : nullptr, st ? st->f : nullptr,
-                            st ? st->p : nullptr, st ? st->loss : nullptr, s);
+                            w->b_r, w->noise, c->noise_std, w->b_sel, lg, idx, gate, c->T, c->N,
+                            c->K, c->gate, c->aux_alpha, count, f, p, loss, entropy, b_out,
+                            c->bias_rate, s);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
   hipError_t e = launch_router_logits(x, bf16, w->w_r, w->b_r, at<float>(ws, L.split), lg, c->T,
                                       c->d, c->N, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_router_topk(lg, w->b_sel, idx, gate, at<float>(ws, L.part_p),
+  e = launch_router_topk(lg, w->noise, c->noise_std, w->b_sel, idx, gate, at<float>(ws, L.part_p),
                          at<int32_t>(ws, L.part_cnt), at<float>(ws, L.part_z), c->T, c->N, c->K,
                          c->gate, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  if (st && (st->count || st->f || st->p || st->loss)) {
+  if (count || f || p || loss || entropy || b_out) {
     e = launch_router_stats(at<float>(ws, L.part_p), at<int32_t>(ws, L.part_cnt),
                             at<float>(ws, L.part_z), at<float>(ws, L.part_fp),
-                            router_num_blocks(c->T), c->T, c->N, c->K,
-                            c->aux_alpha, st->count, st->f, st->p, st->loss, s);
+                            router_num_blocks(c->T), c->T, c->N, c->K, c->aux_alpha, count, f, p,
+                            loss, entropy, w->b_sel, b_out, c->bias_rate, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;

@@ -24,11 +24,15 @@ hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, co
                                 float* part, float* logits, int64_t T, int d, int N,
                                 hipStream_t stream, bool reduce_splits = true);
 
-// Selection, gates and per-block partial statistics:
-//   part_p [nblk, N] fp32, part_cnt [nblk, N] int32, part_z [nblk, 2] fp32
-hipError_t launch_router_topk(const float* logits, const float* b_sel, int32_t* idx, float* gate,
-                              float* part_p, int32_t* part_cnt, float* part_z, int64_t T, int N,
-                              int K, int gate_mode, hipStream_t stream);
+// Selection, gates and per-block partial statistics on logits + noise_std *
+// noise (noise nullable):
+//   part_p [nblk, N] fp32, part_cnt [nblk, N] int32,
+//   part_z [nblk, 3] fp32 (sum of squared logits, of squared log-sum-exp, of
+//   routing entropy)
+hipError_t launch_router_topk(const float* logits, const float* noise, float noise_std,
+                              const float* b_sel, int32_t* idx, float* gate, float* part_p,
+                              int32_t* part_cnt, float* part_z, int64_t T, int N, int K,
+                              int gate_mode, hipStream_t stream);
 
 // Small batches (router_small_path): one workgroup reduces the logit splits
 // (part from launch_router_logits without its reduction; nsplit =
@@ -36,16 +40,20 @@ hipError_t launch_router_topk(const float* logits, const float* b_sel, int32_t* 
 // count / f / p / loss are skipped.
 constexpr int64_t kRouterSmallT = 64;
 bool router_small_path(int64_t T, int N);
-hipError_t launch_router_small(const float* part, int nsplit, const float* b_r, const float* b_sel,
-                               float* logits, int32_t* idx, float* gate, int64_t T, int N, int K,
-                               int gate_mode, float alpha, int32_t* count, float* f, float* p,
-                               float* loss, hipStream_t stream);
+hipError_t launch_router_small(const float* part, int nsplit, const float* b_r, const float* noise,
+                               float noise_std, const float* b_sel, float* logits, int32_t* idx,
+                               float* gate, int64_t T, int N, int K, int gate_mode, float alpha,
+                               int32_t* count, float* f, float* p, float* loss, float* entropy,
+                               float* b_sel_out, float bias_rate, hipStream_t stream);
 
 // part_fp: [ceil(N / 64)] fp32 scratch (per-expert-block sums of f_e * p_e)
+// Every output nullable; b_sel_out gets one auxiliary-loss-free step of
+// b_sel (nullable = 0) and may alias it.
 hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
                                const float* part_z, float* part_fp, int64_t nblk, int64_t T,
                                int N, int K, float alpha, int32_t* count,
-                               float* f, float* p, float* loss,
+                               float* f, float* p, float* loss, float* entropy,
+                               const float* b_sel, float* b_sel_out, float bias_rate,
                                hipStream_t stream);
 
 // -------------------------------------------------------------- dispatch --

@@ -280,19 +280,20 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 // One token's softmax statistics, top-K selection and gates, computed by
 // one wave: lane l holds the logits of experts l, l + 64, ... in l[].  Adds
 // the token's probabilities to pacc, its sum of squared logits to zsum and
-// its squared log-sum-exp to lsum; writes K ids and gates; counts each
-// chosen expert in scnt (LDS, integer atomics).
+// its squared log-sum-exp to lsum and the entropy of its routing
+// distribution to hsum; writes K ids and gates; counts each chosen expert in
+// scnt (LDS, integer atomics).
 template <int NJ>
 __device__ __forceinline__ void topk_one_token(const float (&l)[NJ], const float (&bsel)[NJ],
                                                int lane, int N, int K, int gate_mode,
                                                float (&pacc)[NJ], float& zsum, float& lsum,
-                                               int32_t* __restrict__ idx_t,
+                                               float& hsum, int32_t* __restrict__ idx_t,
                                                float* __restrict__ gate_t, int32_t* scnt) {
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) m = fmaxf(m, l[j]);
   m = wave_max(m);
-  float ssum = 0.f, sq = 0.f;
+  float ssum = 0.f, sq = 0.f, gap = 0.f;
   float ex[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -300,15 +301,19 @@ __device__ __forceinline__ void topk_one_token(const float (&l)[NJ], const float
     ex[j] = (e < N) ? expf(l[j] - m) : 0.f;
     ssum += ex[j];
     sq += (e < N) ? l[j] * l[j] : 0.f;
+    gap += (ex[j] > 0.f) ? ex[j] * (m - l[j]) : 0.f;
   }
   ssum = wave_sum(ssum);
   sq = wave_sum(sq);
+  gap = wave_sum(gap);
   const float inv = 1.0f / ssum;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) pacc[j] += ex[j] * inv;
   const float lse = m + logf(ssum);
   zsum += sq;
   lsum += lse * lse;
+  // entropy -sum P log P = log(ssum) + sum P (m - l): two non-negative terms
+  hsum += logf(ssum) + gap * inv;
 
   // K rounds of arg-max over the not-yet-taken experts
   uint32_t taken = 0;
@@ -356,15 +361,15 @@ __device__ __forceinline__ void topk_one_token(const float (&l)[NJ], const float
 
 template <int NJ>
 __global__ __launch_bounds__(256) void router_topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ b_sel,
-    int32_t* __restrict__ idx, float* __restrict__ gate,
+    const float* __restrict__ logits, const float* __restrict__ noise, float noise_std,
+    const float* __restrict__ b_sel, int32_t* __restrict__ idx, float* __restrict__ gate,
     float* __restrict__ part_p, int32_t* __restrict__ part_cnt,
     float* __restrict__ part_z, int64_t T, int N, int K, int gate_mode,
     int tpb) {
   extern __shared__ unsigned char smem_raw[];
   float* sp = (float*)smem_raw;                  // [4][N] per-wave prob sums
   int32_t* scnt = (int32_t*)(sp + 4 * N);        // [N] block counts
-  float* sz = (float*)(scnt + N);                // [4][2]
+  float* sz = (float*)(scnt + N);                // [4][3]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < N; e += 256) scnt[e] = 0;
   __syncthreads();
@@ -377,7 +382,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     int e = lane + 64 * j;
     bsel[j] = (b_sel && e < N) ? b_sel[e] : 0.f;
   }
-  float zsum = 0.f, lsum = 0.f;
+  float zsum = 0.f, lsum = 0.f, hsum = 0.f;
 
   const int64_t tb0 = (int64_t)blockIdx.x * tpb;
   const int per_wave = tpb / 4;
@@ -389,9 +394,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     for (int j = 0; j < NJ; ++j) {
       int e = lane + 64 * j;
       l[j] = (e < N) ? logits[t * N + e] : -INFINITY;
+      if (noise && e < N) l[j] += noise_std * noise[t * N + e];
     }
-    topk_one_token<NJ>(l, bsel, lane, N, K, gate_mode, pacc, zsum, lsum, idx + t * K, gate + t * K,
-                       scnt);
+    topk_one_token<NJ>(l, bsel, lane, N, K, gate_mode, pacc, zsum, lsum, hsum, idx + t * K,
+                       gate + t * K, scnt);
   }
   // fixed-order reduction of the block's partial sums
 #pragma unroll
@@ -399,7 +405,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     int e = lane + 64 * j;
     if (e < N) sp[wave * N + e] = pacc[j];
   }
-  if (lane == 0) { sz[wave * 2] = zsum; sz[wave * 2 + 1] = lsum; }
+  if (lane == 0) { sz[wave * 3] = zsum; sz[wave * 3 + 1] = lsum; sz[wave * 3 + 2] = hsum; }
   __syncthreads();
   for (int e = tid; e < N; e += 256) {
     float s = sp[e];
@@ -409,13 +415,20 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     part_p[(int64_t)blockIdx.x * N + e] = s;
     part_cnt[(int64_t)blockIdx.x * N + e] = scnt[e];
   }
-  if (tid == 0) {
-    part_z[blockIdx.x * 2] = ((sz[0] + sz[2]) + sz[4]) + sz[6];
-    part_z[blockIdx.x * 2 + 1] = ((sz[1] + sz[3]) + sz[5]) + sz[7];
-  }
+  if (tid < 3) part_z[blockIdx.x * 3 + tid] = ((sz[tid] + sz[3 + tid]) + sz[6 + tid]) + sz[9 + tid];
 }
 
 // --------------------------------------------------------------- stats ----
+// One auxiliary-loss-free step of the selection bias: up by bias_rate if the
+// expert's count is below the mean load T*K/N, down if above, unchanged at
+// it (compared exactly, as count*N against T*K).  b_sel may be null (0).
+__device__ __forceinline__ float bias_step(const float* b_sel, int e, int64_t count, int64_t T,
+                                           int K, int N, float bias_rate) {
+  const int64_t diff = T * (int64_t)K - count * (int64_t)N;
+  const float b = b_sel ? b_sel[e] : 0.f;
+  return diff > 0 ? b + bias_rate : (diff < 0 ? b - bias_rate : b);
+}
+
 // Per-expert statistics.  Block b owns experts [64 b, 64 b + 64).  Thread t
 // sums, for expert 64 b + t % 64, the block partials j = c, c + 16, ...
 // (c = t / 64) in increasing j; the first 64 threads add the 16 chunk sums
@@ -424,7 +437,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
 __global__ __launch_bounds__(1024) void router_stats_expert_kernel(
     const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt, int64_t nblk,
     int64_t T, int N, int K, int32_t* __restrict__ count, float* __restrict__ f,
-    float* __restrict__ p, float* __restrict__ part_fp) {
+    float* __restrict__ p, float* __restrict__ part_fp, const float* b_sel, float* b_out,
+    float bias_rate) {
   __shared__ float sp[1024];
   __shared__ int64_t sc[1024];
   __shared__ float red[64];
@@ -455,6 +469,7 @@ __global__ __launch_bounds__(1024) void router_stats_expert_kernel(
       if (count) count[e] = (int32_t)ct;
       if (f) f[e] = fe;
       if (p) p[e] = pe;
+      if (b_out) b_out[e] = bias_step(b_sel, e, ct, T, K, N, bias_rate);
       fp = fe * pe;
     }
     red[tid] = fp;
@@ -471,31 +486,37 @@ __global__ __launch_bounds__(1024) void router_stats_expert_kernel(
 // from the per-token-block partials (strided sums, then a fixed tree).
 __global__ __launch_bounds__(1024) void router_stats_final_kernel(
     const float* __restrict__ part_fp, int nfp, const float* __restrict__ part_z, int64_t nblk,
-    int64_t T, int N, float alpha, float* __restrict__ loss) {
-  __shared__ float rz[1024], rl[1024];
+    int64_t T, int N, float alpha, float* __restrict__ loss, float* __restrict__ entropy) {
+  __shared__ float rz[1024], rl[1024], rh[1024];
   const int tid = threadIdx.x;
-  float z = 0.f, zl = 0.f;
+  float z = 0.f, zl = 0.f, h = 0.f;
   for (int64_t b = tid; b < nblk; b += 1024) {
-    z += part_z[2 * b];
-    zl += part_z[2 * b + 1];
+    z += part_z[3 * b];
+    zl += part_z[3 * b + 1];
+    h += part_z[3 * b + 2];
   }
   rz[tid] = z;
   rl[tid] = zl;
+  rh[tid] = h;
   __syncthreads();
   for (int o = 512; o > 0; o >>= 1) {
     if (tid < o) {
       rz[tid] += rz[tid + o];
       rl[tid] += rl[tid + o];
+      rh[tid] += rh[tid + o];
     }
     __syncthreads();
   }
   if (tid == 0) {
-    float aux = 0.f;
-    for (int i = 0; i < nfp; ++i) aux += part_fp[i];
     const float invT = 1.0f / (float)T;
-    loss[0] = alpha * (float)N * aux;
-    loss[1] = rz[0] * invT;
-    loss[2] = rl[0] * invT;
+    if (loss) {
+      float aux = 0.f;
+      for (int i = 0; i < nfp; ++i) aux += part_fp[i];
+      loss[0] = alpha * (float)N * aux;
+      loss[1] = rz[0] * invT;
+      loss[2] = rl[0] * invT;
+    }
+    if (entropy) entropy[0] = rh[0] * invT;
   }
 }
 
@@ -510,15 +531,16 @@ __global__ __launch_bounds__(1024) void router_stats_final_kernel(
 template <int NJ>
 __global__ __launch_bounds__(1024) void router_small_kernel(
     const float* __restrict__ part, int nsplit, const float* __restrict__ b_r,
-    const float* __restrict__ b_sel, float* __restrict__ logits, int32_t* __restrict__ idx,
-    float* __restrict__ gate, int64_t T, int N, int K, int gate_mode, float alpha,
-    int32_t* __restrict__ count, float* __restrict__ f, float* __restrict__ p,
-    float* __restrict__ loss) {
+    const float* __restrict__ noise, float noise_std, const float* b_sel,
+    float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ gate, int64_t T,
+    int N, int K, int gate_mode, float alpha, int32_t* __restrict__ count, float* __restrict__ f,
+    float* __restrict__ p, float* __restrict__ loss, float* __restrict__ entropy, float* b_out,
+    float bias_rate) {
   extern __shared__ unsigned char smem_raw[];
   float* sp = (float*)smem_raw;                  // [16][N] per-wave prob sums
   int32_t* scnt = (int32_t*)(sp + 16 * N);       // [N] counts
   float* sfp = (float*)(scnt + N);               // [N] f_e * p_e
-  float* sz = sfp + N;                           // [16][2]
+  float* sz = sfp + N;                           // [16][3]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < N; e += 1024) scnt[e] = 0;
   __syncthreads();
@@ -530,7 +552,7 @@ __global__ __launch_bounds__(1024) void router_small_kernel(
     const int e = lane + 64 * j;
     bsel[j] = (b_sel && e < N) ? b_sel[e] : 0.f;
   }
-  float zsum = 0.f, lsum = 0.f;
+  float zsum = 0.f, lsum = 0.f, hsum = 0.f;
   const int64_t n = T * (int64_t)N;
   for (int64_t t = wave; t < T; t += 16) {
     float l[NJ];
@@ -547,19 +569,22 @@ __global__ __launch_bounds__(1024) void router_small_kernel(
         } else {
           l[j] = logits[i];
         }
+        if (noise) l[j] += noise_std * noise[i];
       } else {
         l[j] = -INFINITY;
       }
     }
-    topk_one_token<NJ>(l, bsel, lane, N, K, gate_mode, pacc, zsum, lsum, idx + t * K, gate + t * K,
-                       scnt);
+    topk_one_token<NJ>(l, bsel, lane, N, K, gate_mode, pacc, zsum, lsum, hsum, idx + t * K,
+                       gate + t * K, scnt);
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     if (e < N) sp[wave * N + e] = pacc[j];
   }
-  if (lane == 0) { sz[wave * 2] = zsum; sz[wave * 2 + 1] = lsum; }
+  if (lane == 0) { sz[wave * 3] = zsum; sz[wave * 3 + 1] = lsum; sz[wave * 3 + 2] = hsum; }
+  // every wave has read b_sel (bsel[] above) before this barrier, so b_out
+  // may alias it
   __syncthreads();
   for (int e = tid; e < N; e += 1024) {
     float st = 0.f;
@@ -570,21 +595,26 @@ __global__ __launch_bounds__(1024) void router_small_kernel(
     if (count) count[e] = ct;
     if (f) f[e] = fe;
     if (p) p[e] = pe;
+    if (b_out) b_out[e] = bias_step(b_sel, e, ct, T, K, N, bias_rate);
     sfp[e] = fe * pe;
   }
   __syncthreads();
-  if (tid == 0 && loss) {
+  if (tid == 0) {
     float aux = 0.f;
     for (int e = 0; e < N; ++e) aux += sfp[e];
-    float z = 0.f, zl = 0.f;
+    float z = 0.f, zl = 0.f, h = 0.f;
     for (int w = 0; w < 16; ++w) {
-      z += sz[2 * w];
-      zl += sz[2 * w + 1];
+      z += sz[3 * w];
+      zl += sz[3 * w + 1];
+      h += sz[3 * w + 2];
     }
     const float invT = 1.0f / (float)T;
-    loss[0] = alpha * (float)N * aux;
-    loss[1] = z * invT;
-    loss[2] = zl * invT;
+    if (loss) {
+      loss[0] = alpha * (float)N * aux;
+      loss[1] = z * invT;
+      loss[2] = zl * invT;
+    }
+    if (entropy) entropy[0] = h * invT;
   }
 }
 }  // namespace
@@ -644,17 +674,18 @@ hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, co
   return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const float* logits, const float* b_sel, int32_t* idx, float* gate,
-                              float* part_p, int32_t* part_cnt, float* part_z, int64_t T, int N,
-                              int K, int gate_mode, hipStream_t stream) {
+hipError_t launch_router_topk(const float* logits, const float* noise, float noise_std,
+                              const float* b_sel, int32_t* idx, float* gate, float* part_p,
+                              int32_t* part_cnt, float* part_z, int64_t T, int N, int K,
+                              int gate_mode, hipStream_t stream) {
   const int tpb = router_tokens_per_block(T);
   const unsigned nblk = (unsigned)((T + tpb - 1) / tpb);
-  const size_t smem = (size_t)4 * N * sizeof(float) + (size_t)N * sizeof(int32_t) + 8 * sizeof(float);
+  const size_t smem = (size_t)4 * N * sizeof(float) + (size_t)N * sizeof(int32_t) + 12 * sizeof(float);
   const int nj = (N + 63) / 64;
 #define MOE_TOPK_CASE(NJV)                                                              \
   case NJV:                                                                             \
-    router_topk_kernel<NJV><<<nblk, 256, smem, stream>>>(logits, b_sel, idx, gate,      \
-        part_p, part_cnt, part_z, T, N, K, gate_mode, tpb);                            \
+    router_topk_kernel<NJV><<<nblk, 256, smem, stream>>>(logits, noise, noise_std, b_sel,  \
+        idx, gate, part_p, part_cnt, part_z, T, N, K, gate_mode, tpb);                 \
     break;
   switch (nj) {
     MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
@@ -670,29 +701,34 @@ hipError_t launch_router_topk(const float* logits, const float* b_sel, int32_t* 
 hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
                                const float* part_z, float* part_fp, int64_t nblk, int64_t T,
                                int N, int K, float alpha, int32_t* count,
-                               float* f, float* p, float* loss,
+                               float* f, float* p, float* loss, float* entropy,
+                               const float* b_sel, float* b_sel_out, float bias_rate,
                                hipStream_t stream) {
   const int nfp = (N + 63) / 64;
   router_stats_expert_kernel<<<nfp, 1024, 0, stream>>>(part_p, part_cnt, nblk, T, N, K, count,
-                                                       f, p, part_fp);
+                                                       f, p, part_fp, b_sel, b_sel_out,
+                                                       bias_rate);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !loss) return e;
-  router_stats_final_kernel<<<1, 1024, 0, stream>>>(part_fp, nfp, part_z, nblk, T, N, alpha, loss);
+  if (e != hipSuccess || (!loss && !entropy)) return e;
+  router_stats_final_kernel<<<1, 1024, 0, stream>>>(part_fp, nfp, part_z, nblk, T, N, alpha, loss,
+                                                    entropy);
   return hipGetLastError();
 }
 
 bool router_small_path(int64_t T, int N) { return T <= kRouterSmallT && N <= 256; }
 
-hipError_t launch_router_small(const float* part, int nsplit, const float* b_r, const float* b_sel,
-                               float* logits, int32_t* idx, float* gate, int64_t T, int N, int K,
-                               int gate_mode, float alpha, int32_t* count, float* f, float* p,
-                               float* loss, hipStream_t stream) {
-  const size_t smem = (size_t)18 * N * sizeof(float) + 32 * sizeof(float);
+hipError_t launch_router_small(const float* part, int nsplit, const float* b_r, const float* noise,
+                               float noise_std, const float* b_sel, float* logits, int32_t* idx,
+                               float* gate, int64_t T, int N, int K, int gate_mode, float alpha,
+                               int32_t* count, float* f, float* p, float* loss, float* entropy,
+                               float* b_sel_out, float bias_rate, hipStream_t stream) {
+  const size_t smem = (size_t)18 * N * sizeof(float) + 48 * sizeof(float);
   const int nj = (N + 63) / 64;
 #define MOE_SMALL_CASE(NJV)                                                                    \
   case NJV:                                                                                    \
-    router_small_kernel<NJV><<<1, 1024, smem, stream>>>(part, nsplit, b_r, b_sel, logits, idx, \
-        gate, T, N, K, gate_mode, alpha, count, f, p, loss);                                  \
+    router_small_kernel<NJV><<<1, 1024, smem, stream>>>(part, nsplit, b_r, noise, noise_std,  \
+        b_sel, logits, idx, gate, T, N, K, gate_mode, alpha, count, f, p, loss, entropy,       \
+        b_sel_out, bias_rate);                                                                \
     break;
   switch (nj) {
     MOE_SMALL_CASE(1) MOE_SMALL_CASE(2) MOE_SMALL_CASE(3) MOE_SMALL_CASE(4)

@@ -100,6 +100,8 @@ def test_workspace_sizes_are_sane(lib, name):
     (dict(T=-1), L.MOE_ERR_INVALID_ARG),
     (dict(N=0), L.MOE_ERR_INVALID_ARG),
     (dict(flags=1), L.MOE_ERR_INVALID_ARG),
+    (dict(noise_std=float("nan")), L.MOE_ERR_INVALID_ARG),
+    (dict(bias_rate=float("inf")), L.MOE_ERR_INVALID_ARG),
     (dict(N=2048, K=2), L.MOE_ERR_UNSUPPORTED),
     (dict(K=17, N=64), L.MOE_ERR_UNSUPPORTED),
     (dict(d=100), L.MOE_ERR_UNSUPPORTED),
