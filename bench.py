@@ -11,7 +11,9 @@ synthetic input already resident in HBM.  Prints ONE JSON line.
 Default workload: Mixtral-shaped prefill (T=4096, d=4096, N=8, top-2, SwiGLU
 F=14336, bf16).  Unless --no-decode, the line also carries the decode-shaped
 DeepSeek-V3 layer (T=128, d=7168, N=256, top-8, F=2048 + shared expert)
-measured the same way, as HBM GB/s on the expert weights it touches.
+measured the same way, as HBM GB/s on the expert weights it touches.  For
+each workload the router entry point is also timed alone, plain and with the
+training-time variants (noise, entropy, bias update): "router_train".
 """
 from __future__ import annotations
 
@@ -165,6 +167,54 @@ def run_workload(w, steps, warmup, ev):
     return res
 
 
+def router_train_timing(w, inp, steps, warmup, noise_std=0.1, bias_rate=1e-3):
+    """moe_router_topk alone on the workload's inputs, plain and with the
+    training variants on (router noise, routing entropy, a bias-update step
+    written to a separate buffer).  Torch events on torch's current stream
+    around graph replays of one captured call."""
+    import torch
+
+    from sparse_mixture_experts_46_amd import api
+
+    cfg = api.config_for(w)
+    cfg_t = api.config_for(w)
+    cfg_t.noise_std, cfg_t.bias_rate = noise_std, bias_rate
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    winp = dict(inp)
+    winp["noise"] = torch.randn((w.T, w.N), generator=g, device="cuda", dtype=torch.float32)
+    b_out = torch.empty(w.N, dtype=torch.float32, device="cuda")
+
+    def timed(c, wd, bo):
+        # one call captured into a HIP graph and replayed, so the host-side
+        # marshalling of the Python binding is not timed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            api.moe_router_topk(c, wd, inp["x"], b_sel_out=bo)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            api.moe_router_topk(c, wd, inp["x"], b_sel_out=bo)
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del graph
+        return e0.elapsed_time(e1) / steps
+
+    plain = timed(cfg, inp, None)
+    train = timed(cfg_t, winp, b_out)
+    return {"entry_point": "moe_router_topk (logits, selection, gates, statistics)",
+            "plain_ms": plain, "train_ms": train, "noise_std": noise_std, "bias_rate": bias_rate,
+            "noise_bytes": 4.0 * w.T * w.N}
+
+
 def cpu_baseline(w, inp, sample):
     """The oracle, as it stands, on the first `sample` tokens of the same
     workload (routing over those tokens, capacity, experts, combine)."""
@@ -271,6 +321,7 @@ def main():
         "stage_ms": {k: float(v) for k, v in zip(STAGES, r["stage_ms"])},
         "kept_rows": r["kept_rows"],
     }
+    line["router_train"] = router_train_timing(w, r["inp"], a.steps, a.warmup)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["inp"], min(a.cpu_sample or w.T, w.T))
     del r
@@ -287,6 +338,7 @@ def main():
             "hbm_gbs": gbs, "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
             "stage_ms": {k: float(v) for k, v in zip(STAGES, rd["stage_ms"])},
+            "router_train": router_train_timing(wd, rd["inp"], a.steps, a.warmup),
         }
     print(json.dumps(line), flush=True)
 
