@@ -70,6 +70,50 @@ class Bf16Stack:
 
 # ---------------------------------------------------------------- router ---
 
+# ------------------------------------------------- weight-only INT8 ---
+
+def quantize_int8_rows(w):
+    """Weight-only INT8 with one scale per output channel (row), symmetric
+    absmax quantization as published by Dettmers et al., "LLM.int8(): 8-bit
+    Matrix Multiplication for Transformers at Scale" (2022), section 2: the
+    row's largest magnitude maps to 127.  The pages give no scheme.
+
+    Both steps are defined in fp32 so that codes are decided identically
+    everywhere: s = absmax(row) / 127 and q = rint(w / s) (round half to
+    even), clamped to [-127, 127]; an all-zero row gets s = 0 and q = 0.
+    w: float array [..., rows, cols] (bf16 values are exact in fp32).
+    Returns (q int8, s float32 [..., rows])."""
+    w32 = np.asarray(w, dtype=np.float32)
+    amax = np.max(np.abs(w32), axis=-1)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint((w32 / safe[..., None]).astype(np.float32))
+    q = np.where(scale[..., None] > 0, q, 0.0)
+    q = np.clip(q, -127, 127).astype(np.int8)
+    return q, scale
+
+
+def dequantize_int8_rows(q, scale):
+    """The weights an INT8 layer computes with: q * s, exact in float64."""
+    return np.asarray(q, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+class Int8Stack:
+    """Per-expert INT8 weights (q [E, rows, cols], s [E, rows]); indexing one
+    expert returns its dequantized matrix in float64."""
+
+    def __init__(self, q, scale):
+        self.q = np.asarray(q, dtype=np.int8)
+        self.scale = np.asarray(scale, dtype=np.float32)
+        self.shape = self.q.shape
+
+    def __getitem__(self, e):
+        return dequantize_int8_rows(self.q[e], self.scale[e])
+
+    def __len__(self):
+        return self.shape[0]
+
+
 def router_logits(x: np.ndarray, w_r: np.ndarray, b_r: np.ndarray | None = None):
     """logits[t, e] = sum_j x[t, j] * w_r[e, j] (+ b_r[e]).
 

@@ -491,3 +491,57 @@ def test_bias_update_uses_exact_mean():
     in opposite directions; no rounding of the mean may merge them."""
     out = ref.bias_update(None, np.array([2, 3, 2]), T=7, K=1, rate=1.0)
     assert np.array_equal(out, [1.0, -1.0, 1.0])
+
+
+# ------------------------------------------------ weight-only INT8 pins
+
+def test_int8_hand_worked_row():
+    """Row (2, -1.5, 0.3, 0): absmax 2, s = 2/127; codes 127, -95 (-95.25),
+    19 (19.05), 0.  A second row scaled by -1 gives the negated codes."""
+    w = np.array([[2.0, -1.5, 0.3, 0.0], [-2.0, 1.5, -0.3, 0.0]])
+    q, s = ref.quantize_int8_rows(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert q[0].tolist() == [127, -95, 19, 0]
+    assert q[1].tolist() == [-127, 95, -19, 0]
+    assert s[0] == np.float32(2.0) / np.float32(127.0) and s[1] == s[0]
+
+
+def test_int8_error_bound_and_extremes():
+    """|w - q s| <= s/2 (plus fp32 slack), the absmax entry codes to +-127,
+    a zero row stays zero, and the codes are odd-symmetric."""
+    r = rng(61)
+    w = (r.normal(size=(40, 96)) * r.uniform(0.01, 3.0, size=(40, 1))).astype(np.float32)
+    w[7] = 0.0
+    q, s = ref.quantize_int8_rows(w)
+    deq = ref.dequantize_int8_rows(q, s)
+    err = np.abs(deq - w.astype(np.float64))
+    assert np.all(err <= s.astype(np.float64)[:, None] * (0.5 + 1e-6) + 1e-30)
+    amax_col = np.argmax(np.abs(w), axis=1)
+    for i in range(40):
+        if i == 7:
+            continue
+        assert abs(int(q[i, amax_col[i]])) == 127
+    assert np.all(q[7] == 0) and s[7] == 0 and np.all(deq[7] == 0)
+    qn, sn = ref.quantize_int8_rows(-w)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    assert np.abs(q.astype(int)).max() <= 127
+
+
+def test_int8_stack_feeds_the_expert_ffn():
+    """An expert FFN on Int8Stack weights equals the same FFN on the dense
+    dequantized matrices, and differs from the unquantized FFN by no more
+    than the weight error allows (a first-order bound on the output)."""
+    r = rng(62)
+    N, F, d, M = 3, 64, 32, 5
+    W = {"w1": r.normal(size=(N, F, d)) / math.sqrt(d),
+         "w3": r.normal(size=(N, F, d)) / math.sqrt(d),
+         "w2": r.normal(size=(N, d, F)) / math.sqrt(F)}
+    Wq = {k: ref.Int8Stack(*ref.quantize_int8_rows(v)) for k, v in W.items()}
+    xr = r.normal(size=(M, d))
+    for e in range(N):
+        dense = {k: ref.dequantize_int8_rows(*ref.quantize_int8_rows(W[k][e])) for k in W}
+        a = ref.run_expert("swiglu", xr, e, Wq)
+        b = ref.expert_swiglu(xr, dense["w1"], dense["w3"], dense["w2"])
+        assert np.array_equal(a, b)
+        full = ref.run_expert("swiglu", xr, e, W)
+        assert np.max(np.abs(a - full)) < 0.05 * np.max(np.abs(full))
