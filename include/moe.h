@@ -69,6 +69,14 @@ typedef enum {
 } moe_act_t;
 
 typedef enum {
+  MOE_WEIGHTS_DTYPE = 0,  /* expert weights in cfg->dtype                       */
+  MOE_WEIGHTS_INT8 = 1    /* expert weights as int8 codes q with one fp32 scale
+                             per output row s (W = q * s), from
+                             moe_quantize_int8; bf16 SwiGLU layers at decode
+                             sizes only (T*K/N <= 24), else UNSUPPORTED     */
+} moe_weight_format_t;
+
+typedef enum {
   MOE_GATE_RENORM_ALL = 0,     /* softmax over all N, divided by the top-K sum */
   MOE_GATE_SOFTMAX_TOPK = 1,   /* softmax of the K chosen logits (same value)  */
   MOE_GATE_PROB_NO_RENORM = 2  /* softmax over all N, not renormalised         */
@@ -101,6 +109,7 @@ typedef struct {
   float noise_std;    /* scale of moe_weights_t.noise (used only with it)    */
   float bias_rate;    /* step of the selection-bias update written to
                          moe_stats_t.b_sel_out (used only with it)           */
+  int32_t weight_format; /* moe_weight_format_t of w1, w3, w2, ws1, ws3, ws2 */
 } moe_config_t;
 
 /* Weights.  Router: w_r [N, d] fp32, b_r [N] fp32 (nullable; also carries any
@@ -113,7 +122,11 @@ typedef struct {
  * noise [T, N] fp32 (nullable): this step's standard-normal draws, from
  * the caller's generator.  With it the router works on
  * logits + noise_std * noise from selection on (top-K, gates and every
- * statistic); the logits output still holds the noise-free logits.        */
+ * statistic); the logits output still holds the noise-free logits.
+ * With weight_format MOE_WEIGHTS_INT8, w1/w3/w2/ws1/ws3/ws2 hold int8 codes
+ * in the same layouts and the *_scale arrays their per-output-row fp32
+ * scales: w1_scale, w3_scale [N, F], w2_scale [N, d], ws1_scale,
+ * ws3_scale [F_shared], ws2_scale [d] (all required then, else ignored).  */
 typedef struct {
   const float* w_r;
   const float* b_r;
@@ -127,6 +140,12 @@ typedef struct {
   const void* ws3;
   const void* ws2;
   const float* noise;
+  const float* w1_scale;
+  const float* w3_scale;
+  const float* w2_scale;
+  const float* ws1_scale;
+  const float* ws3_scale;
+  const float* ws2_scale;
 } moe_weights_t;
 
 /* Router statistics (each pointer nullable):
@@ -265,6 +284,19 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
                                const void* x, const moe_layer_out_t* out,
                                void* ws, size_t ws_bytes, const moe_trace_t* trace,
                                void* stream);
+
+/* Weight-only INT8 quantization of a bf16 weight matrix w [rows, cols]
+ * (linear-layer layout [out, in]): q [rows, cols] int8 and scale [rows] fp32
+ * with s = absmax(row) / 127 and q = rint(w / s) (fp32, correctly rounded
+ * division, ties to even), clamped to [-127, 127]; a zero row gets s = 0,
+ * q = 0.  Symmetric per-row absmax quantization as published by Dettmers et
+ * al., "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale"
+ * (2022), section 2; the pages name no scheme.  Expert stacks [N, R, C] are
+ * quantized as rows = N*R.  Errors: INVALID_ARG for null pointers, rows < 0
+ * or cols <= 0; UNSUPPORTED for cols % 64 != 0 or rows*cols >= 2^40.
+ * rows == 0 enqueues nothing.                                              */
+moe_status_t moe_quantize_int8(const void* w, int64_t rows, int32_t cols, int8_t* q,
+                               float* scale, void* stream);
 
 #ifdef __cplusplus
 }

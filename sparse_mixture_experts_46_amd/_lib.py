@@ -11,12 +11,13 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_GELU_TANH = 0, 1
 MOE_GATE_RENORM_ALL, MOE_GATE_SOFTMAX_TOPK, MOE_GATE_PROB_NO_RENORM = 0, 1, 2
+MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_INT8 = 0, 1
 MOE_TRACE_EVENTS = 7
 
 EXPORTED = ("moe_status_string", "moe_capacity", "moe_workspace_size",
             "moe_router_workspace_size", "moe_dispatch_workspace_size",
             "moe_ffn_workspace_size", "moe_router_topk", "moe_dispatch",
-            "moe_expert_ffn", "moe_combine", "moe_layer_forward")
+            "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_quantize_int8")
 
 
 class MoeConfig(C.Structure):
@@ -24,12 +25,13 @@ class MoeConfig(C.Structure):
                 ("F", C.c_int32), ("F_shared", C.c_int32), ("dtype", C.c_int32),
                 ("act", C.c_int32), ("gate", C.c_int32), ("capacity", C.c_int64),
                 ("aux_alpha", C.c_float), ("flags", C.c_uint32), ("noise_std", C.c_float),
-                ("bias_rate", C.c_float)]
+                ("bias_rate", C.c_float), ("weight_format", C.c_int32)]
 
 
 class MoeWeights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("w_r", "b_r", "b_sel", "w1", "w3", "w2", "b1", "b2",
-                                          "ws1", "ws3", "ws2", "noise")]
+                                          "ws1", "ws3", "ws2", "noise", "w1_scale", "w3_scale",
+                                          "w2_scale", "ws1_scale", "ws3_scale", "ws2_scale")]
 
 
 class MoeStats(C.Structure):
@@ -83,6 +85,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.moe_expert_ffn.argtypes = [cfgp, wp, P, P, P, P, P, P, P, S, P]
     lib.moe_combine.restype = C.c_int
     lib.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
+    lib.moe_quantize_int8.restype = C.c_int
+    lib.moe_quantize_int8.argtypes = [P, C.c_int64, C.c_int32, P, P, P]
     lib.moe_layer_forward.restype = C.c_int
     lib.moe_layer_forward.argtypes = [cfgp, wp, P, C.POINTER(MoeLayerOut), P, S,
                                       C.POINTER(MoeTrace), P]

@@ -34,6 +34,7 @@ class Config:
     aux_alpha: float = 1.0
     noise_std: float = 0.0   # scale of the router noise (used with w["noise"])
     bias_rate: float = 0.0   # step of the selection-bias update (used with b_sel_out)
+    weight_format: str = "dtype"  # "dtype" or "int8" (see moe_quantize_int8)
 
     @property
     def torch_dtype(self):
@@ -45,7 +46,9 @@ class Config:
                            dtype=L.MOE_BF16 if self.dtype == "bf16" else L.MOE_F32,
                            act=_ACT[self.act], gate=_GATE[self.gate], capacity=self.capacity,
                            aux_alpha=self.aux_alpha, flags=0, noise_std=self.noise_std,
-                           bias_rate=self.bias_rate)
+                           bias_rate=self.bias_rate,
+                           weight_format=(L.MOE_WEIGHTS_INT8 if self.weight_format == "int8"
+                                          else L.MOE_WEIGHTS_DTYPE))
 
 
 def config_for(w: Workload) -> Config:
@@ -89,10 +92,35 @@ def moe_workspace_size(cfg: Config) -> int:
 
 def weights_struct(t: dict) -> L.MoeWeights:
     w = L.MoeWeights()
-    for k in ("w_r", "b_r", "b_sel", "w1", "w3", "w2", "b1", "b2", "ws1", "ws3", "ws2", "noise"):
+    for k in ("w_r", "b_r", "b_sel", "w1", "w3", "w2", "b1", "b2", "ws1", "ws3", "ws2", "noise",
+              "w1_scale", "w3_scale", "w2_scale", "ws1_scale", "ws3_scale", "ws2_scale"):
         v = t.get(k)
         setattr(w, k, None if v is None else _p(v).value)
     return w
+
+
+def moe_quantize_int8(w: torch.Tensor):
+    """bf16 weights [..., rows, cols] -> (int8 codes of the same shape, fp32
+    per-row scales [..., rows])."""
+    if w.dtype != torch.bfloat16:
+        raise ValueError("moe_quantize_int8 takes bf16 weights")
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    q = torch.empty(w.shape, dtype=torch.int8, device=w.device)
+    s = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    L.check(L.load().moe_quantize_int8(_p(w), rows, cols, _p(q), _p(s), _stream()),
+            "moe_quantize_int8")
+    return q, s
+
+
+def quantize_expert_weights(w: dict) -> dict:
+    """A copy of the weight dict with every expert matrix (w1, w3, w2 and the
+    shared ws1, ws3, ws2) replaced by int8 codes plus its *_scale."""
+    out = dict(w)
+    for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2"):
+        if w.get(k) is not None:
+            out[k], out[k + "_scale"] = moe_quantize_int8(w[k])
+    return out
 
 
 def moe_router_topk(cfg: Config, w: dict, x: torch.Tensor, want_logits=False,

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["moe_api.cpp", "router.hip", "dispatch.hip", "gemm_bf16.hip", "ffn_f32.hip",
+SOURCES = ["moe_api.cpp", "router.hip", "dispatch.hip", "gemm_bf16.hip", "ffn_f32.hip", "quant.hip",
            "combine.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

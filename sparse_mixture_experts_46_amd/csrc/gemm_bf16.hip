@@ -82,15 +82,20 @@ hipError_t run_skinny(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   const int64_t cap = (int64_t)num_cus() * 16;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
-  gemm_skinny_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);
+  if (a.sc0)
+    gemm_skinny_q8_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);
+  else
+    gemm_skinny_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 // Tile shapes by the expected rows per expert.
 enum Kind { K_SKINNY = 0, K_SMALL = 1, K_MID = 2, K_BIG = 3, K_TAIL = 4, K_TAIL64 = 5 };
 
+constexpr double kSkinnyRows = 24.0;  // rows per expert up to which the skinny kernel runs
+
 Kind pick_kind(double rows_per_expert) {
-  if (rows_per_expert <= 24.0) return K_SKINNY;
+  if (rows_per_expert <= kSkinnyRows) return K_SKINNY;
   if (rows_per_expert <= 96.0) return K_SMALL;
   // 256-row tiles move fewer operand bytes per flop than 128-row ones; they
   // pay off from ~160 rows per expert on (DeepSeek-shaped prefill, ~256 rows
@@ -142,6 +147,10 @@ int64_t max_tiles_for(int64_t rows, int G, int bm, int64_t cols, int bno) {
 }  // namespace
 
 hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream);
+
+bool ffn_int8_supported(int64_t T, int K, int N) {
+  return pick_kind((double)(T * K) / (double)N) == K_SKINNY;
+}
 
 size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared, bool bf16) {
   (void)d; (void)N;
@@ -226,6 +235,13 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   g1.G = G;
   g1.split_bm = 0;
   g1.region = 0;
+  if (p.int8) {
+    if (k != K_SKINNY) return hipErrorNotSupported;  // checked on the host before
+    g1.sc0 = p.w1_scale;
+    g1.sc1 = p.w3_scale;
+    g1.scs0 = p.ws1_scale;
+    g1.scs1 = p.ws3_scale;
+  }
   if ((err = mark(0)) != hipSuccess) return err;
   const int64_t mt1 = max_tiles_for(rows + srows, G, bm1, Fm, bno1);
   err = swiglu ? run_kind<true, EPI_SILU_MUL>(k, g1, mt1, stream)
@@ -258,6 +274,10 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   g2.G = G;
   g2.split_bm = sbm2;
   g2.region = 0;
+  if (p.int8) {
+    g2.sc0 = p.w2_scale;
+    g2.scs0 = p.ws2_scale;
+  }
   const int64_t mt2 = max_tiles_for(rows + srows, G, bm2, p.d, bno2);
   err = run_kind<false, EPI_BIAS>(k, g2, mt2, stream);
   if (err != hipSuccess) return err;

@@ -35,6 +35,12 @@ struct GemmArgs {
   int G;
   int split_bm;             // 0: one launch covers every row; else see main_rows()
   int region;               // 0: main rows of each group, 1: the tail rows
+  // weight-only INT8 (skinny kernel only): b0/b1/bs0/bs1 then hold int8
+  // codes and these the per-output-row scales, [n_routed, Nout] / [Nout]
+  const float* sc0;
+  const float* sc1;
+  const float* scs0;
+  const float* scs1;
 };
 
 // Rows [0, main_rows) of a group go to the main launch, in tiles of split_bm

@@ -27,6 +27,11 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->flags != 0) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->aux_alpha)) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->noise_std) || !std::isfinite(c->bias_rate)) return MOE_ERR_INVALID_ARG;
+  if (c->weight_format != MOE_WEIGHTS_DTYPE && c->weight_format != MOE_WEIGHTS_INT8)
+    return MOE_ERR_INVALID_ARG;
+  if (c->weight_format == MOE_WEIGHTS_INT8 &&
+      (c->dtype != MOE_BF16 || c->act != MOE_ACT_SWIGLU || !ffn_int8_supported(c->T, c->K, c->N)))
+    return MOE_ERR_UNSUPPORTED;
   if (c->N > MOE_MAX_EXPERTS || c->K > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (c->d % 64 || c->F % 64 || c->F_shared % 64) return MOE_ERR_UNSUPPORTED;
   if (c->F_shared != 0 && (c->F_shared != c->F || c->act != MOE_ACT_SWIGLU)) return MOE_ERR_UNSUPPORTED;
@@ -144,7 +149,20 @@ moe_status_t check_weights_ffn(const moe_config_t* c, const moe_weights_t* w) {
   if (c->act == MOE_ACT_SWIGLU && !w->w3) return MOE_ERR_INVALID_ARG;
   if (c->act == MOE_ACT_SWIGLU && (w->b1 || w->b2)) return MOE_ERR_UNSUPPORTED;
   if (c->F_shared > 0 && (!w->ws1 || !w->ws3 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+  if (c->weight_format == MOE_WEIGHTS_INT8) {
+    if (!w->w1_scale || !w->w3_scale || !w->w2_scale) return MOE_ERR_INVALID_ARG;
+    if (c->F_shared > 0 && (!w->ws1_scale || !w->ws3_scale || !w->ws2_scale))
+      return MOE_ERR_INVALID_ARG;
+  }
   return MOE_OK;
+}
+
+void set_weights(FfnProblem& p, const moe_config_t* c, const moe_weights_t* w) {
+  p.w1 = w->w1; p.w3 = w->w3; p.w2 = w->w2; p.b1 = w->b1; p.b2 = w->b2;
+  p.ws1 = w->ws1; p.ws3 = w->ws3; p.ws2 = w->ws2;
+  p.int8 = c->weight_format == MOE_WEIGHTS_INT8;
+  p.w1_scale = w->w1_scale; p.w3_scale = w->w3_scale; p.w2_scale = w->w2_scale;
+  p.ws1_scale = w->ws1_scale; p.ws3_scale = w->ws3_scale; p.ws2_scale = w->ws2_scale;
 }
 
 // ---- stages ----------------------------------------------------------------
@@ -301,8 +319,7 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, const moe_weights_t* w, con
   p.T = cfg->T; p.d = cfg->d; p.N = cfg->N; p.K = cfg->K; p.F = cfg->F;
   p.F_shared = cfg->F_shared; p.act = cfg->act; p.bf16 = cfg->dtype == MOE_BF16;
   p.a = a; p.a_rows = a_rows; p.offset = offset;
-  p.w1 = w->w1; p.w3 = w->w3; p.w2 = w->w2; p.b1 = w->b1; p.b2 = w->b2;
-  p.ws1 = w->ws1; p.ws3 = w->ws3; p.ws2 = w->ws2;
+  set_weights(p, cfg, w);
   p.x_shared = x_shared; p.y_perm = y_perm; p.y_shared = y_shared;
   p.h = at<void>(ws, L.h);
   p.tile_base = at<int32_t>(ws, L.tile_base);
@@ -360,8 +377,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   p.T = cfg->T; p.d = cfg->d; p.N = cfg->N; p.K = cfg->K; p.F = cfg->F;
   p.F_shared = cfg->F_shared; p.act = cfg->act; p.bf16 = cfg->dtype == MOE_BF16;
   p.a = x; p.a_rows = d.row_pair; p.offset = d.offset;  // rows gathered in the GEMM
-  p.w1 = w->w1; p.w3 = w->w3; p.w2 = w->w2; p.b1 = w->b1; p.b2 = w->b2;
-  p.ws1 = w->ws1; p.ws3 = w->ws3; p.ws2 = w->ws2;
+  set_weights(p, cfg, w);
   p.x_shared = x;
   p.y_perm = at<void>(ws, L.y_perm);
   p.y_shared = cfg->F_shared > 0 ? at<void>(ws, L.y_shared) : nullptr;
@@ -375,6 +391,16 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
                      p.bf16, s) != hipSuccess)
     return MOE_ERR_HIP;
   return mark(6);
+}
+
+moe_status_t moe_quantize_int8(const void* w, int64_t rows, int32_t cols, int8_t* q, float* scale,
+                               void* stream) {
+  if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!w || !q || !scale) return MOE_ERR_INVALID_ARG;
+  if (cols % 64) return MOE_ERR_UNSUPPORTED;
+  if (rows * (int64_t)cols >= (int64_t(1) << 40)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_quantize_int8(w, rows, cols, q, scale, (hipStream_t)stream));
 }
 
 }  // extern "C"

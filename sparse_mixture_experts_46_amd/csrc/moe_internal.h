@@ -89,7 +89,14 @@ struct FfnProblem {
   void* y_perm;     // [T*K, d]
   void* y_shared;   // [T, d]
   int32_t* tile_base;  // [3 * (N + 2)] scratch: three tile tables
+  // weight-only INT8 (w1/w3/w2/ws* hold int8 codes): per-output-row scales
+  bool int8;
+  const float *w1_scale, *w3_scale, *w2_scale, *ws1_scale, *ws3_scale, *ws2_scale;
 };
+
+// INT8 weights are supported where the skinny (decode) kernel runs: at most
+// this many routed rows per expert on average.
+bool ffn_int8_supported(int64_t T, int K, int N);
 
 size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared,
                            bool bf16);
@@ -97,6 +104,11 @@ size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared,
 // GEMM, after it, after the main launch of the second grouped GEMM and after
 // its tail launch.
 hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipEvent_t* ev);
+
+// ----------------------------------------------------------- quantization --
+// w bf16 [rows, cols] -> q int8 [rows, cols], scale fp32 [rows]; cols % 8 == 0
+hipError_t launch_quantize_int8(const void* w, int64_t rows, int cols, int8_t* q, float* scale,
+                                hipStream_t stream);
 
 // --------------------------------------------------------------- combine --
 hipError_t launch_combine(const void* y_perm, const int32_t* pair_row,

@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def declared_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", txt)))
 
 
 @pytest.fixture(scope="module")
@@ -172,3 +172,33 @@ def test_zero_tokens_is_a_noop(lib):
     assert lib.moe_layer_forward(C.byref(c), C.byref(w), None, C.byref(out), None, 0, None,
                                  None) == L.MOE_OK
     assert lib.moe_combine(C.byref(c), None, None, None, None, None, None) == L.MOE_OK
+
+
+def test_int8_config_rules(lib):
+    """INT8 expert weights: bf16 SwiGLU layers at decode sizes only; the
+    scales are required; unknown formats are argument errors."""
+    dec = cfg_of(WL.MIXTRAL_DECODE, weight_format="int8")
+    assert dec.weight_format == L.MOE_WEIGHTS_INT8
+    assert ws_size(lib, dec)[0] == L.MOE_OK
+    assert ws_size(lib, cfg_of(WL.DEEPSEEK_DECODE, weight_format="int8"))[0] == L.MOE_OK
+    assert ws_size(lib, cfg_of(WL.MIXTRAL_PREFILL, weight_format="int8"))[0] == \
+        L.MOE_ERR_UNSUPPORTED  # 1024 rows per expert: not a decode size
+    assert ws_size(lib, cfg_of(WL.TINY, weight_format="int8"))[0] == \
+        L.MOE_ERR_UNSUPPORTED  # fp32 GELU layer
+    bad = cfg_of(WL.MIXTRAL_DECODE)
+    bad.weight_format = 2
+    assert ws_size(lib, bad)[0] == L.MOE_ERR_INVALID_ARG
+    fake = C.c_void_p(0x1000)
+    w = L.MoeWeights(w_r=0x1000, w1=0x1000, w3=0x1000, w2=0x1000)  # scales missing
+    assert lib.moe_expert_ffn(C.byref(dec), C.byref(w), fake, None, fake, fake, None, None, fake,
+                              1 << 40, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_quantize_rejects_before_launch(lib):
+    P = C.c_void_p
+    fake = P(0x1000)
+    assert lib.moe_quantize_int8(fake, -1, 64, fake, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_int8(fake, 4, 0, fake, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_int8(None, 4, 64, fake, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_int8(fake, 4, 96, fake, fake, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_int8(None, 0, 64, None, None, None) == L.MOE_OK  # nothing to do
