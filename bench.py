@@ -11,9 +11,11 @@ synthetic input already resident in HBM.  Prints ONE JSON line.
 Default workload: Mixtral-shaped prefill (T=4096, d=4096, N=8, top-2, SwiGLU
 F=14336, bf16).  Unless --no-decode, the line also carries the decode-shaped
 DeepSeek-V3 layer (T=128, d=7168, N=256, top-8, F=2048 + shared expert)
-measured the same way, as HBM GB/s on the expert weights it touches.  For
-each workload the router entry point is also timed alone, plain and with the
-training-time variants (noise, entropy, bias update): "router_train".
+measured the same way, as HBM GB/s on the expert weights it touches, and
+again with weight-only INT8 expert weights ("int8", the same for a
+decode-sized main workload).  For each workload the router entry point is
+also timed alone, plain and with the training-time variants (noise,
+entropy, bias update): "router_train".
 """
 from __future__ import annotations
 
@@ -103,7 +105,7 @@ def active_work(w, kept_rows):
     return flops_routed + flops_shared, g1_flops
 
 
-def run_workload(w, steps, warmup, ev):
+def run_workload(w, steps, warmup, ev, int8=False):
     import numpy as np
     import torch
 
@@ -113,6 +115,12 @@ def run_workload(w, steps, warmup, ev):
 
     inp = make_inputs(w, device="cuda")
     cfg = api.config_for(w)
+    if int8:
+        # weight-only INT8 expert weights (quantized once, outside the timing)
+        inp = api.quantize_expert_weights(inp)
+        cfg.weight_format = "int8"
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     bufs = api.LayerBuffers(cfg, torch.device("cuda"))
     wst = api.weights_struct(inp)
     traces = []
@@ -162,9 +170,28 @@ def run_workload(w, steps, warmup, ev):
     total_flops, g1_flops = active_work(w, kept_rows)
     mats = 3 if w.act == "swiglu" else 2
     wbytes = 2.0 * (touched * mats * w.d * w.F + (3 * w.d * w.F_shared if w.F_shared else 0))
+    if int8:  # one byte per weight plus a 4-byte scale per output row
+        wbytes = (touched * (mats * w.d * w.F + 4.0 * (2 * w.F + w.d)) +
+                  (3.0 * w.d * w.F_shared + 4.0 * (2 * w.F_shared + w.d) if w.F_shared else 0.0))
     res = dict(inp=inp, bufs=bufs, wall=wall, wall_graph=wall_graph, stage_ms=stage, kept_rows=kept_rows,
                touched=touched, total_flops=total_flops, g1_flops=g1_flops, wbytes=wbytes)
     return res
+
+
+def decode_record(w, steps, warmup, ev, int8=False):
+    """A decode-sized layer: step time and HBM GB/s on the expert weights it
+    touches (bf16 weights, or INT8 codes plus scales)."""
+    rd = run_workload(w, steps, warmup, ev, int8=int8)
+    msd = rd["wall_graph"] * 1e3 / steps
+    gbs = rd["wbytes"] / (msd * 1e-3) / 1e9
+    rec = {"workload": w.name, "T": w.T, "weights": "int8 + fp32 row scales" if int8 else w.dtype,
+           "ms_per_step": msd, "tokens_per_s": w.T / (msd * 1e-3),
+           "eager_ms_per_step": rd["wall"] * 1e3 / steps,
+           "touched_experts": rd["touched"], "weight_bytes": rd["wbytes"],
+           "hbm_gbs": gbs, "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                        "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
+           "stage_ms": {k: float(v) for k, v in zip(STAGES, rd["stage_ms"])}}
+    return rec, rd
 
 
 def router_train_timing(w, inp, steps, warmup, noise_std=0.1, bias_rate=1e-3):
@@ -326,20 +353,18 @@ def main():
         line["cpu_baseline"] = cpu_baseline(w, r["inp"], min(a.cpu_sample or w.T, w.T))
     del r
     torch.cuda.empty_cache()
+    if w.T * w.K <= 24 * w.N and w.act == "swiglu" and w.dtype == "bf16":
+        # a decode-sized main workload: also its INT8-weight variant
+        line["int8"], _ = decode_record(w, a.steps, a.warmup, ev, int8=True)
+        torch.cuda.empty_cache()
     if not a.no_decode:
         wd = WL.DEEPSEEK_DECODE
-        rd = run_workload(wd, a.steps, a.warmup, ev)
-        msd = rd["wall_graph"] * 1e3 / a.steps
-        gbs = rd["wbytes"] / (msd * 1e-3) / 1e9
-        line["decode"] = {
-            "workload": wd.name, "T": wd.T, "ms_per_step": msd, "tokens_per_s": wd.T / (msd * 1e-3),
-            "eager_ms_per_step": rd["wall"] * 1e3 / a.steps,
-            "touched_experts": rd["touched"], "weight_bytes": rd["wbytes"],
-            "hbm_gbs": gbs, "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
-            "stage_ms": {k: float(v) for k, v in zip(STAGES, rd["stage_ms"])},
-            "router_train": router_train_timing(wd, rd["inp"], a.steps, a.warmup),
-        }
+        rec, rd = decode_record(wd, a.steps, a.warmup, ev)
+        rec["router_train"] = router_train_timing(wd, rd["inp"], a.steps, a.warmup)
+        del rd
+        torch.cuda.empty_cache()
+        rec["int8"], _ = decode_record(wd, a.steps, a.warmup, ev, int8=True)
+        line["decode"] = rec
     print(json.dumps(line), flush=True)
 
 

@@ -17,6 +17,7 @@
 #include "gemm_common.h"
 #include "gemm_pingpong.h"
 #include "gemm_skinny.h"
+#include "gemm_decode.h"
 #include "gemm_tile.h"
 #include "moe_internal.h"
 
@@ -82,10 +83,19 @@ hipError_t run_skinny(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   const int64_t cap = (int64_t)num_cus() * 16;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
-  if (a.sc0)
-    gemm_skinny_q8_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);
-  else
-    gemm_skinny_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);
+  gemm_skinny_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// INT8 weights at decode sizes: one workgroup per 16-row x 64-column tile
+// (tile table built with those dims), up to 8 workgroups per CU.
+template <bool DUAL, int EPI>
+hipError_t run_decode_q8(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
+  int64_t grid = max_tiles;
+  const int64_t cap = (int64_t)num_cus() * 8;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  gemm_decode_q8_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -120,7 +130,8 @@ void kind_dims(Kind k, bool dual, int* bm, int* bno) {
 template <bool DUAL, int EPI>
 hipError_t run_kind(Kind k, const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   switch (k) {
-    case K_SKINNY: return run_skinny<DUAL, EPI>(a, max_tiles, s);
+    case K_SKINNY:
+      return a.sc0 ? run_decode_q8<DUAL, EPI>(a, max_tiles, s) : run_skinny<DUAL, EPI>(a, max_tiles, s);
     // swizzles: (row >> 1) & 7 for 128-byte rows, (row >> 2) & 3 for 64-byte
     // rows: conflict-free fragment reads on the 64-bank LDS
     case K_SMALL:  return run_tile<64, 256, 64, 1, 4, 2, 1, DUAL, EPI>(a, max_tiles, s);
@@ -192,6 +203,7 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   int bm1, bno1, bm2, bno2, tbm, tbno;
   kind_dims(k, swiglu, &bm1, &bno1);
   kind_dims(k, false, &bm2, &bno2);
+  if (p.int8) bno1 = bno2 = 64;  // the INT8 decode kernel's 16 x 64 tiles
   const Kind tk = (p.F % 128 == 0) ? K_TAIL : K_TAIL64;  // K of GEMM 2 is F
   kind_dims(tk, false, &tbm, &tbno);
   const int sbm2 = split2 ? bm2 : 0;
