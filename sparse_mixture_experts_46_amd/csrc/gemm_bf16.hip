@@ -13,10 +13,10 @@
 //
 // Host side: tile-shape choice per layer shape, the device tile tables, and
 // the two launches (gate/up with the fused activation, then down).  The
-// kernels are in gemm_tile.h (prefill) and gemm_skinny.h (decode).
+// kernels are in gemm_pingpong.h and gemm_tile.h (prefill) and gemm_decode.h
+// (decode).
 #include "gemm_common.h"
 #include "gemm_pingpong.h"
-#include "gemm_skinny.h"
 #include "gemm_decode.h"
 #include "gemm_tile.h"
 #include "moe_internal.h"
@@ -77,35 +77,28 @@ hipError_t run_pingpong(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Decode sizes: one workgroup per 16-row x 64-column tile (the tile table is
+// built with those dims), up to 16 workgroups per CU; bf16 or INT8 weights.
 template <bool DUAL, int EPI>
-hipError_t run_skinny(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
-  int64_t grid = (max_tiles + 3) / 4;
+hipError_t run_decode(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
+  int64_t grid = max_tiles;
   const int64_t cap = (int64_t)num_cus() * 16;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
-  gemm_skinny_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);
-  return hipGetLastError();
-}
-
-// INT8 weights at decode sizes: one workgroup per 16-row x 64-column tile
-// (tile table built with those dims), up to 8 workgroups per CU.
-template <bool DUAL, int EPI>
-hipError_t run_decode_q8(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
-  int64_t grid = max_tiles;
-  const int64_t cap = (int64_t)num_cus() * 8;
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
-  gemm_decode_q8_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);
+  if (a.sc0)
+    gemm_decode_kernel<DUAL, EPI, true><<<(unsigned)grid, 256, 0, s>>>(a);
+  else
+    gemm_decode_kernel<DUAL, EPI, false><<<(unsigned)grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 // Tile shapes by the expected rows per expert.
-enum Kind { K_SKINNY = 0, K_SMALL = 1, K_MID = 2, K_BIG = 3, K_TAIL = 4, K_TAIL64 = 5 };
+enum Kind { K_DECODE = 0, K_SMALL = 1, K_MID = 2, K_BIG = 3, K_TAIL = 4, K_TAIL64 = 5 };
 
-constexpr double kSkinnyRows = 24.0;  // rows per expert up to which the skinny kernel runs
+constexpr double kDecodeRows = 24.0;  // rows per expert up to which the decode kernel runs
 
 Kind pick_kind(double rows_per_expert) {
-  if (rows_per_expert <= kSkinnyRows) return K_SKINNY;
+  if (rows_per_expert <= kDecodeRows) return K_DECODE;
   if (rows_per_expert <= 96.0) return K_SMALL;
   // 256-row tiles move fewer operand bytes per flop than 128-row ones; they
   // pay off from ~160 rows per expert on (DeepSeek-shaped prefill, ~256 rows
@@ -118,7 +111,7 @@ Kind pick_kind(double rows_per_expert) {
 // (BM, BN) per kind; BNo = BN/2 for the dual (SwiGLU gate/up) GEMM.
 void kind_dims(Kind k, bool dual, int* bm, int* bno) {
   switch (k) {
-    case K_SKINNY: *bm = 16; *bno = 16; return;
+    case K_DECODE: *bm = 16; *bno = 64; return;
     case K_SMALL:  *bm = 64; *bno = dual ? 128 : 256; return;
     case K_MID:    *bm = 128; *bno = dual ? 128 : 256; return;
     case K_TAIL:   *bm = 32; *bno = dual ? 32 : 64; return;
@@ -130,8 +123,7 @@ void kind_dims(Kind k, bool dual, int* bm, int* bno) {
 template <bool DUAL, int EPI>
 hipError_t run_kind(Kind k, const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   switch (k) {
-    case K_SKINNY:
-      return a.sc0 ? run_decode_q8<DUAL, EPI>(a, max_tiles, s) : run_skinny<DUAL, EPI>(a, max_tiles, s);
+    case K_DECODE: return run_decode<DUAL, EPI>(a, max_tiles, s);
     // swizzles: (row >> 1) & 7 for 128-byte rows, (row >> 2) & 3 for 64-byte
     // rows: conflict-free fragment reads on the 64-bank LDS
     case K_SMALL:  return run_tile<64, 256, 64, 1, 4, 2, 1, DUAL, EPI>(a, max_tiles, s);
@@ -160,7 +152,7 @@ int64_t max_tiles_for(int64_t rows, int G, int bm, int64_t cols, int bno) {
 hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream);
 
 bool ffn_int8_supported(int64_t T, int K, int N) {
-  return pick_kind((double)(T * K) / (double)N) == K_SKINNY;
+  return pick_kind((double)(T * K) / (double)N) == K_DECODE;
 }
 
 size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared, bool bf16) {
@@ -203,7 +195,6 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   int bm1, bno1, bm2, bno2, tbm, tbno;
   kind_dims(k, swiglu, &bm1, &bno1);
   kind_dims(k, false, &bm2, &bno2);
-  if (p.int8) bno1 = bno2 = 64;  // the INT8 decode kernel's 16 x 64 tiles
   const Kind tk = (p.F % 128 == 0) ? K_TAIL : K_TAIL64;  // K of GEMM 2 is F
   kind_dims(tk, false, &tbm, &tbno);
   const int sbm2 = split2 ? bm2 : 0;
@@ -248,7 +239,7 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   g1.split_bm = 0;
   g1.region = 0;
   if (p.int8) {
-    if (k != K_SKINNY) return hipErrorNotSupported;  // checked on the host before
+    if (k != K_DECODE) return hipErrorNotSupported;  // checked on the host before
     g1.sc0 = p.w1_scale;
     g1.sc1 = p.w3_scale;
     g1.scs0 = p.ws1_scale;

@@ -1,4 +1,4 @@
-// Grouped-GEMM plumbing shared by the tile (prefill) and skinny (decode)
+// Grouped-GEMM plumbing shared by the tile (prefill) and decode
 // kernels: the argument block, the device-side tile table and epilogues.
 //
 // A group g is one expert: rows [offset[g], offset[g+1]) of the
@@ -35,7 +35,7 @@ struct GemmArgs {
   int G;
   int split_bm;             // 0: one launch covers every row; else see main_rows()
   int region;               // 0: main rows of each group, 1: the tail rows
-  // weight-only INT8 (skinny kernel only): b0/b1/bs0/bs1 then hold int8
+  // weight-only INT8 (decode kernel only): b0/b1/bs0/bs1 then hold int8
   // codes and these the per-output-row scales, [n_routed, Nout] / [Nout]
   const float* sc0;
   const float* sc1;

@@ -1,6 +1,8 @@
-// Grouped GEMM for decode-sized batches with weight-only INT8 weights.
+// Grouped GEMM for decode-sized batches (at most 24 rows per expert on
+// average), bf16 weights or weight-only INT8 weights (Q8).  The stream over
+// the touched experts' weights is what bounds it (HBM).
 //
-// W = q * s: int8 codes q [Nout, Kdim] per group with one fp32 scale per
+// Q8: W = q * s, int8 codes q [Nout, Kdim] per group with one fp32 scale per
 // output row.  q converts exactly to bf16 (|q| <= 127), the MFMAs
 // (v_mfma_f32_16x16x32_bf16) accumulate x * q in fp32 and the epilogue
 // multiplies by s.
@@ -12,10 +14,12 @@
 //    16 bytes apart so the fragment reads of 16 rows hit 16 distinct bank
 //    groups), double-buffered.  Every wave therefore reads the activations
 //    once from LDS instead of each wave loading them from L2.
-//  * Each wave streams only its 16 weight rows into registers, 16 bytes per
-//    lane per 64-wide K block (8 blocks per chunk), double-buffered across
-//    chunks, so the next chunk's weights are in flight while the current one
-//    is multiplied.
+//  * Each wave streams only its 16 weight rows into registers (per lane and
+//    64-wide K block: 16 bytes of int8 codes, or 32 bytes of bf16) in stages
+//    of 8 blocks (int8) or 4 blocks (bf16), double-buffered, so the next
+//    stage's weights are in flight while the current one is multiplied.
+//    Each stage's weights are issued before the next activation chunk, so
+//    waiting for them does not wait for that chunk.
 //  * K is walked in 64-wide blocks; within a block, lane part p (lane / 16)
 //    takes elements [16p, 16p + 16): the first 8 feed one MFMA and the last
 //    8 the next.  The same permutation of K applies to both operands, so the
@@ -25,15 +29,30 @@
 
 #include "gemm_common.h"
 #include "gemm_pingpong.h"  // buf_dma16
-#include "gemm_skinny.h"    // i8x8_to_bf16
 
 namespace moe {
 
-template <bool DUAL, int EPI>
-__global__ __launch_bounds__(256) void gemm_decode_q8_kernel(GemmArgs p) {
-  constexpr int KC = 512;        // K columns per chunk
-  constexpr int NB = KC / 64;    // 64-wide blocks per chunk
+// int8 codes (|q| <= 127) to bf16, exactly: 8 codes packed in two words.
+__device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  bf16x8_t r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = i < 4 ? lo : hi;
+    const int v = (int)(int8_t)((w >> (8 * (i & 3))) & 0xffu);
+    // exact: an integer of magnitude <= 128 has at most 8 significant bits
+    r[i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint((float)v) >> 16));
+  }
+  return r;
+}
+
+template <bool DUAL, int EPI, bool Q8>
+__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
+  constexpr int KC = 512;          // K columns per staged activation chunk
   constexpr int RB = KC * 2 + 16;  // LDS bytes per staged activation row
+  constexpr int BPB = Q8 ? 1 : 2;  // 16-byte weight loads per lane per 64-wide block
+  constexpr int SB = Q8 ? 8 : 4;   // 64-wide blocks per weight stage
+  constexpr int SPC = (KC / 64) / SB;  // weight stages per activation chunk
+  constexpr int ESZ = Q8 ? 1 : 2;  // weight element bytes
   __shared__ __attribute__((aligned(16))) char abuf[2][16 * RB];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -42,7 +61,8 @@ __global__ __launch_bounds__(256) void gemm_decode_q8_kernel(GemmArgs p) {
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const TileInfo ti = resolve_tile(p, tile, 16, 64);
     const int64_t Kd = p.Kdim;
-    const int nk = (int)((Kd + KC - 1) / KC);
+    const int nblk = (int)(Kd / 64);               // 64-wide blocks in K
+    const int nstage = (nblk + SB - 1) / SB;
     const uint32_t row_bytes = (uint32_t)Kd * 2;
     // wave w stages activation rows 4w .. 4w+3 of the tile
     const char* arow_ptr[4];
@@ -60,10 +80,10 @@ __global__ __launch_bounds__(256) void gemm_decode_q8_kernel(GemmArgs p) {
     }
     int n = ti.nt * 64 + wave * 16 + row;
     if (n >= ti.Nout) n = ti.Nout - 1;
-    const int64_t wrow = (ti.shared ? 0 : (int64_t)ti.g * p.b_stride) + (int64_t)n * Kd + part * 16;
-    const int8_t* pb0 = (const int8_t*)(ti.shared ? (const void*)p.bs0 : (const void*)p.b0) + wrow;
-    const int8_t* pb1 = DUAL ? (const int8_t*)(ti.shared ? (const void*)p.bs1 : (const void*)p.b1) + wrow
-                             : nullptr;
+    const int64_t wrow = ((ti.shared ? 0 : (int64_t)ti.g * p.b_stride) + (int64_t)n * Kd + part * 16) * ESZ;
+    const char* pb0 = (const char*)(ti.shared ? (const void*)p.bs0 : (const void*)p.b0) + wrow;
+    const char* pb1 = DUAL ? (const char*)(ti.shared ? (const void*)p.bs1 : (const void*)p.b1) + wrow
+                           : nullptr;
 
     auto issue_a = [&](int c, int buf) {
       uint32_t koff = (uint32_t)c * KC * 2 + (uint32_t)lane * 16;
@@ -71,53 +91,78 @@ __global__ __launch_bounds__(256) void gemm_decode_q8_kernel(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) buf_dma16(arow_ptr[i], koff, abuf[buf] + (wave * 4 + i) * RB);
     };
-    uint4 b0[2][NB], b1[2][NB];
-    auto issue_b = [&](int c, int set) {
-      const int nbl = (int)((Kd - (int64_t)c * KC) / 64) < NB ? (int)((Kd - (int64_t)c * KC) / 64) : NB;
+    uint4 b0[2][SB * BPB], b1[2][SB * BPB];
+    auto issue_b = [&](int st, int set) {
+      const int left = nblk - st * SB;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (j < nbl) {
-          const int64_t off = (int64_t)c * KC + j * 64;
-          b0[set][j] = *(const uint4*)(pb0 + off);
-          if (DUAL) b1[set][j] = *(const uint4*)(pb1 + off);
-        }
-      }
-    };
-
-    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int c, int buf, int set) {
-      const int nbl = (int)((Kd - (int64_t)c * KC) / 64) < NB ? (int)((Kd - (int64_t)c * KC) / 64) : NB;
-      const char* arow_l = abuf[buf] + row * RB + part * 32;
+      for (int j = 0; j < SB; ++j) {
+        if (j < left) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (j < nbl) {
-          const bf16x8_t fa0 = __builtin_bit_cast(bf16x8_t, *(const uint4*)(arow_l + j * 128));
-          const bf16x8_t fa1 = __builtin_bit_cast(bf16x8_t, *(const uint4*)(arow_l + j * 128 + 16));
-          const uint4 bb = b0[set][j];
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, i8x8_to_bf16(bb.x, bb.y), acc0, 0, 0, 0);
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa1, i8x8_to_bf16(bb.z, bb.w), acc0, 0, 0, 0);
-          if (DUAL) {
-            const uint4 cc = b1[set][j];
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, i8x8_to_bf16(cc.x, cc.y), acc1, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa1, i8x8_to_bf16(cc.z, cc.w), acc1, 0, 0, 0);
+          for (int u = 0; u < BPB; ++u) {
+            const int64_t off = ((int64_t)(st * SB + j) * 64) * ESZ + u * 16;
+            b0[set][j * BPB + u] = *(const uint4*)(pb0 + off);
+            if (DUAL) b1[set][j * BPB + u] = *(const uint4*)(pb1 + off);
           }
         }
       }
     };
 
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int st, int buf, int set) {
+      const int left = nblk - st * SB;
+      const char* arow_l = abuf[buf] + row * RB + part * 32 + ((st % SPC) * SB) * 128;
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        if (j < left) {
+          const bf16x8_t fa0 = __builtin_bit_cast(bf16x8_t, *(const uint4*)(arow_l + j * 128));
+          const bf16x8_t fa1 = __builtin_bit_cast(bf16x8_t, *(const uint4*)(arow_l + j * 128 + 16));
+          bf16x8_t w0a, w0b, w1a, w1b;
+          if (Q8) {
+            const uint4 bb = b0[set][j];
+            w0a = i8x8_to_bf16(bb.x, bb.y);
+            w0b = i8x8_to_bf16(bb.z, bb.w);
+            if (DUAL) {
+              const uint4 cc = b1[set][j];
+              w1a = i8x8_to_bf16(cc.x, cc.y);
+              w1b = i8x8_to_bf16(cc.z, cc.w);
+            }
+          } else {
+            w0a = __builtin_bit_cast(bf16x8_t, b0[set][2 * j]);
+            w0b = __builtin_bit_cast(bf16x8_t, b0[set][2 * j + 1]);
+            if (DUAL) {
+              w1a = __builtin_bit_cast(bf16x8_t, b1[set][2 * j]);
+              w1b = __builtin_bit_cast(bf16x8_t, b1[set][2 * j + 1]);
+            }
+          }
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, w0a, acc0, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa1, w0b, acc0, 0, 0, 0);
+          if (DUAL) {
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa0, w1a, acc1, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa1, w1b, acc1, 0, 0, 0);
+          }
+        }
+      }
+    };
+
+    constexpr int NA = 4;  // activation DMA instructions per wave per chunk
     issue_a(0, 0);
     issue_b(0, 0);
-    for (int c = 0; c < nk; ++c) {
-      const int cur = c & 1;
-      wait_vmcnt<0>();   // chunk c: this wave's activation rows and weights landed
-      __syncthreads();   // every wave's rows of chunk c; buffer cur ^ 1 no longer read
-      if (c + 1 < nk) {
-        issue_a(c + 1, cur ^ 1);
-        if (cur) issue_b(c + 1, 0);
-        else issue_b(c + 1, 1);
+    for (int st = 0; st < nstage; ++st) {
+      const int c = st / SPC;
+      const bool first = (st % SPC) == 0;
+      // weights of stage st landed (and, at a chunk's first stage, its
+      // activations: issued before stage st's weights); a later chunk's
+      // activations may still be in flight
+      if (first) wait_vmcnt<0>();
+      else wait_vmcnt<NA>();
+      if (first) __syncthreads();  // every wave's rows of chunk c; buffer (c+1)&1 free
+      if (st + 1 < nstage) {
+        if (st & 1) issue_b(st + 1, 0);
+        else issue_b(st + 1, 1);
       }
-      if (cur) compute(c, 1, 1);
-      else compute(c, 0, 0);
+      if (first && c + 1 < (nstage + SPC - 1) / SPC) issue_a(c + 1, (c + 1) & 1);
+      if (st & 1) compute(st, c & 1, 1);
+      else compute(st, c & 1, 0);
     }
     __syncthreads();  // the last buffer is read before the next tile stages into it
 
@@ -125,9 +170,12 @@ __global__ __launch_bounds__(256) void gemm_decode_q8_kernel(GemmArgs p) {
     const int col = ti.nt * 64 + wave * 16 + (lane & 15);
     if (col < ti.Nout) {
       uint16_t* cbase = ti.shared ? p.c_shared : p.c;
-      const int64_t si = ti.shared ? col : (int64_t)ti.g * p.Nout + col;
-      const float s0 = (ti.shared ? p.scs0 : p.sc0)[si];
-      const float s1 = DUAL ? (ti.shared ? p.scs1 : p.sc1)[si] : 0.f;
+      float s0 = 1.f, s1 = 1.f;  // bf16 weights carry no scales
+      if (Q8) {
+        const int64_t si = ti.shared ? col : (int64_t)ti.g * p.Nout + col;
+        s0 = (ti.shared ? p.scs0 : p.sc0)[si];
+        if (DUAL) s1 = (ti.shared ? p.scs1 : p.sc1)[si];
+      }
       float bias = 0.f;
       if (EPI != EPI_SILU_MUL && p.bias && !ti.shared)
         bias = bf16_to_f32(p.bias[(int64_t)ti.g * p.Nout + col]);

@@ -94,7 +94,7 @@ struct FfnProblem {
   const float *w1_scale, *w3_scale, *w2_scale, *ws1_scale, *ws3_scale, *ws2_scale;
 };
 
-// INT8 weights are supported where the skinny (decode) kernel runs: at most
+// INT8 weights are supported where the decode kernel runs: at most
 // this many routed rows per expert on average.
 bool ffn_int8_supported(int64_t T, int K, int N);
 

@@ -22,8 +22,7 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-GEMM_SRCS = ["gemm_bf16.hip", "gemm_common.h", "gemm_pingpong.h", "gemm_tile.h", "gemm_skinny.h",
-             "gemm_decode.h"]
+GEMM_SRCS = ["gemm_bf16.hip", "gemm_common.h", "gemm_pingpong.h", "gemm_tile.h", "gemm_decode.h"]
 
 
 def gemm_source_sha256() -> str:

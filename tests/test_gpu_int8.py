@@ -2,7 +2,7 @@
 
 moe_quantize_int8 must produce the oracle's codes and scales bit for bit
 (both decide them in fp32).  The whole layer with INT8 expert weights (its
-grouped GEMMs run the INT8 skinny kernel) is compared with the oracle
+grouped GEMMs run the INT8 decode kernel) is compared with the oracle
 computing on its own dequantized weights (q * s in float64), under the
 bf16 bar: max|err| <= 2e-2 max|oracle|.
 """

@@ -199,8 +199,8 @@ def test_dispatch_bad_ids_are_counted_and_dropped():
 
 FFN_CASES = [
     # name, act, dtype, rows per expert (list), d, F, shared
-    ("skinny_swiglu", "swiglu", "bf16", [3, 0, 1, 16, 17, 5, 2, 9], 256, 384, 0),
-    ("skinny_shared", "swiglu", "bf16", [4, 7, 1, 0] * 8, 192, 128, 128),
+    ("decode_swiglu", "swiglu", "bf16", [3, 0, 1, 16, 17, 5, 2, 9], 256, 384, 0),
+    ("decode_shared", "swiglu", "bf16", [4, 7, 1, 0] * 8, 192, 128, 128),
     ("small_gelu", "gelu_tanh", "bf16", [40, 0, 97, 64, 1, 33, 80, 65], 128, 512, 0),
     ("small_swiglu", "swiglu", "bf16", [50, 70, 3, 64, 65, 90, 11, 60], 256, 320, 0),
     ("mid_swiglu", "swiglu", "bf16", [300, 129, 1, 0, 257, 400, 128, 250], 192, 384, 0),
