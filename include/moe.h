@@ -195,7 +195,9 @@ typedef struct {
 } moe_dispatch_t;
 
 /* Outputs of the whole layer.  y [T, d] (dtype) is required; every other
- * pointer is nullable and, when NULL, the value lives in the workspace.   */
+ * pointer is nullable and, when NULL, the value lives in the workspace.
+ * y_perm [T*K, d] (dtype): each kept row's expert output before its gate
+ * (rows at and after offset[N] untouched); the backward pass reads it.   */
 typedef struct {
   void* y;
   int32_t* topk_idx;    /* [T, K] */
@@ -203,6 +205,7 @@ typedef struct {
   float* logits;        /* [T, N] */
   moe_stats_t stats;
   moe_dispatch_t dispatch;  /* x_perm is ignored (rows are gathered in place) */
+  void* y_perm;
 } moe_layer_out_t;
 
 /* Optional timing hooks: hipEvent_t handles recorded on `stream` at stage
@@ -297,6 +300,120 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
  * rows == 0 enqueues nothing.                                              */
 moe_status_t moe_quantize_int8(const void* w, int64_t rows, int32_t cols, int8_t* q,
                                float* scale, void* stream);
+
+/* ======================================================== backward ===
+ * The backward pass: for upstream gradients dy [T, d] of y and
+ * (aux, z, z_lse) of the three router losses, the gradient of
+ *     L = sum_{t,j} dy[t,j] y[t,j] + aux_g * aux + z_g * z + zlse_g * z_lse
+ * with respect to x, the router weights and every expert weight, i.e. what
+ * automatic differentiation computes through the PyTorch modules of mzlw.cn
+ * "MoE 混合专家模型稀疏激活的架构原理与负载均衡挑战" section 三 plus its
+ * 2.2 loss and the z-loss of wmrh.cn/news/98181 (Router Z-Loss).  Top-K
+ * selection, the capacity cut and the counts f are piecewise constant and
+ * pass no gradient (mstx.cn "MoE 如何替代 FFN？…", challenges: routing is a
+ * discrete choice); the selection-only bias gets none; the routing entropy is
+ * a diagnostic without gradient.  Router noise is additive, so with
+ * w->noise the gradient with respect to the logits equals that with respect
+ * to the noisy logits.  Only cfg->weight_format MOE_WEIGHTS_DTYPE is
+ * supported (UNSUPPORTED otherwise).  Expert weight gradients are in
+ * cfg->dtype (fp32 accumulation, rounded once); router gradients in fp32.
+ * Every pointer is a device pointer unless noted; the caller owns all
+ * memory; nothing is allocated or synchronised.  T == 0 zero-fills every
+ * gradient output and launches nothing else.                             */
+
+/* Forward values the backward pass reads (all required): what
+ * moe_layer_forward (or the staged entry points) wrote for the same x.   */
+typedef struct {
+  const float* logits;      /* [T, N] noise-free router logits              */
+  const int32_t* topk_idx;  /* [T, K]                                       */
+  const float* topk_gate;   /* [T, K]                                       */
+  const int32_t* count;     /* [N] pairs per expert before capacity         */
+  const int32_t* offset;    /* [N+1]                                        */
+  const int32_t* pair_row;  /* [T*K]                                        */
+  const int32_t* row_pair;  /* [T*K]                                        */
+  const void* y_perm;       /* [T*K, d] dtype, expert output per kept row   */
+} moe_saved_t;
+
+/* Gradient outputs.  dx [T, d] dtype; dw_r [N, d] fp32; db_r [N] fp32
+ * (nullable); dw1 [N, F, d], dw2 [N, d, F] and, SwiGLU, dw3 [N, F, d];
+ * GELU: db1 [N, F], db2 [N, d] (nullable; meaningful for layers with the
+ * biases); shared expert (F_shared > 0): dws1, dws3 [F, d], dws2 [d, F];
+ * dlogits [T, N] fp32 (nullable).  Experts that keep no row get zeros.   */
+typedef struct {
+  void* dx;
+  float* dw_r;
+  float* db_r;
+  void* dw1;
+  void* dw3;
+  void* dw2;
+  void* db1;
+  void* db2;
+  void* dws1;
+  void* dws3;
+  void* dws2;
+  float* dlogits;
+} moe_grads_t;
+
+/* Upstream gradients of the router losses (host values).                 */
+typedef struct {
+  float aux;
+  float z;
+  float z_lse;
+} moe_loss_grad_t;
+
+/* Bytes of workspace moe_layer_backward needs (host only); the staged
+ * entry points need at most as much.                                     */
+moe_status_t moe_backward_workspace_size(const moe_config_t* cfg, size_t* bytes);
+
+/* Combine backward (the transpose of moe_combine): for every kept pair
+ * d_perm[pair_row[p]] = topk_gate[p] * dy[p / K] and
+ * dgate[p] = dy[p / K] . y_perm[pair_row[p]] (fp32, a fixed-order wave
+ * reduction); a dropped pair gets dgate = 0.  d_perm [T*K, d] dtype
+ * (rows >= offset[N] untouched), dgate [T*K] fp32.                       */
+moe_status_t moe_combine_backward(const moe_config_t* cfg, const void* dy, const void* y_perm,
+                                  const float* topk_gate, const int32_t* pair_row,
+                                  void* d_perm, float* dgate, void* stream);
+
+/* Router backward: dlogits [T, N] from the gates (per cfg->gate, using only
+ * the kept pairs' dgate), the aux loss through p (f = count / (T K) fixed),
+ * z and z_lse, all on logits + noise_std * w->noise when w->noise is set;
+ * then dw_r = dlogits^T x and db_r = the column sums of dlogits (nullable),
+ * each reduced in a fixed order.  w->w_r is not read (x is).              */
+moe_status_t moe_router_backward(const moe_config_t* cfg, const moe_weights_t* w,
+                                 const void* x, const float* logits, const int32_t* topk_idx,
+                                 const int32_t* pair_row, const float* dgate,
+                                 const int32_t* count, moe_loss_grad_t loss_grad,
+                                 float* dlogits, float* dw_r, float* db_r,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFN backward over the expert-contiguous rows (the forward's
+ * first GEMM is recomputed from x): given d_perm (gradient of each kept
+ * row's expert output) and, with a shared expert, dy (its output's
+ * gradient), writes dx_perm [T*K, d] (each kept row's input gradient),
+ * dx_shared [T, d] (shared expert only, else NULL) and the weight members
+ * of grads (dw1, dw3, dw2, db1, db2, dws1, dws3, dws2 as described above).  */
+moe_status_t moe_expert_ffn_backward(const moe_config_t* cfg, const moe_weights_t* w,
+                                     const void* x, const int32_t* row_pair,
+                                     const int32_t* offset, const void* d_perm, const void* dy,
+                                     void* dx_perm, void* dx_shared, const moe_grads_t* grads,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch backward (the transpose of the row gather): dx[t] = sum over
+ * k of [pair_row[t,k] >= 0] dx_perm[pair_row[t,k]] (+ dx_shared[t]) (+ the
+ * router term dlogits[t] . w_r), fp32 in that order, rounded once.
+ * dx_shared, dlogits (with w_r) nullable.                               */
+moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dx_perm,
+                                   const int32_t* pair_row, const void* dx_shared,
+                                   const float* dlogits, const float* w_r, void* dx,
+                                   void* stream);
+
+/* The whole backward pass: combine, router, expert FFN and dispatch
+ * backward in that order.  ws must hold moe_backward_workspace_size(cfg)
+ * bytes.                                                                 */
+moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                                const moe_saved_t* saved, const void* dy,
+                                moe_loss_grad_t loss_grad, const moe_grads_t* grads,
+                                void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

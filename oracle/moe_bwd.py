@@ -203,7 +203,7 @@ class LayerGrads:
 
 def layer_backward(x, W, dy, *, K, act, gate_mode, cf=None, alpha=1.0, b_r=None,
                    b_sel=None, shared=None, noise=None, noise_std=0.0,
-                   c_aux=0.0, c_z=0.0, c_zlse=0.0):
+                   c_aux=0.0, c_z=0.0, c_zlse=0.0, idx=None):
     """All gradients of L (module docstring) for the layer that
     moe_ref.layer_forward computes with the same arguments.
 
@@ -211,21 +211,22 @@ def layer_backward(x, W, dy, *, K, act, gate_mode, cf=None, alpha=1.0, b_r=None,
     each expert's FFN backward over its kept rows, scattered back to the
     tokens; the shared expert's backward (its output enters with weight 1,
     [P5] section 5); the gate and loss gradients on the logits; the router
-    linear layer."""
+    linear layer.  idx: optional routing to use instead of this oracle's own
+    top-K choice (moe_ref.layer_forward)."""
     x = np.asarray(x, np.float64)
     T, d = x.shape
     N = W["w_r"].shape[0]
     dy = np.asarray(dy, np.float64)
     fwd = ref.layer_forward(x, W, K=K, act=act, gate_mode=gate_mode, cf=cf, alpha=alpha,
                             b_r=b_r, b_sel=b_sel, shared=shared, noise=noise,
-                            noise_std=noise_std)
+                            noise_std=noise_std, idx=idx)
     asg = fwd.asg
     d_perm, dgate = combine_backward(dy, fwd.y_perm, asg.pair_row, fwd.gates)
 
     dx = np.zeros((T, d))
-    dw1 = np.zeros(np.shape(W["w1"]))
-    dw2 = np.zeros(np.shape(W["w2"]))
-    dw3 = np.zeros(np.shape(W["w3"])) if act == "swiglu" else None
+    dw1 = np.zeros(W["w1"].shape)   # arrays, or stacks widened one expert at a time
+    dw2 = np.zeros(W["w2"].shape)
+    dw3 = np.zeros(W["w3"].shape) if act == "swiglu" else None
     has_b = act == "gelu_tanh" and W.get("b1") is not None
     db1 = np.zeros(np.shape(W["b1"])) if has_b else None
     db2 = np.zeros(np.shape(W["b2"])) if act == "gelu_tanh" and W.get("b2") is not None else None

@@ -432,7 +432,7 @@ class LayerResult:
 
 def layer_forward(x, W, *, K, act, gate_mode, cf=None, alpha=1.0,
                   b_r=None, b_sel=None, shared=None, tokens=None,
-                  experts_needed=True, noise=None, noise_std=0.0):
+                  experts_needed=True, noise=None, noise_std=0.0, idx=None):
     """Whole layer, in the order the pages give it: router logits, selection
     (scores + optional selection-only bias, [P4] 结构 4), gates (from the raw
     logits only), statistics, capacity and dispatch, per-expert FFN, shared
@@ -446,6 +446,10 @@ def layer_forward(x, W, *, K, act, gate_mode, cf=None, alpha=1.0,
     tokens (y rows of other tokens are NaN).
     noise: optional [T, N] standard-normal draws; with it the router works on
     noisy_logits(logits, noise, noise_std) from selection on.
+    idx: optional [T, K] chosen experts that replace this oracle's own top-K
+    choice (another implementation's decisions on near-tie tokens, so that
+    every later step can be compared from the same routing); the margin is
+    still this oracle's.
     """
     x = np.asarray(x, dtype=np.float64)
     T, d = x.shape
@@ -453,7 +457,8 @@ def layer_forward(x, W, *, K, act, gate_mode, cf=None, alpha=1.0,
     logits = router_logits(x, W["w_r"], b_r)
     used = logits if noise is None else noisy_logits(logits, noise, noise_std)
     scores = used if b_sel is None else used + np.asarray(b_sel, np.float64)[None, :]
-    idx, margin = select_topk(scores, K)
+    own, margin = select_topk(scores, K)
+    idx = own if idx is None else np.asarray(idx, dtype=np.int64)
     gates = gate_weights(used, idx, gate_mode)
     stats = router_stats(used, idx, alpha)
     cap = capacity(K, N, T, cf)

@@ -17,7 +17,9 @@ MOE_TRACE_EVENTS = 7
 EXPORTED = ("moe_status_string", "moe_capacity", "moe_workspace_size",
             "moe_router_workspace_size", "moe_dispatch_workspace_size",
             "moe_ffn_workspace_size", "moe_router_topk", "moe_dispatch",
-            "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_quantize_int8")
+            "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_quantize_int8",
+            "moe_backward_workspace_size", "moe_combine_backward", "moe_router_backward",
+            "moe_expert_ffn_backward", "moe_dispatch_backward", "moe_layer_backward")
 
 
 class MoeConfig(C.Structure):
@@ -45,7 +47,22 @@ class MoeDispatch(C.Structure):
 
 class MoeLayerOut(C.Structure):
     _fields_ = [("y", C.c_void_p), ("topk_idx", C.c_void_p), ("topk_gate", C.c_void_p),
-                ("logits", C.c_void_p), ("stats", MoeStats), ("dispatch", MoeDispatch)]
+                ("logits", C.c_void_p), ("stats", MoeStats), ("dispatch", MoeDispatch),
+                ("y_perm", C.c_void_p)]
+
+
+class MoeSaved(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("logits", "topk_idx", "topk_gate", "count", "offset",
+                                          "pair_row", "row_pair", "y_perm")]
+
+
+class MoeGrads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("dx", "dw_r", "db_r", "dw1", "dw3", "dw2", "db1",
+                                          "db2", "dws1", "dws3", "dws2", "dlogits")]
+
+
+class MoeLossGrad(C.Structure):
+    _fields_ = [("aux", C.c_float), ("z", C.c_float), ("z_lse", C.c_float)]
 
 
 class MoeTrace(C.Structure):
@@ -73,7 +90,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.moe_capacity.restype = C.c_int64
     lib.moe_capacity.argtypes = [C.c_int32, C.c_int32, C.c_int64, C.c_double]
     for name in ("moe_workspace_size", "moe_router_workspace_size",
-                 "moe_dispatch_workspace_size", "moe_ffn_workspace_size"):
+                 "moe_dispatch_workspace_size", "moe_ffn_workspace_size",
+                 "moe_backward_workspace_size"):
         f = getattr(lib, name)
         f.restype = C.c_int
         f.argtypes = [cfgp, C.POINTER(S)]
@@ -90,6 +108,19 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.moe_layer_forward.restype = C.c_int
     lib.moe_layer_forward.argtypes = [cfgp, wp, P, C.POINTER(MoeLayerOut), P, S,
                                       C.POINTER(MoeTrace), P]
+    gp = C.POINTER(MoeGrads)
+    lib.moe_combine_backward.restype = C.c_int
+    lib.moe_combine_backward.argtypes = [cfgp, P, P, P, P, P, P, P]
+    lib.moe_router_backward.restype = C.c_int
+    lib.moe_router_backward.argtypes = [cfgp, wp, P, P, P, P, P, P, MoeLossGrad, P, P, P, P, S,
+                                        P]
+    lib.moe_expert_ffn_backward.restype = C.c_int
+    lib.moe_expert_ffn_backward.argtypes = [cfgp, wp, P, P, P, P, P, P, P, gp, P, S, P]
+    lib.moe_dispatch_backward.restype = C.c_int
+    lib.moe_dispatch_backward.argtypes = [cfgp, P, P, P, P, P, P, P]
+    lib.moe_layer_backward.restype = C.c_int
+    lib.moe_layer_backward.argtypes = [cfgp, wp, P, C.POINTER(MoeSaved), P, MoeLossGrad, gp, P,
+                                       S, P]
     _lib = lib
     return lib
 

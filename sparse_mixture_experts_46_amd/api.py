@@ -206,9 +206,10 @@ def moe_combine(cfg: Config, y_perm: torch.Tensor, pair_row: torch.Tensor, gate:
 class LayerBuffers:
     """Preallocated outputs and workspace for repeated moe_layer_forward calls."""
 
-    def __init__(self, cfg: Config, device, want_logits=False):
+    def __init__(self, cfg: Config, device, want_logits=False, save_for_backward=False):
         T, N, K = cfg.T, cfg.N, cfg.K
         self.cfg = cfg
+        want_logits = want_logits or save_for_backward
         self.y = torch.empty((T, cfg.d), dtype=cfg.torch_dtype, device=device)
         self.idx = torch.empty((T, K), dtype=torch.int32, device=device)
         self.gate = torch.empty((T, K), dtype=torch.float32, device=device)
@@ -225,6 +226,8 @@ class LayerBuffers:
         self.row_pair = torch.empty(T * K, dtype=torch.int32, device=device)
         self.dropped = torch.empty(T * K, dtype=torch.uint8, device=device)
         self.counters = torch.empty(4, dtype=torch.int32, device=device)
+        self.y_perm = (torch.empty((T * K, cfg.d), dtype=cfg.torch_dtype, device=device)
+                       if save_for_backward else None)
         self.ws = _ws(moe_workspace_size(cfg), device)
         self.out = L.MoeLayerOut()
         self.out.y = _p(self.y).value
@@ -238,6 +241,7 @@ class LayerBuffers:
             kept=_p(self.kept).value, offset=_p(self.offset).value,
             pair_row=_p(self.pair_row).value, row_pair=_p(self.row_pair).value,
             dropped=_p(self.dropped).value, counters=_p(self.counters).value, x_perm=None)
+        self.out.y_perm = None if self.y_perm is None else _p(self.y_perm).value
         self.ccfg = cfg.c()
 
     def as_dict(self) -> dict:
@@ -248,10 +252,11 @@ class LayerBuffers:
 
 def moe_layer_forward(cfg: Config, w: dict, x: torch.Tensor, bufs: LayerBuffers | None = None,
                       wstruct: L.MoeWeights | None = None, trace: L.MoeTrace | None = None,
-                      want_logits=False) -> LayerBuffers:
+                      want_logits=False, save_for_backward=False) -> LayerBuffers:
     lib = L.load()
     if bufs is None:
-        bufs = LayerBuffers(cfg, x.device, want_logits=want_logits)
+        bufs = LayerBuffers(cfg, x.device, want_logits=want_logits,
+                            save_for_backward=save_for_backward)
     if wstruct is None:
         wstruct = weights_struct(w)
     L.check(lib.moe_layer_forward(C.byref(bufs.ccfg), C.byref(wstruct), _p(x), C.byref(bufs.out),
@@ -259,3 +264,137 @@ def moe_layer_forward(cfg: Config, w: dict, x: torch.Tensor, bufs: LayerBuffers 
                                   C.byref(trace) if trace is not None else None, _stream()),
             "moe_layer_forward")
     return bufs
+
+
+# ------------------------------------------------------------- backward ---
+
+def moe_backward_workspace_size(cfg: Config) -> int:
+    return _size(L.load().moe_backward_workspace_size, cfg)
+
+
+def _loss_grad(loss_grad) -> L.MoeLossGrad:
+    a, z, zl = loss_grad
+    return L.MoeLossGrad(aux=float(a), z=float(z), z_lse=float(zl))
+
+
+class BackwardBuffers:
+    """Gradient outputs and workspace for repeated moe_layer_backward calls."""
+
+    def __init__(self, cfg: Config, device):
+        T, d, N, F, Fs = cfg.T, cfg.d, cfg.N, cfg.F, cfg.F_shared
+        dt, f32 = cfg.torch_dtype, torch.float32
+        e = lambda *shape, dtype=dt: torch.empty(shape, dtype=dtype, device=device)  # noqa: E731
+        swiglu = cfg.act == "swiglu"
+        self.dx = e(T, d)
+        self.dw_r = e(N, d, dtype=f32)
+        self.db_r = e(N, dtype=f32)
+        self.dw1 = e(N, F, d)
+        self.dw3 = e(N, F, d) if swiglu else None
+        self.dw2 = e(N, d, F)
+        self.db1 = None if swiglu else e(N, F)
+        self.db2 = None if swiglu else e(N, d)
+        self.dws1 = e(Fs, d) if Fs else None
+        self.dws3 = e(Fs, d) if Fs else None
+        self.dws2 = e(d, Fs) if Fs else None
+        self.dlogits = e(T, N, dtype=f32)
+        self.ws = _ws(moe_backward_workspace_size(cfg), device)
+        self.grads = L.MoeGrads(**{k: (None if getattr(self, k) is None
+                                       else _p(getattr(self, k)).value)
+                                   for k in ("dx", "dw_r", "db_r", "dw1", "dw3", "dw2", "db1",
+                                             "db2", "dws1", "dws3", "dws2", "dlogits")})
+        self.ccfg = cfg.c()
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k in ("dx", "dw_r", "db_r", "dw1", "dw3", "dw2", "db1",
+                                               "db2", "dws1", "dws3", "dws2", "dlogits")}
+
+
+def saved_struct(fwd: LayerBuffers) -> L.MoeSaved:
+    if fwd.y_perm is None or fwd.logits is None:
+        raise ValueError("run moe_layer_forward with save_for_backward=True first")
+    return L.MoeSaved(logits=_p(fwd.logits).value, topk_idx=_p(fwd.idx).value,
+                      topk_gate=_p(fwd.gate).value, count=_p(fwd.count).value,
+                      offset=_p(fwd.offset).value, pair_row=_p(fwd.pair_row).value,
+                      row_pair=_p(fwd.row_pair).value, y_perm=_p(fwd.y_perm).value)
+
+
+def moe_layer_backward(cfg: Config, w: dict, x: torch.Tensor, fwd: LayerBuffers,
+                       dy: torch.Tensor, loss_grad=(0.0, 0.0, 0.0),
+                       bufs: BackwardBuffers | None = None,
+                       wstruct: L.MoeWeights | None = None,
+                       saved: L.MoeSaved | None = None) -> BackwardBuffers:
+    """Gradients of sum(dy * y) + aux_g * aux + z_g * z + zlse_g * z_lse for
+    the forward recorded in ``fwd`` (loss_grad = (aux_g, z_g, zlse_g))."""
+    lib = L.load()
+    if bufs is None:
+        bufs = BackwardBuffers(cfg, x.device)
+    if wstruct is None:
+        wstruct = weights_struct(w)
+    if saved is None:
+        saved = saved_struct(fwd)
+    L.check(lib.moe_layer_backward(C.byref(bufs.ccfg), C.byref(wstruct), _p(x), C.byref(saved),
+                                   _p(dy), _loss_grad(loss_grad), C.byref(bufs.grads),
+                                   _p(bufs.ws), bufs.ws.numel(), _stream()),
+            "moe_layer_backward")
+    return bufs
+
+
+def moe_combine_backward(cfg: Config, dy: torch.Tensor, y_perm: torch.Tensor,
+                         gate: torch.Tensor, pair_row: torch.Tensor):
+    """-> (d_perm [T*K, d], dgate [T, K] fp32)."""
+    lib = L.load()
+    d_perm = torch.zeros((cfg.T * cfg.K, cfg.d), dtype=cfg.torch_dtype, device=dy.device)
+    dgate = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device=dy.device)
+    L.check(lib.moe_combine_backward(C.byref(cfg.c()), _p(dy), _p(y_perm), _p(gate),
+                                     _p(pair_row), _p(d_perm), _p(dgate), _stream()),
+            "moe_combine_backward")
+    return d_perm, dgate
+
+
+def moe_router_backward(cfg: Config, w: dict, x: torch.Tensor, logits: torch.Tensor,
+                        idx: torch.Tensor, pair_row: torch.Tensor, dgate: torch.Tensor,
+                        count: torch.Tensor, loss_grad=(0.0, 0.0, 0.0)):
+    """-> (dlogits [T, N], dw_r [N, d], db_r [N]), all fp32."""
+    lib = L.load()
+    dev = x.device
+    dl = torch.empty((cfg.T, cfg.N), dtype=torch.float32, device=dev)
+    dw_r = torch.empty((cfg.N, cfg.d), dtype=torch.float32, device=dev)
+    db_r = torch.empty(cfg.N, dtype=torch.float32, device=dev)
+    ws = _ws(moe_backward_workspace_size(cfg), dev)
+    L.check(lib.moe_router_backward(C.byref(cfg.c()), C.byref(weights_struct(w)), _p(x),
+                                    _p(logits), _p(idx), _p(pair_row), _p(dgate), _p(count),
+                                    _loss_grad(loss_grad), _p(dl), _p(dw_r), _p(db_r), _p(ws),
+                                    ws.numel(), _stream()), "moe_router_backward")
+    return dl, dw_r, db_r
+
+
+def moe_expert_ffn_backward(cfg: Config, w: dict, x: torch.Tensor, row_pair: torch.Tensor,
+                            offset: torch.Tensor, d_perm: torch.Tensor,
+                            dy: torch.Tensor | None = None) -> dict:
+    """-> dict of dx_perm [T*K, d], dx_shared [T, d] (shared expert) and the
+    weight gradients dw1, dw3, dw2, db1, db2, dws1, dws3, dws2."""
+    lib = L.load()
+    dev = x.device
+    g = BackwardBuffers(cfg, dev)
+    dx_perm = torch.zeros((cfg.T * cfg.K, cfg.d), dtype=cfg.torch_dtype, device=dev)
+    dx_shared = (torch.empty((cfg.T, cfg.d), dtype=cfg.torch_dtype, device=dev)
+                 if cfg.F_shared else None)
+    L.check(lib.moe_expert_ffn_backward(C.byref(cfg.c()), C.byref(weights_struct(w)), _p(x),
+                                        _p(row_pair), _p(offset), _p(d_perm), _p(dy),
+                                        _p(dx_perm), _p(dx_shared), C.byref(g.grads), _p(g.ws),
+                                        g.ws.numel(), _stream()), "moe_expert_ffn_backward")
+    out = {k: getattr(g, k) for k in ("dw1", "dw3", "dw2", "db1", "db2", "dws1", "dws3", "dws2")}
+    out.update(dx_perm=dx_perm, dx_shared=dx_shared, _ws=g.ws)
+    return out
+
+
+def moe_dispatch_backward(cfg: Config, dx_perm: torch.Tensor, pair_row: torch.Tensor,
+                          dx_shared: torch.Tensor | None = None,
+                          dlogits: torch.Tensor | None = None,
+                          w_r: torch.Tensor | None = None) -> torch.Tensor:
+    lib = L.load()
+    dx = torch.empty((cfg.T, cfg.d), dtype=cfg.torch_dtype, device=dx_perm.device)
+    L.check(lib.moe_dispatch_backward(C.byref(cfg.c()), _p(dx_perm), _p(pair_row), _p(dx_shared),
+                                      _p(dlogits), _p(w_r), _p(dx), _stream()),
+            "moe_dispatch_backward")
+    return dx

@@ -133,7 +133,7 @@ struct TileSpecs {
 
 // base[k][g] = sum_{g' < g} tiles of group g' under spec k (k < nspec);
 // tables are (n_routed + 2) apart.  One block of 1024 threads.
-__global__ __launch_bounds__(1024) void tile_setup_kernel(
+static __global__ __launch_bounds__(1024) void tile_setup_kernel(
     const int32_t* __restrict__ offset, int n_routed, int64_t shared_rows, TileSpecs specs,
     int nspec, int32_t* __restrict__ base) {
   __shared__ int32_t cnt[4][1040];

@@ -132,6 +132,43 @@ LayerWs layer_ws(const moe_config_t* c) {
   return w;
 }
 
+// Backward: router scratch (db_r block sums, dW_r split partials), the
+// expert FFN backward scratch, and the layer's intermediates.
+struct RouterBwdWs {
+  size_t part_db, part_dw, total;
+};
+RouterBwdWs router_bwd_ws(const moe_config_t* c) {
+  RouterBwdWs w;
+  size_t o = 0;
+  w.part_db = o; o = align_up(o + (size_t)router_bwd_num_blocks(c->T) * c->N * 4);
+  const int ns = router_dw_splits(c->T);
+  w.part_dw = o; o = align_up(o + (ns > 1 ? (size_t)ns * c->N * c->d * 4 : 0));
+  w.total = o;
+  return w;
+}
+
+struct BwdWs {
+  RouterBwdWs r;
+  size_t router, ffn, d_perm, dgate, dlogits, dx_perm, dx_shared, total;
+};
+BwdWs bwd_ws(const moe_config_t* c) {
+  BwdWs w;
+  w.r = router_bwd_ws(c);
+  const size_t pairs = (size_t)c->T * c->K;
+  const size_t eb = c->dtype == MOE_BF16 ? 2 : 4;
+  size_t o = 0;
+  w.router = o; o = align_up(o + w.r.total);
+  w.ffn = o; o = align_up(o + ffn_backward_workspace_bytes(c->T, c->d, c->N, c->K, c->F,
+                                                           c->F_shared, c->dtype == MOE_BF16));
+  w.d_perm = o; o = align_up(o + pairs * c->d * eb);
+  w.dgate = o; o = align_up(o + pairs * 4);
+  w.dlogits = o; o = align_up(o + (size_t)c->T * c->N * 4);
+  w.dx_perm = o; o = align_up(o + pairs * c->d * eb);
+  w.dx_shared = o; o = align_up(o + (c->F_shared > 0 ? (size_t)c->T * c->d * eb : 0));
+  w.total = o;
+  return w;
+}
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<unsigned char*>(ws) + off);
@@ -379,7 +416,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   p.a = x; p.a_rows = d.row_pair; p.offset = d.offset;  // rows gathered in the GEMM
   set_weights(p, cfg, w);
   p.x_shared = x;
-  p.y_perm = at<void>(ws, L.y_perm);
+  p.y_perm = out->y_perm ? out->y_perm : at<void>(ws, L.y_perm);
   p.y_shared = cfg->F_shared > 0 ? at<void>(ws, L.y_shared) : nullptr;
   p.h = fws + FL.h;
   p.tile_base = (int32_t*)(fws + FL.tile_base);
@@ -401,6 +438,187 @@ moe_status_t moe_quantize_int8(const void* w, int64_t rows, int32_t cols, int8_t
   if (cols % 64) return MOE_ERR_UNSUPPORTED;
   if (rows * (int64_t)cols >= (int64_t(1) << 40)) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_quantize_int8(w, rows, cols, q, scale, (hipStream_t)stream));
+}
+
+// ---- backward ---------------------------------------------------------------
+moe_status_t moe_backward_workspace_size(const moe_config_t* cfg, size_t* bytes) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  if (cfg->weight_format != MOE_WEIGHTS_DTYPE) return MOE_ERR_UNSUPPORTED;
+  *bytes = bwd_ws(cfg).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_combine_backward(const moe_config_t* cfg, const void* dy, const void* y_perm,
+                                  const float* topk_gate, const int32_t* pair_row, void* d_perm,
+                                  float* dgate, void* stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!dy || !y_perm || !topk_gate || !pair_row || !d_perm || !dgate) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine_backward(dy, y_perm, topk_gate, pair_row, cfg->T, cfg->K,
+                                            cfg->d, cfg->dtype == MOE_BF16, d_perm, dgate,
+                                            (hipStream_t)stream));
+}
+
+moe_status_t moe_router_backward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                                 const float* logits, const int32_t* topk_idx,
+                                 const int32_t* pair_row, const float* dgate,
+                                 const int32_t* count, moe_loss_grad_t lg, float* dlogits,
+                                 float* dw_r, float* db_r, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!w || !dw_r) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(lg.aux) || !std::isfinite(lg.z) || !std::isfinite(lg.z_lse))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (cfg->T == 0) {
+    if (launch_zero(dw_r, (size_t)cfg->N * cfg->d * 4, s) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(launch_zero(db_r, db_r ? (size_t)cfg->N * 4 : 0, s));
+  }
+  if (!x || !logits || !topk_idx || !pair_row || !dgate || !count || !dlogits)
+    return MOE_ERR_INVALID_ARG;
+  const RouterBwdWs R = router_bwd_ws(cfg);
+  if (!ws || ws_bytes < R.total) return MOE_ERR_WORKSPACE;
+  if (launch_router_backward(logits, w->noise, cfg->noise_std, topk_idx, pair_row, dgate, count,
+                             cfg->T, cfg->N, cfg->K, cfg->gate, cfg->aux_alpha, lg.aux, lg.z,
+                             lg.z_lse, dlogits, at<float>(ws, R.part_db), db_r, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return hip_status(launch_router_dw(dlogits, x, cfg->dtype == MOE_BF16, cfg->T, cfg->N, cfg->d,
+                                     at<float>(ws, R.part_dw), dw_r, s));
+}
+
+namespace {
+moe_status_t check_grads_ffn(const moe_config_t* c, const moe_grads_t* g) {
+  if (!g || !g->dw1 || !g->dw2) return MOE_ERR_INVALID_ARG;
+  if (c->act == MOE_ACT_SWIGLU && !g->dw3) return MOE_ERR_INVALID_ARG;
+  if (c->F_shared > 0 && (!g->dws1 || !g->dws3 || !g->dws2)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// Zero every weight gradient (T == 0: no rows, so every gradient is 0).
+moe_status_t zero_grads(const moe_config_t* c, const moe_grads_t* g, hipStream_t s) {
+  const size_t eb = c->dtype == MOE_BF16 ? 2 : 4;
+  const size_t fd = (size_t)c->F * c->d;
+  const size_t fs = (size_t)c->F_shared * c->d;
+  struct { void* p; size_t n; } z[] = {
+      {g->dw1, c->N * fd * eb}, {g->dw3, c->N * fd * eb}, {g->dw2, c->N * fd * eb},
+      {g->db1, (size_t)c->N * c->F * eb}, {g->db2, (size_t)c->N * c->d * eb},
+      {g->dws1, fs * eb}, {g->dws3, fs * eb}, {g->dws2, fs * eb}};
+  for (auto& e : z)
+    if (launch_zero(e.p, e.n, s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status_t do_ffn_backward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                             const int32_t* row_pair, const int32_t* offset, const void* d_perm,
+                             const void* dy, void* dx_perm, void* dx_shared,
+                             const moe_grads_t* g, void* ws, hipStream_t s) {
+  FfnBwdProblem p = {};
+  p.T = cfg->T; p.d = cfg->d; p.N = cfg->N; p.K = cfg->K; p.F = cfg->F;
+  p.F_shared = cfg->F_shared; p.act = cfg->act; p.bf16 = cfg->dtype == MOE_BF16;
+  p.x = x; p.row_pair = row_pair; p.offset = offset;
+  p.w1 = w->w1; p.w3 = w->w3; p.w2 = w->w2; p.b1 = w->b1;
+  p.ws1 = w->ws1; p.ws3 = w->ws3; p.ws2 = w->ws2;
+  p.d_perm = d_perm; p.dy = dy; p.dx_perm = dx_perm; p.dx_shared = dx_shared;
+  p.dw1 = g->dw1; p.dw3 = g->dw3; p.dw2 = g->dw2;
+  // bias gradients only for layers that have the biases
+  p.db1 = w->b1 ? g->db1 : nullptr;
+  p.db2 = w->b2 ? g->db2 : nullptr;
+  p.dws1 = g->dws1; p.dws3 = g->dws3; p.dws2 = g->dws2;
+  p.ws = ws;
+  if (launch_expert_ffn_backward(p, s) != hipSuccess) return MOE_ERR_HIP;
+  const size_t eb = p.bf16 ? 2 : 4;
+  if (!w->b1 && g->db1 && launch_zero(g->db1, (size_t)cfg->N * cfg->F * eb, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (!w->b2 && g->db2 && launch_zero(g->db2, (size_t)cfg->N * cfg->d * eb, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status_t moe_expert_ffn_backward(const moe_config_t* cfg, const moe_weights_t* w,
+                                     const void* x, const int32_t* row_pair,
+                                     const int32_t* offset, const void* d_perm, const void* dy,
+                                     void* dx_perm, void* dx_shared, const moe_grads_t* grads,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->weight_format != MOE_WEIGHTS_DTYPE) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_weights_ffn(cfg, w)) != MOE_OK) return st;
+  if ((st = check_grads_ffn(cfg, grads)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (cfg->T == 0) return zero_grads(cfg, grads, s);
+  if (!x || !row_pair || !offset || !d_perm || !dx_perm) return MOE_ERR_INVALID_ARG;
+  if (cfg->F_shared > 0 && (!dy || !dx_shared)) return MOE_ERR_INVALID_ARG;
+  const size_t need = ffn_backward_workspace_bytes(cfg->T, cfg->d, cfg->N, cfg->K, cfg->F,
+                                                   cfg->F_shared, cfg->dtype == MOE_BF16);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return do_ffn_backward(cfg, w, x, row_pair, offset, d_perm, dy, dx_perm,
+                         cfg->F_shared > 0 ? dx_shared : nullptr, grads, ws, s);
+}
+
+moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dx_perm,
+                                   const int32_t* pair_row, const void* dx_shared,
+                                   const float* dlogits, const float* w_r, void* dx,
+                                   void* stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!dx_perm || !pair_row || !dx || (dlogits && !w_r)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_dx(dx_perm, pair_row, cfg->K, dx_shared, dlogits, w_r, cfg->N, cfg->T,
+                              cfg->d, cfg->dtype == MOE_BF16, dx, (hipStream_t)stream));
+}
+
+moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                                const moe_saved_t* sv, const void* dy, moe_loss_grad_t lg,
+                                const moe_grads_t* g, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->weight_format != MOE_WEIGHTS_DTYPE) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_weights_router(w)) != MOE_OK) return st;
+  if ((st = check_weights_ffn(cfg, w)) != MOE_OK) return st;
+  if ((st = check_grads_ffn(cfg, g)) != MOE_OK) return st;
+  if (!g->dw_r) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(lg.aux) || !std::isfinite(lg.z) || !std::isfinite(lg.z_lse))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (cfg->T == 0) {
+    if ((st = zero_grads(cfg, g, s)) != MOE_OK) return st;
+    if (launch_zero(g->dw_r, (size_t)cfg->N * cfg->d * 4, s) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(launch_zero(g->db_r, g->db_r ? (size_t)cfg->N * 4 : 0, s));
+  }
+  if (!x || !dy || !g->dx || !sv) return MOE_ERR_INVALID_ARG;
+  if (!sv->logits || !sv->topk_idx || !sv->topk_gate || !sv->count || !sv->offset ||
+      !sv->pair_row || !sv->row_pair || !sv->y_perm)
+    return MOE_ERR_INVALID_ARG;
+  const BwdWs B = bwd_ws(cfg);
+  if (!ws || ws_bytes < B.total) return MOE_ERR_WORKSPACE;
+  const bool bf16 = cfg->dtype == MOE_BF16;
+  void* d_perm = at<void>(ws, B.d_perm);
+  float* dgate = at<float>(ws, B.dgate);
+  float* dl = g->dlogits ? g->dlogits : at<float>(ws, B.dlogits);
+  void* dx_perm = at<void>(ws, B.dx_perm);
+  void* dx_shared = cfg->F_shared > 0 ? at<void>(ws, B.dx_shared) : nullptr;
+  if (launch_combine_backward(dy, sv->y_perm, sv->topk_gate, sv->pair_row, cfg->T, cfg->K, cfg->d,
+                              bf16, d_perm, dgate, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  void* rws = at<void>(ws, B.router);
+  if (launch_router_backward(sv->logits, w->noise, cfg->noise_std, sv->topk_idx, sv->pair_row,
+                             dgate, sv->count, cfg->T, cfg->N, cfg->K, cfg->gate, cfg->aux_alpha,
+                             lg.aux, lg.z, lg.z_lse, dl, at<float>(rws, B.r.part_db), g->db_r,
+                             s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (launch_router_dw(dl, x, bf16, cfg->T, cfg->N, cfg->d, at<float>(rws, B.r.part_dw), g->dw_r,
+                       s) != hipSuccess)
+    return MOE_ERR_HIP;
+  st = do_ffn_backward(cfg, w, x, sv->row_pair, sv->offset, d_perm, dy, dx_perm, dx_shared, g,
+                       at<void>(ws, B.ffn), s);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_dx(dx_perm, sv->pair_row, cfg->K, dx_shared, dl, w->w_r, cfg->N,
+                              cfg->T, cfg->d, bf16, g->dx, s));
 }
 
 }  // extern "C"

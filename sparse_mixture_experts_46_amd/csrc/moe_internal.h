@@ -116,4 +116,53 @@ hipError_t launch_combine(const void* y_perm, const int32_t* pair_row,
                           int64_t T, int d, int K, bool bf16,
                           hipStream_t stream);
 
+// -------------------------------------------------------------- backward --
+// The backward pass (backward.hip).  Every GEMM operand and output is in the
+// layer dtype unless noted; rows = T*K routed rows then T shared rows.
+hipError_t launch_combine_backward(const void* dy, const void* y_perm, const float* gate,
+                                   const int32_t* pair_row, int64_t T, int K, int d, bool bf16,
+                                   void* d_perm, float* dgate, hipStream_t stream);
+
+// part: [router_bwd_num_blocks(T), N] fp32 scratch; db_r nullable.
+int64_t router_bwd_num_blocks(int64_t T);
+hipError_t launch_router_backward(const float* logits, const float* noise, float noise_std,
+                                  const int32_t* idx, const int32_t* pair_row, const float* dgate,
+                                  const int32_t* count, int64_t T, int N, int K, int gate_mode,
+                                  float alpha, float c_aux, float c_z, float c_zlse,
+                                  float* dlogits, float* part, float* db_r, hipStream_t stream);
+
+// dW_r = dlogits^T x; part: [router_dw_splits(T), N, d] fp32 scratch (unused
+// with one split).  T > 0.
+int router_dw_splits(int64_t T);
+hipError_t launch_router_dw(const float* dl, const void* x, bool bf16, int64_t T, int N, int d,
+                            float* part, float* dw_r, hipStream_t stream);
+
+// dx = sum of the token's kept rows of dx_perm (+ dx_shared) (+ dl W_r).
+hipError_t launch_dx(const void* dx_perm, const int32_t* pair_row, int K, const void* dx_shared,
+                     const float* dl, const float* w_r, int N, int64_t T, int d, bool bf16,
+                     void* dx, hipStream_t stream);
+
+struct FfnBwdProblem {
+  int64_t T;
+  int d, N, K, F, F_shared;
+  int act;  // moe_act_t
+  bool bf16;
+  const void* x;            // [T, d] layer input (rows gathered through row_pair / K)
+  const int32_t* row_pair;  // [T*K]
+  const int32_t* offset;    // [N+1]
+  const void *w1, *w3, *w2, *b1;
+  const void *ws1, *ws3, *ws2;
+  const void* d_perm;       // [T*K, d] gradient of each kept row's expert output
+  const void* dy;           // [T, d] gradient of the shared expert's output
+  void* dx_perm;            // [T*K, d] out: gradient of each kept row's input
+  void* dx_shared;          // [T, d] out (shared expert only)
+  void *dw1, *dw3, *dw2, *db1, *db2, *dws1, *dws3, *dws2;  // out
+  void* ws;                 // ffn_backward_workspace_bytes
+};
+size_t ffn_backward_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared, bool bf16);
+hipError_t launch_expert_ffn_backward(const FfnBwdProblem& p, hipStream_t stream);
+
+// Fill n bytes at p with zeros (a kernel, so it can be captured in a graph).
+hipError_t launch_zero(void* p, size_t n, hipStream_t stream);
+
 }  // namespace moe

@@ -16,6 +16,7 @@ round-to-nearest-even where the layer runs in bf16):
   w2       [N, d, F]  down projection, N(0, 1/F)
   b1, b2   [N, F], [N, d]  expert biases (uniform init only)
   ws1/ws3  [Fs, d], ws2 [d, Fs]  the shared expert
+  dy       [T, d]     upstream gradient of the layer output (backward), N(0, 1)
 Large weight tensors are drawn one expert slab at a time, so the fp32
 temporaries stay small.
 """
@@ -28,7 +29,7 @@ import torch
 from .workloads import Workload
 
 ROLE = dict(x=1, w_r=2, b_r=3, b_sel=4, w1=5, w3=6, w2=7, b1=8, b2=9,
-            ws1=10, ws3=11, ws2=12)
+            ws1=10, ws3=11, ws2=12, dy=13)
 
 
 def _gen(w: Workload, role: str, device) -> torch.Generator:
@@ -98,6 +99,13 @@ def make_inputs(w: Workload, device="cpu") -> dict:
     else:
         t["ws1"] = t["ws3"] = t["ws2"] = None
     return t
+
+
+def make_dy(w: Workload, device="cpu") -> torch.Tensor:
+    """The upstream gradient of the layer output for a backward pass of
+    workload ``w``: [T, d] N(0, 1) in the layer dtype."""
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return _draw((w.T, w.d), "normal", 1.0, _gen(w, "dy", device), device, dt)
 
 
 def random_topk_indices(T: int, N: int, K: int, seed: int, skew: float = 0.0,
