@@ -15,7 +15,9 @@ measured the same way, as HBM GB/s on the expert weights it touches, and
 again with weight-only INT8 expert weights ("int8", the same for a
 decode-sized main workload).  For each workload the router entry point is
 also timed alone, plain and with the training-time variants (noise,
-entropy, bias update): "router_train".
+entropy, bias update): "router_train".  Unless --no-backward, "backward"
+times moe_layer_backward on the main workload (gradients of every input and
+weight for an upstream dy and the aux loss), with its stages.
 """
 from __future__ import annotations
 
@@ -43,6 +45,7 @@ def parse():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens the oracle runs for the CPU baseline (0: all T tokens)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -192,6 +195,104 @@ def decode_record(w, steps, warmup, ev, int8=False):
                                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
            "stage_ms": {k: float(v) for k, v in zip(STAGES, rd["stage_ms"])}}
     return rec, rd
+
+
+BWD_STAGES = ["combine_bwd", "router_bwd", "recompute_gemm1", "dh_gemm", "dw2_gemm",
+              "dx_perm_gemm", "dw1_dw3_gemm", "bias_grads", "dx"]
+
+
+def backward_work(w, kept_rows):
+    """Algorithmic flops of the backward's expert GEMMs (dgrad + wgrad: twice
+    the forward's), and the flops of each GEMM stage as launched (the
+    recompute of the first GEMM is extra work, not part of the algorithm)."""
+    rows, rs = kept_rows, (w.T if w.F_shared else 0)
+    dF = 2.0 * w.d * w.F
+    m = 2 if w.act == "swiglu" else 1  # first-GEMM weight matrices
+    stage = {"recompute_gemm1": dF * m * (rows + rs), "dh_gemm": dF * (rows + rs),
+             "dw2_gemm": dF * (rows + rs), "dx_perm_gemm": dF * m * (rows + rs),
+             "dw1_dw3_gemm": dF * m * (rows + rs)}
+    algo = stage["dh_gemm"] + stage["dw2_gemm"] + stage["dx_perm_gemm"] + stage["dw1_dw3_gemm"]
+    return algo, stage
+
+
+def backward_record(w, steps, warmup, ev):
+    """moe_layer_backward on the workload (aux-loss gradient 1, as in
+    training): graph-replayed step time, per-stage times from HIP events on
+    the library's stream, and the dominant GEMM's roofline."""
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_46_amd import _lib as L
+    from sparse_mixture_experts_46_amd import api
+    from sparse_mixture_experts_46_amd.inputs import make_dy, make_inputs
+
+    inp = make_inputs(w, device="cuda")
+    dy = make_dy(w, device="cuda")
+    cfg = api.config_for(w)
+    fwd = api.moe_layer_forward(cfg, inp, inp["x"], save_for_backward=True)
+    bufs = api.BackwardBuffers(cfg, torch.device("cuda"))
+    wst = api.weights_struct(inp)
+    saved = api.saved_struct(fwd)
+    lg = (1.0, 0.0, 0.0)
+
+    def step(trace=None):
+        api.moe_layer_backward(cfg, inp, inp["x"], fwd, dy, lg, bufs=bufs, wstruct=wst,
+                               saved=saved, trace=trace)
+
+    traces = []
+    for _ in range(steps):
+        t = L.MoeBwdTrace()
+        for i in range(L.MOE_BWD_TRACE_EVENTS):
+            t.ev[i] = ev.create()
+        traces.append(t)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(traces[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = np.zeros(len(BWD_STAGES))
+    for t in traces:
+        for j in range(len(BWD_STAGES)):
+            stage[j] += ev.elapsed(t.ev[j], t.ev[j + 1])
+        for i in range(L.MOE_BWD_TRACE_EVENTS):
+            ev.destroy(t.ev[i])
+    stage /= steps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del graph
+    kept = int(fwd.counters.cpu()[0])
+    algo, sflops = backward_work(w, kept)
+    st = {k: float(v) for k, v in zip(BWD_STAGES, stage)}
+    gemm = {k: sflops[k] / (st[k] * 1e-3) / 1e12 for k in sflops if st[k] > 0}
+    dom = max(sflops, key=lambda k: st[k])
+    tf = gemm[dom]
+    return {"workload": w.name, "ms_per_step": ms, "eager_ms_per_step": wall * 1e3 / steps,
+            "tokens_per_s": w.T / (ms * 1e-3), "loss_grad": {"aux": lg[0], "z": lg[1], "z_lse": lg[2]},
+            "algorithmic_tflop": algo / 1e12,
+            "active_tflops": algo / (ms * 1e-3) / 1e12,
+            "active_frac_of_bf16_peak": algo / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "stage_ms": st, "gemm_tflops": gemm,
+            "roofline": {"bound": "mfma", "kernel": dom, "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
+                         "avg_ms": st[dom], "flops_per_launch": sflops[dom]}}
 
 
 def router_train_timing(w, inp, steps, warmup, noise_std=0.1, bias_rate=1e-3):
@@ -353,6 +454,9 @@ def main():
         line["cpu_baseline"] = cpu_baseline(w, r["inp"], min(a.cpu_sample or w.T, w.T))
     del r
     torch.cuda.empty_cache()
+    if not a.no_backward:
+        line["backward"] = backward_record(w, a.steps, a.warmup, ev)
+        torch.cuda.empty_cache()
     if w.T * w.K <= 24 * w.N and w.act == "swiglu" and w.dtype == "bf16":
         # a decode-sized main workload: also its INT8-weight variant
         line["int8"], _ = decode_record(w, a.steps, a.warmup, ev, int8=True)

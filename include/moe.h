@@ -407,13 +407,26 @@ moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dx_perm,
                                    const float* dlogits, const float* w_r, void* dx,
                                    void* stream);
 
+/* Optional timing hooks of moe_layer_backward: hipEvent_t handles recorded
+ * on `stream` (any may be NULL): ev[0] before the combine backward, ev[1]
+ * after it, ev[2] after the router backward (dlogits, db_r, dw_r), ev[3]
+ * after the recompute of the first expert GEMM, ev[4] after the dh GEMM
+ * (with the activation backward), ev[5] after dw2, ev[6] after dx_perm,
+ * ev[7] after dw1 (and dw3), ev[8] after the bias gradients, ev[9] after
+ * the dispatch backward (dx).                                            */
+#define MOE_BWD_TRACE_EVENTS 10
+typedef struct {
+  void* ev[MOE_BWD_TRACE_EVENTS];
+} moe_bwd_trace_t;
+
 /* The whole backward pass: combine, router, expert FFN and dispatch
  * backward in that order.  ws must hold moe_backward_workspace_size(cfg)
- * bytes.                                                                 */
+ * bytes.  trace is nullable.                                             */
 moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
                                 const moe_saved_t* saved, const void* dy,
                                 moe_loss_grad_t loss_grad, const moe_grads_t* grads,
-                                void* ws, size_t ws_bytes, void* stream);
+                                void* ws, size_t ws_bytes, const moe_bwd_trace_t* trace,
+                                void* stream);
 
 #ifdef __cplusplus
 }

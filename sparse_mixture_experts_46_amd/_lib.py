@@ -13,6 +13,7 @@ MOE_ACT_SWIGLU, MOE_ACT_GELU_TANH = 0, 1
 MOE_GATE_RENORM_ALL, MOE_GATE_SOFTMAX_TOPK, MOE_GATE_PROB_NO_RENORM = 0, 1, 2
 MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_INT8 = 0, 1
 MOE_TRACE_EVENTS = 7
+MOE_BWD_TRACE_EVENTS = 10
 
 EXPORTED = ("moe_status_string", "moe_capacity", "moe_workspace_size",
             "moe_router_workspace_size", "moe_dispatch_workspace_size",
@@ -69,6 +70,10 @@ class MoeTrace(C.Structure):
     _fields_ = [("ev", C.c_void_p * MOE_TRACE_EVENTS)]
 
 
+class MoeBwdTrace(C.Structure):
+    _fields_ = [("ev", C.c_void_p * MOE_BWD_TRACE_EVENTS)]
+
+
 _lib = None
 
 
@@ -120,7 +125,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.moe_dispatch_backward.argtypes = [cfgp, P, P, P, P, P, P, P]
     lib.moe_layer_backward.restype = C.c_int
     lib.moe_layer_backward.argtypes = [cfgp, wp, P, C.POINTER(MoeSaved), P, MoeLossGrad, gp, P,
-                                       S, P]
+                                       S, C.POINTER(MoeBwdTrace), P]
     _lib = lib
     return lib
 

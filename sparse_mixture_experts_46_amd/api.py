@@ -322,7 +322,8 @@ def moe_layer_backward(cfg: Config, w: dict, x: torch.Tensor, fwd: LayerBuffers,
                        dy: torch.Tensor, loss_grad=(0.0, 0.0, 0.0),
                        bufs: BackwardBuffers | None = None,
                        wstruct: L.MoeWeights | None = None,
-                       saved: L.MoeSaved | None = None) -> BackwardBuffers:
+                       saved: L.MoeSaved | None = None,
+                       trace: L.MoeBwdTrace | None = None) -> BackwardBuffers:
     """Gradients of sum(dy * y) + aux_g * aux + z_g * z + zlse_g * z_lse for
     the forward recorded in ``fwd`` (loss_grad = (aux_g, z_g, zlse_g))."""
     lib = L.load()
@@ -334,7 +335,8 @@ def moe_layer_backward(cfg: Config, w: dict, x: torch.Tensor, fwd: LayerBuffers,
         saved = saved_struct(fwd)
     L.check(lib.moe_layer_backward(C.byref(bufs.ccfg), C.byref(wstruct), _p(x), C.byref(saved),
                                    _p(dy), _loss_grad(loss_grad), C.byref(bufs.grads),
-                                   _p(bufs.ws), bufs.ws.numel(), _stream()),
+                                   _p(bufs.ws), bufs.ws.numel(),
+                                   C.byref(trace) if trace is not None else None, _stream()),
             "moe_layer_backward")
     return bufs
 

@@ -473,7 +473,7 @@ hipError_t launch_zero(void* p, size_t n, hipStream_t s) {
 // ======================================================== expert GEMMs ====
 namespace {
 
-template <bool WG, bool BS, bool DUALB, bool DUALK, int EPI>
+template <int R, bool WG, bool BS, bool DUALB, bool DUALK, int EPI>
 hipError_t run_bwd(const BwdArgs& a, int64_t max_tiles, bool bf16, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   if (!bf16) {
@@ -481,8 +481,8 @@ hipError_t run_bwd(const BwdArgs& a, int64_t max_tiles, bool bf16, hipStream_t s
     gemm_bwd_f32_kernel<WG, BS, DUALB, DUALK, EPI><<<(unsigned)grid, 256, 0, s>>>(a, (int)max_tiles);
     return hipGetLastError();
   }
-  auto kern = gemm_bwd_kernel<WG, BS, DUALB, DUALK, EPI>;
-  constexpr size_t smem = 2 * 256 * 8 * 16;
+  auto kern = gemm_bwd_kernel<R, WG, BS, DUALB, DUALK, EPI>;
+  constexpr size_t smem = (size_t)2 * (2 * R) * 8 * 16;  // two stages of 2R rows x 128 bytes
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -490,9 +490,9 @@ hipError_t run_bwd(const BwdArgs& a, int64_t max_tiles, bool bf16, hipStream_t s
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  int64_t grid = (int64_t)cus() * 2;
+  int64_t grid = (int64_t)cus() * (R == 128 ? 2 : 1);
   if (max_tiles < grid) grid = ((max_tiles + 7) / 8) * 8;
-  kern<<<(unsigned)grid, 256, smem, s>>>(a, (int)max_tiles);
+  kern<<<(unsigned)grid, 2 * R, smem, s>>>(a, (int)max_tiles);
   return hipGetLastError();
 }
 
@@ -508,23 +508,47 @@ size_t ffn_backward_workspace_bytes(int64_t T, int d, int N, int K, int F, int F
                                     bool bf16) {
   const size_t el = bf16 ? 2 : 4;
   const int64_t rows = T * K + (F_shared > 0 ? T : 0);
-  (void)d;
   size_t o = (size_t)3 * (N + 2) * 4;
   o = (o + 255) / 256 * 256;
+  o += ((size_t)T * K * d * el + 255) / 256 * 256;  // x_perm
   return o + 3 * ((size_t)rows * F * el + 256);
 }
 
+namespace {
+// Tile side of the recompute and of the SwiGLU dx_perm GEMM (both with
+// K-contiguous loads or one strided operand that fits the registers at 256):
+// 256 with many rows per expert, else 128.  The other GEMMs (a K-strided B,
+// or the weight gradients) use 128: at 256 their loader state spills.
+int rows_tile(int64_t rows, int N) { return rows >= (int64_t)384 * N ? 256 : 128; }
+}  // namespace
+
+template <int RR>
+hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s);
+
 hipError_t launch_expert_ffn_backward(const FfnBwdProblem& p, hipStream_t s) {
+  if (p.bf16 && rows_tile(p.T * p.K, p.N) == 256) return ffn_backward_gemms<256>(p, s);
+  return ffn_backward_gemms<128>(p, s);  // fp32: 16 x 16 tiles whatever RR
+}
+
+template <int RR>
+hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
+  auto mark = [&](int i) -> hipError_t {
+    return (p.ev && p.ev[i]) ? hipEventRecord(p.ev[i], s) : hipSuccess;
+  };
   const bool bf16 = p.bf16, swiglu = p.act == 0;
   const int64_t rows = p.T * p.K;
   const int64_t srows = p.F_shared > 0 ? p.T : 0;
   const int G = p.N + (srows > 0 ? 1 : 0);
   const size_t el = bf16 ? 2 : 4;
   const int F = p.F, d = p.d;
-  // scratch: tile tables, then u (-> du), v (-> dv), h, each [rows + srows, F]
+  // scratch: tile tables, x_perm [rows, d] (x gathered into the expert-
+  // contiguous rows once, so no GEMM gathers in its K loop), then u (-> du),
+  // v (-> dv), h, each [rows + srows, F]
   unsigned char* w = (unsigned char*)p.ws;
   int32_t* tb = (int32_t*)w;
   size_t o = ((size_t)3 * (p.N + 2) * 4 + 255) / 256 * 256;
+  unsigned char* Xp = w + o;
+  o += ((size_t)rows * d * el + 255) / 256 * 256;
   const size_t buf = ((size_t)(rows + srows) * F * el + 255) / 256 * 256;
   unsigned char* U = w + o;
   unsigned char* V = U + buf;
@@ -533,33 +557,40 @@ hipError_t launch_expert_ffn_backward(const FfnBwdProblem& p, hipStream_t s) {
   unsigned char* Vs = V + (size_t)rows * F * el;
   unsigned char* Hs = H + (size_t)rows * F * el;
 
-  const int bm = bf16 ? 128 : 16;
-  const int bn = bf16 ? 128 : 16;
-  const int bno1 = (bf16 && swiglu) ? 64 : bn;  // dual B: half the tile's columns are outputs
+  constexpr int RX = RR;             // dual-K dx_perm (SwiGLU)
+  const int bm1 = bf16 ? RR : 16;    // recompute tiles
+  const int bm2 = bf16 ? 128 : 16;   // dh tiles
+  const int bm4 = bf16 ? (swiglu ? RX : 128) : 16;  // dx_perm tiles
+  const int wbm = bf16 ? 128 : 16;   // weight-gradient tiles
+  const int bno1 = (bf16 && swiglu) ? bm1 / 2 : bm1;  // dual B: half the tile's columns are outputs
   int32_t* base[3] = {tb, tb + (p.N + 2), tb + 2 * (p.N + 2)};
   TileSpecs specs = {};
-  specs.s[0] = {bm, bno1, F, p.F_shared, 0, 0};  // recompute: [rows, F]
-  specs.s[1] = {bm, bn, F, p.F_shared, 0, 0};    // dh: [rows, F]
-  specs.s[2] = {bm, bn, d, d, 0, 0};             // dx_perm: [rows, d]
+  specs.s[0] = {bm1, bno1, F, p.F_shared, 0, 0};  // recompute: [rows, F]
+  specs.s[1] = {bm2, bm2, F, p.F_shared, 0, 0};   // dh: [rows, F]
+  specs.s[2] = {bm4, bm4, d, d, 0, 0};            // dx_perm: [rows, d]
   tile_setup_kernel<<<1, 1024, 0, s>>>(p.offset, p.N, srows, specs, 3, tb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (rows > 0 && (e = launch_permute(p.x, (int)el, p.row_pair, p.offset, p.N, p.K, d, rows, Xp,
+                                      s)) != hipSuccess)
+    return e;
   const int64_t all_rows = rows + srows;
 
   // ---- 1. recompute u = x W1^T (+ b1) and v = x W3^T
   {
     BwdArgs a = {};
     a.offset = p.offset; a.n_routed = p.N; a.shared_rows = srows; a.tile_base = base[0]; a.G = G;
-    a.a = p.x; a.a_rows = p.row_pair; a.a_div = p.K; a.lda = d; a.a_shared = p.x;
+    a.a = Xp; a.lda = d; a.a_shared = p.x;
     a.b0 = p.w1; a.b1 = p.w3; a.b_stride = (int64_t)F * d; a.ldb = d;
     a.bs0 = p.ws1; a.bs1 = p.ws3;
     a.Nout = F; a.Nout_shared = p.F_shared; a.Kdim = d;
     a.bias = p.b1;
     a.c = U; a.c2 = V; a.c_shared = Us; a.c2_shared = Vs; a.ldc = F;
-    const int64_t mt = row_tiles_bound(all_rows, G, bm, F, bno1);
-    e = swiglu ? run_bwd<false, false, true, false, BEPI_UV>(a, mt, bf16, s)
-               : run_bwd<false, false, false, false, BEPI_STORE>(a, mt, bf16, s);
+    const int64_t mt = row_tiles_bound(all_rows, G, bm1, F, bno1);
+    e = swiglu ? run_bwd<RR, false, false, true, false, BEPI_UV>(a, mt, bf16, s)
+               : run_bwd<RR, false, false, false, false, BEPI_STORE>(a, mt, bf16, s);
     if (e != hipSuccess) return e;
+    if ((e = mark(0)) != hipSuccess) return e;
   }
   // ---- 2. dh = d_perm W2 (W2 [d, F] read transposed); du, dv, h in the epilogue
   {
@@ -569,10 +600,11 @@ hipError_t launch_expert_ffn_backward(const FfnBwdProblem& p, hipStream_t s) {
     a.b0 = p.w2; a.b_stride = (int64_t)d * F; a.ldb = F; a.bs0 = p.ws2;
     a.Nout = F; a.Nout_shared = p.F_shared; a.Kdim = d;
     a.c = U; a.c2 = V; a.c3 = H; a.c_shared = Us; a.c2_shared = Vs; a.c3_shared = Hs; a.ldc = F;
-    const int64_t mt = row_tiles_bound(all_rows, G, bm, F, bn);
-    e = swiglu ? run_bwd<false, true, false, false, BEPI_SWIGLU_BWD>(a, mt, bf16, s)
-               : run_bwd<false, true, false, false, BEPI_GELU_BWD>(a, mt, bf16, s);
+    const int64_t mt = row_tiles_bound(all_rows, G, bm2, F, bm2);
+    e = swiglu ? run_bwd<128, false, true, false, false, BEPI_SWIGLU_BWD>(a, mt, bf16, s)
+               : run_bwd<128, false, true, false, false, BEPI_GELU_BWD>(a, mt, bf16, s);
     if (e != hipSuccess) return e;
+    if ((e = mark(1)) != hipSuccess) return e;
   }
   // ---- 3. dW2[g] = d_perm_g^T h_g  ([d, F])
   {
@@ -582,9 +614,10 @@ hipError_t launch_expert_ffn_backward(const FfnBwdProblem& p, hipStream_t s) {
     a.b0 = H; a.ldb = F; a.bs0 = Hs;
     a.Mout = d; a.Nout = F; a.Nout_shared = F;
     a.c = p.dw2; a.c_shared = p.dws2; a.ldc = F; a.c_gstride = (int64_t)d * F;
-    const int64_t tiles = (int64_t)G * ((d + bm - 1) / bm) * ((F + bn - 1) / bn);
-    e = run_bwd<true, false, false, false, BEPI_STORE>(a, tiles, bf16, s);
+    const int64_t tiles = (int64_t)G * ((d + wbm - 1) / wbm) * ((F + wbm - 1) / wbm);
+    e = run_bwd<128, true, false, false, false, BEPI_STORE>(a, tiles, bf16, s);
     if (e != hipSuccess) return e;
+    if ((e = mark(2)) != hipSuccess) return e;
   }
   // ---- 4. dx_perm = du W1 (+ dv W3)  (W1, W3 [F, d] read transposed)
   {
@@ -595,24 +628,26 @@ hipError_t launch_expert_ffn_backward(const FfnBwdProblem& p, hipStream_t s) {
     a.bs0 = p.ws1; a.bs1 = p.ws3;
     a.Nout = d; a.Nout_shared = d; a.Kdim = F;
     a.c = p.dx_perm; a.c_shared = p.dx_shared; a.ldc = d;
-    const int64_t mt = row_tiles_bound(all_rows, G, bm, d, bn);
-    e = swiglu ? run_bwd<false, true, false, true, BEPI_STORE>(a, mt, bf16, s)
-               : run_bwd<false, true, false, false, BEPI_STORE>(a, mt, bf16, s);
+    const int64_t mt = row_tiles_bound(all_rows, G, bm4, d, bm4);
+    e = swiglu ? run_bwd<RX, false, true, false, true, BEPI_STORE>(a, mt, bf16, s)
+               : run_bwd<128, false, true, false, false, BEPI_STORE>(a, mt, bf16, s);
     if (e != hipSuccess) return e;
+    if ((e = mark(3)) != hipSuccess) return e;
   }
   // ---- 5. dW1[g] = du_g^T x_g, dW3[g] = dv_g^T x_g  ([F, d])
   for (int pass = 0; pass < (swiglu ? 2 : 1); ++pass) {
     BwdArgs a = {};
     a.offset = p.offset; a.n_routed = p.N; a.shared_rows = srows; a.G = G;
     a.a = pass ? V : U; a.lda = F; a.a_shared = pass ? Vs : Us;
-    a.b0 = p.x; a.b_rows = p.row_pair; a.b_div = p.K; a.ldb = d; a.bs0 = p.x;
+    a.b0 = Xp; a.ldb = d; a.bs0 = p.x;
     a.Mout = F; a.Nout = d; a.Nout_shared = d;
     a.c = pass ? p.dw3 : p.dw1; a.c_shared = pass ? p.dws3 : p.dws1; a.ldc = d;
     a.c_gstride = (int64_t)F * d;
-    const int64_t tiles = (int64_t)G * ((F + bm - 1) / bm) * ((d + bn - 1) / bn);
-    e = run_bwd<true, false, false, false, BEPI_STORE>(a, tiles, bf16, s);
+    const int64_t tiles = (int64_t)G * ((F + wbm - 1) / wbm) * ((d + wbm - 1) / wbm);
+    e = run_bwd<128, true, false, false, false, BEPI_STORE>(a, tiles, bf16, s);
     if (e != hipSuccess) return e;
   }
+  if ((e = mark(4)) != hipSuccess) return e;
   // ---- 6. GELU biases: db1 = column sums of du, db2 = column sums of d_perm
   if (!swiglu && p.db1) {
     dim3 grid((unsigned)((F + 255) / 256), (unsigned)p.N);

@@ -14,10 +14,11 @@
 //    ragged.  A group with no rows gets C_g = 0.
 //
 // bf16 kernel (gfx950 matrix cores, v_mfma_f32_32x32x16_bf16, fp32
-// accumulation): 128 x 128 output tiles, 4 waves of 64 x 64, K in 64-wide
-// steps.  Waves 0-1 stage the A tile and waves 2-3 the B tile, global ->
-// registers -> LDS, the next step's loads in flight while the current one is
-// multiplied (two LDS buffers, one barrier per step).  A K-contiguous tile
+// accumulation): R x R output tiles (R = 128: 4 waves of 64 x 64; R = 256:
+// 8 waves of 128 x 64), K in 64-wide steps.  The first half of the waves
+// stage the A tile and the second half the B tile, global -> registers ->
+// LDS, the next step's loads in flight while the current one is multiplied
+// (two LDS buffers, one barrier per step).  A K-contiguous tile
 // row goes as 16-byte chunks.  A K-strided tile is read as 8 x 8 blocks (8 K
 // rows of 8 contiguous elements, each load a 16-byte run of one K row),
 // transposed in registers, and written as 8 K-contiguous 16-byte chunks.
@@ -103,11 +104,18 @@ __device__ __forceinline__ BwdTile bwd_tile(const BwdArgs& p, bool wgroups, int 
   BwdTile t;
   int local;
   if (wgroups) {
+    // the index over the smaller operand runs fastest, so the tiles of one
+    // round (one XCD's contiguous run) share slabs of the larger operand
     const int mtiles = (p.Mout + BM - 1) / BM, ntiles = (p.Nout + BN - 1) / BN;
     t.g = tile / (mtiles * ntiles);
     local = tile - t.g * mtiles * ntiles;
-    t.mt = local % mtiles;
-    t.nt = local / mtiles;
+    if (p.Mout > p.Nout) {
+      t.nt = local % ntiles;
+      t.mt = local / ntiles;
+    } else {
+      t.mt = local % mtiles;
+      t.nt = local / mtiles;
+    }
   } else {
     t.g = find_group(p.tile_base, p.G, tile);
     local = tile - p.tile_base[t.g];
@@ -129,55 +137,68 @@ __device__ __forceinline__ int64_t bwd_row(const BwdTile& t, const int32_t* rows
                                            int64_t ld, int r) {
   if (t.shared) return (int64_t)r * ld;
   const int64_t gr = t.row0 + r;
-  return (rows_map ? (int64_t)(rows_map[gr] / div) : gr) * ld;
+  if (!rows_map) return gr * ld;
+  const int32_t v = rows_map[gr];
+  return (int64_t)(div == 1 ? v : v / div) * ld;
 }
 
 __device__ __forceinline__ int bwd_swz(int row) { return (row >> 1) & 7; }
 
-// 8 x 8 transpose of 16-bit elements: in[i] holds row i (8 elements), out[j]
-// gets column j (element j of every in[i], in order of i).
-__device__ __forceinline__ void transpose8x8_b16(const uint4 (&in)[8], uint4 (&out)[8]) {
-  const uint32_t* w = (const uint32_t*)in;  // w[4 * i + c]: elements 2c, 2c+1 of row i
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int c = j >> 1;
-    uint32_t o[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint32_t lo = w[4 * (2 * v) + c], hi = w[4 * (2 * v + 1) + c];
-      o[v] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    out[j] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+// Column j of an 8 x 8 block of 16-bit elements whose row i is in[i]:
+// element j of every in[i], in order of i.  Word c of a row holds elements
+// 2c (low half) and 2c + 1 (high half).
+__device__ __forceinline__ uint32_t word_b32(const uint4& v, int c) {
+  return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
 }
 
-// WG: weight groups (else row groups).  BS: row groups with a K-strided B.
-// DUALB: B rows split gate/up (row groups, K-contiguous B).  DUALK: K runs
-// over (a, b0) then (a2, b1).
-template <bool WG, bool BS, bool DUALB, bool DUALK, int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_bwd_kernel(BwdArgs p, int total_tiles) {
-  constexpr int BM = 128, BN = 128, BK = 64, CH = 8;
+__device__ __forceinline__ uint4 transpose8x8_col_b16(const uint4 (&in)[8], int j) {
+  const int c = j >> 1;
+  uint32_t o[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint32_t lo = word_b32(in[2 * v], c), hi = word_b32(in[2 * v + 1], c);
+    o[v] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// R: tile side (R x R outputs; 2R threads, R / 32 waves, half of them
+// staging A and half B).  WG: weight groups (else row groups).  BS: row
+// groups with a K-strided B.  DUALB: B rows split gate/up (row groups,
+// K-contiguous B).  DUALK: K runs over (a, b0) then (a2, b1).
+template <int R, bool WG, bool BS, bool DUALB, bool DUALK, int EPI>
+__global__ __launch_bounds__(2 * R, R == 128 ? 2 : 1) void gemm_bwd_kernel(BwdArgs p,
+                                                                         int total_tiles) {
+  constexpr int BM = R, BN = R, BK = 64, CH = 8;
+  constexpr int NW = R / 32;                    // waves
+  constexpr int WM = 2, WN = NW / 2;            // wave grid
+  constexpr int TM = BM / WM, TN = BN / WN;     // wave tile
+  constexpr int FM = TM / 32, FN = TN / 32;     // 32 x 32 fragments per wave
   constexpr int BNo = DUALB ? BN / 2 : BN;
+  constexpr int RG = R / 8;                     // 8-row groups per operand tile
   constexpr bool A_STRIDED = WG;
   constexpr bool B_STRIDED = WG || BS;
+  static_assert(R == 128 || R == 256, "tile side");
   static_assert(!(DUALB && B_STRIDED), "dual B needs the K-contiguous layout");
+  static_assert(!DUALB || FN % 2 == 0, "dual B pairs gate and up fragments");
   extern __shared__ uint4 lds[];  // [2][(BM + BN) * CH]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const bool loads_a = wave < 2;
-  const int q = tid & 127;
+  const int wm = wave / WN, wn = wave % WN;
+  const bool loads_a = wave < NW / 2;
+  const int q = tid & (R - 1);
   const int khalf = lane >> 5;
   const int total = WG ? total_tiles : p.tile_base[p.G];
   const TileWalk walk = tile_walk(total);
 
-  int arow[2], brow[2];
+  int arow[FM], brow[FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) arow[i] = wm * 64 + i * 32 + (lane & 31);
+  for (int i = 0; i < FM; ++i) arow[i] = wm * TM + i * 32 + (lane & 31);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = DUALB ? (j == 0 ? wn * 32 : BN / 2 + wn * 32) : wn * 64 + j * 32;
+  for (int j = 0; j < FN; ++j) {
+    const int r = DUALB ? (j < FN / 2 ? wn * (TN / 2) + j * 32 : BN / 2 + wn * (TN / 2) + (j - FN / 2) * 32)
+                        : wn * TN + j * 32;
     brow[j] = BM + r + (lane & 31);
   }
 
@@ -187,30 +208,29 @@ __global__ __launch_bounds__(256, 2) void gemm_bwd_kernel(BwdArgs p, int total_t
     const int nk = (Ktot + BK - 1) / BK;
     // this thread's operand, wave-uniform
     const char* base0;  // first (or only) K half
-    const char* base1;  // second K half (dual K)
+    const char* base1;  // second K half (dual K) or the up rows (dual B)
     int64_t ld;
     if (loads_a) {
       base0 = (const char*)(ti.shared ? p.a_shared : p.a);
       base1 = DUALK ? (const char*)(ti.shared ? p.a2_shared : p.a2) : base0;
       ld = p.lda;
     } else {
-      const int64_t goff = ti.shared ? 0 : (int64_t)ti.g * p.b_stride * 2;
-      base0 = WG ? (const char*)(ti.shared ? p.bs0 : p.b0)
-                 : (const char*)(ti.shared ? p.bs0 : p.b0) + goff;
+      const int64_t goff = (ti.shared || WG) ? 0 : (int64_t)ti.g * p.b_stride * 2;
+      base0 = (const char*)(ti.shared ? p.bs0 : p.b0) + goff;
       base1 = (DUALK || DUALB) ? (const char*)(ti.shared ? p.bs1 : p.b1) + goff : base0;
       ld = p.ldb;
     }
     const bool strided = loads_a ? A_STRIDED : B_STRIDED;
-    // tile-row origin of this operand and its row limit
+    // tile-row origin of this thread's operand and its row limit
     const int r_org = loads_a ? ti.mt * BM : ti.nt * (WG ? BN : BNo);
     const int r_lim = loads_a ? (WG ? p.Mout : ti.rows) : ti.nout;
 
-    // K-contiguous operand: chunk c = q + 128 i -> tile row (q >> 3) + 16 i, chunk q & 7
+    // K-contiguous operand: chunk c = q + R i -> tile row (q >> 3) + RG i, chunk q & 7
     int64_t roff[8];
     if (!strided) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int tr = (q >> 3) + 16 * i;
+        const int tr = (q >> 3) + RG * i;
         if (loads_a) {
           int lr = r_org + tr;
           if (lr >= r_lim) lr = r_lim - 1;
@@ -224,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bwd_kernel(BwdArgs p, int total_t
       }
     }
     // K-strided operand: 8 x 8 block, tile rows rg*8 .. +7, K rows kg*8 .. +7
-    const int rg = q & 15, kg = q >> 4;
+    const int rg = q % RG, kg = q / RG;
     int col0 = r_org + rg * 8;
     if (col0 > r_lim - 8) col0 = r_lim - 8;  // past the edge: valid memory, never stored
 
@@ -239,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bwd_kernel(BwdArgs p, int total_t
       if (!strided) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const char* src = ((DUALB && !loads_a && (q >> 3) + 16 * i >= BN / 2) ? base1 : bs) + roff[i];
+          const char* src = ((DUALB && !loads_a && (q >> 3) + RG * i >= BN / 2) ? base1 : bs) + roff[i];
           st[i] = *(const uint4*)(src + (int64_t)(k0 + (q & 7) * 8) * 2);
         }
       } else {
@@ -265,25 +285,25 @@ __global__ __launch_bounds__(256, 2) void gemm_bwd_kernel(BwdArgs p, int total_t
       if (!strided) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int tr = (q >> 3) + 16 * i, ch = q & 7;
+          const int tr = (q >> 3) + RG * i, ch = q & 7;
           L[tr * CH + (ch ^ bwd_swz(tr))] = st[i];
         }
       } else {
-        uint4 tr8[8];
-        transpose8x8_b16(st, tr8);
+        // column j of the 8 x 8 block is tile row rg*8 + j at K chunk kg,
+        // written as soon as it is formed
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int tr = rg * 8 + j;
-          L[tr * CH + (kg ^ bwd_swz(tr))] = tr8[j];
+          L[tr * CH + (kg ^ bwd_swz(tr))] = transpose8x8_col_b16(st, j);
         }
       }
     };
 
-    f32x16_t acc[2][2];  // [weight fragment][token fragment]
+    f32x16_t acc[FN][FM];  // [weight fragment][token fragment]
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
 
@@ -298,17 +318,17 @@ __global__ __launch_bounds__(256, 2) void gemm_bwd_kernel(BwdArgs p, int total_t
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
         const int ch = ks * 2 + khalf;
-        bf16x8_t fa[2], fb[2];
+        bf16x8_t fa[FM], fb[FN];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FM; ++i)
           fa[i] = __builtin_bit_cast(bf16x8_t, s[arow[i] * CH + (ch ^ bwd_swz(arow[i]))]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
           fb[j] = __builtin_bit_cast(bf16x8_t, s[brow[j] * CH + (ch ^ bwd_swz(brow[j]))]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < FM; ++i)
             acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[j][i], 0, 0, 0);
       }
       if (kt + 1 < nk) store((kt + 1) & 1);
@@ -318,16 +338,16 @@ __global__ __launch_bounds__(256, 2) void gemm_bwd_kernel(BwdArgs p, int total_t
     // ---- epilogue.  acc[j][i][v]: output row = fragment i row lane % 32,
     // output column = fragment j column 8 * (v / 4) + 4 * (lane / 32) + v % 4.
     const int mlim = WG ? p.Mout : ti.rows;
-    constexpr int FO = DUALB ? 1 : 2;
+    constexpr int FO = DUALB ? FN / 2 : FN;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int m = ti.mt * BM + wm * 64 + i * 32 + (lane & 31);
+    for (int i = 0; i < FM; ++i) {
+      const int m = ti.mt * BM + wm * TM + i * 32 + (lane & 31);
       if (m >= mlim) continue;
       const int64_t rowoff = WG ? (ti.shared ? 0 : (int64_t)ti.g * p.c_gstride) + (int64_t)m * p.ldc
                                 : (ti.row0 + m) * p.ldc;
 #pragma unroll
       for (int j = 0; j < FO; ++j) {
-        const int cb = ti.nt * BNo + (DUALB ? wn * 32 : wn * 64 + j * 32) + 4 * khalf;
+        const int cb = ti.nt * BNo + (DUALB ? wn * (TN / 2) : wn * TN) + j * 32 + 4 * khalf;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int col = cb + 8 * qq;
@@ -337,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bwd_kernel(BwdArgs p, int total_t
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             r0[u] = acc[j][i][4 * qq + u];
-            r1[u] = DUALB ? acc[1][i][4 * qq + u] : 0.f;
+            r1[u] = DUALB ? acc[j + FN / 2][i][4 * qq + u] : 0.f;
           }
           if (EPI == BEPI_STORE_F32) {
             float* C = (float*)(ti.shared ? p.c_shared : p.c);
@@ -370,9 +390,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bwd_kernel(BwdArgs p, int total_t
               float dv[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const float s = silu_f(u[e]);
-                h[e] = s * v[e];
-                dv[e] = r0[e] * s;
+                const float sg = silu_f(u[e]);
+                h[e] = sg * v[e];
+                dv[e] = r0[e] * sg;
                 du[e] = r0[e] * v[e] * silu_grad_f(u[e]);
               }
               *(uint2*)(V + o) = make_uint2(pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]));

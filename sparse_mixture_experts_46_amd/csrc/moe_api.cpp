@@ -515,7 +515,8 @@ moe_status_t zero_grads(const moe_config_t* c, const moe_grads_t* g, hipStream_t
 moe_status_t do_ffn_backward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
                              const int32_t* row_pair, const int32_t* offset, const void* d_perm,
                              const void* dy, void* dx_perm, void* dx_shared,
-                             const moe_grads_t* g, void* ws, hipStream_t s) {
+                             const moe_grads_t* g, void* ws, hipStream_t s,
+                             const hipEvent_t* ev = nullptr) {
   FfnBwdProblem p = {};
   p.T = cfg->T; p.d = cfg->d; p.N = cfg->N; p.K = cfg->K; p.F = cfg->F;
   p.F_shared = cfg->F_shared; p.act = cfg->act; p.bf16 = cfg->dtype == MOE_BF16;
@@ -529,6 +530,7 @@ moe_status_t do_ffn_backward(const moe_config_t* cfg, const moe_weights_t* w, co
   p.db2 = w->b2 ? g->db2 : nullptr;
   p.dws1 = g->dws1; p.dws3 = g->dws3; p.dws2 = g->dws2;
   p.ws = ws;
+  p.ev = ev;
   if (launch_expert_ffn_backward(p, s) != hipSuccess) return MOE_ERR_HIP;
   const size_t eb = p.bf16 ? 2 : 4;
   if (!w->b1 && g->db1 && launch_zero(g->db1, (size_t)cfg->N * cfg->F * eb, s) != hipSuccess)
@@ -574,7 +576,8 @@ moe_status_t moe_dispatch_backward(const moe_config_t* cfg, const void* dx_perm,
 
 moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
                                 const moe_saved_t* sv, const void* dy, moe_loss_grad_t lg,
-                                const moe_grads_t* g, void* ws, size_t ws_bytes, void* stream) {
+                                const moe_grads_t* g, void* ws, size_t ws_bytes,
+                                const moe_bwd_trace_t* trace, void* stream) {
   moe_status_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (cfg->weight_format != MOE_WEIGHTS_DTYPE) return MOE_ERR_UNSUPPORTED;
@@ -602,9 +605,15 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   float* dl = g->dlogits ? g->dlogits : at<float>(ws, B.dlogits);
   void* dx_perm = at<void>(ws, B.dx_perm);
   void* dx_shared = cfg->F_shared > 0 ? at<void>(ws, B.dx_shared) : nullptr;
+  auto mark = [&](int i) -> moe_status_t {
+    if (trace && trace->ev[i]) return hip_status(hipEventRecord((hipEvent_t)trace->ev[i], s));
+    return MOE_OK;
+  };
+  if ((st = mark(0)) != MOE_OK) return st;
   if (launch_combine_backward(dy, sv->y_perm, sv->topk_gate, sv->pair_row, cfg->T, cfg->K, cfg->d,
                               bf16, d_perm, dgate, s) != hipSuccess)
     return MOE_ERR_HIP;
+  if ((st = mark(1)) != MOE_OK) return st;
   void* rws = at<void>(ws, B.router);
   if (launch_router_backward(sv->logits, w->noise, cfg->noise_std, sv->topk_idx, sv->pair_row,
                              dgate, sv->count, cfg->T, cfg->N, cfg->K, cfg->gate, cfg->aux_alpha,
@@ -614,11 +623,18 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   if (launch_router_dw(dl, x, bf16, cfg->T, cfg->N, cfg->d, at<float>(rws, B.r.part_dw), g->dw_r,
                        s) != hipSuccess)
     return MOE_ERR_HIP;
+  if ((st = mark(2)) != MOE_OK) return st;
+  hipEvent_t fev[5] = {};
+  if (trace)
+    for (int i = 0; i < 5; ++i) fev[i] = (hipEvent_t)trace->ev[3 + i];
   st = do_ffn_backward(cfg, w, x, sv->row_pair, sv->offset, d_perm, dy, dx_perm, dx_shared, g,
-                       at<void>(ws, B.ffn), s);
+                       at<void>(ws, B.ffn), s, fev);
   if (st != MOE_OK) return st;
-  return hip_status(launch_dx(dx_perm, sv->pair_row, cfg->K, dx_shared, dl, w->w_r, cfg->N,
-                              cfg->T, cfg->d, bf16, g->dx, s));
+  if ((st = mark(8)) != MOE_OK) return st;
+  if (launch_dx(dx_perm, sv->pair_row, cfg->K, dx_shared, dl, w->w_r, cfg->N, cfg->T, cfg->d, bf16,
+                g->dx, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return mark(9);
 }
 
 }  // extern "C"

@@ -158,6 +158,9 @@ struct FfnBwdProblem {
   void* dx_shared;          // [T, d] out (shared expert only)
   void *dw1, *dw3, *dw2, *db1, *db2, *dws1, *dws3, *dws2;  // out
   void* ws;                 // ffn_backward_workspace_bytes
+  // nullable, else 5 nullable events recorded after the recompute, the dh
+  // GEMM, dw2, dx_perm and dw1 (dw3)
+  const hipEvent_t* ev;
 };
 size_t ffn_backward_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared, bool bf16);
 hipError_t launch_expert_ffn_backward(const FfnBwdProblem& p, hipStream_t stream);

@@ -50,6 +50,8 @@ CASES = [
        gate="prob_no_renorm", cf=1.0, expert_bias=True, init="uniform", seed=46),
      (0.6, 0.2, 0.1), 0.0),
     (W(name="bwd_noise_swiglu", T=128, d=128, N=8, K=2, F=128, seed=47), (0.8, 0.0, 0.0), 0.5),
+    # >= 384 rows per expert: the 256-row tiles, ragged in rows, F and d
+    (W(name="bwd_big_tiles", T=1100, d=320, N=4, K=2, F=448, seed=52), (1.0, 0.1, 0.0), 0.0),
 ]
 
 
@@ -186,7 +188,8 @@ def test_zero_tokens_zero_fills_the_gradients():
     import ctypes as C
     st = lib.moe_layer_backward(C.byref(cfg.c()), C.byref(api.weights_struct(inp)), None,
                                 C.byref(saved), None, api._loss_grad((1.0, 1.0, 1.0)),
-                                C.byref(g.grads), api._p(g.ws), g.ws.numel(), api._stream())
+                                C.byref(g.grads), api._p(g.ws), g.ws.numel(), None,
+                                api._stream())
     assert st == api.L.MOE_OK
     torch.cuda.synchronize()
     for k in ("dw_r", "db_r", "dw1", "dw3", "dw2"):
