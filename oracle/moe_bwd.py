@@ -165,16 +165,19 @@ def gate_backward(used, idx, dgate, mode):
     return softmax_backward(P, dP)
 
 
-def stats_backward(used, count, K, alpha, c_aux=0.0, c_z=0.0, c_zlse=0.0):
+def stats_backward(used, count, K, alpha, c_aux=0.0, c_z=0.0, c_zlse=0.0, T=None):
     """dL/d(logits) through the losses of moe_ref.router_stats:
     aux = alpha N sum_e f_e p_e with p_e = mean_t P_te and f fixed
     ([P3] 2.2), z = mean_t sum_e l_te^2 ([P1] Router Z-Loss, literal
-    reading) and z_lse = mean_t lse_t^2 (not from the pages)."""
+    reading) and z_lse = mean_t lse_t^2 (not from the pages).  Each token's
+    row depends only on its own logits, so `used` may hold a subset of the
+    rows; T is then the batch's token count (default: the rows given)."""
     used = np.asarray(used, np.float64)
-    T, N = used.shape
+    N = used.shape[1]
+    T = used.shape[0] if T is None else T
     P = ref.softmax_rows(used)
     f = np.asarray(count, np.float64) / float(T * K)
-    dP = np.broadcast_to(c_aux * alpha * N * f / T, (T, N))
+    dP = np.broadcast_to(c_aux * alpha * N * f / T, used.shape)
     out = softmax_backward(P, dP)
     out = out + c_z * 2.0 * used / T
     lse = ref.logsumexp_rows(used)
@@ -275,3 +278,118 @@ def layer_loss(x, W, dy, *, K, act, gate_mode, cf=None, alpha=1.0, b_r=None, b_s
     s = r.stats
     return (float(np.sum(np.asarray(dy, np.float64) * r.y)) + c_aux * s.aux + c_z * s.z
             + c_zlse * s.z_lse), r
+
+
+# ------------------------------------------------------- sampled entries ---
+
+def _row(stack, e, f):
+    """Row f of expert e's matrix, widened alone when the stack keeps bits."""
+    if hasattr(stack, "bits"):
+        return ref.bf16_bits_to_f64(stack.bits[e, f])
+    return np.asarray(stack[e][f], np.float64)
+
+
+def _col(stack, e, f):
+    if hasattr(stack, "bits"):
+        return ref.bf16_bits_to_f64(stack.bits[e][:, f])
+    return np.asarray(stack[e][:, f], np.float64)
+
+
+def layer_backward_sampled(x, W, dy, *, K, act, gate_mode, cf=None, alpha=1.0, b_r=None,
+                           b_sel=None, shared=None, noise=None, noise_std=0.0, c_aux=0.0,
+                           c_z=0.0, c_zlse=0.0, idx=None, tokens=(), wcols=()):
+    """Selected entries of layer_backward's result, for sizes where the whole
+    backward is too slow.  The definitions are the same, restricted to what
+    the entries depend on: a token's rows (dx, dlogits, dgate) need only its
+    own K expert rows and the shared expert; row f of dw1 / dw3 and column f
+    of dw2 of expert e need only column f of the first expert GEMM over that
+    expert's rows.
+
+    tokens: token ids -> dict t -> {"dx", "dlogits", "dgate"}.
+    wcols: (e, f) pairs, e == N meaning the shared expert ->
+      dict (e, f) -> {"dw1": [d], "dw3": [d] (SwiGLU), "dw2": [d] (column f),
+      "db1": float and "db2": [d] (GELU layers with biases)}.
+    Returns (fwd, tok, wts) with fwd the routing-only forward result."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    T, d = x.shape
+    N = W["w_r"].shape[0]
+    fwd = ref.layer_forward(x, W, K=K, act=act, gate_mode=gate_mode, cf=cf, alpha=alpha, b_r=b_r,
+                            b_sel=b_sel, shared=shared, noise=noise, noise_std=noise_std,
+                            experts_needed=False, idx=idx)
+    asg, gates = fwd.asg, fwd.gates
+    tokens = [int(t) for t in tokens]
+    # ---- token rows: each expert's sampled rows through that expert's FFN
+    dxr = {t: np.zeros(d) for t in tokens}
+    dg = {t: np.zeros(K) for t in tokens}
+    for e in range(N):
+        pairs = [(t, k) for t in tokens for k in range(K)
+                 if fwd.idx[t, k] == e and asg.pair_row[t, k] >= 0]
+        if not pairs:
+            continue
+        ts = [t for t, _ in pairs]
+        X = x[ts]
+        o = ref.run_expert(act, X, e, W)
+        g = np.array([gates[t, k] for t, k in pairs])
+        do = g[:, None] * dy[ts]
+        if act == "swiglu":
+            dX = expert_swiglu_backward(X, W["w1"][e], W["w3"][e], W["w2"][e], do)[0]
+        else:
+            b1 = None if W.get("b1") is None else W["b1"][e]
+            dX = expert_gelu_backward(X, W["w1"][e], W["w2"][e], b1, None, do)[0]
+        for i, (t, k) in enumerate(pairs):
+            dg[t][k] = float(np.dot(dy[t], o[i]))
+            dxr[t] = dxr[t] + dX[i]
+    if shared is not None and tokens:
+        dxs = expert_swiglu_backward(x[tokens], shared["w1"], shared["w3"], shared["w2"],
+                                     dy[tokens])[0]
+        for i, t in enumerate(tokens):
+            dxr[t] = dxr[t] + dxs[i]
+    tok = {}
+    if tokens:
+        used = fwd.logits_used[tokens]
+        dgm = np.stack([dg[t] for t in tokens])
+        dl = gate_backward(used, fwd.idx[tokens], dgm, gate_mode)
+        dl = dl + stats_backward(used, fwd.stats.count, K, alpha, c_aux, c_z, c_zlse, T=T)
+        w_r = np.asarray(W["w_r"], np.float64)
+        for i, t in enumerate(tokens):
+            tok[t] = {"dx": dxr[t] + dl[i] @ w_r, "dlogits": dl[i], "dgate": dg[t]}
+    # ---- weight rows / columns
+    wts = {}
+    for e, f in wcols:
+        e, f = int(e), int(f)
+        if e < N:
+            lo, hi = int(asg.offset[e]), int(asg.offset[e + 1])
+            pr = asg.row_pair[lo:hi]
+            toks, ks = pr // K, pr % K
+            g = gates[toks, ks]
+            src = {k: W.get(k) for k in ("w1", "w3", "w2")}
+        else:
+            toks = np.arange(T)
+            g = np.ones(T)
+            src = {k: (None if shared is None else shared[k][None]) for k in ("w1", "w3", "w2")}
+        X = x[toks]
+        ee = e if e < N else 0
+        u = X @ _row(src["w1"], ee, f)
+        if act == "gelu_tanh" and e < N and W.get("b1") is not None:
+            u = u + float(np.asarray(W["b1"][e], np.float64)[f])
+        dog = g[:, None] * dy[toks]                       # d(expert output) rows
+        dh = dog @ _col(src["w2"], ee, f)                 # column f of dh
+        rec = {}
+        if act == "swiglu":
+            v = X @ _row(src["w3"], ee, f)
+            sg = ref.silu(u)
+            du = dh * v * silu_grad(u)
+            rec["dw3"] = (dh * sg) @ X
+            h = sg * v
+        else:
+            du = dh * gelu_tanh_grad(u)
+            h = ref.gelu_tanh(u)
+            if e < N and W.get("b1") is not None:
+                rec["db1"] = float(du.sum())
+            if e < N and W.get("b2") is not None:
+                rec["db2"] = dog.sum(axis=0)
+        rec["dw1"] = du @ X
+        rec["dw2"] = dog.T @ h                            # column f of dw2
+        wts[(e, f)] = rec
+    return fwd, tok, wts

@@ -194,3 +194,68 @@ def test_zero_tokens_zero_fills_the_gradients():
     torch.cuda.synchronize()
     for k in ("dw_r", "db_r", "dw1", "dw3", "dw2"):
         assert torch.count_nonzero(getattr(g, k)).item() == 0, k
+
+
+# ------------------------------------------------------------ full size ---
+
+FULL = [(WL.MIXTRAL_PREFILL, 6, 8), (WL.SWITCH_TOP1, 8, 8), (WL.DEEPSEEK_PREFILL, 3, 8)]
+
+
+@pytest.mark.parametrize("w,ntok,ncol", FULL, ids=lambda v: getattr(v, "name", str(v)))
+def test_backward_full_size(w, ntok, ncol):
+    """The full workloads in the launch configuration the benchmark times
+    (aux-loss gradient 1): seeded samples of token rows (dx, dlogits, dgate)
+    and of weight-gradient rows and columns (dw1[e, f], dw3[e, f],
+    dw2[e, :, f], the shared expert's too) against the oracle; dw_r and db_r
+    over all tokens against dlogits^T x and the column sums of dlogits (a
+    property that holds at any size), dlogits itself being checked on the
+    sampled tokens."""
+    say("backward full", w.name, ntok, ncol)
+    inp = make_inputs(w, device=DEV)
+    dy = make_dy(w, DEV)
+    lg = (1.0, 0.0, 0.0)
+    cfg, fwd, g = run_gpu(w, inp, dy, lg, 0.0)
+    rng = np.random.default_rng(4321)
+    tokens = sorted(rng.choice(w.T, size=ntok, replace=False).tolist())
+    if w.cf is not None:  # dropped tokens in the sample
+        dr = fwd.dropped.cpu().numpy().reshape(w.T, w.K).any(axis=1)
+        tokens = sorted(set(tokens) | set(np.nonzero(dr)[0][:3].tolist()))
+    wcols = [(int(e), int(f)) for e, f in zip(rng.integers(0, w.N, ncol), rng.integers(0, w.F, ncol))]
+    if w.F_shared:
+        wcols += [(w.N, int(f)) for f in rng.integers(0, w.F_shared, 2)]
+    Wt, shared = oracle_weights(inp, True)
+    idx = fwd.idx.cpu().numpy().astype(np.int64)
+    _, tok, wts = bwd.layer_backward_sampled(
+        f64(inp["x"]), Wt, f64(dy), K=w.K, act=w.act, gate_mode=w.gate, cf=w.cf,
+        alpha=w.aux_alpha, b_r=f64(inp["b_r"]), b_sel=f64(inp["b_sel"]), shared=shared,
+        c_aux=lg[0], idx=idx, tokens=tokens, wcols=wcols)
+    errs = {}
+
+    def cmp(name, got, want):
+        errs[name] = rel_err(np.asarray(got, np.float64), np.asarray(want, np.float64))
+
+    cmp("dx", f64(g.dx[tokens]), np.stack([tok[t]["dx"] for t in tokens]))
+    cmp("dlogits", f64(g.dlogits[tokens]), np.stack([tok[t]["dlogits"] for t in tokens]))
+    keys = [(e, f) for e, f in wcols]
+    got1 = [f64(g.dw1[e, f] if e < w.N else g.dws1[f]) for e, f in keys]
+    got2 = [f64(g.dw2[e, :, f] if e < w.N else g.dws2[:, f]) for e, f in keys]
+    cmp("dw1 rows", np.stack(got1), np.stack([wts[k]["dw1"] for k in keys]))
+    cmp("dw2 cols", np.stack(got2), np.stack([wts[k]["dw2"] for k in keys]))
+    if w.act == "swiglu":
+        got3 = [f64(g.dw3[e, f] if e < w.N else g.dws3[f]) for e, f in keys]
+        cmp("dw3 rows", np.stack(got3), np.stack([wts[k]["dw3"] for k in keys]))
+    print("[errs]", w.name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    bad = {k: v for k, v in errs.items() if v > TOL_BF16}
+    assert not bad, (w.name, bad)
+    # router weight gradient over all tokens: dw_r = dlogits^T x and
+    # db_r = sum_t dlogits, each within the fp32 summation bound
+    # |err| <= 2 T u sum_t |term| (u = 2^-24; T-term accumulation, any order)
+    dl = g.dlogits.double()
+    xd = inp["x"].double()
+    want = dl.T.contiguous() @ xd
+    bound = 2.0 * w.T * 2.0 ** -24 * (dl.abs().T.contiguous() @ xd.abs())
+    assert bool(((g.dw_r.double() - want).abs() <= bound).all())
+    if w.router_bias != "none":
+        want_b = dl.sum(dim=0)
+        bound_b = 2.0 * w.T * 2.0 ** -24 * dl.abs().sum(dim=0)
+        assert bool(((g.db_r.double() - want_b).abs() <= bound_b).all())

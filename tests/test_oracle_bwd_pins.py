@@ -258,3 +258,37 @@ def test_gate_jacobian_invariants(mode):
     idx1, _ = ref.select_topk(l, 1)
     if mode != "prob_no_renorm":
         assert np.abs(bwd.gate_backward(l, idx1, dg[:, :1], mode)).max() < 1e-16
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_sampled_entries_equal_the_full_backward(case):
+    """layer_backward_sampled (what the full-size GPU tests compare against)
+    gives exactly the entries of layer_backward."""
+    name, shape, act, mode, cf, flags, coef = case
+    x, W, shared, extra, dy = make_case(len(name) * 13 + shape["T"], act=act, **shape, **flags)
+    args = dict(K=shape["K"], act=act, gate_mode=mode, cf=cf, alpha=0.37, b_r=extra["b_r"],
+                b_sel=extra["b_sel"], shared=shared, noise=extra["noise"],
+                noise_std=extra["noise_std"], c_aux=coef[0], c_z=coef[1], c_zlse=coef[2])
+    G = bwd.layer_backward(x, W, dy, **args)
+    N, F = shape["N"], shape["F"]
+    tokens = list(range(0, shape["T"], 2))
+    wcols = [(e, f) for e in range(N) for f in (0, F - 1)]
+    if shared is not None:
+        wcols += [(N, 0), (N, shared["w1"].shape[0] - 1)]
+    fwd, tok, wts = bwd.layer_backward_sampled(x, W, dy, tokens=tokens, wcols=wcols, **args)
+    for t in tokens:
+        assert np.allclose(tok[t]["dx"], G.dx[t], rtol=0, atol=1e-12)
+        assert np.allclose(tok[t]["dlogits"], G.dlogits[t], rtol=0, atol=1e-12)
+        assert np.allclose(tok[t]["dgate"], G.dgate[t], rtol=0, atol=1e-12)
+    for (e, f), rec in wts.items():
+        if e < N:
+            w1, w2, w3 = G.dw1[e], G.dw2[e], (G.dw3[e] if act == "swiglu" else None)
+        else:
+            w1, w2, w3 = G.shared["w1"], G.shared["w2"], G.shared["w3"]
+        assert np.allclose(rec["dw1"], w1[f], rtol=0, atol=1e-12)
+        assert np.allclose(rec["dw2"], w2[:, f], rtol=0, atol=1e-12)
+        if act == "swiglu":
+            assert np.allclose(rec["dw3"], w3[f], rtol=0, atol=1e-12)
+        if "db1" in rec:
+            assert abs(rec["db1"] - G.db1[e, f]) < 1e-12
+            assert np.allclose(rec["db2"], G.db2[e], rtol=0, atol=1e-12)
