@@ -284,6 +284,8 @@ def backward_record(w, steps, warmup, ev):
     gemm = {k: sflops[k] / (st[k] * 1e-3) / 1e12 for k in sflops if st[k] > 0}
     dom = max(sflops, key=lambda k: st[k])
     tf = gemm[dom]
+    # the dW1 + dW3 stage is two launches of one kernel (SwiGLU)
+    launches = 2 if (dom == "dw1_dw3_gemm" and w.act == "swiglu") else 1
     return {"workload": w.name, "ms_per_step": ms, "eager_ms_per_step": wall * 1e3 / steps,
             "tokens_per_s": w.T / (ms * 1e-3), "loss_grad": {"aux": lg[0], "z": lg[1], "z_lse": lg[2]},
             "algorithmic_tflop": algo / 1e12,
@@ -292,7 +294,8 @@ def backward_record(w, steps, warmup, ev):
             "stage_ms": st, "gemm_tflops": gemm,
             "roofline": {"bound": "mfma", "kernel": dom, "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
-                         "avg_ms": st[dom], "flops_per_launch": sflops[dom]}}
+                         "launches": launches, "avg_ms": st[dom] / launches,
+                         "flops_per_launch": sflops[dom] / launches}}
 
 
 def router_train_timing(w, inp, steps, warmup, noise_std=0.1, bias_rate=1e-3):

@@ -103,6 +103,15 @@ def main():
                       f"{b['roofline']['achieved']:.0f} TFLOP/s.", "",
                       "| stage | ms |", "|---|---|"]
             lines += [f"| {k} | {v:.3f} |" for k, v in b["stage_ms"].items()]
+            if "backward" in b:
+                bb = b["backward"]
+                rf = bb["roofline"]
+                lines += ["", f"Backward ({bb['workload']}): ms_per_step {bb['ms_per_step']:.3f}, "
+                              f"{bb['active_tflops']:.0f} TFLOP/s algorithmic; dominant stage "
+                              f"`{rf['kernel']}` {rf['avg_ms'] * 1e3:.1f} us, "
+                              f"{rf['achieved']:.0f} TFLOP/s.", "",
+                          "| stage | ms |", "|---|---|"]
+                lines += [f"| {k} | {v:.3f} |" for k, v in bb["stage_ms"].items()]
             if "decode" in b:
                 dd = b["decode"]
                 lines += ["", f"Decode ({dd['workload']}): ms_per_step {dd['ms_per_step']:.3f}, "
