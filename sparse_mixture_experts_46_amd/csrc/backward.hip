@@ -21,6 +21,7 @@
 //   dx                 sum over the token's kept rows of dx_perm, + the shared
 //                      expert's dx, + dlogits W_r
 #include "gemm_bwd.h"
+#include "gemm_bwd_tr.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -496,6 +497,25 @@ hipError_t run_bwd(const BwdArgs& a, int64_t max_tiles, bool bf16, hipStream_t s
   return hipGetLastError();
 }
 
+// The 256 x 256 DMA kernel (gemm_bwd_tr.h): one workgroup per CU.
+template <bool WG, bool BS, bool DUALB, bool DUALK, int EPI>
+hipError_t run_bwd_tr(const BwdArgs& a, int64_t max_tiles, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  auto kern = gemm_bwd_tr_kernel<WG, BS, DUALB, DUALK, EPI>;
+  constexpr size_t smem = 2 * 2 * 32768;  // two stages of A and B
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int64_t grid = cus();
+  if (max_tiles < grid) grid = ((max_tiles + 7) / 8) * 8;
+  kern<<<(unsigned)grid, 512, smem, s>>>(a, (int)max_tiles);
+  return hipGetLastError();
+}
+
 // Upper bound on the tiles of a row-group table: sum over groups of
 // ceil(M_g / bm) * ceil(nout / bno) with sum M_g <= rows.
 int64_t row_tiles_bound(int64_t rows, int G, int bm, int nout, int bno) {
@@ -515,11 +535,13 @@ size_t ffn_backward_workspace_bytes(int64_t T, int d, int N, int K, int F, int F
 }
 
 namespace {
-// Tile side of the recompute and of the SwiGLU dx_perm GEMM (both with
-// K-contiguous loads or one strided operand that fits the registers at 256):
-// 256 with many rows per expert, else 128.  The other GEMMs (a K-strided B,
-// or the weight gradients) use 128: at 256 their loader state spills.
+// Row-group GEMMs (the recompute, dh, dx_perm) use the 256 x 256 DMA kernel
+// with many rows per expert (a 256-row tile of a ~256-row expert would be
+// half empty), else the 128 x 128 register-staged kernel.  The weight-
+// gradient GEMMs tile F x d, whatever the rows: the DMA kernel when both are
+// at least 256.
 int rows_tile(int64_t rows, int N) { return rows >= (int64_t)384 * N ? 256 : 128; }
+bool weight_tr(int F, int d) { return F >= 256 && d >= 256; }
 }  // namespace
 
 template <int RR>
@@ -557,11 +579,12 @@ hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
   unsigned char* Vs = V + (size_t)rows * F * el;
   unsigned char* Hs = H + (size_t)rows * F * el;
 
-  constexpr int RX = RR;             // dual-K dx_perm (SwiGLU)
-  const int bm1 = bf16 ? RR : 16;    // recompute tiles
-  const int bm2 = bf16 ? 128 : 16;   // dh tiles
-  const int bm4 = bf16 ? (swiglu ? RX : 128) : 16;  // dx_perm tiles
-  const int wbm = bf16 ? 128 : 16;   // weight-gradient tiles
+  constexpr bool TR = RR == 256;     // row groups on the DMA kernel
+  const bool wtr = bf16 && weight_tr(F, d);
+  const int bm1 = bf16 ? RR : 16;    // row-group tiles (recompute, dh, dx_perm)
+  const int bm2 = bm1;
+  const int bm4 = bm1;
+  const int wbm = bf16 ? (wtr ? 256 : 128) : 16;  // weight-gradient tiles
   const int bno1 = (bf16 && swiglu) ? bm1 / 2 : bm1;  // dual B: half the tile's columns are outputs
   int32_t* base[3] = {tb, tb + (p.N + 2), tb + 2 * (p.N + 2)};
   TileSpecs specs = {};
@@ -587,8 +610,12 @@ hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
     a.bias = p.b1;
     a.c = U; a.c2 = V; a.c_shared = Us; a.c2_shared = Vs; a.ldc = F;
     const int64_t mt = row_tiles_bound(all_rows, G, bm1, F, bno1);
-    e = swiglu ? run_bwd<RR, false, false, true, false, BEPI_UV>(a, mt, bf16, s)
-               : run_bwd<RR, false, false, false, false, BEPI_STORE>(a, mt, bf16, s);
+    if (TR)
+      e = swiglu ? run_bwd_tr<false, false, true, false, BEPI_UV>(a, mt, s)
+                 : run_bwd_tr<false, false, false, false, BEPI_STORE>(a, mt, s);
+    else
+      e = swiglu ? run_bwd<128, false, false, true, false, BEPI_UV>(a, mt, bf16, s)
+                 : run_bwd<128, false, false, false, false, BEPI_STORE>(a, mt, bf16, s);
     if (e != hipSuccess) return e;
     if ((e = mark(0)) != hipSuccess) return e;
   }
@@ -601,8 +628,12 @@ hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
     a.Nout = F; a.Nout_shared = p.F_shared; a.Kdim = d;
     a.c = U; a.c2 = V; a.c3 = H; a.c_shared = Us; a.c2_shared = Vs; a.c3_shared = Hs; a.ldc = F;
     const int64_t mt = row_tiles_bound(all_rows, G, bm2, F, bm2);
-    e = swiglu ? run_bwd<128, false, true, false, false, BEPI_SWIGLU_BWD>(a, mt, bf16, s)
-               : run_bwd<128, false, true, false, false, BEPI_GELU_BWD>(a, mt, bf16, s);
+    if (TR)
+      e = swiglu ? run_bwd_tr<false, true, false, false, BEPI_SWIGLU_BWD>(a, mt, s)
+                 : run_bwd_tr<false, true, false, false, BEPI_GELU_BWD>(a, mt, s);
+    else
+      e = swiglu ? run_bwd<128, false, true, false, false, BEPI_SWIGLU_BWD>(a, mt, bf16, s)
+                 : run_bwd<128, false, true, false, false, BEPI_GELU_BWD>(a, mt, bf16, s);
     if (e != hipSuccess) return e;
     if ((e = mark(1)) != hipSuccess) return e;
   }
@@ -615,7 +646,8 @@ hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
     a.Mout = d; a.Nout = F; a.Nout_shared = F;
     a.c = p.dw2; a.c_shared = p.dws2; a.ldc = F; a.c_gstride = (int64_t)d * F;
     const int64_t tiles = (int64_t)G * ((d + wbm - 1) / wbm) * ((F + wbm - 1) / wbm);
-    e = run_bwd<128, true, false, false, false, BEPI_STORE>(a, tiles, bf16, s);
+    e = wtr ? run_bwd_tr<true, false, false, false, BEPI_STORE>(a, tiles, s)
+            : run_bwd<128, true, false, false, false, BEPI_STORE>(a, tiles, bf16, s);
     if (e != hipSuccess) return e;
     if ((e = mark(2)) != hipSuccess) return e;
   }
@@ -629,8 +661,12 @@ hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
     a.Nout = d; a.Nout_shared = d; a.Kdim = F;
     a.c = p.dx_perm; a.c_shared = p.dx_shared; a.ldc = d;
     const int64_t mt = row_tiles_bound(all_rows, G, bm4, d, bm4);
-    e = swiglu ? run_bwd<RX, false, true, false, true, BEPI_STORE>(a, mt, bf16, s)
-               : run_bwd<128, false, true, false, false, BEPI_STORE>(a, mt, bf16, s);
+    if (TR)
+      e = swiglu ? run_bwd_tr<false, true, false, true, BEPI_STORE>(a, mt, s)
+                 : run_bwd_tr<false, true, false, false, BEPI_STORE>(a, mt, s);
+    else
+      e = swiglu ? run_bwd<128, false, true, false, true, BEPI_STORE>(a, mt, bf16, s)
+                 : run_bwd<128, false, true, false, false, BEPI_STORE>(a, mt, bf16, s);
     if (e != hipSuccess) return e;
     if ((e = mark(3)) != hipSuccess) return e;
   }
@@ -644,7 +680,8 @@ hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
     a.c = pass ? p.dw3 : p.dw1; a.c_shared = pass ? p.dws3 : p.dws1; a.ldc = d;
     a.c_gstride = (int64_t)F * d;
     const int64_t tiles = (int64_t)G * ((F + wbm - 1) / wbm) * ((d + wbm - 1) / wbm);
-    e = run_bwd<128, true, false, false, false, BEPI_STORE>(a, tiles, bf16, s);
+    e = wtr ? run_bwd_tr<true, false, false, false, BEPI_STORE>(a, tiles, s)
+            : run_bwd<128, true, false, false, false, BEPI_STORE>(a, tiles, bf16, s);
     if (e != hipSuccess) return e;
   }
   if ((e = mark(4)) != hipSuccess) return e;

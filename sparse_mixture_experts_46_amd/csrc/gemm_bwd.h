@@ -144,6 +144,60 @@ __device__ __forceinline__ int64_t bwd_row(const BwdTile& t, const int32_t* rows
 
 __device__ __forceinline__ int bwd_swz(int row) { return (row >> 1) & 7; }
 
+// Epilogue of 4 consecutive output columns col .. col+3 at element offset o
+// (r0: the accumulators; r1: the up half of a dual-B tile).
+template <int EPI, bool WG>
+__device__ __forceinline__ void bwd_epilogue4(const BwdArgs& p, const BwdTile& ti, int64_t o, int col,
+                                              float (&r0)[4], const float (&r1)[4]) {
+  if (EPI == BEPI_STORE_F32) {
+    float* C = (float*)(ti.shared ? p.c_shared : p.c);
+    *(float4*)(C + o) = make_float4(r0[0], r0[1], r0[2], r0[3]);
+  } else if (EPI == BEPI_STORE) {
+    uint16_t* C = (uint16_t*)(ti.shared ? p.c_shared : p.c);
+    if (p.bias && !ti.shared && !WG) {
+      const uint16_t* b = (const uint16_t*)p.bias + (int64_t)ti.g * p.Nout + col;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r0[u] += bf16_to_f32(b[u]);
+    }
+    *(uint2*)(C + o) = make_uint2(pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]));
+  } else if (EPI == BEPI_UV) {
+    uint16_t* C = (uint16_t*)(ti.shared ? p.c_shared : p.c);
+    uint16_t* C2 = (uint16_t*)(ti.shared ? p.c2_shared : p.c2);
+    *(uint2*)(C + o) = make_uint2(pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]));
+    *(uint2*)(C2 + o) = make_uint2(pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3]));
+  } else {  // BEPI_SWIGLU_BWD / BEPI_GELU_BWD: r0 = dh
+    uint16_t* U = (uint16_t*)(ti.shared ? p.c_shared : p.c);
+    uint16_t* H = (uint16_t*)(ti.shared ? p.c3_shared : p.c3);
+    const uint2 uu = *(const uint2*)(U + o);
+    float u[4] = {__uint_as_float(uu.x << 16), __uint_as_float(uu.x & 0xffff0000u),
+                  __uint_as_float(uu.y << 16), __uint_as_float(uu.y & 0xffff0000u)};
+    float du[4], h[4];
+    if (EPI == BEPI_SWIGLU_BWD) {
+      uint16_t* V = (uint16_t*)(ti.shared ? p.c2_shared : p.c2);
+      const uint2 vv = *(const uint2*)(V + o);
+      const float v[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
+                          __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
+      float dv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sg = silu_f(u[e]);
+        h[e] = sg * v[e];
+        dv[e] = r0[e] * sg;
+        du[e] = r0[e] * v[e] * silu_grad_f(u[e]);
+      }
+      *(uint2*)(V + o) = make_uint2(pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = gelu_tanh_f(u[e]);
+        du[e] = r0[e] * gelu_tanh_grad_f(u[e]);
+      }
+    }
+    *(uint2*)(U + o) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+    *(uint2*)(H + o) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+  }
+}
+
 // Column j of an 8 x 8 block of 16-bit elements whose row i is in[i]:
 // element j of every in[i], in order of i.  Word c of a row holds elements
 // 2c (low half) and 2c + 1 (high half).
@@ -359,53 +413,7 @@ __global__ __launch_bounds__(2 * R, R == 128 ? 2 : 1) void gemm_bwd_kernel(BwdAr
             r0[u] = acc[j][i][4 * qq + u];
             r1[u] = DUALB ? acc[j + FN / 2][i][4 * qq + u] : 0.f;
           }
-          if (EPI == BEPI_STORE_F32) {
-            float* C = (float*)(ti.shared ? p.c_shared : p.c);
-            *(float4*)(C + o) = make_float4(r0[0], r0[1], r0[2], r0[3]);
-          } else if (EPI == BEPI_STORE) {
-            uint16_t* C = (uint16_t*)(ti.shared ? p.c_shared : p.c);
-            if (p.bias && !ti.shared && !WG) {
-              const uint16_t* b = (const uint16_t*)p.bias + (int64_t)ti.g * p.Nout + col;
-#pragma unroll
-              for (int u = 0; u < 4; ++u) r0[u] += bf16_to_f32(b[u]);
-            }
-            *(uint2*)(C + o) = make_uint2(pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]));
-          } else if (EPI == BEPI_UV) {
-            uint16_t* C = (uint16_t*)(ti.shared ? p.c_shared : p.c);
-            uint16_t* C2 = (uint16_t*)(ti.shared ? p.c2_shared : p.c2);
-            *(uint2*)(C + o) = make_uint2(pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]));
-            *(uint2*)(C2 + o) = make_uint2(pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3]));
-          } else {  // BEPI_SWIGLU_BWD / BEPI_GELU_BWD: r0 = dh
-            uint16_t* U = (uint16_t*)(ti.shared ? p.c_shared : p.c);
-            uint16_t* H = (uint16_t*)(ti.shared ? p.c3_shared : p.c3);
-            const uint2 uu = *(const uint2*)(U + o);
-            float u[4] = {__uint_as_float(uu.x << 16), __uint_as_float(uu.x & 0xffff0000u),
-                          __uint_as_float(uu.y << 16), __uint_as_float(uu.y & 0xffff0000u)};
-            float du[4], h[4];
-            if (EPI == BEPI_SWIGLU_BWD) {
-              uint16_t* V = (uint16_t*)(ti.shared ? p.c2_shared : p.c2);
-              const uint2 vv = *(const uint2*)(V + o);
-              const float v[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
-                                  __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
-              float dv[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float sg = silu_f(u[e]);
-                h[e] = sg * v[e];
-                dv[e] = r0[e] * sg;
-                du[e] = r0[e] * v[e] * silu_grad_f(u[e]);
-              }
-              *(uint2*)(V + o) = make_uint2(pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]));
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                h[e] = gelu_tanh_f(u[e]);
-                du[e] = r0[e] * gelu_tanh_grad_f(u[e]);
-              }
-            }
-            *(uint2*)(U + o) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-            *(uint2*)(H + o) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-          }
+          bwd_epilogue4<EPI, WG>(p, ti, o, col, r0, r1);
         }
       }
     }

@@ -1,0 +1,242 @@
+// Grouped GEMMs of the backward pass, 256 x 256 tiles fed by DMA.
+//
+// The same problems as gemm_bwd_kernel (gemm_bwd.h: row groups and weight
+// groups, K-contiguous or K-strided operands, the same epilogues), with no
+// operand passing through registers:
+//  * Every operand tile goes global -> LDS by DMA (buffer_load ... lds, 16
+//    bytes per lane, 1 KB per wave instruction), two stages of 64-wide K.
+//  * A K-contiguous tile is stored [row][64 K] (128 B per row, 16-byte chunk
+//    c of row r at c ^ ((r >> 1) & 7)) and read with ds_read_b128, as in
+//    gemm_bwd.h.
+//  * A K-strided tile is stored as it lies in memory, [64 K][256 columns]
+//    (512 B per K row, chunk c of K row k at c ^ ((k & 3) << 2)), and the
+//    MFMA fragments (8 consecutive K of one column per lane) are formed by
+//    gfx950's transposing LDS read, ds_read_b64_tr_b16.  Within each group
+//    of 16 lanes, lane s supplies the address of 4 consecutive 16-bit
+//    elements and lane i receives element i % 4 of lanes i / 4 + 4 j,
+//    j = 0..3.  Lane s pointing at [k0 + s / 4][n0 + 4 (s % 4)] thus gives
+//    lane i the 4 values K = k0 .. k0 + 3 of column n0 + i; two such reads
+//    make the 8 K of a fragment.  The swizzle keeps the 4 K rows x 64 bytes
+//    that 32 lanes read in one pass on distinct banks.
+//  * Buffer descriptors sized to each group's extent make rows past the end
+//    (a group's last row tile, a weight gradient's ragged K) read as zeros.
+//  * 8 waves of 128 x 64 outputs (v_mfma_f32_32x32x16_bf16, weight fragment
+//    first); waves 0-3 issue the A tile's DMA, waves 4-7 the B tile's.
+#pragma once
+
+#include "gemm_bwd.h"
+#include "gemm_tile.h"  // wait_vmcnt, lds_void_t
+
+namespace moe {
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// 16-byte DMA global -> LDS through a buffer descriptor of nrec bytes from
+// base: offsets at or past nrec read as zero.
+__device__ __forceinline__ void dma16_bounded(const void* base, uint32_t nrec, uint32_t voff,
+                                              void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nrec, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, 0, 0, 0);
+#endif
+}
+
+// Chunk swizzle of a K-strided stage (32 chunks of 16 bytes per K row).
+__device__ __forceinline__ int tr_swz(int k) { return (k & 3) << 2; }
+
+// Byte offset, within a K-strided stage, of the 8 bytes at [k][n] (n % 4 == 0).
+__device__ __forceinline__ uint32_t tr_off(int k, int n) {
+  return (uint32_t)(k * 512 + (((n >> 3) ^ tr_swz(k)) << 4) + ((n & 4) << 1));
+}
+
+template <bool WG, bool BS, bool DUALB, bool DUALK, int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int total_tiles) {
+  constexpr int BM = 256, BN = 256, BK = 64, CH = 8;
+  constexpr int WN = 4, TM = 128, TN = 64, FM = 4, FN = 2;
+  constexpr int BNo = DUALB ? BN / 2 : BN;
+  constexpr bool A_STRIDED = WG;
+  constexpr bool B_STRIDED = WG || BS;
+  constexpr int OPB = 32768;      // bytes of one operand's stage
+  constexpr int STB = 2 * OPB;    // bytes of one stage (A then B)
+  static_assert(!(DUALB && B_STRIDED), "dual B needs the K-contiguous layout");
+  extern __shared__ uint4 lds[];  // [2 stages][A | B]
+  char* L = (char*)lds;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const bool loads_a = wave < 4;
+  const int qw = wave & 3;  // this wave's quarter of its operand's 32 DMA instructions
+  const int khalf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+  const int total = WG ? total_tiles : p.tile_base[p.G];
+  const TileWalk walk = tile_walk(total);
+
+  // first row (A) / column (B) of this wave's fragments within the tile
+  int am[FM], bn[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) am[i] = wm * TM + i * 32;
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    bn[j] = DUALB ? (j < FN / 2 ? wn * (TN / 2) + j * 32 : BN / 2 + wn * (TN / 2) + (j - FN / 2) * 32)
+                  : wn * TN + j * 32;
+
+  for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
+    const BwdTile ti = bwd_tile(p, WG, tile, BM, BN);
+    const int Ktot = WG ? ti.rows : (DUALK ? 2 * p.Kdim : p.Kdim);
+    const int nk = (Ktot + BK - 1) / BK;
+
+    // ---- this wave's DMA source: base, extent and per-lane offsets
+    const char* base0;
+    const char* base1;  // dual K: second half; dual B: up rows
+    uint32_t nrec, soff_step;
+    const bool strided = loads_a ? A_STRIDED : B_STRIDED;
+    uint32_t voff[8];
+    {
+      int64_t ld;
+      if (loads_a) {
+        ld = p.lda;
+        const char* a0 = (const char*)(ti.shared ? p.a_shared : p.a);
+        const char* a1 = DUALK ? (const char*)(ti.shared ? p.a2_shared : p.a2) : a0;
+        // row groups: the tile's first row; weight groups: the group's first row
+        const int64_t r0 = (ti.shared ? 0 : ti.row0) + (WG ? 0 : (int64_t)ti.mt * BM);
+        base0 = a0 + r0 * ld * 2;
+        base1 = a1 + r0 * ld * 2;
+        const int64_t rows_left = WG ? ti.rows : ti.rows - (int64_t)ti.mt * BM;
+        nrec = (uint32_t)(rows_left * ld * 2);
+      } else {
+        ld = p.ldb;
+        if (WG) {
+          const int64_t r0 = ti.shared ? 0 : ti.row0;
+          base0 = (const char*)(ti.shared ? p.bs0 : p.b0) + r0 * ld * 2;
+          base1 = base0;
+          nrec = (uint32_t)((int64_t)ti.rows * ld * 2);
+        } else {
+          const int64_t goff = ti.shared ? 0 : (int64_t)ti.g * p.b_stride * 2;
+          base0 = (const char*)(ti.shared ? p.bs0 : p.b0) + goff;
+          base1 = (DUALB || DUALK) ? (const char*)(ti.shared ? p.bs1 : p.b1) + goff : base0;
+          // one weight matrix: [nout, Kdim] (K-contiguous) or [Kdim, nout]
+          nrec = (uint32_t)((int64_t)ti.nout * p.Kdim * 2);
+        }
+      }
+      soff_step = strided ? (uint32_t)(BK * ld * 2) : (uint32_t)(BK * 2);
+      const int org = loads_a ? (WG ? ti.mt * BM : 0) : ti.nt * (WG ? BN : BNo);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = qw * 8 + u;  // instruction: 1 KB of the operand's stage
+        if (!strided) {
+          // 8 tile rows x 8 chunks; dual B: instructions 16.. hold the up rows
+          const int r = t * 8 + (lane >> 3);
+          const int c = (lane & 7) ^ ((r >> 1) & 7);
+          int64_t row;
+          if (loads_a) row = r;  // relative to the tile's first row
+          else row = org + ((DUALB && r >= BN / 2) ? r - BN / 2 : r);
+          voff[u] = (uint32_t)(row * ld * 2 + c * 16);
+        } else {
+          // 2 K rows x 32 chunks
+          const int k = t * 2 + (lane >> 5);
+          const int c = (lane & 31) ^ tr_swz(k);
+          voff[u] = (uint32_t)((int64_t)k * ld * 2 + (int64_t)(org + c * 8) * 2);
+        }
+      }
+    }
+    // the K step moves the descriptor's base (and shrinks its extent), so the
+    // range check stays on the group's own rows
+    auto issue = [&](int kt, int buf) {
+      int kk = kt;
+      const char* b = base0;
+      if (DUALK && kt * BK >= p.Kdim) {
+        kk = kt - p.Kdim / BK;
+        b = base1;
+      }
+      const uint32_t step = (uint32_t)kk * soff_step;
+      const uint32_t nk_rec = nrec > step ? nrec - step : 0u;
+      char* dst = L + buf * STB + (loads_a ? 0 : OPB);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = qw * 8 + u;
+        const char* bb = (DUALB && !loads_a && t >= 16) ? base1 : b;
+        dma16_bounded(bb + step, nk_rec, voff[u], dst + t * 1024);
+      }
+    };
+
+    f32x16_t acc[FN][FM];  // [weight fragment][token fragment]
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
+
+    // fragment of a K-contiguous stage: rows r0 + lane % 32, K chunk ch
+    auto frag_c = [&](const char* S, int r0, int ch) -> bf16x8_t {
+      const int r = r0 + (lane & 31);
+      return __builtin_bit_cast(bf16x8_t, *(const uint4*)(S + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4)));
+    };
+    // fragment of a K-strided stage: columns n0 + lane % 32, K = 16 ks + 8 (lane / 32) + 0..7
+    auto frag_t = [&](const char* S, int n0, int ks) -> bf16x8_t {
+      const int k = ks * 16 + 8 * (g16 >> 1) + (i16 >> 2);
+      const int n = n0 + 16 * (g16 & 1) + 4 * (i16 & 3);
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(S + tr_off(k, n)));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(S + tr_off(k + 4, n)));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    if (nk > 0) issue(0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+      const char* SA = L + (kt & 1) * STB;
+      const char* SB = SA + OPB;
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        bf16x8_t fa[FM], fb[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          fa[i] = A_STRIDED ? frag_t(SA, am[i], ks) : frag_c(SA, am[i], ks * 2 + khalf);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fb[j] = B_STRIDED ? frag_t(SB, bn[j], ks) : frag_c(SB, bn[j], ks * 2 + khalf);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[j][i], 0, 0, 0);
+      }
+      wait_vmcnt<0>();  // this wave's DMA of stage kt + 1
+      __syncthreads();  // everyone's; and stage kt read by all before it is refilled
+    }
+
+    // ---- epilogue (as gemm_bwd_kernel)
+    const int mlim = WG ? p.Mout : ti.rows;
+    constexpr int FO = DUALB ? FN / 2 : FN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = ti.mt * BM + am[i] + (lane & 31);
+      if (m >= mlim) continue;
+      const int64_t rowoff = WG ? (ti.shared ? 0 : (int64_t)ti.g * p.c_gstride) + (int64_t)m * p.ldc
+                                : (ti.row0 + m) * p.ldc;
+#pragma unroll
+      for (int j = 0; j < FO; ++j) {
+        const int cb = ti.nt * BNo + (DUALB ? wn * (TN / 2) : wn * TN) + j * 32 + 4 * khalf;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int col = cb + 8 * qq;
+          if (col >= ti.nout) continue;
+          const int64_t o = rowoff + col;
+          float r0[4], r1[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            r0[u] = acc[j][i][4 * qq + u];
+            r1[u] = DUALB ? acc[j + FN / 2][i][4 * qq + u] : 0.f;
+          }
+          bwd_epilogue4<EPI, WG>(p, ti, o, col, r0, r1);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace moe
