@@ -22,6 +22,9 @@
 //    (a group's last row tile, a weight gradient's ragged K) read as zeros.
 //  * 8 waves of 128 x 64 outputs (v_mfma_f32_32x32x16_bf16, weight fragment
 //    first); waves 0-3 issue the A tile's DMA, waves 4-7 the B tile's.
+//  * SK2 (with dual K): the two halves of K are separate tiles, the first
+//    half's results going to c and the second's to c2 (the caller adds
+//    them), which doubles the tiles of a GEMM with few output tiles.
 #pragma once
 
 #include "gemm_bwd.h"
@@ -51,7 +54,7 @@ __device__ __forceinline__ uint32_t tr_off(int k, int n) {
   return (uint32_t)(k * 512 + (((n >> 3) ^ tr_swz(k)) << 4) + ((n & 4) << 1));
 }
 
-template <bool WG, bool BS, bool DUALB, bool DUALK, int EPI>
+template <bool WG, bool BS, bool DUALB, bool DUALK, int EPI, bool SK2 = false>
 __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int total_tiles) {
   constexpr int BM = 256, BN = 256, BK = 64, CH = 8;
   constexpr int WN = 4, TM = 128, TN = 64, FM = 4, FN = 2;
@@ -61,6 +64,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
   constexpr int OPB = 32768;      // bytes of one operand's stage
   constexpr int STB = 2 * OPB;    // bytes of one stage (A then B)
   static_assert(!(DUALB && B_STRIDED), "dual B needs the K-contiguous layout");
+  static_assert(!SK2 || (DUALK && !WG), "split K applies to a dual-K row-group GEMM");
   extern __shared__ uint4 lds[];  // [2 stages][A | B]
   char* L = (char*)lds;
 
@@ -70,7 +74,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
   const bool loads_a = wave < 4;
   const int qw = wave & 3;  // this wave's quarter of its operand's 32 DMA instructions
   const int khalf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
-  const int total = WG ? total_tiles : p.tile_base[p.G];
+  const int total1 = WG ? total_tiles : p.tile_base[p.G];
+  const int total = SK2 ? 2 * total1 : total1;
   const TileWalk walk = tile_walk(total);
 
   // first row (A) / column (B) of this wave's fragments within the tile
@@ -83,9 +88,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
                   : wn * TN + j * 32;
 
   for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
-    const BwdTile ti = bwd_tile(p, WG, tile, BM, BN);
-    const int Ktot = WG ? ti.rows : (DUALK ? 2 * p.Kdim : p.Kdim);
+    const int half = (SK2 && tile >= total1) ? 1 : 0;  // split K: which half
+    const BwdTile ti = bwd_tile(p, WG, tile - half * total1, BM, BN);
+    const int Ktot = WG ? ti.rows : ((DUALK && !SK2) ? 2 * p.Kdim : p.Kdim);
     const int nk = (Ktot + BK - 1) / BK;
+    const int kt0 = half * (p.Kdim / BK);  // first K step of this tile's half
 
     // ---- this wave's DMA source: base, extent and per-lane offsets
     const char* base0;
@@ -144,10 +151,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
     // the K step moves the descriptor's base (and shrinks its extent), so the
     // range check stays on the group's own rows
     auto issue = [&](int kt, int buf) {
-      int kk = kt;
+      int kk = kt + kt0;
       const char* b = base0;
-      if (DUALK && kt * BK >= p.Kdim) {
-        kk = kt - p.Kdim / BK;
+      if (DUALK && kk * BK >= p.Kdim) {
+        kk -= p.Kdim / BK;
         b = base1;
       }
       const uint32_t step = (uint32_t)kk * soff_step;
@@ -209,7 +216,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
       __syncthreads();  // everyone's; and stage kt read by all before it is refilled
     }
 
-    // ---- epilogue (as gemm_bwd_kernel)
+    // ---- epilogue (as gemm_bwd_kernel); the second K half writes c2
+    BwdArgs pe = p;
+    if (SK2 && half) {
+      pe.c = p.c2;
+      pe.c_shared = p.c2_shared;
+    }
     const int mlim = WG ? p.Mout : ti.rows;
     constexpr int FO = DUALB ? FN / 2 : FN;
 #pragma unroll
@@ -232,7 +244,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
             r0[u] = acc[j][i][4 * qq + u];
             r1[u] = DUALB ? acc[j + FN / 2][i][4 * qq + u] : 0.f;
           }
-          bwd_epilogue4<EPI, WG>(p, ti, o, col, r0, r1);
+          bwd_epilogue4<EPI, WG>(pe, ti, o, col, r0, r1);
         }
       }
     }

@@ -149,7 +149,7 @@ RouterBwdWs router_bwd_ws(const moe_config_t* c) {
 
 struct BwdWs {
   RouterBwdWs r;
-  size_t router, ffn, d_perm, dgate, dlogits, dx_perm, dx_shared, total;
+  size_t router, ffn, d_perm, dgate, dlogits, dx_perm, dx_shared, dx_perm2, dx_shared2, total;
 };
 BwdWs bwd_ws(const moe_config_t* c) {
   BwdWs w;
@@ -165,6 +165,8 @@ BwdWs bwd_ws(const moe_config_t* c) {
   w.dlogits = o; o = align_up(o + (size_t)c->T * c->N * 4);
   w.dx_perm = o; o = align_up(o + pairs * c->d * eb);
   w.dx_shared = o; o = align_up(o + (c->F_shared > 0 ? (size_t)c->T * c->d * eb : 0));
+  w.dx_perm2 = o; o = align_up(o + pairs * c->d * eb);
+  w.dx_shared2 = o; o = align_up(o + (c->F_shared > 0 ? (size_t)c->T * c->d * eb : 0));
   w.total = o;
   return w;
 }
@@ -516,7 +518,8 @@ moe_status_t do_ffn_backward(const moe_config_t* cfg, const moe_weights_t* w, co
                              const int32_t* row_pair, const int32_t* offset, const void* d_perm,
                              const void* dy, void* dx_perm, void* dx_shared,
                              const moe_grads_t* g, void* ws, hipStream_t s,
-                             const hipEvent_t* ev = nullptr) {
+                             const hipEvent_t* ev = nullptr, void* dx_perm2 = nullptr,
+                             void* dx_shared2 = nullptr) {
   FfnBwdProblem p = {};
   p.T = cfg->T; p.d = cfg->d; p.N = cfg->N; p.K = cfg->K; p.F = cfg->F;
   p.F_shared = cfg->F_shared; p.act = cfg->act; p.bf16 = cfg->dtype == MOE_BF16;
@@ -524,6 +527,7 @@ moe_status_t do_ffn_backward(const moe_config_t* cfg, const moe_weights_t* w, co
   p.w1 = w->w1; p.w3 = w->w3; p.w2 = w->w2; p.b1 = w->b1;
   p.ws1 = w->ws1; p.ws3 = w->ws3; p.ws2 = w->ws2;
   p.d_perm = d_perm; p.dy = dy; p.dx_perm = dx_perm; p.dx_shared = dx_shared;
+  p.dx_perm2 = dx_perm2; p.dx_shared2 = dx_shared2;
   p.dw1 = g->dw1; p.dw3 = g->dw3; p.dw2 = g->dw2;
   // bias gradients only for layers that have the biases
   p.db1 = w->b1 ? g->db1 : nullptr;
@@ -627,12 +631,18 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   hipEvent_t fev[5] = {};
   if (trace)
     for (int i = 0; i < 5; ++i) fev[i] = (hipEvent_t)trace->ev[3 + i];
+  // dx_perm in two parts (du W1, dv W3) that the dx kernel adds
+  void* dx_perm2 = at<void>(ws, B.dx_perm2);
+  void* dx_shared2 = cfg->F_shared > 0 ? at<void>(ws, B.dx_shared2) : nullptr;
   st = do_ffn_backward(cfg, w, x, sv->row_pair, sv->offset, d_perm, dy, dx_perm, dx_shared, g,
-                       at<void>(ws, B.ffn), s, fev);
+                       at<void>(ws, B.ffn), s, fev, dx_perm2, dx_shared2);
   if (st != MOE_OK) return st;
   if ((st = mark(8)) != MOE_OK) return st;
+  // the FFN backward fills the second parts only when it splits (else null)
+  const bool split = ffn_backward_splits_dx(cfg->T, cfg->N, cfg->K, cfg->F, cfg->act,
+                                            cfg->dtype == MOE_BF16);
   if (launch_dx(dx_perm, sv->pair_row, cfg->K, dx_shared, dl, w->w_r, cfg->N, cfg->T, cfg->d, bf16,
-                g->dx, s) != hipSuccess)
+                g->dx, s, split ? dx_perm2 : nullptr, split ? dx_shared2 : nullptr) != hipSuccess)
     return MOE_ERR_HIP;
   return mark(9);
 }

@@ -137,10 +137,12 @@ int router_dw_splits(int64_t T);
 hipError_t launch_router_dw(const float* dl, const void* x, bool bf16, int64_t T, int N, int d,
                             float* part, float* dw_r, hipStream_t stream);
 
-// dx = sum of the token's kept rows of dx_perm (+ dx_shared) (+ dl W_r).
+// dx = sum of the token's kept rows of dx_perm (+ dx_perm2) (+ dx_shared
+// (+ dx_shared2)) (+ dl W_r); the second buffers are nullable.
 hipError_t launch_dx(const void* dx_perm, const int32_t* pair_row, int K, const void* dx_shared,
                      const float* dl, const float* w_r, int N, int64_t T, int d, bool bf16,
-                     void* dx, hipStream_t stream);
+                     void* dx, hipStream_t stream, const void* dx_perm2 = nullptr,
+                     const void* dx_shared2 = nullptr);
 
 struct FfnBwdProblem {
   int64_t T;
@@ -156,6 +158,10 @@ struct FfnBwdProblem {
   const void* dy;           // [T, d] gradient of the shared expert's output
   void* dx_perm;            // [T*K, d] out: gradient of each kept row's input
   void* dx_shared;          // [T, d] out (shared expert only)
+  // nullable: with them (SwiGLU, 256-row tiles) dx_perm / dx_shared get the
+  // du W1 part and these the dv W3 part; the caller adds the two
+  void* dx_perm2;
+  void* dx_shared2;
   void *dw1, *dw3, *dw2, *db1, *db2, *dws1, *dws3, *dws2;  // out
   void* ws;                 // ffn_backward_workspace_bytes
   // nullable, else 5 nullable events recorded after the recompute, the dh
@@ -163,6 +169,9 @@ struct FfnBwdProblem {
   const hipEvent_t* ev;
 };
 size_t ffn_backward_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared, bool bf16);
+// Whether launch_expert_ffn_backward, given dx_perm2 / dx_shared2, splits
+// dx_perm into its two parts for this shape (else it leaves them unwritten).
+bool ffn_backward_splits_dx(int64_t T, int N, int K, int F, int act, bool bf16);
 hipError_t launch_expert_ffn_backward(const FfnBwdProblem& p, hipStream_t stream);
 
 // Fill n bytes at p with zeros (a kernel, so it can be captured in a graph).

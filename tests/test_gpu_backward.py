@@ -139,7 +139,10 @@ def test_untouched_experts_get_zero_gradient():
 
 def test_staged_entry_points_match_the_layer():
     """combine -> router -> expert FFN -> dispatch backward, called one by
-    one, give the layer entry point's gradients bit for bit."""
+    one, give the layer entry point's gradients bit for bit.  (At this size
+    the layer computes dx_perm in one piece, as the staged call does; with
+    256-row tiles it adds two bf16 halves instead and the two agree to
+    rounding, which the parity cases cover.)"""
     w = W(name="bwd_staged", T=144, d=192, N=8, K=3, F=192, F_shared=192, seed=49)
     say("staged backward", w.name)
     inp = gpu_inputs(w, 0.0)
