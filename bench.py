@@ -230,6 +230,33 @@ def backward_record(w, steps, warmup, ev):
     dy = make_dy(w, device="cuda")
     cfg = api.config_for(w)
     fwd = api.moe_layer_forward(cfg, inp, inp["x"], save_for_backward=True)
+    wst0 = api.weights_struct(inp)
+
+    def graph_ms(fn):
+        # one call captured into a HIP graph, replayed `steps` times
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        del graph
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    # the forward a training step runs: it also keeps what the backward reads
+    # (logits, y_perm and, where stored, gate(x) / up(x))
+    fwd_save_ms = graph_ms(lambda: api.moe_layer_forward(cfg, inp, inp["x"], bufs=fwd,
+                                                         wstruct=wst0))
     bufs = api.BackwardBuffers(cfg, torch.device("cuda"))
     wst = api.weights_struct(inp)
     saved = api.saved_struct(fwd)
@@ -287,6 +314,7 @@ def backward_record(w, steps, warmup, ev):
     # the dW1 + dW3 stage is two launches of one kernel (SwiGLU)
     launches = 2 if (dom == "dw1_dw3_gemm" and w.act == "swiglu") else 1
     return {"workload": w.name, "ms_per_step": ms, "eager_ms_per_step": wall * 1e3 / steps,
+            "forward_saving_ms": fwd_save_ms, "saves_gate_up": fwd.u is not None,
             "tokens_per_s": w.T / (ms * 1e-3), "loss_grad": {"aux": lg[0], "z": lg[1], "z_lse": lg[2]},
             "algorithmic_tflop": algo / 1e12,
             "active_tflops": algo / (ms * 1e-3) / 1e12,

@@ -197,7 +197,12 @@ typedef struct {
 /* Outputs of the whole layer.  y [T, d] (dtype) is required; every other
  * pointer is nullable and, when NULL, the value lives in the workspace.
  * y_perm [T*K, d] (dtype): each kept row's expert output before its gate
- * (rows at and after offset[N] untouched); the backward pass reads it.   */
+ * (rows at and after offset[N] untouched); the backward pass reads it.
+ * u, v [T*K + (F_shared > 0 ? T : 0), F] (dtype), nullable, given together:
+ * the first expert GEMM's gate(x) = x W1^T and up(x) = x W3^T of every kept
+ * row (the shared expert's T rows after the T*K routed rows), written only
+ * where moe_layer_saves_uv(cfg) is 1.  Saved for the backward pass, which
+ * then skips recomputing them.                                           */
 typedef struct {
   void* y;
   int32_t* topk_idx;    /* [T, K] */
@@ -206,6 +211,8 @@ typedef struct {
   moe_stats_t stats;
   moe_dispatch_t dispatch;  /* x_perm is ignored (rows are gathered in place) */
   void* y_perm;
+  void* u;
+  void* v;
 } moe_layer_out_t;
 
 /* Optional timing hooks: hipEvent_t handles recorded on `stream` at stage
@@ -332,6 +339,8 @@ typedef struct {
   const int32_t* pair_row;  /* [T*K]                                        */
   const int32_t* row_pair;  /* [T*K]                                        */
   const void* y_perm;       /* [T*K, d] dtype, expert output per kept row   */
+  const void* u;            /* nullable: moe_layer_out_t.u / .v, used where */
+  const void* v;            /* moe_layer_saves_uv(cfg) is 1                 */
 } moe_saved_t;
 
 /* Gradient outputs.  dx [T, d] dtype; dw_r [N, d] fp32; db_r [N] fp32
@@ -360,6 +369,11 @@ typedef struct {
   float z;
   float z_lse;
 } moe_loss_grad_t;
+
+/* 1 if moe_layer_forward writes moe_layer_out_t.u / .v for this layer
+ * (bf16 SwiGLU layers with more than 96 rows per expert on average, whose
+ * first grouped GEMM runs the large-tile kernel), else 0 (host only).     */
+int32_t moe_layer_saves_uv(const moe_config_t* cfg);
 
 /* Bytes of workspace moe_layer_backward needs (host only); the staged
  * entry points need at most as much.                                     */

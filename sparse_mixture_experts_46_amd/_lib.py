@@ -20,7 +20,8 @@ EXPORTED = ("moe_status_string", "moe_capacity", "moe_workspace_size",
             "moe_ffn_workspace_size", "moe_router_topk", "moe_dispatch",
             "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_quantize_int8",
             "moe_backward_workspace_size", "moe_combine_backward", "moe_router_backward",
-            "moe_expert_ffn_backward", "moe_dispatch_backward", "moe_layer_backward")
+            "moe_expert_ffn_backward", "moe_dispatch_backward", "moe_layer_backward",
+            "moe_layer_saves_uv")
 
 
 class MoeConfig(C.Structure):
@@ -49,12 +50,12 @@ class MoeDispatch(C.Structure):
 class MoeLayerOut(C.Structure):
     _fields_ = [("y", C.c_void_p), ("topk_idx", C.c_void_p), ("topk_gate", C.c_void_p),
                 ("logits", C.c_void_p), ("stats", MoeStats), ("dispatch", MoeDispatch),
-                ("y_perm", C.c_void_p)]
+                ("y_perm", C.c_void_p), ("u", C.c_void_p), ("v", C.c_void_p)]
 
 
 class MoeSaved(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("logits", "topk_idx", "topk_gate", "count", "offset",
-                                          "pair_row", "row_pair", "y_perm")]
+                                          "pair_row", "row_pair", "y_perm", "u", "v")]
 
 
 class MoeGrads(C.Structure):
@@ -113,6 +114,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.moe_layer_forward.restype = C.c_int
     lib.moe_layer_forward.argtypes = [cfgp, wp, P, C.POINTER(MoeLayerOut), P, S,
                                       C.POINTER(MoeTrace), P]
+    lib.moe_layer_saves_uv.restype = C.c_int32
+    lib.moe_layer_saves_uv.argtypes = [cfgp]
     gp = C.POINTER(MoeGrads)
     lib.moe_combine_backward.restype = C.c_int
     lib.moe_combine_backward.argtypes = [cfgp, P, P, P, P, P, P, P]

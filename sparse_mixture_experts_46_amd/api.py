@@ -86,6 +86,10 @@ def moe_capacity(K: int, N: int, T: int, cf) -> int:
     return int(L.load().moe_capacity(K, N, T, -1.0 if cf is None else float(cf)))
 
 
+def moe_layer_saves_uv(cfg: Config) -> bool:
+    return bool(L.load().moe_layer_saves_uv(C.byref(cfg.c())))
+
+
 def moe_workspace_size(cfg: Config) -> int:
     return _size(L.load().moe_workspace_size, cfg)
 
@@ -228,6 +232,13 @@ class LayerBuffers:
         self.counters = torch.empty(4, dtype=torch.int32, device=device)
         self.y_perm = (torch.empty((T * K, cfg.d), dtype=cfg.torch_dtype, device=device)
                        if save_for_backward else None)
+        # gate(x) and up(x) of the first GEMM, where the forward stores them
+        uv_rows = T * K + (T if cfg.F_shared else 0)
+        keep_uv = save_for_backward and moe_layer_saves_uv(cfg)
+        self.u = (torch.empty((uv_rows, cfg.F), dtype=cfg.torch_dtype, device=device)
+                  if keep_uv else None)
+        self.v = (torch.empty((uv_rows, cfg.F), dtype=cfg.torch_dtype, device=device)
+                  if keep_uv else None)
         self.ws = _ws(moe_workspace_size(cfg), device)
         self.out = L.MoeLayerOut()
         self.out.y = _p(self.y).value
@@ -242,6 +253,8 @@ class LayerBuffers:
             pair_row=_p(self.pair_row).value, row_pair=_p(self.row_pair).value,
             dropped=_p(self.dropped).value, counters=_p(self.counters).value, x_perm=None)
         self.out.y_perm = None if self.y_perm is None else _p(self.y_perm).value
+        self.out.u = None if self.u is None else _p(self.u).value
+        self.out.v = None if self.v is None else _p(self.v).value
         self.ccfg = cfg.c()
 
     def as_dict(self) -> dict:
@@ -315,7 +328,9 @@ def saved_struct(fwd: LayerBuffers) -> L.MoeSaved:
     return L.MoeSaved(logits=_p(fwd.logits).value, topk_idx=_p(fwd.idx).value,
                       topk_gate=_p(fwd.gate).value, count=_p(fwd.count).value,
                       offset=_p(fwd.offset).value, pair_row=_p(fwd.pair_row).value,
-                      row_pair=_p(fwd.row_pair).value, y_perm=_p(fwd.y_perm).value)
+                      row_pair=_p(fwd.row_pair).value, y_perm=_p(fwd.y_perm).value,
+                      u=None if fwd.u is None else _p(fwd.u).value,
+                      v=None if fwd.v is None else _p(fwd.v).value)
 
 
 def moe_layer_backward(cfg: Config, w: dict, x: torch.Tensor, fwd: LayerBuffers,

@@ -614,8 +614,10 @@ hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
     return e;
   const int64_t all_rows = rows + srows;
 
-  // ---- 1. recompute u = x W1^T (+ b1) and v = x W3^T
-  {
+  // ---- 1. recompute u = x W1^T (+ b1) and v = x W3^T, unless the forward
+  // saved them
+  const bool saved_uv = bf16 && swiglu && p.u_in && p.v_in;
+  if (!saved_uv) {
     BwdArgs a = {};
     a.offset = p.offset; a.n_routed = p.N; a.shared_rows = srows; a.tile_base = base[0]; a.G = G;
     a.a = Xp; a.lda = d; a.a_shared = p.x;
@@ -632,8 +634,8 @@ hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
       e = swiglu ? run_bwd<128, false, false, true, false, BEPI_UV>(a, mt, bf16, s)
                  : run_bwd<128, false, false, false, false, BEPI_STORE>(a, mt, bf16, s);
     if (e != hipSuccess) return e;
-    if ((e = mark(0)) != hipSuccess) return e;
   }
+  if ((e = mark(0)) != hipSuccess) return e;  // recorded whether or not it ran
   // ---- 2. dh = d_perm W2 (W2 [d, F] read transposed); du, dv, h in the epilogue
   {
     BwdArgs a = {};
@@ -642,6 +644,12 @@ hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
     a.b0 = p.w2; a.b_stride = (int64_t)d * F; a.ldb = F; a.bs0 = p.ws2;
     a.Nout = F; a.Nout_shared = p.F_shared; a.Kdim = d;
     a.c = U; a.c2 = V; a.c3 = H; a.c_shared = Us; a.c2_shared = Vs; a.c3_shared = Hs; a.ldc = F;
+    if (saved_uv) {
+      a.cin = p.u_in;
+      a.cin2 = p.v_in;
+      a.cin_shared = (const char*)p.u_in + (size_t)rows * F * el;
+      a.cin2_shared = (const char*)p.v_in + (size_t)rows * F * el;
+    }
     const int64_t mt = row_tiles_bound(all_rows, G, bm2, F, bm2);
     if (TR)
       e = swiglu ? run_bwd_tr<false, true, false, false, BEPI_SWIGLU_BWD>(a, mt, s)

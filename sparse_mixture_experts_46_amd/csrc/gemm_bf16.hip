@@ -155,6 +155,11 @@ bool ffn_int8_supported(int64_t T, int K, int N) {
   return pick_kind((double)(T * K) / (double)N) == K_DECODE;
 }
 
+bool ffn_saves_uv(int64_t T, int K, int N, int act, bool bf16) {
+  const Kind k = pick_kind((double)(T * K) / (double)N);
+  return bf16 && act == 0 && (k == K_MID || k == K_BIG);
+}
+
 size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared, bool bf16) {
   (void)d; (void)N;
   const size_t el = bf16 ? 2 : 4;
@@ -238,6 +243,12 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   g1.G = G;
   g1.split_bm = 0;
   g1.region = 0;
+  if (p.save_u && p.save_v && swiglu && (k == K_MID || k == K_BIG)) {
+    g1.c_u = (uint16_t*)p.save_u;
+    g1.c_v = (uint16_t*)p.save_v;
+    g1.cs_u = g1.c_u + (size_t)rows * p.F;  // shared rows after the routed ones (F_shared == F)
+    g1.cs_v = g1.c_v + (size_t)rows * p.F;
+  }
   if (p.int8) {
     if (k != K_DECODE) return hipErrorNotSupported;  // checked on the host before
     g1.sc0 = p.w1_scale;

@@ -78,6 +78,12 @@ struct BwdArgs {
   void* c3_shared;
   int64_t ldc;
   int64_t c_gstride;         // weight groups: elements between groups' outputs
+  // nullable (BEPI_SWIGLU_BWD / BEPI_GELU_BWD): read u (and v) from here
+  // instead of c (c2); the results still go to c, c2, c3
+  const void* cin;
+  const void* cin2;
+  const void* cin_shared;
+  const void* cin2_shared;
 };
 
 __device__ __forceinline__ float silu_grad_f(float u) {
@@ -168,13 +174,15 @@ __device__ __forceinline__ void bwd_epilogue4(const BwdArgs& p, const BwdTile& t
   } else {  // BEPI_SWIGLU_BWD / BEPI_GELU_BWD: r0 = dh
     uint16_t* U = (uint16_t*)(ti.shared ? p.c_shared : p.c);
     uint16_t* H = (uint16_t*)(ti.shared ? p.c3_shared : p.c3);
-    const uint2 uu = *(const uint2*)(U + o);
+    const uint16_t* Ur = p.cin ? (const uint16_t*)(ti.shared ? p.cin_shared : p.cin) : U;
+    const uint2 uu = *(const uint2*)(Ur + o);
     float u[4] = {__uint_as_float(uu.x << 16), __uint_as_float(uu.x & 0xffff0000u),
                   __uint_as_float(uu.y << 16), __uint_as_float(uu.y & 0xffff0000u)};
     float du[4], h[4];
     if (EPI == BEPI_SWIGLU_BWD) {
       uint16_t* V = (uint16_t*)(ti.shared ? p.c2_shared : p.c2);
-      const uint2 vv = *(const uint2*)(V + o);
+      const uint16_t* Vr = p.cin2 ? (const uint16_t*)(ti.shared ? p.cin2_shared : p.cin2) : V;
+      const uint2 vv = *(const uint2*)(Vr + o);
       const float v[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
                           __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
       float dv[4];

@@ -41,6 +41,12 @@ struct GemmArgs {
   const float* sc1;
   const float* scs0;
   const float* scs1;
+  // nullable (SwiGLU first GEMM, ping-pong kernel only): also store the
+  // gate and up products A W1^T and A W3^T, routed [rows, Nout] / shared
+  uint16_t* c_u;
+  uint16_t* c_v;
+  uint16_t* cs_u;
+  uint16_t* cs_v;
 };
 
 // Rows [0, main_rows) of a group go to the main launch, in tiles of split_bm

@@ -261,6 +261,15 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
             pk.x = pack_bf16x2(o[0], o[1]);
             pk.y = pack_bf16x2(o[2], o[3]);
             *(uint2*)(crow + col) = pk;
+            if (DUAL && p.c_u) {  // also keep gate(x) and up(x) for the backward
+              const int64_t ro = (ti.row0 + lr) * ldc + col;
+              const f32x16_t& ga = acc[j][i];
+              const f32x16_t& up = acc[j + FN / 2][i];
+              *(uint2*)((ti.shared ? p.cs_u : p.c_u) + ro) =
+                  make_uint2(pack_bf16x2(ga[4 * q], ga[4 * q + 1]), pack_bf16x2(ga[4 * q + 2], ga[4 * q + 3]));
+              *(uint2*)((ti.shared ? p.cs_v : p.c_v) + ro) =
+                  make_uint2(pack_bf16x2(up[4 * q], up[4 * q + 1]), pack_bf16x2(up[4 * q + 2], up[4 * q + 3]));
+            }
           }
         }
       }

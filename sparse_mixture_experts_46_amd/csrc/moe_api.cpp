@@ -419,6 +419,8 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   set_weights(p, cfg, w);
   p.x_shared = x;
   p.y_perm = out->y_perm ? out->y_perm : at<void>(ws, L.y_perm);
+  p.save_u = out->u;
+  p.save_v = out->v;
   p.y_shared = cfg->F_shared > 0 ? at<void>(ws, L.y_shared) : nullptr;
   p.h = fws + FL.h;
   p.tile_base = (int32_t*)(fws + FL.tile_base);
@@ -440,6 +442,11 @@ moe_status_t moe_quantize_int8(const void* w, int64_t rows, int32_t cols, int8_t
   if (cols % 64) return MOE_ERR_UNSUPPORTED;
   if (rows * (int64_t)cols >= (int64_t(1) << 40)) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_quantize_int8(w, rows, cols, q, scale, (hipStream_t)stream));
+}
+
+int32_t moe_layer_saves_uv(const moe_config_t* cfg) {
+  if (check_config(cfg) != MOE_OK || cfg->weight_format != MOE_WEIGHTS_DTYPE) return 0;
+  return ffn_saves_uv(cfg->T, cfg->K, cfg->N, cfg->act, cfg->dtype == MOE_BF16) ? 1 : 0;
 }
 
 // ---- backward ---------------------------------------------------------------
@@ -519,7 +526,8 @@ moe_status_t do_ffn_backward(const moe_config_t* cfg, const moe_weights_t* w, co
                              const void* dy, void* dx_perm, void* dx_shared,
                              const moe_grads_t* g, void* ws, hipStream_t s,
                              const hipEvent_t* ev = nullptr, void* dx_perm2 = nullptr,
-                             void* dx_shared2 = nullptr) {
+                             void* dx_shared2 = nullptr, const void* u_in = nullptr,
+                             const void* v_in = nullptr) {
   FfnBwdProblem p = {};
   p.T = cfg->T; p.d = cfg->d; p.N = cfg->N; p.K = cfg->K; p.F = cfg->F;
   p.F_shared = cfg->F_shared; p.act = cfg->act; p.bf16 = cfg->dtype == MOE_BF16;
@@ -528,6 +536,7 @@ moe_status_t do_ffn_backward(const moe_config_t* cfg, const moe_weights_t* w, co
   p.ws1 = w->ws1; p.ws3 = w->ws3; p.ws2 = w->ws2;
   p.d_perm = d_perm; p.dy = dy; p.dx_perm = dx_perm; p.dx_shared = dx_shared;
   p.dx_perm2 = dx_perm2; p.dx_shared2 = dx_shared2;
+  p.u_in = u_in; p.v_in = v_in;
   p.dw1 = g->dw1; p.dw3 = g->dw3; p.dw2 = g->dw2;
   // bias gradients only for layers that have the biases
   p.db1 = w->b1 ? g->db1 : nullptr;
@@ -634,8 +643,12 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   // dx_perm in two parts (du W1, dv W3) that the dx kernel adds
   void* dx_perm2 = at<void>(ws, B.dx_perm2);
   void* dx_shared2 = cfg->F_shared > 0 ? at<void>(ws, B.dx_shared2) : nullptr;
+  // the forward's gate(x) and up(x), where it stores them: no recompute
+  const bool have_uv = sv->u && sv->v &&
+                       ffn_saves_uv(cfg->T, cfg->K, cfg->N, cfg->act, cfg->dtype == MOE_BF16);
   st = do_ffn_backward(cfg, w, x, sv->row_pair, sv->offset, d_perm, dy, dx_perm, dx_shared, g,
-                       at<void>(ws, B.ffn), s, fev, dx_perm2, dx_shared2);
+                       at<void>(ws, B.ffn), s, fev, dx_perm2, dx_shared2,
+                       have_uv ? sv->u : nullptr, have_uv ? sv->v : nullptr);
   if (st != MOE_OK) return st;
   if ((st = mark(8)) != MOE_OK) return st;
   // the FFN backward fills the second parts only when it splits (else null)

@@ -89,6 +89,11 @@ struct FfnProblem {
   void* y_perm;     // [T*K, d]
   void* y_shared;   // [T, d]
   int32_t* tile_base;  // [3 * (N + 2)] scratch: three tile tables
+  // nullable, SwiGLU: also store gate(x) = A W1^T and up(x) = A W3^T
+  // ([T*K + T_shared, F], shared rows after the routed ones) when the first
+  // GEMM runs the ping-pong kernel (ffn_saves_uv)
+  void* save_u;
+  void* save_v;
   // weight-only INT8 (w1/w3/w2/ws* hold int8 codes): per-output-row scales
   bool int8;
   const float *w1_scale, *w3_scale, *w2_scale, *ws1_scale, *ws3_scale, *ws2_scale;
@@ -97,6 +102,10 @@ struct FfnProblem {
 // INT8 weights are supported where the decode kernel runs: at most
 // this many routed rows per expert on average.
 bool ffn_int8_supported(int64_t T, int K, int N);
+
+// Whether launch_expert_ffn stores gate(x) and up(x) when asked (bf16
+// SwiGLU layers whose first GEMM runs the ping-pong kernel).
+bool ffn_saves_uv(int64_t T, int K, int N, int act, bool bf16);
 
 size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared,
                            bool bf16);
@@ -162,6 +171,10 @@ struct FfnBwdProblem {
   // du W1 part and these the dv W3 part; the caller adds the two
   void* dx_perm2;
   void* dx_shared2;
+  // nullable: gate(x) and up(x) saved by the forward (layout of save_u /
+  // save_v); with them the first GEMM is not recomputed
+  const void* u_in;
+  const void* v_in;
   void *dw1, *dw3, *dw2, *db1, *db2, *dws1, *dws3, *dws2;  // out
   void* ws;                 // ffn_backward_workspace_bytes
   // nullable, else 5 nullable events recorded after the recompute, the dh

@@ -202,3 +202,17 @@ def test_quantize_rejects_before_launch(lib):
     assert lib.moe_quantize_int8(None, 4, 64, fake, fake, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_quantize_int8(fake, 4, 96, fake, fake, None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_quantize_int8(None, 0, 64, None, None, None) == L.MOE_OK  # nothing to do
+
+
+def test_layer_saves_uv_rule(lib):
+    """The forward stores gate(x) / up(x) for bf16 SwiGLU layers whose first
+    GEMM runs the large-tile kernel (more than 96 rows per expert)."""
+    rule = {"mixtral_prefill": 1, "deepseek_prefill": 1, "mixtral_decode": 0,
+            "deepseek_decode": 0, "switch_top1_cap": 0, "tiny_f32": 0}
+    for name, want in rule.items():
+        assert lib.moe_layer_saves_uv(C.byref(cfg_of(WL.ALL[name]))) == want, name
+    small = cfg_of(WL.MIXTRAL_PREFILL, T=384)   # 96 rows per expert
+    assert lib.moe_layer_saves_uv(C.byref(small)) == 0
+    small.T = 388                               # 97
+    assert lib.moe_layer_saves_uv(C.byref(small)) == 1
+    assert lib.moe_layer_saves_uv(C.byref(cfg_of(WL.MIXTRAL_PREFILL, K=9))) == 0  # invalid

@@ -262,3 +262,46 @@ def test_backward_full_size(w, ntok, ncol):
         want_b = dl.sum(dim=0)
         bound_b = 2.0 * w.T * 2.0 ** -24 * dl.abs().sum(dim=0)
         assert bool(((g.db_r.double() - want_b).abs() <= bound_b).all())
+
+
+def test_forward_saves_gate_and_up_for_the_backward():
+    """Where the forward stores gate(x) = x W1^T and up(x) = x W3^T (256 rows
+    per expert here, with a shared expert), they match the oracle's per kept
+    row, and the backward that reads them instead of recomputing matches the
+    oracle as the recomputing one does."""
+    w = W(name="bwd_saved_uv", T=512, d=256, N=4, K=2, F=320, F_shared=320, seed=53)
+    say("saved u/v", w.name)
+    inp = gpu_inputs(w, 0.0)
+    dy = make_dy(w, DEV)
+    cfg = api.config_for(w)
+    assert api.moe_layer_saves_uv(cfg)
+    fwd = api.moe_layer_forward(cfg, inp, inp["x"], save_for_backward=True)
+    torch.cuda.synchronize()
+    assert fwd.u is not None
+    # gate / up of every kept row, and of the shared expert's rows
+    x = f64(inp["x"])
+    rows = int(fwd.offset[-1].item())
+    rp = fwd.row_pair[:rows].cpu().numpy()
+    off = fwd.offset.cpu().numpy()
+    Wt, shared = oracle_weights(inp, True)
+    u_ref = np.zeros((rows + w.T, w.F))
+    v_ref = np.zeros((rows + w.T, w.F))
+    for e in range(w.N):
+        xr = x[rp[off[e]:off[e + 1]] // w.K]
+        u_ref[off[e]:off[e + 1]] = xr @ Wt["w1"][e].T
+        v_ref[off[e]:off[e + 1]] = xr @ Wt["w3"][e].T
+    u_ref[rows:] = x @ shared["w1"].T
+    v_ref[rows:] = x @ shared["w3"].T
+    keep = np.r_[np.arange(rows), w.T * w.K + np.arange(w.T)]
+    assert rel_err(f64(fwd.u)[keep], u_ref) <= TOL_BF16
+    assert rel_err(f64(fwd.v)[keep], v_ref) <= TOL_BF16
+    lg = (0.5, 0.1, 0.0)
+    g_saved = api.moe_layer_backward(cfg, inp, inp["x"], fwd, dy, lg)
+    torch.cuda.synchronize()
+    saved = api.saved_struct(fwd)
+    saved.u = saved.v = None  # the recomputing path on the same forward
+    g_re = api.moe_layer_backward(cfg, inp, inp["x"], fwd, dy, lg, saved=saved)
+    torch.cuda.synchronize()
+    o = run_oracle(w, inp, dy, lg, 0.0, fwd.idx.cpu().numpy().astype(np.int64))
+    compare(w, g_saved, o, TOL_BF16)
+    compare(w, g_re, o, TOL_BF16)
