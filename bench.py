@@ -486,6 +486,8 @@ def main():
     del r
     torch.cuda.empty_cache()
     if not a.no_backward:
+        if a.copy_probe_mib:  # a second probe marks where the backward's launches begin
+            copy_probe(a.copy_probe_mib)
         line["backward"] = backward_record(w, a.steps, a.warmup, ev)
         torch.cuda.empty_cache()
     if w.T * w.K <= 24 * w.N and w.act == "swiglu" and w.dtype == "bf16":

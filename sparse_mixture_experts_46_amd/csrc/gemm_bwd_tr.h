@@ -22,6 +22,10 @@
 //    (a group's last row tile, a weight gradient's ragged K) read as zeros.
 //  * 8 waves of 128 x 64 outputs (v_mfma_f32_32x32x16_bf16, weight fragment
 //    first); waves 0-3 issue the A tile's DMA, waves 4-7 the B tile's.
+//  * Each wave reads the fragments of the next 16-wide K slice while the
+//    MFMAs of the current one run; the stage's one barrier sits before its
+//    last slice's MFMAs, so the next stage's first fragments are read under
+//    them too.
 //  * SK2 (with dual K): the two halves of K are separate tiles, the first
 //    half's results going to c and the second's to c2 (the caller adds
 //    them), which doubles the tiles of a GEMM with few output tiles.
@@ -40,8 +44,13 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 __device__ __forceinline__ void dma16_bounded(const void* base, uint32_t nrec, uint32_t voff,
                                               void* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)nrec, 0x00020000);
+  // base and extent are wave-uniform: saying so keeps the descriptor in SGPRs
+  // (else every load becomes a loop over the lanes' descriptors)
+  const uint64_t b = (uint64_t)base;
+  const uint64_t ub = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ub, (short)0, __builtin_amdgcn_readfirstlane((int)nrec), 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, 0, 0, 0);
 #endif
 }
@@ -190,30 +199,47 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
       return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
+    // fragments of K slice ks of a stage
+    auto read_frags = [&](int stage, int ks, bf16x8_t* xa, bf16x8_t* xb) {
+      const char* SA = L + stage * STB;
+      const char* SB = SA + OPB;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        xa[i] = A_STRIDED ? frag_t(SA, am[i], ks) : frag_c(SA, am[i], ks * 2 + khalf);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        xb[j] = B_STRIDED ? frag_t(SB, bn[j], ks) : frag_c(SB, bn[j], ks * 2 + khalf);
+    };
+    bf16x8_t fa[FM], fb[FN];
     if (nk > 0) issue(0, 0);
     wait_vmcnt<0>();
     __syncthreads();
+    if (nk > 0) read_frags(0, 0, fa, fb);
     for (int kt = 0; kt < nk; ++kt) {
       if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-      const char* SA = L + (kt & 1) * STB;
-      const char* SB = SA + OPB;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
-        bf16x8_t fa[FM], fb[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          fa[i] = A_STRIDED ? frag_t(SA, am[i], ks) : frag_c(SA, am[i], ks * 2 + khalf);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          fb[j] = B_STRIDED ? frag_t(SB, bn[j], ks) : frag_c(SB, bn[j], ks * 2 + khalf);
+        // the next slice's fragments are read while this slice's MFMAs run
+        bf16x8_t na[FM], nb[FN];
+        if (ks + 1 < BK / 16) {
+          read_frags(kt & 1, ks + 1, na, nb);
+        } else {
+          // stage kt + 1 landed for every wave, and every wave holds stage
+          // kt's last fragments in registers before the stage is refilled
+          wait_vmcnt<0>();
+          __syncthreads();
+          if (kt + 1 < nk) read_frags((kt + 1) & 1, 0, na, nb);
+        }
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int i = 0; i < FM; ++i)
             acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[j][i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[i] = na[i];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[j] = nb[j];
       }
-      wait_vmcnt<0>();  // this wave's DMA of stage kt + 1
-      __syncthreads();  // everyone's; and stage kt read by all before it is refilled
     }
 
     // ---- epilogue (as gemm_bwd_kernel); the second K half writes c2

@@ -43,7 +43,12 @@ namespace moe {
 // 16-byte-per-lane global -> LDS copy through a raw buffer resource.
 __device__ __forceinline__ void buf_dma16(const void* base, uint32_t voff, void* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000);
+  // base is wave-uniform: saying so keeps the descriptor in SGPRs (else every
+  // load becomes a loop over the lanes' descriptors)
+  const uint64_t b = (uint64_t)base;
+  const uint64_t ub = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0, -1, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, 0, 0, 0);
 #endif
 }

@@ -63,13 +63,38 @@ def stats_table(trace_dir):
     return out
 
 
+PROBE = "torch neg (copy probe)"
+
+
 def counters(pmc_dir, counter):
+    """{(kernel, section): [value per launch]}.  bench.py runs the copy probe
+    once before the forward and again before the backward: launches after the
+    second probe are the backward section's (whose forward also keeps gate and
+    up, so the same GEMM 1 kernel writes more there)."""
     rows = list(csv.DictReader(open(one(os.path.join(pmc_dir, "**", "*counter_collection.csv")))))
+    rows = [r for r in rows if r["Counter_Name"] == counter]
+    probes = sorted(int(r["Dispatch_Id"]) for r in rows if short(r["Kernel_Name"]) == PROBE)
+    edge = probes[1] if len(probes) > 1 else float("inf")
     by = {}
     for r in rows:
-        if r["Counter_Name"] != counter:
-            continue
-        by.setdefault(short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        k = short(r["Kernel_Name"])
+        sec = "" if k == PROBE else ("backward" if int(r["Dispatch_Id"]) > edge else "forward")
+        by.setdefault((k, sec), []).append(float(r["Counter_Value"]))
+    return by
+
+
+def section_durations(trace_dir):
+    """{(kernel, section): [duration us per launch]} from the kernel trace,
+    split at the second copy probe as in counters()."""
+    rows = list(csv.DictReader(open(one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))))
+    probes = sorted(int(r["Dispatch_Id"]) for r in rows if short(r["Kernel_Name"]) == PROBE)
+    edge = probes[1] if len(probes) > 1 else float("inf")
+    by = {}
+    for r in rows:
+        k = short(r["Kernel_Name"])
+        sec = "" if k == PROBE else ("later" if int(r["Dispatch_Id"]) > edge else "forward")
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        by.setdefault((k, sec), []).append(us)
     return by
 
 
@@ -92,6 +117,14 @@ def main():
              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
     for n, c, avg, tot, pct in tab[:25]:
         lines.append(f"| `{n}` | {c} | {avg:.1f} | {tot:.3f} | {pct:.2f} |")
+    dur = section_durations(a.trace)
+    lines += ["", "## The same kernel trace split at the second copy probe", "",
+              "forward: the prefill forward's launches; later: the backward (with the forward "
+              "that keeps gate and up), then the decode.", "",
+              "| section | kernel | launches | avg us |", "|---|---|---|---|"]
+    for (k, sec), v in sorted(dur.items(), key=lambda kv: -sum(kv[1]))[:30]:
+        if "moe::" in k:
+            lines.append(f"| {sec} | `{k}` | {len(v)} | {sum(v) / len(v):.1f} |")
     if a.bench_log:
         js = [json.loads(l) for l in open(a.bench_log) if l.startswith("{")]
         if js:
@@ -122,30 +155,29 @@ def main():
         f = counters(a.fetch, "FETCH_SIZE")
         w = counters(a.write, "WRITE_SIZE")
         probe_bytes = a.probe_mib * (1 << 20)
-        fk = f["torch neg (copy probe)"][0]
-        wk = w["torch neg (copy probe)"][0]
+        fk = f[(PROBE, "")][0]
+        wk = w[(PROBE, "")][0]
         fscale = probe_bytes / (fk * 1024.0)
         wscale = probe_bytes / (wk * 1024.0)
         lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
                   f"Copy probe: {a.probe_mib} MiB read + {a.probe_mib} MiB written; "
                   f"FETCH_SIZE read {fk:.0f} KiB (scale x{fscale:.3f}), "
                   f"WRITE_SIZE read {wk:.0f} KiB (scale x{wscale:.3f}).", "",
-                  "| kernel | fetch MB/launch (scaled) | write MB/launch (scaled) |",
-                  "|---|---|---|"]
+                  "| section | kernel | launches | fetch MB/launch (scaled) | write MB/launch (scaled) |",
+                  "|---|---|---|---|---|"]
         rec = {}
-        for k in sorted(set(f) & set(w)):
-            if "moe::" not in k and not k.startswith("gemm") and "moe" not in k:
-                if not any(s in k for s in ("gemm", "router", "dispatch", "combine", "tile_setup")):
-                    continue
-            fb = sum(f[k]) / len(f[k]) * 1024 * fscale
-            wb = sum(w[k]) / len(w[k]) * 1024 * wscale
-            rec[k] = (fb, wb)
-            lines.append(f"| `{k}` | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
-        g1 = [k for k in rec if a.gemm1 in k]
+        for k, sec in sorted(set(f) & set(w), key=lambda ks: (ks[1] != "forward", ks[0])):
+            if "moe::" not in k:
+                continue
+            fb = sum(f[(k, sec)]) / len(f[(k, sec)]) * 1024 * fscale
+            wb = sum(w[(k, sec)]) / len(w[(k, sec)]) * 1024 * wscale
+            rec[(k, sec)] = (fb, wb)
+            lines.append(f"| {sec} | `{k}` | {len(f[(k, sec)])} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+        g1 = [k for k in rec if a.gemm1 in k[0] and k[1] == "forward"]
         if g1:
             fb, wb = rec[g1[0]]
             sha = gemm_source_sha256()
-            json.dump({"workload": a.workload, "kernel": g1[0], "fetch_bytes": fb,
+            json.dump({"workload": a.workload, "kernel": g1[0][0], "fetch_bytes": fb,
                        "write_bytes": wb, "bytes_per_launch": fb + wb,
                        "fetch_scale": fscale, "write_scale": wscale,
                        "gemm_source_sha256": sha, "cmd": a.cmd.strip()},
