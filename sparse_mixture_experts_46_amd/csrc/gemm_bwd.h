@@ -152,6 +152,110 @@ __device__ __forceinline__ int bwd_swz(int row) { return (row >> 1) & 7; }
 
 // Epilogue of 4 consecutive output columns col .. col+3 at element offset o
 // (r0: the accumulators; r1: the up half of a dual-B tile).
+//
+// The activation-backward epilogues (BEPI_SWIGLU_BWD / BEPI_GELU_BWD) in two
+// halves: the bf16 u (and v) of 4 columns, then du (dv) and h from them.  The
+// results may overwrite u and v in place, so a caller that loads several
+// runs before storing any keeps the loads from waiting on the stores.
+template <int EPI>
+__device__ __forceinline__ void act_bwd_load4(const BwdArgs& p, const BwdTile& ti, int64_t o, uint2& uu,
+                                              uint2& vv) {
+  const uint16_t* Ur = (const uint16_t*)(p.cin ? (ti.shared ? p.cin_shared : p.cin)
+                                                : (ti.shared ? p.c_shared : p.c));
+  uu = *(const uint2*)(Ur + o);
+  if (EPI == BEPI_SWIGLU_BWD) {
+    const uint16_t* Vr = (const uint16_t*)(p.cin2 ? (ti.shared ? p.cin2_shared : p.cin2)
+                                                   : (ti.shared ? p.c2_shared : p.c2));
+    vv = *(const uint2*)(Vr + o);
+  } else {
+    vv = make_uint2(0u, 0u);
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void act_bwd_store4(const BwdArgs& p, const BwdTile& ti, int64_t o,
+                                               const float (&r0)[4], const uint2& uu, const uint2& vv) {
+  uint16_t* U = (uint16_t*)(ti.shared ? p.c_shared : p.c);
+  uint16_t* H = (uint16_t*)(ti.shared ? p.c3_shared : p.c3);
+  const float u[4] = {__uint_as_float(uu.x << 16), __uint_as_float(uu.x & 0xffff0000u),
+                      __uint_as_float(uu.y << 16), __uint_as_float(uu.y & 0xffff0000u)};
+  float du[4], h[4];
+  if (EPI == BEPI_SWIGLU_BWD) {
+    uint16_t* V = (uint16_t*)(ti.shared ? p.c2_shared : p.c2);
+    const float v[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
+                        __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
+    float dv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sg = silu_f(u[e]);
+      h[e] = sg * v[e];
+      dv[e] = r0[e] * sg;
+      du[e] = r0[e] * v[e] * silu_grad_f(u[e]);
+    }
+    *(uint2*)(V + o) = make_uint2(pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = gelu_tanh_f(u[e]);
+      du[e] = r0[e] * gelu_tanh_grad_f(u[e]);
+    }
+  }
+  *(uint2*)(U + o) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+  *(uint2*)(H + o) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+}
+
+// The same on 8 columns (16-byte runs).
+template <int EPI>
+__device__ __forceinline__ void act_bwd_load8(const BwdArgs& p, const BwdTile& ti, int64_t o, uint4& uu,
+                                              uint4& vv) {
+  const uint16_t* Ur = (const uint16_t*)(p.cin ? (ti.shared ? p.cin_shared : p.cin)
+                                                : (ti.shared ? p.c_shared : p.c));
+  uu = *(const uint4*)(Ur + o);
+  if (EPI == BEPI_SWIGLU_BWD) {
+    const uint16_t* Vr = (const uint16_t*)(p.cin2 ? (ti.shared ? p.cin2_shared : p.cin2)
+                                                   : (ti.shared ? p.c2_shared : p.c2));
+    vv = *(const uint4*)(Vr + o);
+  } else {
+    vv = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void act_bwd_store8(const BwdArgs& p, const BwdTile& ti, int64_t o,
+                                               const float (&r0)[8], const uint4& uu, const uint4& vv) {
+  uint16_t* U = (uint16_t*)(ti.shared ? p.c_shared : p.c);
+  uint16_t* H = (uint16_t*)(ti.shared ? p.c3_shared : p.c3);
+  const uint32_t uw[4] = {uu.x, uu.y, uu.z, uu.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
+  uint32_t du[4], dv[4], h[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float u2[2] = {__uint_as_float(uw[c] << 16), __uint_as_float(uw[c] & 0xffff0000u)};
+    float du2[2], dv2[2], h2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float g = r0[2 * c + e];
+      if (EPI == BEPI_SWIGLU_BWD) {
+        const float v = __uint_as_float(e ? (vw[c] & 0xffff0000u) : (vw[c] << 16));
+        const float sg = silu_f(u2[e]);
+        h2[e] = sg * v;
+        dv2[e] = g * sg;
+        du2[e] = g * v * silu_grad_f(u2[e]);
+      } else {
+        h2[e] = gelu_tanh_f(u2[e]);
+        du2[e] = g * gelu_tanh_grad_f(u2[e]);
+        dv2[e] = 0.f;
+      }
+    }
+    du[c] = pack_bf16x2(du2[0], du2[1]);
+    dv[c] = pack_bf16x2(dv2[0], dv2[1]);
+    h[c] = pack_bf16x2(h2[0], h2[1]);
+  }
+  if (EPI == BEPI_SWIGLU_BWD)
+    *(uint4*)((uint16_t*)(ti.shared ? p.c2_shared : p.c2) + o) = make_uint4(dv[0], dv[1], dv[2], dv[3]);
+  *(uint4*)(U + o) = make_uint4(du[0], du[1], du[2], du[3]);
+  *(uint4*)(H + o) = make_uint4(h[0], h[1], h[2], h[3]);
+}
+
 template <int EPI, bool WG>
 __device__ __forceinline__ void bwd_epilogue4(const BwdArgs& p, const BwdTile& ti, int64_t o, int col,
                                               float (&r0)[4], const float (&r1)[4]) {
@@ -172,37 +276,9 @@ __device__ __forceinline__ void bwd_epilogue4(const BwdArgs& p, const BwdTile& t
     *(uint2*)(C + o) = make_uint2(pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]));
     *(uint2*)(C2 + o) = make_uint2(pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3]));
   } else {  // BEPI_SWIGLU_BWD / BEPI_GELU_BWD: r0 = dh
-    uint16_t* U = (uint16_t*)(ti.shared ? p.c_shared : p.c);
-    uint16_t* H = (uint16_t*)(ti.shared ? p.c3_shared : p.c3);
-    const uint16_t* Ur = p.cin ? (const uint16_t*)(ti.shared ? p.cin_shared : p.cin) : U;
-    const uint2 uu = *(const uint2*)(Ur + o);
-    float u[4] = {__uint_as_float(uu.x << 16), __uint_as_float(uu.x & 0xffff0000u),
-                  __uint_as_float(uu.y << 16), __uint_as_float(uu.y & 0xffff0000u)};
-    float du[4], h[4];
-    if (EPI == BEPI_SWIGLU_BWD) {
-      uint16_t* V = (uint16_t*)(ti.shared ? p.c2_shared : p.c2);
-      const uint16_t* Vr = p.cin2 ? (const uint16_t*)(ti.shared ? p.cin2_shared : p.cin2) : V;
-      const uint2 vv = *(const uint2*)(Vr + o);
-      const float v[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xffff0000u),
-                          __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xffff0000u)};
-      float dv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float sg = silu_f(u[e]);
-        h[e] = sg * v[e];
-        dv[e] = r0[e] * sg;
-        du[e] = r0[e] * v[e] * silu_grad_f(u[e]);
-      }
-      *(uint2*)(V + o) = make_uint2(pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[e] = gelu_tanh_f(u[e]);
-        du[e] = r0[e] * gelu_tanh_grad_f(u[e]);
-      }
-    }
-    *(uint2*)(U + o) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-    *(uint2*)(H + o) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+    uint2 uu, vv;
+    act_bwd_load4<EPI>(p, ti, o, uu, vv);
+    act_bwd_store4<EPI>(p, ti, o, r0, uu, vv);
   }
 }
 
@@ -401,12 +477,37 @@ __global__ __launch_bounds__(2 * R, R == 128 ? 2 : 1) void gemm_bwd_kernel(BwdAr
     // output column = fragment j column 8 * (v / 4) + 4 * (lane / 32) + v % 4.
     const int mlim = WG ? p.Mout : ti.rows;
     constexpr int FO = DUALB ? FN / 2 : FN;
+    constexpr bool ACT = EPI == BEPI_SWIGLU_BWD || EPI == BEPI_GELU_BWD;
+    static_assert(!(ACT && DUALB), "the activation epilogues take one B operand");
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int m = ti.mt * BM + wm * TM + i * 32 + (lane & 31);
       if (m >= mlim) continue;
       const int64_t rowoff = WG ? (ti.shared ? 0 : (int64_t)ti.g * p.c_gstride) + (int64_t)m * p.ldc
                                 : (ti.row0 + m) * p.ldc;
+      if constexpr (ACT) {
+        // all of this row's u (and v) runs first, then the stores
+        uint2 uu[FO][4], vv[FO][4];
+#pragma unroll
+        for (int j = 0; j < FO; ++j)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int col = ti.nt * BNo + wn * TN + j * 32 + 4 * khalf + 8 * qq;
+            if (col < ti.nout) act_bwd_load4<EPI>(p, ti, rowoff + col, uu[j][qq], vv[j][qq]);
+          }
+#pragma unroll
+        for (int j = 0; j < FO; ++j)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int col = ti.nt * BNo + wn * TN + j * 32 + 4 * khalf + 8 * qq;
+            if (col >= ti.nout) continue;
+            float r0[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) r0[u] = acc[j][i][4 * qq + u];
+            act_bwd_store4<EPI>(p, ti, rowoff + col, r0, uu[j][qq], vv[j][qq]);
+          }
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < FO; ++j) {
         const int cb = ti.nt * BNo + (DUALB ? wn * (TN / 2) : wn * TN) + j * 32 + 4 * khalf;

@@ -88,13 +88,17 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
   const TileWalk walk = tile_walk(total);
 
   // first row (A) / column (B) of this wave's fragments within the tile
+  // (the activation epilogues: fragment j of the 4 wave columns covers tile
+  // columns 128 j .. 128 j + 127, which the epilogue stages one j at a time)
+  constexpr bool ACT = EPI == BEPI_SWIGLU_BWD || EPI == BEPI_GELU_BWD;
+  static_assert(!(ACT && (DUALB || WG || SK2 || FN != 2)), "activation epilogues: row groups, one B");
   int am[FM], bn[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) am[i] = wm * TM + i * 32;
 #pragma unroll
   for (int j = 0; j < FN; ++j)
     bn[j] = DUALB ? (j < FN / 2 ? wn * (TN / 2) + j * 32 : BN / 2 + wn * (TN / 2) + (j - FN / 2) * 32)
-                  : wn * TN + j * 32;
+                  : (ACT ? j * 128 + wn * 32 : wn * TN + j * 32);
 
   for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
     const int half = (SK2 && tile >= total1) ? 1 : 0;  // split K: which half
@@ -247,6 +251,56 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
     if (SK2 && half) {
       pe.c = p.c2;
       pe.c_shared = p.c2_shared;
+    }
+    if constexpr (ACT) {
+      // Through LDS, 128 columns at a time: every wave puts its fragment j
+      // of dh there as fp32 [256 rows][128] (16-byte chunk c of row r at
+      // c ^ (r & 31)); then each thread takes 8 consecutive columns of a row,
+      // so u, v, du, dv and h move as whole 128-byte lines.  No wave reads
+      // the stages after the K loop's last barrier, so the first pass needs
+      // no barrier before it writes.
+      float* E = (float*)L;
+      const int cp = tid & 15;  // this thread's 8 columns of the pass: 8 cp .. 8 cp + 7
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int r = am[i] + (lane & 31);
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int c = wn * 8 + 2 * qq + khalf;
+            *(float4*)(E + r * 128 + ((c ^ (r & 31)) << 2)) =
+                make_float4(acc[j][i][4 * qq], acc[j][i][4 * qq + 1], acc[j][i][4 * qq + 2],
+                            acc[j][i][4 * qq + 3]);
+          }
+        }
+        __syncthreads();
+        const int col = ti.nt * BN + j * 128 + 8 * cp;
+        // 32 rows per pass of the 512 threads; 4 rows' u (and v) loaded
+        // before any of their results is stored (which may be in place)
+#pragma unroll
+        for (int b = 0; b < 8; b += 4) {
+          uint4 uu[4], vv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int m = ti.mt * BM + (b + q) * 32 + (tid >> 4);
+            if (m < ti.rows && col < ti.nout)
+              act_bwd_load8<EPI>(p, ti, (ti.row0 + m) * p.ldc + col, uu[q], vv[q]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = (b + q) * 32 + (tid >> 4);
+            const int m = ti.mt * BM + r;
+            if (m >= ti.rows || col >= ti.nout) continue;
+            const float4 d0 = *(const float4*)(E + r * 128 + (((2 * cp) ^ (r & 31)) << 2));
+            const float4 d1 = *(const float4*)(E + r * 128 + (((2 * cp + 1) ^ (r & 31)) << 2));
+            const float g[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            act_bwd_store8<EPI>(p, ti, (ti.row0 + m) * p.ldc + col, g, uu[q], vv[q]);
+          }
+        }
+        __syncthreads();  // E read by all before it is refilled (next pass, next tile's DMA)
+      }
+      continue;
     }
     const int mlim = WG ? p.Mout : ti.rows;
     constexpr int FO = DUALB ? FN / 2 : FN;
