@@ -362,7 +362,8 @@ hipError_t launch_router_dw(const float* dl, const void* x, bool bf16, int64_t T
 // tiles of 16 experts; the row gathers afterwards, in slot order.
 template <bool BF16>
 __global__ __launch_bounds__(256) void dx_kernel(const void* __restrict__ dx_perm,
-                                                 const void* __restrict__ dx_perm2,
+                                                 const void* __restrict__ dx_perm2, int planes2,
+                                                 int64_t rows,
                                                  const int32_t* __restrict__ pair_row, int K,
                                                  const void* __restrict__ dx_shared,
                                                  const void* __restrict__ dx_shared2,
@@ -425,11 +426,12 @@ __global__ __launch_bounds__(256) void dx_kernel(const void* __restrict__ dx_per
       const int r = pair_row[t * K + k];
       if (r >= 0) {
         add_row(dx_perm, r);
-        if (dx_perm2) add_row(dx_perm2, r);
+        for (int q = 0; q < planes2; ++q) add_row(dx_perm2, q * rows + r);
       }
     }
     if (dx_shared) add_row(dx_shared, t);
-    if (dx_shared2) add_row(dx_shared2, t);
+    if (dx_shared2)
+      for (int q = 0; q < planes2; ++q) add_row(dx_shared2, q * T + t);
     if (BF16)
       *(uint2*)((uint16_t*)dx + t * d + i) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     else
@@ -439,15 +441,17 @@ __global__ __launch_bounds__(256) void dx_kernel(const void* __restrict__ dx_per
 
 hipError_t launch_dx(const void* dx_perm, const int32_t* pair_row, int K, const void* dx_shared,
                      const float* dl, const float* w_r, int N, int64_t T, int d, bool bf16,
-                     void* dx, hipStream_t s, const void* dx_perm2, const void* dx_shared2) {
+                     void* dx, hipStream_t s, const void* dx_perm2, const void* dx_shared2,
+                     int planes2) {
   if (T == 0) return hipSuccess;
+  if (!dx_perm2) planes2 = 0;
   dim3 grid((unsigned)((T + 63) / 64), (unsigned)((d + 63) / 64));
   if (bf16)
-    dx_kernel<true><<<grid, 256, 0, s>>>(dx_perm, dx_perm2, pair_row, K, dx_shared, dx_shared2,
-                                         dl, w_r, N, T, d, dx);
+    dx_kernel<true><<<grid, 256, 0, s>>>(dx_perm, dx_perm2, planes2, T * K, pair_row, K, dx_shared,
+                                         dx_shared2, dl, w_r, N, T, d, dx);
   else
-    dx_kernel<false><<<grid, 256, 0, s>>>(dx_perm, dx_perm2, pair_row, K, dx_shared, dx_shared2,
-                                          dl, w_r, N, T, d, dx);
+    dx_kernel<false><<<grid, 256, 0, s>>>(dx_perm, dx_perm2, planes2, T * K, pair_row, K, dx_shared,
+                                          dx_shared2, dl, w_r, N, T, d, dx);
   return hipGetLastError();
 }
 
@@ -508,10 +512,10 @@ hipError_t run_bwd(const BwdArgs& a, int64_t max_tiles, bool bf16, hipStream_t s
 }
 
 // The 256 x 256 DMA kernel (gemm_bwd_tr.h): one workgroup per CU.
-template <bool WG, bool BS, bool DUALB, bool DUALK, int EPI, bool SK2 = false>
+template <bool WG, bool BS, bool DUALB, bool DUALK, int EPI, int SPLIT = 1>
 hipError_t run_bwd_tr(const BwdArgs& a, int64_t max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  auto kern = gemm_bwd_tr_kernel<WG, BS, DUALB, DUALK, EPI, SK2>;
+  auto kern = gemm_bwd_tr_kernel<WG, BS, DUALB, DUALK, EPI, SPLIT>;
   constexpr size_t smem = 2 * 2 * 32768;  // two stages of A and B
   static bool attr_set = false;
   if (!attr_set) {
@@ -554,9 +558,9 @@ int rows_tile(int64_t rows, int N) { return rows >= (int64_t)384 * N ? 256 : 128
 bool weight_tr(int F, int d) { return F >= 256 && d >= 256; }
 }  // namespace
 
-bool ffn_backward_splits_dx(int64_t T, int N, int K, int F, int act, bool bf16) {
-  (void)F;
-  return bf16 && act == 0 && rows_tile(T * K, N) == 256;
+int ffn_backward_dx_parts(int64_t T, int N, int K, int F, int act, bool bf16) {
+  if (!(bf16 && act == 0 && rows_tile(T * K, N) == 256)) return 1;
+  return (2 * F / 64) % 4 == 0 ? 4 : 2;  // parts of whole 64-wide K steps
 }
 
 template <int RR>
@@ -684,9 +688,14 @@ hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
     a.Nout = d; a.Nout_shared = d; a.Kdim = F;
     a.c = p.dx_perm; a.c_shared = p.dx_shared; a.ldc = d;
     a.c2 = p.dx_perm2; a.c2_shared = p.dx_shared2;
+    a.c2_plane = (int64_t)rows * d * el;
+    a.c2_plane_shared = (int64_t)srows * d * el;
     const int64_t mt = row_tiles_bound(all_rows, G, bm4, d, bm4);
-    if (TR && swiglu && p.dx_perm2)  // the K halves as separate tiles (twice the tiles)
-      e = run_bwd_tr<false, true, false, true, BEPI_STORE, true>(a, 2 * mt, s);
+    const int parts = p.dx_perm2 ? ffn_backward_dx_parts(p.T, p.N, p.K, F, p.act, bf16) : 1;
+    if (TR && parts == 4)  // K cut in parts that are separate tiles
+      e = run_bwd_tr<false, true, false, true, BEPI_STORE, 4>(a, 4 * mt, s);
+    else if (TR && parts == 2)
+      e = run_bwd_tr<false, true, false, true, BEPI_STORE, 2>(a, 2 * mt, s);
     else if (TR)
       e = swiglu ? run_bwd_tr<false, true, false, true, BEPI_STORE>(a, mt, s)
                  : run_bwd_tr<false, true, false, false, BEPI_STORE>(a, mt, s);

@@ -76,6 +76,9 @@ struct BwdArgs {
   void* c_shared;
   void* c2_shared;
   void* c3_shared;
+  // split K (gemm_bwd_tr_kernel, SPLIT > 1): part q >= 1 of the K range
+  // writes c2 (c2_shared) + (q - 1) * these bytes
+  int64_t c2_plane, c2_plane_shared;
   int64_t ldc;
   int64_t c_gstride;         // weight groups: elements between groups' outputs
   // nullable (BEPI_SWIGLU_BWD / BEPI_GELU_BWD): read u (and v) from here

@@ -26,9 +26,12 @@
 //    MFMAs of the current one run; the stage's one barrier sits before its
 //    last slice's MFMAs, so the next stage's first fragments are read under
 //    them too.
-//  * SK2 (with dual K): the two halves of K are separate tiles, the first
-//    half's results going to c and the second's to c2 (the caller adds
-//    them), which doubles the tiles of a GEMM with few output tiles.
+//  * SPLIT > 1 (with dual K): the K range (both halves) is cut into SPLIT
+//    equal parts that are separate tiles; part 0 writes c, part q >= 1 the
+//    plane q - 1 of c2 (the caller adds them).  A GEMM with few output
+//    tiles gets SPLIT times the tiles, and the last round of the persistent
+//    walk, which ragged groups leave partly empty, costs 1 / SPLIT of a
+//    whole tile.
 #pragma once
 
 #include "gemm_bwd.h"
@@ -63,7 +66,7 @@ __device__ __forceinline__ uint32_t tr_off(int k, int n) {
   return (uint32_t)(k * 512 + (((n >> 3) ^ tr_swz(k)) << 4) + ((n & 4) << 1));
 }
 
-template <bool WG, bool BS, bool DUALB, bool DUALK, int EPI, bool SK2 = false>
+template <bool WG, bool BS, bool DUALB, bool DUALK, int EPI, int SPLIT = 1>
 __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int total_tiles) {
   constexpr int BM = 256, BN = 256, BK = 64, CH = 8;
   constexpr int WN = 4, TM = 128, TN = 64, FM = 4, FN = 2;
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
   constexpr int OPB = 32768;      // bytes of one operand's stage
   constexpr int STB = 2 * OPB;    // bytes of one stage (A then B)
   static_assert(!(DUALB && B_STRIDED), "dual B needs the K-contiguous layout");
-  static_assert(!SK2 || (DUALK && !WG), "split K applies to a dual-K row-group GEMM");
+  static_assert(SPLIT == 1 || (DUALK && !WG), "split K applies to a dual-K row-group GEMM");
   extern __shared__ uint4 lds[];  // [2 stages][A | B]
   char* L = (char*)lds;
 
@@ -84,14 +87,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
   const int qw = wave & 3;  // this wave's quarter of its operand's 32 DMA instructions
   const int khalf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
   const int total1 = WG ? total_tiles : p.tile_base[p.G];
-  const int total = SK2 ? 2 * total1 : total1;
+  const int total = SPLIT * total1;
   const TileWalk walk = tile_walk(total);
 
   // first row (A) / column (B) of this wave's fragments within the tile
   // (the activation epilogues: fragment j of the 4 wave columns covers tile
   // columns 128 j .. 128 j + 127, which the epilogue stages one j at a time)
   constexpr bool ACT = EPI == BEPI_SWIGLU_BWD || EPI == BEPI_GELU_BWD;
-  static_assert(!(ACT && (DUALB || WG || SK2 || FN != 2)), "activation epilogues: row groups, one B");
+  static_assert(!(ACT && (DUALB || WG || SPLIT > 1 || FN != 2)), "activation epilogues: row groups, one B");
   int am[FM], bn[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) am[i] = wm * TM + i * 32;
@@ -101,11 +104,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
                   : (ACT ? j * 128 + wn * 32 : wn * TN + j * 32);
 
   for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
-    const int half = (SK2 && tile >= total1) ? 1 : 0;  // split K: which half
-    const BwdTile ti = bwd_tile(p, WG, tile - half * total1, BM, BN);
-    const int Ktot = WG ? ti.rows : ((DUALK && !SK2) ? 2 * p.Kdim : p.Kdim);
-    const int nk = (Ktot + BK - 1) / BK;
-    const int kt0 = half * (p.Kdim / BK);  // first K step of this tile's half
+    const int part = SPLIT > 1 ? tile / total1 : 0;  // split K: which part
+    const BwdTile ti = bwd_tile(p, WG, tile - part * total1, BM, BN);
+    const int Ktot = WG ? ti.rows : (DUALK ? 2 * p.Kdim : p.Kdim);
+    const int nk = SPLIT > 1 ? Ktot / BK / SPLIT : (Ktot + BK - 1) / BK;
+    const int kt0 = part * nk;  // first K step of this tile's part
 
     // ---- this wave's DMA source: base, extent and per-lane offsets
     const char* base0;
@@ -230,6 +233,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
         } else {
           // stage kt + 1 landed for every wave, and every wave holds stage
           // kt's last fragments in registers before the stage is refilled
+          // (the barrier alone does not wait for the LDS reads to return)
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
           wait_vmcnt<0>();
           __syncthreads();
           if (kt + 1 < nk) read_frags((kt + 1) & 1, 0, na, nb);
@@ -246,11 +251,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
       }
     }
 
-    // ---- epilogue (as gemm_bwd_kernel); the second K half writes c2
+    // ---- epilogue (as gemm_bwd_kernel); split K: parts 1.. write c2's planes
     BwdArgs pe = p;
-    if (SK2 && half) {
-      pe.c = p.c2;
-      pe.c_shared = p.c2_shared;
+    if (SPLIT > 1 && part > 0) {
+      pe.c = (char*)p.c2 + (part - 1) * p.c2_plane;
+      pe.c_shared = (char*)p.c2_shared + (part - 1) * p.c2_plane_shared;
     }
     if constexpr (ACT) {
       // Through LDS, 128 columns at a time: every wave puts its fragment j

@@ -165,8 +165,9 @@ BwdWs bwd_ws(const moe_config_t* c) {
   w.dlogits = o; o = align_up(o + (size_t)c->T * c->N * 4);
   w.dx_perm = o; o = align_up(o + pairs * c->d * eb);
   w.dx_shared = o; o = align_up(o + (c->F_shared > 0 ? (size_t)c->T * c->d * eb : 0));
-  w.dx_perm2 = o; o = align_up(o + pairs * c->d * eb);
-  w.dx_shared2 = o; o = align_up(o + (c->F_shared > 0 ? (size_t)c->T * c->d * eb : 0));
+  // the other parts of a split dx_perm (dx_shared): up to 3 planes
+  w.dx_perm2 = o; o = align_up(o + 3 * pairs * c->d * eb);
+  w.dx_shared2 = o; o = align_up(o + (c->F_shared > 0 ? 3 * (size_t)c->T * c->d * eb : 0));
   w.total = o;
   return w;
 }
@@ -640,7 +641,7 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   hipEvent_t fev[5] = {};
   if (trace)
     for (int i = 0; i < 5; ++i) fev[i] = (hipEvent_t)trace->ev[3 + i];
-  // dx_perm in two parts (du W1, dv W3) that the dx kernel adds
+  // dx_perm in up to four parts of its K sum, which the dx kernel adds
   void* dx_perm2 = at<void>(ws, B.dx_perm2);
   void* dx_shared2 = cfg->F_shared > 0 ? at<void>(ws, B.dx_shared2) : nullptr;
   // the forward's gate(x) and up(x), where it stores them: no recompute
@@ -651,11 +652,12 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
                        have_uv ? sv->u : nullptr, have_uv ? sv->v : nullptr);
   if (st != MOE_OK) return st;
   if ((st = mark(8)) != MOE_OK) return st;
-  // the FFN backward fills the second parts only when it splits (else null)
-  const bool split = ffn_backward_splits_dx(cfg->T, cfg->N, cfg->K, cfg->F, cfg->act,
-                                            cfg->dtype == MOE_BF16);
+  // the FFN backward fills the other parts only when it splits
+  const int parts = ffn_backward_dx_parts(cfg->T, cfg->N, cfg->K, cfg->F, cfg->act,
+                                          cfg->dtype == MOE_BF16);
   if (launch_dx(dx_perm, sv->pair_row, cfg->K, dx_shared, dl, w->w_r, cfg->N, cfg->T, cfg->d, bf16,
-                g->dx, s, split ? dx_perm2 : nullptr, split ? dx_shared2 : nullptr) != hipSuccess)
+                g->dx, s, parts > 1 ? dx_perm2 : nullptr, parts > 1 ? dx_shared2 : nullptr,
+                parts - 1) != hipSuccess)
     return MOE_ERR_HIP;
   return mark(9);
 }

@@ -146,12 +146,13 @@ int router_dw_splits(int64_t T);
 hipError_t launch_router_dw(const float* dl, const void* x, bool bf16, int64_t T, int N, int d,
                             float* part, float* dw_r, hipStream_t stream);
 
-// dx = sum of the token's kept rows of dx_perm (+ dx_perm2) (+ dx_shared
-// (+ dx_shared2)) (+ dl W_r); the second buffers are nullable.
+// dx = sum of the token's kept rows of dx_perm (+ the planes2 planes of
+// dx_perm2, [planes2][T*K, d]) (+ dx_shared (+ the planes of dx_shared2,
+// [planes2][T, d])) (+ dl W_r); the second buffers are nullable.
 hipError_t launch_dx(const void* dx_perm, const int32_t* pair_row, int K, const void* dx_shared,
                      const float* dl, const float* w_r, int N, int64_t T, int d, bool bf16,
                      void* dx, hipStream_t stream, const void* dx_perm2 = nullptr,
-                     const void* dx_shared2 = nullptr);
+                     const void* dx_shared2 = nullptr, int planes2 = 0);
 
 struct FfnBwdProblem {
   int64_t T;
@@ -168,7 +169,8 @@ struct FfnBwdProblem {
   void* dx_perm;            // [T*K, d] out: gradient of each kept row's input
   void* dx_shared;          // [T, d] out (shared expert only)
   // nullable: with them (SwiGLU, 256-row tiles) dx_perm / dx_shared get the
-  // du W1 part and these the dv W3 part; the caller adds the two
+  // first of ffn_backward_dx_parts parts of the K sum (du W1 + dv W3) and
+  // these, [parts - 1][rows, d], the others; the caller adds them
   void* dx_perm2;
   void* dx_shared2;
   // nullable: gate(x) and up(x) saved by the forward (layout of save_u /
@@ -182,9 +184,9 @@ struct FfnBwdProblem {
   const hipEvent_t* ev;
 };
 size_t ffn_backward_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared, bool bf16);
-// Whether launch_expert_ffn_backward, given dx_perm2 / dx_shared2, splits
-// dx_perm into its two parts for this shape (else it leaves them unwritten).
-bool ffn_backward_splits_dx(int64_t T, int N, int K, int F, int act, bool bf16);
+// Parts (1, 2 or 4) in which launch_expert_ffn_backward, given dx_perm2 /
+// dx_shared2, computes dx_perm for this shape (1: it leaves them unwritten).
+int ffn_backward_dx_parts(int64_t T, int N, int K, int F, int act, bool bf16);
 hipError_t launch_expert_ffn_backward(const FfnBwdProblem& p, hipStream_t stream);
 
 // Fill n bytes at p with zeros (a kernel, so it can be captured in a graph).
