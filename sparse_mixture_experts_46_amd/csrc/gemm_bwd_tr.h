@@ -308,6 +308,40 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
       continue;
     }
     const int mlim = WG ? p.Mout : ti.rows;
+    if constexpr (WG && EPI == BEPI_STORE) {
+      // Weight gradients through LDS: the tile as bf16 [256][256] (16-byte
+      // chunk c of row r at c ^ (r & 31)), then 32 threads per row store
+      // whole 512-byte rows.  The stages are free after the K loop's last
+      // barrier.
+      uint16_t* E = (uint16_t*)L;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int r = am[i] + (lane & 31);
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int c = (bn[j] >> 3) + qq;
+            *(uint2*)(E + r * 256 + ((c ^ (r & 31)) << 3) + 4 * khalf) =
+                make_uint2(pack_bf16x2(acc[j][i][4 * qq], acc[j][i][4 * qq + 1]),
+                           pack_bf16x2(acc[j][i][4 * qq + 2], acc[j][i][4 * qq + 3]));
+          }
+        }
+      __syncthreads();
+      uint16_t* C = (uint16_t*)(ti.shared ? p.c_shared : p.c) +
+                    (ti.shared ? 0 : (int64_t)ti.g * p.c_gstride);
+      const int cp = tid & 31;
+      const int col = ti.nt * BN + 8 * cp;
+#pragma unroll 4
+      for (int rp = 0; rp < 16; ++rp) {
+        const int r = rp * 16 + (tid >> 5);
+        const int m = ti.mt * BM + r;
+        if (m < mlim && col < ti.nout)
+          *(uint4*)(C + (int64_t)m * p.ldc + col) = *(const uint4*)(E + r * 256 + ((cp ^ (r & 31)) << 3));
+      }
+      __syncthreads();  // E read by all before the next tile's DMA
+      continue;
+    }
     constexpr int FO = DUALB ? FN / 2 : FN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
