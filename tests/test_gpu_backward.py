@@ -50,8 +50,12 @@ CASES = [
        gate="prob_no_renorm", cf=1.0, expert_bias=True, init="uniform", seed=46),
      (0.6, 0.2, 0.1), 0.0),
     (W(name="bwd_noise_swiglu", T=128, d=128, N=8, K=2, F=128, seed=47), (0.8, 0.0, 0.0), 0.5),
-    # >= 384 rows per expert: the 256-row tiles, ragged in rows, F and d
+    # >= 384 rows per expert: the 256-row tiles, ragged in rows, F and d; dx_perm's
+    # K in two parts (2F / 64 = 14 steps) ...
     (W(name="bwd_big_tiles", T=1100, d=320, N=4, K=2, F=448, seed=52), (1.0, 0.1, 0.0), 0.0),
+    # ... and in four (2F / 64 = 12 steps), with the shared expert's parts too
+    (W(name="bwd_big_tiles_shared", T=1040, d=256, N=4, K=2, F=384, F_shared=384, seed=54),
+     (0.5, 0.0, 0.1), 0.0),
 ]
 
 
