@@ -26,6 +26,10 @@
 //    MFMAs of the current one run; the stage's one barrier sits before its
 //    last slice's MFMAs, so the next stage's first fragments are read under
 //    them too.
+//  * Epilogues: a weight gradient's bf16 tile and dh's activation backward
+//    go through LDS (free after the K loop's last barrier), so global memory
+//    sees whole rows of 128-byte lines; the other epilogues store 4 columns
+//    per lane straight from the accumulators.
 //  * SPLIT > 1 (with dual K): the K range (both halves) is cut into SPLIT
 //    equal parts that are separate tiles; part 0 writes c, part q >= 1 the
 //    plane q - 1 of c2 (the caller adds them).  A GEMM with few output
