@@ -429,8 +429,8 @@ def traffic_record(name):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); the "
-              "multi-GPU expert-parallel path is not part of it", file=sys.stderr)
+        print(f"bench.py: the layer runs on one GPU (asked for --gpus {a.gpus}); the "
+              "multi-GPU expert-parallel path is not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,  /* null pointer, K > N, negative size, ...       */
-  MOE_ERR_UNSUPPORTED = 2,  /* valid but outside this build's limits        */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but outside the library's limits        */
   MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required   */
   MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed   */
 } moe_status_t;
@@ -82,7 +82,7 @@ typedef enum {
   MOE_GATE_PROB_NO_RENORM = 2  /* softmax over all N, not renormalised         */
 } moe_gate_t;
 
-/* Limits of this build (MOE_ERR_UNSUPPORTED outside them):
+/* Limits of the library (MOE_ERR_UNSUPPORTED outside them):
  *   1 <= N <= 1024, 1 <= K <= min(N, 16), d % 64 == 0, F % 64 == 0,
  *   F_shared % 64 == 0, T <= 2^24, bf16 layers need d, F >= 64.
  *   bf16 layers also need every grouped-GEMM operand addressed from one

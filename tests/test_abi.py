@@ -157,7 +157,7 @@ def test_entry_points_reject_before_launch(lib):
     out = L.MoeLayerOut()
     assert lib.moe_layer_forward(C.byref(c), C.byref(w), fake, C.byref(out), fake, 1 << 30, None,
                                  None) == L.MOE_ERR_INVALID_ARG
-    # SwiGLU with expert biases is outside this build
+    # SwiGLU with expert biases is not supported
     c2 = cfg_of(WL.MIXTRAL_PREFILL)
     w2 = L.MoeWeights(w_r=0x1000, w1=0x1000, w3=0x1000, w2=0x1000, b1=0x1000)
     assert lib.moe_expert_ffn(C.byref(c2), C.byref(w2), fake, None, fake, fake, None, None, fake,
