@@ -550,16 +550,21 @@ size_t ffn_backward_workspace_bytes(int64_t T, int d, int N, int K, int F, int F
 
 namespace {
 // Row-group GEMMs (the recompute, dh, dx_perm) use the 256 x 256 DMA kernel
-// with many rows per expert (a 256-row tile of a ~256-row expert would be
-// half empty), else the 128 x 128 register-staged kernel.  The weight-
+// from 192 rows per expert on (about a third of a ~256-row expert's tiles is
+// padding there, and the DMA kernel still wins), else the 128 x 128
+// register-staged kernel.  The weight-
 // gradient GEMMs tile F x d, whatever the rows: the DMA kernel when both are
 // at least 256.
-int rows_tile(int64_t rows, int N) { return rows >= (int64_t)384 * N ? 256 : 128; }
+int rows_tile(int64_t rows, int N) { return rows >= (int64_t)192 * N ? 256 : 128; }
 bool weight_tr(int F, int d) { return F >= 256 && d >= 256; }
 }  // namespace
 
-int ffn_backward_dx_parts(int64_t T, int N, int K, int F, int act, bool bf16) {
+int ffn_backward_dx_parts(int64_t T, int N, int K, int F, int d, int act, bool bf16) {
   if (!(bf16 && act == 0 && rows_tile(T * K, N) == 256)) return 1;
+  // expected tiles: whole row tiles plus half a tile of padding per expert;
+  // with eight rounds of them on the CUs the walk is even enough whole
+  const int64_t tiles = (T * K / 256 + N / 2) * (int64_t)((d + 255) / 256);
+  if (tiles >= (int64_t)8 * cus()) return 1;
   return (2 * F / 64) % 4 == 0 ? 4 : 2;  // parts of whole 64-wide K steps
 }
 
@@ -691,7 +696,7 @@ hipError_t ffn_backward_gemms(const FfnBwdProblem& p, hipStream_t s) {
     a.c2_plane = (int64_t)rows * d * el;
     a.c2_plane_shared = (int64_t)srows * d * el;
     const int64_t mt = row_tiles_bound(all_rows, G, bm4, d, bm4);
-    const int parts = p.dx_perm2 ? ffn_backward_dx_parts(p.T, p.N, p.K, F, p.act, bf16) : 1;
+    const int parts = p.dx_perm2 ? ffn_backward_dx_parts(p.T, p.N, p.K, F, d, p.act, bf16) : 1;
     if (TR && parts == 4)  // K cut in parts that are separate tiles
       e = run_bwd_tr<false, true, false, true, BEPI_STORE, 4>(a, 4 * mt, s);
     else if (TR && parts == 2)

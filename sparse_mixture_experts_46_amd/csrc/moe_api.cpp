@@ -653,7 +653,7 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   if (st != MOE_OK) return st;
   if ((st = mark(8)) != MOE_OK) return st;
   // the FFN backward fills the other parts only when it splits
-  const int parts = ffn_backward_dx_parts(cfg->T, cfg->N, cfg->K, cfg->F, cfg->act,
+  const int parts = ffn_backward_dx_parts(cfg->T, cfg->N, cfg->K, cfg->F, cfg->d, cfg->act,
                                           cfg->dtype == MOE_BF16);
   if (launch_dx(dx_perm, sv->pair_row, cfg->K, dx_shared, dl, w->w_r, cfg->N, cfg->T, cfg->d, bf16,
                 g->dx, s, parts > 1 ? dx_perm2 : nullptr, parts > 1 ? dx_shared2 : nullptr,

@@ -186,7 +186,7 @@ struct FfnBwdProblem {
 size_t ffn_backward_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared, bool bf16);
 // Parts (1, 2 or 4) in which launch_expert_ffn_backward, given dx_perm2 /
 // dx_shared2, computes dx_perm for this shape (1: it leaves them unwritten).
-int ffn_backward_dx_parts(int64_t T, int N, int K, int F, int act, bool bf16);
+int ffn_backward_dx_parts(int64_t T, int N, int K, int F, int d, int act, bool bf16);
 hipError_t launch_expert_ffn_backward(const FfnBwdProblem& p, hipStream_t stream);
 
 // Fill n bytes at p with zeros (a kernel, so it can be captured in a graph).
