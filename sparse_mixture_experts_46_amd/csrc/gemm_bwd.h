@@ -113,18 +113,18 @@ __device__ __forceinline__ BwdTile bwd_tile(const BwdArgs& p, bool wgroups, int 
   BwdTile t;
   int local;
   if (wgroups) {
-    // the index over the smaller operand runs fastest, so the tiles of one
-    // round (one XCD's contiguous run) share slabs of the larger operand
+    // stripes of 4 row tiles, the row index fastest: the 32 tiles one XCD
+    // runs together form a 4 x 8 block, which reads 4 slabs of A and 8 of B
+    // per K step (a 2 x 16 or 16 x 2 run reads 18)
     const int mtiles = (p.Mout + BM - 1) / BM, ntiles = (p.Nout + BN - 1) / BN;
     t.g = tile / (mtiles * ntiles);
     local = tile - t.g * mtiles * ntiles;
-    if (p.Mout > p.Nout) {
-      t.nt = local % ntiles;
-      t.mt = local / ntiles;
-    } else {
-      t.mt = local % mtiles;
-      t.nt = local / mtiles;
-    }
+    constexpr int H = 4;
+    const int stripe = local / (H * ntiles), first = stripe * H;
+    const int sh = mtiles - first < H ? mtiles - first : H;
+    const int w = local - stripe * H * ntiles;
+    t.mt = first + w % sh;
+    t.nt = w / sh;
   } else {
     t.g = find_group(p.tile_base, p.G, tile);
     local = tile - p.tile_base[t.g];
