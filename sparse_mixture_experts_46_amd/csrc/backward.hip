@@ -552,9 +552,8 @@ namespace {
 // Row-group GEMMs (the recompute, dh, dx_perm) use the 256 x 256 DMA kernel
 // from 192 rows per expert on (about a third of a ~256-row expert's tiles is
 // padding there, and the DMA kernel still wins), else the 128 x 128
-// register-staged kernel.  The weight-
-// gradient GEMMs tile F x d, whatever the rows: the DMA kernel when both are
-// at least 256.
+// register-staged kernel.  The weight-gradient GEMMs tile F x d, whatever
+// the rows: the DMA kernel when both are at least 256.
 int rows_tile(int64_t rows, int N) { return rows >= (int64_t)192 * N ? 256 : 128; }
 bool weight_tr(int F, int d) { return F >= 256 && d >= 256; }
 }  // namespace
