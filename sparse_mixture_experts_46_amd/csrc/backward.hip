@@ -278,20 +278,26 @@ hipError_t launch_router_backward(const float* logits, const float* noise, float
 // dW_r[e, i] = sum_t dl[t, e] x[t, i].  Block: 64 experts x 64 columns over
 // a chunk of tokens (grid z), 4 x 4 outputs per thread, 16 tokens per step
 // staged in LDS.  Partial products [nsplit, N, d] reduced in split order.
-constexpr int kRouterDwChunk = 512;
+// With few experts the blocks are few, and each step waits for its loads:
+// shorter chunks put more of them in flight.
+int router_dw_chunk(int N) { return N <= 16 ? 128 : 512; }
 
-int router_dw_splits(int64_t T) { return (int)((T + kRouterDwChunk - 1) / kRouterDwChunk); }
+int router_dw_splits(int64_t T, int N) {
+  const int c = router_dw_chunk(N);
+  return (int)((T + c - 1) / c);
+}
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ dl,
                                                         const void* __restrict__ x, int64_t T,
-                                                        int N, int d, float* __restrict__ out) {
+                                                        int N, int d, int chunk,
+                                                        float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) float sl[16][64];
   __shared__ __attribute__((aligned(16))) float sx[16][64];
   const int tid = threadIdx.x;
   const int i0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int64_t tb = (int64_t)blockIdx.z * kRouterDwChunk;
-  const int64_t te = tb + kRouterDwChunk < T ? tb + kRouterDwChunk : T;
+  const int64_t tb = (int64_t)blockIdx.z * chunk;
+  const int64_t te = tb + chunk < T ? tb + chunk : T;
   const int ty = tid >> 4, tx = tid & 15;  // experts ty*4.., columns tx*4..
   float acc[4][4] = {};
   for (int64_t t0 = tb; t0 < te; t0 += 16) {
@@ -343,12 +349,13 @@ __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict_
 
 hipError_t launch_router_dw(const float* dl, const void* x, bool bf16, int64_t T, int N, int d,
                             float* part, float* dw_r, hipStream_t s) {
-  const int ns = router_dw_splits(T);
+  const int ns = router_dw_splits(T, N);
+  const int chunk = router_dw_chunk(N);
   if (ns == 0) return hipSuccess;  // T == 0 is handled by the caller
   float* dst = ns == 1 ? dw_r : part;
   dim3 grid((unsigned)((d + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)ns);
-  if (bf16) router_dw_kernel<true><<<grid, 256, 0, s>>>(dl, x, T, N, d, dst);
-  else router_dw_kernel<false><<<grid, 256, 0, s>>>(dl, x, T, N, d, dst);
+  if (bf16) router_dw_kernel<true><<<grid, 256, 0, s>>>(dl, x, T, N, d, chunk, dst);
+  else router_dw_kernel<false><<<grid, 256, 0, s>>>(dl, x, T, N, d, chunk, dst);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   const int64_t n = (int64_t)N * d;

@@ -141,7 +141,7 @@ RouterBwdWs router_bwd_ws(const moe_config_t* c) {
   RouterBwdWs w;
   size_t o = 0;
   w.part_db = o; o = align_up(o + (size_t)router_bwd_num_blocks(c->T) * c->N * 4);
-  const int ns = router_dw_splits(c->T);
+  const int ns = router_dw_splits(c->T, c->N);
   w.part_dw = o; o = align_up(o + (ns > 1 ? (size_t)ns * c->N * c->d * 4 : 0));
   w.total = o;
   return w;

@@ -140,9 +140,9 @@ hipError_t launch_router_backward(const float* logits, const float* noise, float
                                   float alpha, float c_aux, float c_z, float c_zlse,
                                   float* dlogits, float* part, float* db_r, hipStream_t stream);
 
-// dW_r = dlogits^T x; part: [router_dw_splits(T), N, d] fp32 scratch (unused
+// dW_r = dlogits^T x; part: [router_dw_splits(T, N), N, d] fp32 scratch (unused
 // with one split).  T > 0.
-int router_dw_splits(int64_t T);
+int router_dw_splits(int64_t T, int N);
 hipError_t launch_router_dw(const float* dl, const void* x, bool bf16, int64_t T, int N, int d,
                             float* part, float* dw_r, hipStream_t stream);
 
