@@ -20,8 +20,11 @@
 //                      dh -> du (dv) and h, dW2, dx_perm, dW1 (dW3), biases
 //   dx                 sum over the token's kept rows of dx_perm, + the shared
 //                      expert's dx, + dlogits W_r
+#include <type_traits>
+
 #include "gemm_bwd.h"
 #include "gemm_bwd_tr.h"
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -367,9 +370,9 @@ hipError_t launch_router_dw(const float* dl, const void* x, bool bf16, int64_t T
 // dx[t, i] = sum_k [kept] dx_perm[row(t,k), i] + dx_shared[t, i] + sum_e dl[t, e] W_r[e, i].
 // Block: 64 tokens x 64 columns, 4 x 4 per thread; the router term from LDS
 // tiles of 16 experts; the row gathers afterwards, in slot order.
-template <bool BF16>
+template <bool BF16, int P2>
 __global__ __launch_bounds__(256) void dx_kernel(const void* __restrict__ dx_perm,
-                                                 const void* __restrict__ dx_perm2, int planes2,
+                                                 const void* __restrict__ dx_perm2,
                                                  int64_t rows,
                                                  const int32_t* __restrict__ pair_row, int K,
                                                  const void* __restrict__ dx_shared,
@@ -412,33 +415,45 @@ __global__ __launch_bounds__(256) void dx_kernel(const void* __restrict__ dx_per
   }
   const int i = i0 + tx * 4;
   if (i >= d) return;
+  // per output: the router term, then slot k's row of dx_perm and of each of
+  // the P2 further planes for k = 0..K-1, then the shared rows; the four
+  // tokens' rows of one slot are loaded together
+  auto add_row = [&](float (&o)[4], const void* base, int64_t row) {
+    if (BF16) {
+      const uint2 v = *(const uint2*)((const uint16_t*)base + row * d + i);
+      o[0] += __uint_as_float(v.x << 16);
+      o[1] += __uint_as_float(v.x & 0xffff0000u);
+      o[2] += __uint_as_float(v.y << 16);
+      o[3] += __uint_as_float(v.y & 0xffff0000u);
+    } else {
+      const float4 v = *(const float4*)((const float*)base + row * d + i);
+      o[0] += v.x; o[1] += v.y; o[2] += v.z; o[3] += v.w;
+    }
+  };
+  for (int k = 0; k < K; ++k) {
+    int r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t t = tb + ty * 4 + u;
+      r[u] = t < T ? pair_row[t * K + k] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (r[u] >= 0) {
+        add_row(acc[u], dx_perm, r[u]);
+#pragma unroll
+        for (int q = 0; q < P2; ++q) add_row(acc[u], dx_perm2, q * rows + r[u]);
+      }
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int64_t t = tb + ty * 4 + u;
     if (t >= T) continue;
-    float o[4] = {acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
-    auto add_row = [&](const void* base, int64_t row) {
-      if (BF16) {
-        const uint2 v = *(const uint2*)((const uint16_t*)base + row * d + i);
-        o[0] += __uint_as_float(v.x << 16);
-        o[1] += __uint_as_float(v.x & 0xffff0000u);
-        o[2] += __uint_as_float(v.y << 16);
-        o[3] += __uint_as_float(v.y & 0xffff0000u);
-      } else {
-        const float4 v = *(const float4*)((const float*)base + row * d + i);
-        o[0] += v.x; o[1] += v.y; o[2] += v.z; o[3] += v.w;
-      }
-    };
-    for (int k = 0; k < K; ++k) {
-      const int r = pair_row[t * K + k];
-      if (r >= 0) {
-        add_row(dx_perm, r);
-        for (int q = 0; q < planes2; ++q) add_row(dx_perm2, q * rows + r);
-      }
-    }
-    if (dx_shared) add_row(dx_shared, t);
+    if (dx_shared) add_row(acc[u], dx_shared, t);
     if (dx_shared2)
-      for (int q = 0; q < planes2; ++q) add_row(dx_shared2, q * T + t);
+#pragma unroll
+      for (int q = 0; q < P2; ++q) add_row(acc[u], dx_shared2, q * T + t);
+    float(&o)[4] = acc[u];
     if (BF16)
       *(uint2*)((uint16_t*)dx + t * d + i) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     else
@@ -452,13 +467,25 @@ hipError_t launch_dx(const void* dx_perm, const int32_t* pair_row, int K, const 
                      int planes2) {
   if (T == 0) return hipSuccess;
   if (!dx_perm2) planes2 = 0;
+  if (planes2 != 0 && planes2 != 1 && planes2 != 3) return hipErrorInvalidValue;
   dim3 grid((unsigned)((T + 63) / 64), (unsigned)((d + 63) / 64));
-  if (bf16)
-    dx_kernel<true><<<grid, 256, 0, s>>>(dx_perm, dx_perm2, planes2, T * K, pair_row, K, dx_shared,
-                                         dx_shared2, dl, w_r, N, T, d, dx);
-  else
-    dx_kernel<false><<<grid, 256, 0, s>>>(dx_perm, dx_perm2, planes2, T * K, pair_row, K, dx_shared,
-                                          dx_shared2, dl, w_r, N, T, d, dx);
+  auto go = [&](auto bf, auto p2) {
+    dx_kernel<decltype(bf)::value, decltype(p2)::value><<<grid, 256, 0, s>>>(
+        dx_perm, dx_perm2, T * K, pair_row, K, dx_shared, dx_shared2, dl, w_r, N, T, d, dx);
+  };
+  using TT = std::true_type;
+  using FF = std::false_type;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P3 = std::integral_constant<int, 3>;
+  if (bf16) {
+    if (planes2 == 0) go(TT{}, P0{});
+    else if (planes2 == 1) go(TT{}, P1{});
+    else go(TT{}, P3{});
+  } else {
+    if (planes2 != 0) return hipErrorInvalidValue;  // the fp32 path never splits dx_perm
+    go(FF{}, P0{});
+  }
   return hipGetLastError();
 }
 
