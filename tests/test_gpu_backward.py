@@ -123,17 +123,22 @@ def test_layer_backward(w, loss_grad, noise_std):
     compare(w, g, o, TOL_BF16 if w.dtype == "bf16" else TOL_F32)
 
 
-def test_untouched_experts_get_zero_gradient():
+@pytest.mark.parametrize("T,d,F", [(96, 128, 128), (768, 256, 256)],
+                         ids=["register_staged", "dma_256"])
+def test_untouched_experts_get_zero_gradient(T, d, F):
     """A router bias that sends every token to experts 0 and 1: the other six
-    experts keep no row, so their weight gradients are exactly zero."""
-    w = W(name="bwd_hot", T=96, d=128, N=8, K=2, F=128, router_bias="uniform", seed=48)
+    experts keep no row, so their weight gradients are exactly zero.  The
+    second shape runs the 256 x 256 DMA kernels: 768 rows per used expert
+    (256-row tiles, dx_perm in four parts) and weight-gradient tiles with no
+    K steps for the unused experts."""
+    w = W(name=f"bwd_hot_{T}", T=T, d=d, N=8, K=2, F=F, router_bias="uniform", seed=48)
     say("untouched experts", w.name)
     inp = gpu_inputs(w, 0.0)
     inp["b_r"] = torch.tensor([9.0, 8.0, -9, -9, -9, -9, -9, -9], dtype=torch.float32, device=DEV)
     dy = make_dy(w, DEV)
     _, fwd, g = run_gpu(w, inp, dy, (1.0, 0.5, 0.5), 0.0)
     kept = fwd.kept.cpu().numpy()
-    assert list(kept[2:]) == [0] * 6 and kept[0] == kept[1] == 96
+    assert list(kept[2:]) == [0] * 6 and kept[0] == kept[1] == T
     for t in (g.dw1, g.dw3, g.dw2):
         assert torch.count_nonzero(t[2:]).item() == 0
         assert torch.count_nonzero(t[:2]).item() > 0
