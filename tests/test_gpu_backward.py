@@ -173,8 +173,12 @@ def test_staged_entry_points_match_the_layer():
         assert torch.equal(a, b), name
 
 
-def test_backward_is_deterministic():
-    w = W(name="bwd_det", T=256, d=256, N=8, K=2, F=256, seed=50)
+@pytest.mark.parametrize("w", [
+    W(name="bwd_det", T=256, d=256, N=8, K=2, F=256, seed=50),
+    # 256-row tiles, dx_perm in four parts, the shared expert
+    W(name="bwd_det_big", T=1040, d=256, N=4, K=2, F=384, F_shared=384, seed=55),
+], ids=lambda w: w.name)
+def test_backward_is_deterministic(w):
     say("backward determinism", w.name)
     inp = gpu_inputs(w, 0.0)
     dy = make_dy(w, DEV)
