@@ -29,7 +29,11 @@
  *   - Every tensor pointer is a DEVICE pointer (HIP device memory of the
  *     current device), row-major, densely packed, 16-byte aligned.  The
  *     caller owns every buffer, including the workspace; the library
- *     allocates nothing and keeps no mutable global state.
+ *     allocates nothing.  Its only process-wide state is write-once facts
+ *     per device (the compute-unit count, whether a kernel's LDS limit was
+ *     raised), held in atomics: any host thread may call any entry point
+ *     for any device.  Calls that share an output or workspace buffer must
+ *     be ordered by the caller (same stream, or events).
  *   - `stream` is a hipStream_t (may be NULL = default stream).  Work is
  *     enqueued asynchronously; no entry point synchronises the host.
  *   - bf16 tensors are IEEE bfloat16 (uint16 storage).  The router weight,
@@ -89,7 +93,8 @@ typedef enum {
  *   base to fit in 4 GiB (the kernels use 32-bit byte offsets):
  *   2*T*d < 2^32 (x) and 2*(T*K + T_shared)*max(F, F_shared) < 2^32 (the
  *   intermediate h; T_shared = T with a shared expert), and one expert's
- *   weight matrix 2*F*d < 2^32.                                          */
+ *   weight matrix 2*F*d < 2^32; moe_expert_ffn given x_perm (a_rows NULL)
+ *   also needs 2*T*K*d < 2^32.                                           */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 
@@ -229,7 +234,7 @@ typedef struct {
   void* ev[MOE_TRACE_EVENTS];
 } moe_trace_t;
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code (static string).  Host only. */
 const char* moe_status_string(moe_status_t s);
 
 /* Capacity floor(K / N * cf * T) (mzlw.cn 2.3, S read as the tokens in the
@@ -247,6 +252,10 @@ moe_status_t moe_dispatch_workspace_size(const moe_config_t* cfg, size_t* bytes)
 moe_status_t moe_ffn_workspace_size(const moe_config_t* cfg, size_t* bytes);
 
 /* Router: logits, selection, gates and statistics.
+ * Pages: logits = x W_r^T, mzlw.cn 2.1 and section 三 (MoERouter); softmax
+ * and top-K, learnagent.wiki 结构 2 and 运行示例; renormalised gates, wmrh.cn
+ * 公式表达重点; selection-only bias, learnagent.wiki 结构 4; f, p and the
+ * auxiliary loss, mzlw.cn 2.2; z-loss, wmrh.cn Router Z-Loss.
  *   x [T, d] (cfg->dtype), w->w_r, w->b_r, w->b_sel as above.
  *   topk_idx [T, K] int32, topk_gate [T, K] fp32 (required);
  *   logits [T, N] fp32 (nullable), stats (nullable, and each member).
@@ -258,7 +267,9 @@ moe_status_t moe_router_topk(const moe_config_t* cfg, const moe_weights_t* w,
 
 /* Dispatch: per-expert counts, capacity clamp in token order, layout of the
  * kept pairs in expert-contiguous rows, and (if out->x_perm) the gathered
- * rows.  topk_idx [T, K] int32 on the device; ids outside [0, N) and ids
+ * rows.  Pages: capacity and token dropping, mzlw.cn 2.3; the per-expert
+ * token lists cut to capacity and the gather x_flat[expert_tokens], mzlw.cn
+ * section 三 (MoELayer.forward).  topk_idx [T, K] int32 on the device; ids outside [0, N) and ids
  * repeated within one token are counted in counters[2] and dropped.
  * out->kept, out->dropped, out->counters, out->x_perm are nullable; x may
  * be NULL when out->x_perm is NULL.                                      */
@@ -266,7 +277,10 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx,
                           const void* x, const moe_dispatch_t* out,
                           void* ws, size_t ws_bytes, void* stream);
 
-/* Expert FFNs as grouped GEMMs over the expert-contiguous rows.
+/* Expert FFNs as grouped GEMMs over the expert-contiguous rows.  Pages:
+ * SwiGLU expert, mzlw.cn section 三 (Expert); GELU expert, learnagent.wiki
+ * 运行示例; grouped GEMM instead of the per-expert loop, the comment in
+ * mzlw.cn section 三 (MoELayer.forward); shared expert, mstx.cn section 5.
  *   a      : x_perm [rows, d] when a_rows == NULL; otherwise x [T, d] and
  *            row r reads x[a_rows[r] / K] (a_rows = row_pair).
  *   offset : [N+1] device row offsets (from moe_dispatch).
@@ -279,7 +293,9 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, const moe_weights_t* w,
                             const void* x_shared, void* y_shared,
                             void* ws, size_t ws_bytes, void* stream);
 
-/* Combine: y[t] = sum_{k=0}^{K-1} [pair_row[t,k] >= 0] gate[t,k] *
+/* Combine (wmrh.cn 公式表达重点; learnagent.wiki 结构 3; dropped pairs add
+ * nothing, mzlw.cn 2.3):
+ * y[t] = sum_{k=0}^{K-1} [pair_row[t,k] >= 0] gate[t,k] *
  * y_perm[pair_row[t,k]]  (+ y_shared[t] when y_shared != NULL), summed in
  * fp32 in that fixed order and rounded once to cfg->dtype.  Dropped pairs
  * add nothing; the remaining gates are not renormalised.                 */
@@ -288,7 +304,8 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_perm,
                          const void* y_shared, void* y, void* stream);
 
 /* The whole layer: router, statistics, dispatch, expert FFNs (+ shared
- * expert), combine.  ws must hold moe_workspace_size(cfg) bytes.  trace
+ * expert), combine, in the order of mzlw.cn section 三 (MoELayer.forward)
+ * and learnagent.wiki 结构 3.  ws must hold moe_workspace_size(cfg) bytes.  trace
  * is nullable.                                                           */
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
                                const void* x, const moe_layer_out_t* out,
@@ -379,7 +396,8 @@ int32_t moe_layer_saves_uv(const moe_config_t* cfg);
  * entry points need at most as much.                                     */
 moe_status_t moe_backward_workspace_size(const moe_config_t* cfg, size_t* bytes);
 
-/* Combine backward (the transpose of moe_combine): for every kept pair
+/* Combine backward (the transpose of moe_combine; the gate-weighted sum of
+ * wmrh.cn 公式表达重点 and mzlw.cn section 三): for every kept pair
  * d_perm[pair_row[p]] = topk_gate[p] * dy[p / K] and
  * dgate[p] = dy[p / K] . y_perm[pair_row[p]] (fp32, a fixed-order wave
  * reduction); a dropped pair gets dgate = 0.  d_perm [T*K, d] dtype
@@ -388,7 +406,9 @@ moe_status_t moe_combine_backward(const moe_config_t* cfg, const void* dy, const
                                   const float* topk_gate, const int32_t* pair_row,
                                   void* d_perm, float* dgate, void* stream);
 
-/* Router backward: dlogits [T, N] from the gates (per cfg->gate, using only
+/* Router backward (the router of mzlw.cn section 三 with the losses of
+ * mzlw.cn 2.2 and wmrh.cn Router Z-Loss; top-K passes no gradient, mstx.cn
+ * challenges): dlogits [T, N] from the gates (per cfg->gate, using only
  * the kept pairs' dgate), the aux loss through p (f = count / (T K) fixed),
  * z and z_lse, all on logits + noise_std * w->noise when w->noise is set;
  * then dw_r = dlogits^T x and db_r = the column sums of dlogits (nullable),
@@ -400,7 +420,9 @@ moe_status_t moe_router_backward(const moe_config_t* cfg, const moe_weights_t* w
                                  float* dlogits, float* dw_r, float* db_r,
                                  void* ws, size_t ws_bytes, void* stream);
 
-/* Expert FFN backward over the expert-contiguous rows (the forward's
+/* Expert FFN backward (the SwiGLU expert of mzlw.cn section 三, the GELU
+ * expert of learnagent.wiki 运行示例, the shared expert of mstx.cn section 5)
+ * over the expert-contiguous rows (the forward's
  * first GEMM is recomputed from x): given d_perm (gradient of each kept
  * row's expert output) and, with a shared expert, dy (its output's
  * gradient), writes dx_perm [T*K, d] (each kept row's input gradient),
@@ -412,7 +434,8 @@ moe_status_t moe_expert_ffn_backward(const moe_config_t* cfg, const moe_weights_
                                      void* dx_perm, void* dx_shared, const moe_grads_t* grads,
                                      void* ws, size_t ws_bytes, void* stream);
 
-/* Dispatch backward (the transpose of the row gather): dx[t] = sum over
+/* Dispatch backward (the transpose of the row gather x_flat[expert_tokens]
+ * of mzlw.cn section 三): dx[t] = sum over
  * k of [pair_row[t,k] >= 0] dx_perm[pair_row[t,k]] (+ dx_shared[t]) (+ the
  * router term dlogits[t] . w_r), fp32 in that order, rounded once.
  * dx_shared, dlogits (with w_r) nullable.                               */
@@ -433,8 +456,9 @@ typedef struct {
   void* ev[MOE_BWD_TRACE_EVENTS];
 } moe_bwd_trace_t;
 
-/* The whole backward pass: combine, router, expert FFN and dispatch
- * backward in that order.  ws must hold moe_backward_workspace_size(cfg)
+/* The whole backward pass (what automatic differentiation computes through
+ * the modules of mzlw.cn section 三, as described above): combine, router,
+ * expert FFN and dispatch backward in that order.  ws must hold moe_backward_workspace_size(cfg)
  * bytes.  trace is nullable.                                             */
 moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
                                 const moe_saved_t* saved, const void* dy,

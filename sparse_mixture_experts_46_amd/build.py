@@ -69,5 +69,51 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD, "san", "libmoe_san.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
+
+
+def sanitizer_runtimes() -> list:
+    """The gcc AddressSanitizer / UndefinedBehaviorSanitizer runtimes, which a
+    process that was not built with them must preload."""
+    out = []
+    for name in ("libasan.so", "libubsan.so"):
+        p = subprocess.run(["gcc", f"-print-file-name={name}"], capture_output=True,
+                           text=True).stdout.strip()
+        if not os.path.isabs(p) or not os.path.exists(p):
+            raise RuntimeError(f"{name} not found")
+        out.append(p)
+    return out
+
+
+def build_sanitized() -> str:
+    """A copy of libmoe whose host code (moe_api.cpp: argument checks,
+    capacity, workspace layouts, launch sequence) is built by g++ with
+    AddressSanitizer and UndefinedBehaviorSanitizer; the kernels' objects
+    come from build().  CPU tests load it through MOE_LIBRARY with the
+    runtimes of sanitizer_runtimes() preloaded.  No GPU code is built with
+    a sanitizer."""
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o"))
+               for s in SOURCES):
+        build()
+    san = os.path.dirname(SAN_LIB)
+    os.makedirs(san, exist_ok=True)
+    obj = os.path.join(san, "moe_api.o")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-fno-omit-frame-pointer"] +
+                   SAN_FLAGS + ["-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", INCLUDE,
+                                "-I", CSRC, "-c", os.path.join(CSRC, "moe_api.cpp"), "-o", obj],
+                   check=True)
+    kernels = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES
+               if s != "moe_api.cpp"]
+    tmp = SAN_LIB + ".tmp"
+    subprocess.run(["g++", "-shared"] + SAN_FLAGS + ["-o", tmp, obj] + kernels +
+                   ["-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"], check=True)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -25,23 +25,14 @@
 #include "gemm_bwd.h"
 #include "gemm_bwd_tr.h"
 
+#include "host_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
 namespace {
 
-int g_cus = 0;
-int cus() {
-  if (g_cus <= 0) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-      g_cus = prop.multiProcessorCount;
-    if (g_cus <= 0) g_cus = 256;
-  }
-  return g_cus;
-}
+int cus() { return device_cus(); }
 
 }  // namespace
 
@@ -532,13 +523,9 @@ hipError_t run_bwd(const BwdArgs& a, int64_t max_tiles, bool bf16, hipStream_t s
   }
   auto kern = gemm_bwd_kernel<R, WG, BS, DUALB, DUALK, EPI>;
   constexpr size_t smem = (size_t)2 * (2 * R) * 8 * 16;  // two stages of 2R rows x 128 bytes
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = set_dynamic_lds_once((const void*)kern, (int)smem, lds_set);
+  if (e != hipSuccess) return e;
   int64_t grid = (int64_t)cus() * (R == 128 ? 2 : 1);
   if (max_tiles < grid) grid = ((max_tiles + 7) / 8) * 8;
   kern<<<(unsigned)grid, 2 * R, smem, s>>>(a, (int)max_tiles);
@@ -551,13 +538,9 @@ hipError_t run_bwd_tr(const BwdArgs& a, int64_t max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   auto kern = gemm_bwd_tr_kernel<WG, BS, DUALB, DUALK, EPI, SPLIT>;
   constexpr size_t smem = 2 * 2 * 32768;  // two stages of A and B
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = set_dynamic_lds_once((const void*)kern, (int)smem, lds_set);
+  if (e != hipSuccess) return e;
   int64_t grid = cus();
   if (max_tiles < grid) grid = ((max_tiles + 7) / 8) * 8;
   kern<<<(unsigned)grid, 512, smem, s>>>(a, (int)max_tiles);

@@ -19,6 +19,7 @@
 #include "gemm_pingpong.h"
 #include "gemm_decode.h"
 #include "gemm_tile.h"
+#include "host_device.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -26,31 +27,16 @@ namespace moe {
 // ============================================================== host =====
 namespace {
 
-int g_num_cus = 0;
-
-int num_cus() {
-  if (g_num_cus <= 0) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-      g_num_cus = prop.multiProcessorCount;
-    if (g_num_cus <= 0) g_num_cus = 256;
-  }
-  return g_num_cus;
-}
+int num_cus() { return device_cus(); }
 
 // wg_per_cu: resident workgroups per CU the grid is sized for
 template <int BM, int BN, int BK, int WM, int WN, int ST, int SW, bool DUAL, int EPI>
 hipError_t run_tile(const GemmArgs& a, int64_t max_tiles, hipStream_t s, int wg_per_cu = 1) {
   auto kern = gemm_tile_kernel<BM, BN, BK, WM, WN, ST, SW, DUAL, EPI>;
   const size_t smem = (size_t)ST * (BM + BN) * BK * 2;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = set_dynamic_lds_once((const void*)kern, (int)smem, lds_set);
+  if (e != hipSuccess) return e;
   int64_t grid = (int64_t)num_cus() * wg_per_cu;
   if (max_tiles < grid) grid = ((max_tiles + 7) / 8) * 8;
   if (grid < 8) grid = 8;
@@ -63,13 +49,9 @@ hipError_t run_pingpong(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   auto kern = gemm_pingpong_kernel<BM, BN, WM, WN, DA, DB, DUAL, EPI>;
   // DA blocks of A and DB blocks of B, 64 K-columns (128 bytes) per row
   const size_t smem = (size_t)DA * BM * 128 + (size_t)DB * BN * 128;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = set_dynamic_lds_once((const void*)kern, (int)smem, lds_set);
+  if (e != hipSuccess) return e;
   int64_t grid = num_cus();
   if (max_tiles < grid) grid = ((max_tiles + 7) / 8) * 8;
   if (grid < 8) grid = 8;

@@ -353,6 +353,11 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, const moe_weights_t* w, con
   if (cfg->T == 0) return MOE_OK;
   if (!a || !offset || !y_perm) return MOE_ERR_INVALID_ARG;
   if (cfg->F_shared > 0 && (!x_shared || !y_shared)) return MOE_ERR_INVALID_ARG;
+  // without a gather map the first GEMM addresses x_perm [T*K, d] from one
+  // base with 32-bit byte offsets (x [T, d] and h are bounded by check_config)
+  if (cfg->dtype == MOE_BF16 && !a_rows &&
+      2 * cfg->T * (int64_t)cfg->K * cfg->d >= (int64_t(1) << 32))
+    return MOE_ERR_UNSUPPORTED;
   const FfnWs L = ffn_ws(cfg);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   FfnProblem p = {};

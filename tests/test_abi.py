@@ -131,6 +131,25 @@ def test_bf16_operand_offsets_fit_32_bits(lib, shape, T_ok):
     assert ws_size(lib, c)[0] == L.MOE_ERR_UNSUPPORTED
 
 
+def test_expert_ffn_x_perm_offsets_fit_32_bits(lib):
+    """moe_expert_ffn given x_perm [T*K, d] (no gather map) addresses it with
+    32-bit byte offsets: 2*T*K*d >= 2^32 is refused before anything is
+    enqueued; with the gather map (rows read from x [T, d]) the same shape
+    passes that check and stops at the missing workspace."""
+    c = cfg_of(WL.DEEPSEEK_PREFILL, F_shared=0)
+    P = C.c_void_p
+    fake = P(0x1000)
+    w = L.MoeWeights(w_r=0x1000, w1=0x1000, w3=0x1000, w2=0x1000)
+    for T, a_rows, code in [(37449, None, L.MOE_ERR_WORKSPACE),   # 2*T*8*7168 < 2^32
+                            (37450, None, L.MOE_ERR_UNSUPPORTED),
+                            (37450, fake, L.MOE_ERR_WORKSPACE)]:
+        c.T = T
+        assert ws_size(lib, c)[0] == L.MOE_OK
+        st = lib.moe_expert_ffn(C.byref(c), C.byref(w), fake, a_rows, fake, fake, None, None,
+                                fake, 16, None)
+        assert st == code, (T, a_rows, st)
+
+
 def test_entry_points_reject_before_launch(lib):
     """Null pointers, short workspaces and bad configs return an error code
     from the host checks, so nothing is ever enqueued."""
