@@ -393,3 +393,23 @@ def layer_backward_sampled(x, W, dy, *, K, act, gate_mode, cf=None, alpha=1.0, b
         rec["dw2"] = dog.T @ h                            # column f of dw2
         wts[(e, f)] = rec
     return fwd, tok, wts
+
+
+def router_backward_full(x, W, dy, *, K, act, gate_mode, cf=None, alpha=1.0, b_r=None,
+                         b_sel=None, shared=None, noise=None, noise_std=0.0, c_aux=0.0,
+                         c_z=0.0, c_zlse=0.0, idx=None):
+    """The router's gradients over every token, without the expert weight
+    gradients (which at full size would not fit in memory as float64): the
+    same steps as layer_backward up to the router linear layer, i.e. the
+    forward, the combine backward's gate gradients, the gate and loss
+    gradients on the logits, then dW_r = dlogits^T x and db_r = the column
+    sums of dlogits.  Returns (fwd, dlogits [T, N], dgate [T, K], dw_r [N, d],
+    db_r [N])."""
+    x = np.asarray(x, np.float64)
+    fwd = ref.layer_forward(x, W, K=K, act=act, gate_mode=gate_mode, cf=cf, alpha=alpha,
+                            b_r=b_r, b_sel=b_sel, shared=shared, noise=noise,
+                            noise_std=noise_std, idx=idx)
+    _, dgate = combine_backward(dy, fwd.y_perm, fwd.asg.pair_row, fwd.gates)
+    dl = gate_backward(fwd.logits_used, fwd.idx, dgate, gate_mode)
+    dl = dl + stats_backward(fwd.logits_used, fwd.stats.count, K, alpha, c_aux, c_z, c_zlse)
+    return fwd, dl, dgate, dl.T @ x, dl.sum(axis=0)

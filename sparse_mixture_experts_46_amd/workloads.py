@@ -65,9 +65,12 @@ DEEPSEEK_PREFILL = Workload(
     act="swiglu", gate="softmax_topk", sel_bias=True, seed=4,
     desc="T=8192 d=7168 N=256 top-8 SwiGLU F=2048 + shared expert, selection bias")
 
+# Decode: the routing should touch about every expert (256 (1 - (1 - 8/256)^128)
+# ~ 251.6 on average for independent choices); a selection bias of +-1/2 on
+# logits of unit scale skews the choice towards ~235, so this shape has none.
 DEEPSEEK_DECODE = DEEPSEEK_PREFILL.with_(
-    name="deepseek_decode", T=128,
-    desc="T=128 decode, DeepSeek-V3 shape (d=7168 N=256 top-8 F=2048 + shared)")
+    name="deepseek_decode", T=128, sel_bias=False,
+    desc="T=128 decode, DeepSeek-V3 shape (d=7168 N=256 top-8 F=2048 + shared), no selection bias")
 
 MIXTRAL_DECODE = MIXTRAL_PREFILL.with_(
     name="mixtral_decode", T=16,

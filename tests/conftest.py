@@ -26,3 +26,17 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Print the near-tie report of the routing comparisons (tokens whose
+    top-K margin is within the tie band, and how many of them the GPU chose
+    differently from the float64 oracle)."""
+    try:
+        from helpers import NEAR_TIE_REPORT
+    except Exception:
+        return
+    if NEAR_TIE_REPORT:
+        terminalreporter.write_sep("-", "near-tie tokens")
+        for line in NEAR_TIE_REPORT:
+            terminalreporter.write_line(line)

@@ -34,11 +34,15 @@ def oracle_weights(inp: dict, bf16: bool):
     return W, shared
 
 
-def run_oracle(w, inp, tokens=None, experts_needed=True):
-    W, shared = oracle_weights(inp, w.dtype == "bf16")
+def run_oracle(w, inp, tokens=None, experts_needed=True, idx=None, weights=None):
+    """The forward oracle on the inputs of workload w (idx: a routing to use
+    instead of the oracle's own top-K choice; weights: oracle_weights(inp)
+    when already built)."""
+    W, shared = weights if weights is not None else oracle_weights(inp, w.dtype == "bf16")
     return ref.layer_forward(f64(inp["x"]), W, K=w.K, act=w.act, gate_mode=w.gate, cf=w.cf,
                              alpha=w.aux_alpha, b_r=f64(inp["b_r"]), b_sel=f64(inp["b_sel"]),
-                             shared=shared, tokens=tokens, experts_needed=experts_needed)
+                             shared=shared, tokens=tokens, experts_needed=experts_needed,
+                             idx=idx)
 
 
 def rel_err(got, want) -> float:
@@ -54,3 +58,12 @@ def rel_err(got, want) -> float:
 TOL_BF16 = 2e-2
 TOL_F32 = 1e-5
 NEAR_TIE = 1e-3
+
+# one line per routing comparison: label, tokens in the near-tie band, and
+# how many of them the GPU chose differently (printed at the end of the run)
+NEAR_TIE_REPORT: list = []
+
+
+def report_near_ties(label, n_band, n_diff, T):
+    NEAR_TIE_REPORT.append(f"{label}: {n_band} of {T} tokens within {NEAR_TIE} of a tie, "
+                           f"{n_diff} chosen differently")

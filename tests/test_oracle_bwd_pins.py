@@ -292,3 +292,18 @@ def test_sampled_entries_equal_the_full_backward(case):
         if "db1" in rec:
             assert abs(rec["db1"] - G.db1[e, f]) < 1e-12
             assert np.allclose(rec["db2"], G.db2[e], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_router_backward_full_equals_the_full_backward(case):
+    """router_backward_full (what the full-size GPU tests compare the router
+    gradients with) gives exactly layer_backward's router gradients."""
+    name, shape, act, mode, cf, flags, coef = case
+    x, W, shared, extra, dy = make_case(len(name) * 13 + shape["T"], act=act, **shape, **flags)
+    args = dict(K=shape["K"], act=act, gate_mode=mode, cf=cf, alpha=0.37, b_r=extra["b_r"],
+                b_sel=extra["b_sel"], shared=shared, noise=extra["noise"],
+                noise_std=extra["noise_std"], c_aux=coef[0], c_z=coef[1], c_zlse=coef[2])
+    G = bwd.layer_backward(x, W, dy, **args)
+    _, dl, dg, dw_r, db_r = bwd.router_backward_full(x, W, dy, **args)
+    for a, b in [(dl, G.dlogits), (dg, G.dgate), (dw_r, G.dw_r), (db_r, G.db_r)]:
+        assert np.allclose(a, b, rtol=0, atol=1e-12)
