@@ -110,12 +110,31 @@ typedef struct {
   int32_t gate;       /* moe_gate_t                                          */
   int64_t capacity;   /* rows each expert may keep; < 0 = unlimited          */
   float aux_alpha;    /* alpha of the Switch auxiliary loss                  */
-  uint32_t flags;     /* reserved, must be 0                                 */
-  float noise_std;    /* scale of moe_weights_t.noise (used only with it)    */
+  uint32_t flags;     /* MOE_FLAG_* bits; others must be 0                   */
+  float noise_std;    /* scale of the router noise (used only with
+                         moe_weights_t.noise or MOE_FLAG_NOISE_PHILOX;
+                         mzlw.cn section 三 uses 0.1)                         */
   float bias_rate;    /* step of the selection-bias update written to
                          moe_stats_t.b_sel_out (used only with it)           */
   int32_t weight_format; /* moe_weight_format_t of w1, w3, w2, ws1, ws3, ws2 */
+  uint64_t noise_seed;   /* MOE_FLAG_NOISE_PHILOX: key of the generator      */
+  uint64_t noise_offset; /* MOE_FLAG_NOISE_PHILOX: stream of this call (e.g.
+                            the training step); one offset per call         */
 } moe_config_t;
+
+/* Router noise drawn inside the kernels (training-time noisy top-K, mzlw.cn
+ * section 三, MoERouter.forward): the router works on
+ * logits + noise_std * z from selection on, with z[t, e] standard-normal
+ * number t*N + e of the stream (noise_seed, noise_offset) of Philox-4x32-10
+ * (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as
+ * 1, 2, 3", SC 2011) and the Box-Muller transform: number i comes from
+ * block i/4 (counter words: block low, block high, offset low, offset high;
+ * key words: seed low, seed high), whose outputs (x0, x1) and (x2, x3) give
+ * numbers 4b..4b+3 as (r cos a, r sin a), u1 = (x_even + 1) 2^-32,
+ * u2 = x_odd 2^-32, r = sqrt(-2 ln u1), a = 2 pi u2, evaluated in double
+ * precision and rounded once to float.  The backward pass draws the same
+ * numbers again.  Not together with moe_weights_t.noise (INVALID_ARG).     */
+#define MOE_FLAG_NOISE_PHILOX 1u
 
 /* Weights.  Router: w_r [N, d] fp32, b_r [N] fp32 (nullable; also carries any
  * fixed per-expert logit offset), b_sel [N] fp32 selection-only bias

@@ -14,6 +14,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_GELU_TANH = 0, 1
 MOE_GATE_RENORM_ALL, MOE_GATE_SOFTMAX_TOPK, MOE_GATE_PROB_NO_RENORM = 0, 1, 2
 MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_INT8 = 0, 1
+MOE_FLAG_NOISE_PHILOX = 1
 MOE_TRACE_EVENTS = 7
 MOE_BWD_TRACE_EVENTS = 10
 
@@ -31,7 +32,8 @@ class MoeConfig(C.Structure):
                 ("F", C.c_int32), ("F_shared", C.c_int32), ("dtype", C.c_int32),
                 ("act", C.c_int32), ("gate", C.c_int32), ("capacity", C.c_int64),
                 ("aux_alpha", C.c_float), ("flags", C.c_uint32), ("noise_std", C.c_float),
-                ("bias_rate", C.c_float), ("weight_format", C.c_int32)]
+                ("bias_rate", C.c_float), ("weight_format", C.c_int32),
+                ("noise_seed", C.c_uint64), ("noise_offset", C.c_uint64)]
 
 
 class MoeWeights(C.Structure):

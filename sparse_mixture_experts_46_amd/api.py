@@ -32,9 +32,16 @@ class Config:
     gate: str = "softmax_topk"
     capacity: int = -1
     aux_alpha: float = 1.0
-    noise_std: float = 0.0   # scale of the router noise (used with w["noise"])
+    # scale of the router noise, used only when noise is on (w["noise"] or
+    # noise_seed); 0.1 is the value of the page's router
+    noise_std: float = 0.1
     bias_rate: float = 0.0   # step of the selection-bias update (used with b_sel_out)
     weight_format: str = "dtype"  # "dtype" or "int8" (see moe_quantize_int8)
+    # router noise drawn in the kernels (Philox-4x32-10 + Box-Muller): the
+    # generator key, or None for no in-kernel noise; noise_offset selects the
+    # stream of a call (e.g. the training step)
+    noise_seed: int | None = None
+    noise_offset: int = 0
 
     @property
     def torch_dtype(self):
@@ -45,10 +52,13 @@ class Config:
                            F_shared=self.F_shared,
                            dtype=L.MOE_BF16 if self.dtype == "bf16" else L.MOE_F32,
                            act=_ACT[self.act], gate=_GATE[self.gate], capacity=self.capacity,
-                           aux_alpha=self.aux_alpha, flags=0, noise_std=self.noise_std,
-                           bias_rate=self.bias_rate,
+                           aux_alpha=self.aux_alpha,
+                           flags=0 if self.noise_seed is None else L.MOE_FLAG_NOISE_PHILOX,
+                           noise_std=self.noise_std, bias_rate=self.bias_rate,
                            weight_format=(L.MOE_WEIGHTS_INT8 if self.weight_format == "int8"
-                                          else L.MOE_WEIGHTS_DTYPE))
+                                          else L.MOE_WEIGHTS_DTYPE),
+                           noise_seed=0 if self.noise_seed is None else self.noise_seed,
+                           noise_offset=self.noise_offset)
 
 
 def config_for(w: Workload) -> Config:
@@ -129,9 +139,10 @@ def quantize_expert_weights(w: dict) -> dict:
 
 def moe_router_topk(cfg: Config, w: dict, x: torch.Tensor, want_logits=False,
                     want_stats=True, b_sel_out: torch.Tensor | None = None) -> dict:
-    """Router entry point.  w may carry "noise" [T, N] fp32 (with
-    cfg.noise_std); b_sel_out [N] fp32 receives one bias-update step (with
-    cfg.bias_rate) and may be w["b_sel"] itself."""
+    """Router entry point.  Router noise (scale cfg.noise_std): w["noise"]
+    [T, N] fp32 draws, or cfg.noise_seed for draws made in the kernels;
+    b_sel_out [N] fp32 receives one bias-update step (with cfg.bias_rate)
+    and may be w["b_sel"] itself."""
     lib = L.load()
     dev = x.device
     T, N, K = cfg.T, cfg.N, cfg.K

@@ -27,6 +27,7 @@
 
 #include "host_device.h"
 #include "moe_internal.h"
+#include "rng.h"
 
 namespace moe {
 
@@ -132,7 +133,7 @@ __device__ __forceinline__ void lane_add(float (&v)[NJ], int e, int lane, float 
 // part [nblk, N]: this block's column sums of dl (for db_r).
 template <int NJ>
 __global__ __launch_bounds__(256) void router_bwd_kernel(
-    const float* __restrict__ logits, const float* __restrict__ noise, float noise_std,
+    const float* __restrict__ logits, RouterNoise noise,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ pair_row,
     const float* __restrict__ dgate, const int32_t* __restrict__ count, int64_t T, int N, int K,
     int gate_mode, float alpha, float c_aux, float c_z, float c_zlse, float* __restrict__ dlogits,
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
       l[j] = -INFINITY;
       if (e < N) {
         l[j] = logits[t * N + e];
-        if (noise) l[j] += noise_std * noise[t * N + e];
+        if (noise_on(noise)) l[j] += noise.std * noise_draw(noise, t * N + e);
       }
       m = fmaxf(m, l[j]);
     }
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(256) void colsum_rows_kernel(const float* __restric
   out[e] = s;
 }
 
-hipError_t launch_router_backward(const float* logits, const float* noise, float noise_std,
+hipError_t launch_router_backward(const float* logits, const RouterNoise& noise,
                                   const int32_t* idx, const int32_t* pair_row, const float* dgate,
                                   const int32_t* count, int64_t T, int N, int K, int gate_mode,
                                   float alpha, float c_aux, float c_z, float c_zlse,
@@ -253,7 +254,7 @@ hipError_t launch_router_backward(const float* logits, const float* noise, float
   const int64_t nb = router_bwd_num_blocks(T);
   const int nj = (N + 63) / 64;
 #define MOE_RB(NJ)                                                                          \
-  router_bwd_kernel<NJ><<<(unsigned)nb, 256, 0, s>>>(logits, noise, noise_std, idx, pair_row, \
+  router_bwd_kernel<NJ><<<(unsigned)nb, 256, 0, s>>>(logits, noise, idx, pair_row,            \
                                                       dgate, count, T, N, K, gate_mode, alpha, \
                                                       c_aux, c_z, c_zlse, dlogits, part)
   if (nj <= 1) MOE_RB(1);

@@ -24,7 +24,7 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (c->act != MOE_ACT_SWIGLU && c->act != MOE_ACT_GELU_TANH) return MOE_ERR_INVALID_ARG;
   if (c->gate < MOE_GATE_RENORM_ALL || c->gate > MOE_GATE_PROB_NO_RENORM) return MOE_ERR_INVALID_ARG;
-  if (c->flags != 0) return MOE_ERR_INVALID_ARG;
+  if (c->flags & ~(uint32_t)MOE_FLAG_NOISE_PHILOX) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->aux_alpha)) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->noise_std) || !std::isfinite(c->bias_rate)) return MOE_ERR_INVALID_ARG;
   if (c->weight_format != MOE_WEIGHTS_DTYPE && c->weight_format != MOE_WEIGHTS_INT8)
@@ -179,8 +179,22 @@ T* at(void* ws, size_t off) {
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-moe_status_t check_weights_router(const moe_weights_t* w) {
+// The router noise of this call: the caller's draws (w->noise), draws made
+// in the kernels (MOE_FLAG_NOISE_PHILOX), or none.
+RouterNoise router_noise(const moe_config_t* c, const moe_weights_t* w) {
+  RouterNoise n = {};
+  n.tensor = w->noise;
+  n.std = c->noise_std;
+  n.philox = (c->flags & MOE_FLAG_NOISE_PHILOX) ? 1 : 0;
+  n.seed = c->noise_seed;
+  n.offset = c->noise_offset;
+  return n;
+}
+
+moe_status_t check_weights_router(const moe_config_t* c, const moe_weights_t* w) {
   if (!w || !w->w_r) return MOE_ERR_INVALID_ARG;
+  // one source of noise at a time
+  if ((c->flags & MOE_FLAG_NOISE_PHILOX) && w->noise) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -223,7 +237,7 @@ moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void
                                         c->d, c->N, s, /*reduce_splits=*/false);
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = launch_router_small(at<float>(ws, L.split), router_num_splits(c->T, c->d, c->N, bf16),
-                            w->b_r, w->noise, c->noise_std, w->b_sel, lg, idx, gate, c->T, c->N,
+                            w->b_r, router_noise(c, w), w->b_sel, lg, idx, gate, c->T, c->N,
                             c->K, c->gate, c->aux_alpha, count, f, p, loss, entropy, b_out,
                             c->bias_rate, s);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -231,7 +245,7 @@ moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void
   hipError_t e = launch_router_logits(x, bf16, w->w_r, w->b_r, at<float>(ws, L.split), lg, c->T,
                                       c->d, c->N, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_router_topk(lg, w->noise, c->noise_std, w->b_sel, idx, gate, at<float>(ws, L.part_p),
+  e = launch_router_topk(lg, router_noise(c, w), w->b_sel, idx, gate, at<float>(ws, L.part_p),
                          at<int32_t>(ws, L.part_cnt), at<float>(ws, L.part_z), c->T, c->N, c->K,
                          c->gate, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
@@ -316,7 +330,7 @@ moe_status_t moe_router_topk(const moe_config_t* cfg, const moe_weights_t* w, co
                              const moe_stats_t* stats, void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if ((st = check_weights_router(w)) != MOE_OK) return st;
+  if ((st = check_weights_router(cfg, w)) != MOE_OK) return st;
   if (cfg->T == 0) return MOE_OK;
   if (!x || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < router_ws(cfg).total) return MOE_ERR_WORKSPACE;
@@ -386,7 +400,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
                                const moe_trace_t* trace, void* stream) {
   moe_status_t st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if ((st = check_weights_router(w)) != MOE_OK) return st;
+  if ((st = check_weights_router(cfg, w)) != MOE_OK) return st;
   if ((st = check_weights_ffn(cfg, w)) != MOE_OK) return st;
   if (!out) return MOE_ERR_INVALID_ARG;
   if (cfg->T == 0) return MOE_OK;
@@ -486,6 +500,7 @@ moe_status_t moe_router_backward(const moe_config_t* cfg, const moe_weights_t* w
   moe_status_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (!w || !dw_r) return MOE_ERR_INVALID_ARG;
+  if ((cfg->flags & MOE_FLAG_NOISE_PHILOX) && w->noise) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(lg.aux) || !std::isfinite(lg.z) || !std::isfinite(lg.z_lse))
     return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
@@ -497,7 +512,7 @@ moe_status_t moe_router_backward(const moe_config_t* cfg, const moe_weights_t* w
     return MOE_ERR_INVALID_ARG;
   const RouterBwdWs R = router_bwd_ws(cfg);
   if (!ws || ws_bytes < R.total) return MOE_ERR_WORKSPACE;
-  if (launch_router_backward(logits, w->noise, cfg->noise_std, topk_idx, pair_row, dgate, count,
+  if (launch_router_backward(logits, router_noise(cfg, w), topk_idx, pair_row, dgate, count,
                              cfg->T, cfg->N, cfg->K, cfg->gate, cfg->aux_alpha, lg.aux, lg.z,
                              lg.z_lse, dlogits, at<float>(ws, R.part_db), db_r, s) != hipSuccess)
     return MOE_ERR_HIP;
@@ -600,7 +615,7 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   moe_status_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (cfg->weight_format != MOE_WEIGHTS_DTYPE) return MOE_ERR_UNSUPPORTED;
-  if ((st = check_weights_router(w)) != MOE_OK) return st;
+  if ((st = check_weights_router(cfg, w)) != MOE_OK) return st;
   if ((st = check_weights_ffn(cfg, w)) != MOE_OK) return st;
   if ((st = check_grads_ffn(cfg, g)) != MOE_OK) return st;
   if (!g->dw_r) return MOE_ERR_INVALID_ARG;
@@ -634,7 +649,7 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
     return MOE_ERR_HIP;
   if ((st = mark(1)) != MOE_OK) return st;
   void* rws = at<void>(ws, B.router);
-  if (launch_router_backward(sv->logits, w->noise, cfg->noise_std, sv->topk_idx, sv->pair_row,
+  if (launch_router_backward(sv->logits, router_noise(cfg, w), sv->topk_idx, sv->pair_row,
                              dgate, sv->count, cfg->T, cfg->N, cfg->K, cfg->gate, cfg->aux_alpha,
                              lg.aux, lg.z, lg.z_lse, dl, at<float>(rws, B.r.part_db), g->db_r,
                              s) != hipSuccess)

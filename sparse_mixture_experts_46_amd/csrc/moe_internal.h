@@ -9,6 +9,14 @@
 
 namespace moe {
 
+// Router noise of one call (the generator is described in rng.h).
+struct RouterNoise {
+  const float* tensor;  // [T, N] standard-normal draws of the caller, or nullptr
+  float std;            // scale of the draws
+  int philox;           // 1: draws made in the kernels (tensor is then nullptr)
+  uint64_t seed, offset;
+};
+
 // ---------------------------------------------------------------- router --
 // Tokens handled by one block of the top-K kernel (multiple of 4).
 int router_tokens_per_block(int64_t T);
@@ -24,12 +32,12 @@ hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, co
                                 float* part, float* logits, int64_t T, int d, int N,
                                 hipStream_t stream, bool reduce_splits = true);
 
-// Selection, gates and per-block partial statistics on logits + noise_std *
-// noise (noise nullable):
+// Selection, gates and per-block partial statistics on logits + noise.std *
+// (the noise draws), when noise_on(noise):
 //   part_p [nblk, N] fp32, part_cnt [nblk, N] int32,
 //   part_z [nblk, 3] fp32 (sum of squared logits, of squared log-sum-exp, of
 //   routing entropy)
-hipError_t launch_router_topk(const float* logits, const float* noise, float noise_std,
+hipError_t launch_router_topk(const float* logits, const RouterNoise& noise,
                               const float* b_sel, int32_t* idx, float* gate, float* part_p,
                               int32_t* part_cnt, float* part_z, int64_t T, int N, int K,
                               int gate_mode, hipStream_t stream);
@@ -40,8 +48,8 @@ hipError_t launch_router_topk(const float* logits, const float* noise, float noi
 // count / f / p / loss are skipped.
 constexpr int64_t kRouterSmallT = 64;
 bool router_small_path(int64_t T, int N);
-hipError_t launch_router_small(const float* part, int nsplit, const float* b_r, const float* noise,
-                               float noise_std, const float* b_sel, float* logits, int32_t* idx,
+hipError_t launch_router_small(const float* part, int nsplit, const float* b_r,
+                               const RouterNoise& noise, const float* b_sel, float* logits, int32_t* idx,
                                float* gate, int64_t T, int N, int K, int gate_mode, float alpha,
                                int32_t* count, float* f, float* p, float* loss, float* entropy,
                                float* b_sel_out, float bias_rate, hipStream_t stream);
@@ -134,7 +142,7 @@ hipError_t launch_combine_backward(const void* dy, const void* y_perm, const flo
 
 // part: [router_bwd_num_blocks(T), N] fp32 scratch; db_r nullable.
 int64_t router_bwd_num_blocks(int64_t T);
-hipError_t launch_router_backward(const float* logits, const float* noise, float noise_std,
+hipError_t launch_router_backward(const float* logits, const RouterNoise& noise,
                                   const int32_t* idx, const int32_t* pair_row, const float* dgate,
                                   const int32_t* count, int64_t T, int N, int K, int gate_mode,
                                   float alpha, float c_aux, float c_z, float c_zlse,

@@ -14,6 +14,7 @@
 //     Router Z-Loss (penalty on the squares of the router logits).
 #include "moe_common.h"
 #include "moe_internal.h"
+#include "rng.h"
 
 namespace moe {
 
@@ -361,7 +362,7 @@ __device__ __forceinline__ void topk_one_token(const float (&l)[NJ], const float
 
 template <int NJ>
 __global__ __launch_bounds__(256) void router_topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ noise, float noise_std,
+    const float* __restrict__ logits, RouterNoise noise,
     const float* __restrict__ b_sel, int32_t* __restrict__ idx, float* __restrict__ gate,
     float* __restrict__ part_p, int32_t* __restrict__ part_cnt,
     float* __restrict__ part_z, int64_t T, int N, int K, int gate_mode,
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     for (int j = 0; j < NJ; ++j) {
       int e = lane + 64 * j;
       l[j] = (e < N) ? logits[t * N + e] : -INFINITY;
-      if (noise && e < N) l[j] += noise_std * noise[t * N + e];
+      if (noise_on(noise) && e < N) l[j] += noise.std * noise_draw(noise, t * N + e);
     }
     topk_one_token<NJ>(l, bsel, lane, N, K, gate_mode, pacc, zsum, lsum, hsum, idx + t * K,
                        gate + t * K, scnt);
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(1024) void router_stats_final_kernel(
 template <int NJ>
 __global__ __launch_bounds__(1024) void router_small_kernel(
     const float* __restrict__ part, int nsplit, const float* __restrict__ b_r,
-    const float* __restrict__ noise, float noise_std, const float* b_sel,
+    RouterNoise noise, const float* b_sel,
     float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ gate, int64_t T,
     int N, int K, int gate_mode, float alpha, int32_t* __restrict__ count, float* __restrict__ f,
     float* __restrict__ p, float* __restrict__ loss, float* __restrict__ entropy, float* b_out,
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(1024) void router_small_kernel(
         } else {
           l[j] = logits[i];
         }
-        if (noise) l[j] += noise_std * noise[i];
+        if (noise_on(noise)) l[j] += noise.std * noise_draw(noise, i);
       } else {
         l[j] = -INFINITY;
       }
@@ -674,7 +675,7 @@ hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, co
   return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const float* logits, const float* noise, float noise_std,
+hipError_t launch_router_topk(const float* logits, const RouterNoise& noise,
                               const float* b_sel, int32_t* idx, float* gate, float* part_p,
                               int32_t* part_cnt, float* part_z, int64_t T, int N, int K,
                               int gate_mode, hipStream_t stream) {
@@ -684,7 +685,7 @@ hipError_t launch_router_topk(const float* logits, const float* noise, float noi
   const int nj = (N + 63) / 64;
 #define MOE_TOPK_CASE(NJV)                                                              \
   case NJV:                                                                             \
-    router_topk_kernel<NJV><<<nblk, 256, smem, stream>>>(logits, noise, noise_std, b_sel,  \
+    router_topk_kernel<NJV><<<nblk, 256, smem, stream>>>(logits, noise, b_sel,             \
         idx, gate, part_p, part_cnt, part_z, T, N, K, gate_mode, tpb);                 \
     break;
   switch (nj) {
@@ -717,8 +718,8 @@ hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
 
 bool router_small_path(int64_t T, int N) { return T <= kRouterSmallT && N <= 256; }
 
-hipError_t launch_router_small(const float* part, int nsplit, const float* b_r, const float* noise,
-                               float noise_std, const float* b_sel, float* logits, int32_t* idx,
+hipError_t launch_router_small(const float* part, int nsplit, const float* b_r,
+                               const RouterNoise& noise, const float* b_sel, float* logits, int32_t* idx,
                                float* gate, int64_t T, int N, int K, int gate_mode, float alpha,
                                int32_t* count, float* f, float* p, float* loss, float* entropy,
                                float* b_sel_out, float bias_rate, hipStream_t stream) {
@@ -726,7 +727,7 @@ hipError_t launch_router_small(const float* part, int nsplit, const float* b_r, 
   const int nj = (N + 63) / 64;
 #define MOE_SMALL_CASE(NJV)                                                                    \
   case NJV:                                                                                    \
-    router_small_kernel<NJV><<<1, 1024, smem, stream>>>(part, nsplit, b_r, noise, noise_std,  \
+    router_small_kernel<NJV><<<1, 1024, smem, stream>>>(part, nsplit, b_r, noise,             \
         b_sel, logits, idx, gate, T, N, K, gate_mode, alpha, count, f, p, loss, entropy,       \
         b_sel_out, bias_rate);                                                                \
     break;

@@ -99,7 +99,7 @@ def test_workspace_sizes_are_sane(lib, name):
     (dict(K=5), L.MOE_ERR_INVALID_ARG),            # K > N
     (dict(T=-1), L.MOE_ERR_INVALID_ARG),
     (dict(N=0), L.MOE_ERR_INVALID_ARG),
-    (dict(flags=1), L.MOE_ERR_INVALID_ARG),
+    (dict(flags=2), L.MOE_ERR_INVALID_ARG),        # unknown flag bit
     (dict(noise_std=float("nan")), L.MOE_ERR_INVALID_ARG),
     (dict(bias_rate=float("inf")), L.MOE_ERR_INVALID_ARG),
     (dict(N=2048, K=2), L.MOE_ERR_UNSUPPORTED),
@@ -148,6 +148,23 @@ def test_expert_ffn_x_perm_offsets_fit_32_bits(lib):
         st = lib.moe_expert_ffn(C.byref(c), C.byref(w), fake, a_rows, fake, fake, None, None,
                                 fake, 16, None)
         assert st == code, (T, a_rows, st)
+
+
+def test_two_noise_sources_are_refused(lib):
+    """In-kernel router noise (MOE_FLAG_NOISE_PHILOX) and caller draws
+    (weights.noise) together are an argument error, found before launch."""
+    c = cfg_of(WL.TINY)
+    c.flags = L.MOE_FLAG_NOISE_PHILOX
+    fake = C.c_void_p(0x1000)
+    w = L.MoeWeights(w_r=0x1000, noise=0x1000)
+    big = C.c_size_t(1 << 30)
+    st = lib.moe_router_topk(C.byref(c), C.byref(w), fake, fake, fake, None, None, fake,
+                             big.value, None)
+    assert st == L.MOE_ERR_INVALID_ARG
+    st = lib.moe_router_backward(C.byref(c), C.byref(w), fake, fake, fake, fake, fake, fake,
+                                 L.MoeLossGrad(aux=0.0, z=0.0, z_lse=0.0), fake, fake, None,
+                                 fake, big.value, None)
+    assert st == L.MOE_ERR_INVALID_ARG
 
 
 def test_entry_points_reject_before_launch(lib):
