@@ -114,6 +114,93 @@ class Int8Stack:
         return self.shape[0]
 
 
+# ------------------------------------------------- weight-only INT4 ---
+
+INT4_GROUP = 128
+
+
+def quantize_int4_groups(w, group=INT4_GROUP):
+    """Weight-only INT4 with one scale per group of `group` consecutive input
+    columns of each row: symmetric absmax round-to-nearest, the RTN
+    quantizer that Frantar et al. ("GPTQ", ICLR 2023) and Lin et al. ("AWQ",
+    MLSys 2024) use as their baseline at group size 128.  [P1] names INT4
+    quantization of the expert weights but gives no scheme.
+
+    In fp32, like quantize_int8_rows: s = absmax(group) / 7 and
+    q = rint(w / s) (round half to even), clamped to [-7, 7]; an all-zero
+    group gets s = 0 and q = 0.  w: float array [..., rows, cols] with cols a
+    multiple of `group`.  Returns (q int8 in [-7, 7], s float32
+    [..., rows, cols / group])."""
+    w32 = np.asarray(w, dtype=np.float32)
+    *lead, cols = w32.shape
+    if cols % group:
+        raise ValueError("cols must be a multiple of the group size")
+    g = w32.reshape(*lead, cols // group, group)
+    amax = np.max(np.abs(g), axis=-1)
+    scale = (amax / np.float32(7.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint((g / safe[..., None]).astype(np.float32))
+    q = np.where(scale[..., None] > 0, q, 0.0)
+    q = np.clip(q, -7, 7).astype(np.int8).reshape(*lead, cols)
+    return q, scale
+
+
+def dequantize_int4_groups(q, scale, group=INT4_GROUP):
+    """The weights an INT4 layer computes with: q * s of its group, exact in
+    float64."""
+    q = np.asarray(q, dtype=np.float64)
+    *lead, cols = q.shape
+    s = np.asarray(scale, dtype=np.float64)
+    return (q.reshape(*lead, cols // group, group) * s[..., None]).reshape(*lead, cols)
+
+
+def pack_int4(q):
+    """The library's storage of INT4 codes (a layout of this library; the
+    pages give none): each code as u = q + 8 in 4 bits; the 8 codes of
+    columns 8j .. 8j+7 of a row fill one little-endian 32-bit word, the code
+    of column 8j + 2i in bits 4i .. 4i+3 and that of column 8j + 2i + 1 in
+    bits 16 + 4i .. 16 + 4i + 3 (i = 0 .. 3).  q int [..., rows, cols] with
+    cols a multiple of 8 -> uint8 [..., rows, cols / 2]."""
+    q = np.asarray(q, dtype=np.int64)
+    *lead, cols = q.shape
+    u = (q + 8).reshape(*lead, cols // 8, 8).astype(np.uint32)
+    word = np.zeros((*lead, cols // 8), dtype=np.uint32)
+    for i in range(4):
+        word |= u[..., 2 * i] << np.uint32(4 * i)
+        word |= u[..., 2 * i + 1] << np.uint32(16 + 4 * i)
+    return word.view(np.uint8).reshape(*lead, cols // 2)
+
+
+def unpack_int4(packed):
+    """Inverse of pack_int4: uint8 [..., rows, cols / 2] -> int8 codes."""
+    b = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
+    *lead, half = b.shape
+    word = b.reshape(*lead, half // 4, 4).view(np.uint32)[..., 0]
+    out = np.zeros((*lead, half // 4, 8), dtype=np.int64)
+    for i in range(4):
+        out[..., 2 * i] = (word >> np.uint32(4 * i)) & np.uint32(15)
+        out[..., 2 * i + 1] = (word >> np.uint32(16 + 4 * i)) & np.uint32(15)
+    return (out - 8).astype(np.int8).reshape(*lead, half * 2)
+
+
+class Int4Stack:
+    """Per-expert INT4 weights (packed codes [E, rows, cols / 2], group scales
+    [E, rows, cols / 128]); indexing one expert returns its dequantized
+    matrix in float64."""
+
+    def __init__(self, packed, scale, group=INT4_GROUP):
+        self.packed = np.asarray(packed, dtype=np.uint8)
+        self.scale = np.asarray(scale, dtype=np.float32)
+        self.group = group
+        self.shape = self.packed.shape[:-1] + (self.packed.shape[-1] * 2,)
+
+    def __getitem__(self, e):
+        return dequantize_int4_groups(unpack_int4(self.packed[e]), self.scale[e], self.group)
+
+    def __len__(self):
+        return self.shape[0]
+
+
 def router_logits(x: np.ndarray, w_r: np.ndarray, b_r: np.ndarray | None = None):
     """logits[t, e] = sum_j x[t, j] * w_r[e, j] (+ b_r[e]).
 

@@ -545,3 +545,98 @@ def test_int8_stack_feeds_the_expert_ffn():
         assert np.array_equal(a, b)
         full = ref.run_expert("swiglu", xr, e, W)
         assert np.max(np.abs(a - full)) < 0.05 * np.max(np.abs(full))
+
+
+# ------------------------------------------------ weight-only INT4 pins
+
+def test_int4_hand_worked_group():
+    """Group (2, -1.5, 0.3, 0, 0 ...): absmax 2, s = 2/7; codes 7, -5
+    (-5.25), 1 (1.05), 0.  The negated group gives the negated codes; a
+    second group of the same row is quantized on its own."""
+    w = np.zeros((2, 256))
+    w[0, :4] = [2.0, -1.5, 0.3, 0.0]
+    w[1, :4] = [-2.0, 1.5, -0.3, 0.0]
+    w[0, 128] = 0.7
+    q, s = ref.quantize_int4_groups(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32 and s.shape == (2, 2)
+    assert q[0, :4].tolist() == [7, -5, 1, 0] and q[1, :4].tolist() == [-7, 5, -1, 0]
+    assert s[0, 0] == np.float32(2.0) / np.float32(7.0) and s[1, 0] == s[0, 0]
+    assert q[0, 128] == 7 and s[0, 1] == np.float32(0.7) / np.float32(7.0)
+    assert s[1, 1] == 0 and np.all(q[1, 128:] == 0)  # an all-zero group
+
+
+def test_int4_round_half_to_even():
+    """With absmax 7 the scale is 1, so w / s = w exactly: 2.5 -> 2, 3.5 -> 4,
+    -0.5 -> 0, -1.5 -> -2 (ties to even)."""
+    w = np.zeros((1, 128))
+    w[0, :5] = [7.0, 2.5, 3.5, -0.5, -1.5]
+    q, s = ref.quantize_int4_groups(w)
+    assert s[0, 0] == 1.0
+    assert q[0, :5].tolist() == [7, 2, 4, 0, -2]
+
+
+def test_int4_error_bound_and_extremes():
+    """|w - q s| <= s/2 (plus fp32 slack) per group, every group's absmax
+    entry codes to +-7, codes stay in [-7, 7], a group's codes do not move
+    when another group of the row changes, and the codes are
+    odd-symmetric."""
+    r = rng(63)
+    w = (r.normal(size=(24, 384)) * r.uniform(0.01, 3.0, size=(24, 1))).astype(np.float32)
+    w[5, 128:256] = 0.0
+    q, s = ref.quantize_int4_groups(w)
+    deq = ref.dequantize_int4_groups(q, s)
+    err = np.abs(deq - w.astype(np.float64))
+    assert np.all(err <= np.repeat(s.astype(np.float64), 128, axis=1) * (0.5 + 1e-6) + 1e-30)
+    assert np.abs(q.astype(int)).max() <= 7
+    g = w.reshape(24, 3, 128)
+    am = np.argmax(np.abs(g), axis=2)
+    for i in range(24):
+        for j in range(3):
+            if i == 5 and j == 1:
+                continue
+            assert abs(int(q[i, 128 * j + am[i, j]])) == 7
+    assert np.all(q[5, 128:256] == 0) and s[5, 1] == 0
+    w2 = w.copy()
+    w2[:, 256:] *= 3.0
+    q2, s2 = ref.quantize_int4_groups(w2)
+    assert np.array_equal(q2[:, :256], q[:, :256]) and np.array_equal(s2[:, :2], s[:, :2])
+    qn, sn = ref.quantize_int4_groups(-w)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+
+
+def test_int4_packing_layout():
+    """Hand-worked word: codes (7, -5, 1, 0, 0, 0, 0, 0) of columns 0..7 are
+    stored as u = q + 8 = (15, 3, 9, 8, 8, 8, 8, 8); even columns fill the
+    low half-word's nibbles 0..3, odd columns the high half-word's, so the
+    word is 0x8883889F (bytes 9F 88 83 88).  Packing round-trips."""
+    q = np.zeros((1, 8), dtype=np.int8)
+    q[0, :3] = [7, -5, 1]
+    p = ref.pack_int4(q)
+    assert p.dtype == np.uint8 and p.shape == (1, 4)
+    assert p[0].tolist() == [0x9F, 0x88, 0x83, 0x88]
+    r = rng(64)
+    qq = r.integers(-7, 8, size=(3, 5, 256)).astype(np.int8)
+    assert np.array_equal(ref.unpack_int4(ref.pack_int4(qq)), qq)
+
+
+def test_int4_stack_feeds_the_expert_ffn():
+    """An expert FFN on Int4Stack weights equals the same FFN on the dense
+    dequantized matrices, and stays near the unquantized FFN (a loose bound:
+    7 levels per side)."""
+    r = rng(65)
+    N, F, d, M = 2, 128, 256, 4
+    W = {"w1": r.normal(size=(N, F, d)) / math.sqrt(d),
+         "w3": r.normal(size=(N, F, d)) / math.sqrt(d),
+         "w2": r.normal(size=(N, d, F)) / math.sqrt(F)}
+    Wq = {}
+    for k, v in W.items():
+        q, s = ref.quantize_int4_groups(v)
+        Wq[k] = ref.Int4Stack(ref.pack_int4(q), s)
+    xr = r.normal(size=(M, d))
+    for e in range(N):
+        dense = {k: ref.dequantize_int4_groups(*ref.quantize_int4_groups(W[k][e])) for k in W}
+        a = ref.run_expert("swiglu", xr, e, Wq)
+        b = ref.expert_swiglu(xr, dense["w1"], dense["w3"], dense["w2"])
+        assert np.array_equal(a, b)
+        full = ref.run_expert("swiglu", xr, e, W)
+        assert np.max(np.abs(a - full)) < 0.3 * np.max(np.abs(full))
