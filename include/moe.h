@@ -331,6 +331,21 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
                                void* ws, size_t ws_bytes, const moe_trace_t* trace,
                                void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): moe_layer_forward with
+ * no ws argument.  The workspace is a fixed device array inside the library,
+ * MOE_NOALLOC_SCRATCH_BYTES on each GPU it runs on, held until the process
+ * ends; layers whose moe_workspace_size exceeds it (e.g. more than about
+ * 350 tokens of the DeepSeek-shaped decode layer) return MOE_ERR_WORKSPACE
+ * before anything is enqueued.  Nothing is allocated.  Every call on one GPU
+ * shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, different host threads) race and must be ordered by the caller.
+ * Outputs, errors and determinism are those of moe_layer_forward.          */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status_t moe_layer_forward_noalloc(const moe_config_t* cfg, const moe_weights_t* w,
+                                       const void* x, const moe_layer_out_t* out,
+                                       const moe_trace_t* trace, void* stream);
+
 /* Weight-only INT8 quantization of a bf16 weight matrix w [rows, cols]
  * (linear-layer layout [out, in]): q [rows, cols] int8 and scale [rows] fp32
  * with s = absmax(row) / 127 and q = rint(w / s) (fp32, correctly rounded

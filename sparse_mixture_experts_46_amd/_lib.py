@@ -24,7 +24,8 @@ EXPORTED = ("moe_status_string", "moe_capacity", "moe_workspace_size",
             "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_quantize_int8",
             "moe_backward_workspace_size", "moe_combine_backward", "moe_router_backward",
             "moe_expert_ffn_backward", "moe_dispatch_backward", "moe_layer_backward",
-            "moe_layer_saves_uv")
+            "moe_layer_saves_uv", "moe_layer_forward_noalloc")
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeConfig(C.Structure):
@@ -118,6 +119,9 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.moe_layer_forward.restype = C.c_int
     lib.moe_layer_forward.argtypes = [cfgp, wp, P, C.POINTER(MoeLayerOut), P, S,
                                       C.POINTER(MoeTrace), P]
+    lib.moe_layer_forward_noalloc.restype = C.c_int
+    lib.moe_layer_forward_noalloc.argtypes = [cfgp, wp, P, C.POINTER(MoeLayerOut),
+                                              C.POINTER(MoeTrace), P]
     lib.moe_layer_saves_uv.restype = C.c_int32
     lib.moe_layer_saves_uv.argtypes = [cfgp]
     gp = C.POINTER(MoeGrads)

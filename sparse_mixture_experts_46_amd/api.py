@@ -290,6 +290,22 @@ def moe_layer_forward(cfg: Config, w: dict, x: torch.Tensor, bufs: LayerBuffers 
     return bufs
 
 
+def moe_layer_forward_noalloc(cfg: Config, w: dict, x: torch.Tensor, bufs: LayerBuffers,
+                              wstruct: L.MoeWeights | None = None,
+                              trace: L.MoeTrace | None = None) -> LayerBuffers:
+    """moe_layer_forward with the library's fixed device scratch as the
+    workspace: allocates nothing (bufs supplies the outputs; bufs.ws is not
+    used)."""
+    lib = L.load()
+    if wstruct is None:
+        wstruct = weights_struct(w)
+    L.check(lib.moe_layer_forward_noalloc(C.byref(bufs.ccfg), C.byref(wstruct), _p(x),
+                                          C.byref(bufs.out),
+                                          C.byref(trace) if trace is not None else None,
+                                          _stream()), "moe_layer_forward_noalloc")
+    return bufs
+
+
 # ------------------------------------------------------------- backward ---
 
 def moe_backward_workspace_size(cfg: Config) -> int:

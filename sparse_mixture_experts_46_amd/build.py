@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["moe_api.cpp", "router.hip", "dispatch.hip", "gemm_bf16.hip", "ffn_f32.hip", "quant.hip",
-           "combine.hip", "backward.hip"]
+           "combine.hip", "backward.hip", "noalloc.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           # no packed fp32 instructions in device code
