@@ -17,7 +17,12 @@ decode-sized main workload).  For each workload the router entry point is
 also timed alone, plain and with the training-time variants (noise,
 entropy, bias update): "router_train".  Unless --no-backward, "backward"
 times moe_layer_backward on the main workload (gradients of every input and
-weight for an upstream dy and the aux loss), with its stages.
+weight for an upstream dy and the aux loss), with its stages.  Unless
+--no-extra, "workloads" holds the other layer shapes measured the same way
+(the Switch-style top-1 layer with capacity, the DeepSeek-shaped prefill,
+the Mixtral-shaped decode, the tiny fp32 layer), each with its step's
+position against both rooflines, its dominant kernel's roofline and its
+own CPU baseline (the oracle on a bounded sample of the same workload).
 """
 from __future__ import annotations
 
@@ -34,6 +39,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE layer fwd tokens/s + active TFLOP/s (prefill); HBM GB/s (decode T=128)"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
@@ -46,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other layer shapes (the \"workloads\" records)")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="tokens the oracle runs for the CPU baseline (0: all T tokens)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -106,6 +114,52 @@ def active_work(w, kept_rows):
     g1_flops = 2.0 * kept_rows * w.d * w.F * (mats - 1) + (
         2.0 * w.T * w.d * w.F_shared * 2 if w.F_shared else 0.0)
     return flops_routed + flops_shared, g1_flops
+
+
+def stage_work(w, kept_rows, touched, int8=False):
+    """Algorithmic flops and HBM bytes of each grouped-GEMM launch and of the
+    whole step.  Bytes: every touched expert's weights once (bf16, or one
+    byte per INT8 code plus a 4-byte scale per output row), each kept row's
+    input read once and its output written once; for the step, the touched
+    weights plus x read and y written once (intermediates are not counted)."""
+    eb = 2 if w.dtype == "bf16" else 4
+    wb = 1 if int8 else eb
+    m1 = 2 if w.act == "swiglu" else 1
+    rows, Fs, T, d, F = kept_rows, w.F_shared, w.T, w.d, w.F
+    sc1 = 4.0 * m1 * F if int8 else 0.0
+    sc2 = 4.0 * d if int8 else 0.0
+    g1_f = 2.0 * rows * d * F * m1 + (2.0 * T * d * Fs * 2 if Fs else 0.0)
+    g1_b = (touched * (m1 * F * d * wb + sc1) + rows * d * eb + rows * F * eb +
+            ((2 * Fs * d * wb + (8.0 * Fs if int8 else 0.0) + T * d * eb + T * Fs * eb)
+             if Fs else 0.0))
+    g2_f = 2.0 * rows * d * F + (2.0 * T * d * Fs if Fs else 0.0)
+    g2_b = (touched * (d * F * wb + sc2) + rows * F * eb + rows * d * eb +
+            ((d * Fs * wb + sc2 + T * Fs * eb + T * d * eb) if Fs else 0.0))
+    step_f = g1_f + g2_f + 2.0 * T * d * w.N   # + the router's fp32 logits
+    wts = touched * ((m1 + 1) * F * d * wb + sc1 + sc2) + (
+        (3 * Fs * d * wb + (4.0 * (2 * Fs + d) if int8 else 0.0)) if Fs else 0.0)
+    step_b = wts + 2.0 * T * d * eb + 4.0 * w.N * d
+    return {"gemm1": (g1_f, g1_b), "gemm2": (g2_f, g2_b), "step": (step_f, step_b),
+            "weight_bytes": wts}
+
+
+def roofline_of(flops, nbytes, ms, peak_tflops=PEAK_BF16_TFLOPS):
+    """Position of a launch (or step) of `flops` and `nbytes` that took `ms`:
+    its bound is whichever of the two peaks allows less (MFMA time
+    flops / peak, 2.5 PF/s for bf16, against HBM time bytes / 8 TB/s); frac
+    is that time over the measured one.  Both fractions are given."""
+    t_mfma = flops / (peak_tflops * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    s = ms * 1e-3
+    if t_mfma >= t_hbm:
+        rec = {"bound": "mfma", "achieved": flops / s / 1e12, "peak": peak_tflops,
+               "unit": "TFLOP/s"}
+    else:
+        rec = {"bound": "hbm", "achieved": nbytes / s / 1e9, "peak": PEAK_HBM_GBS,
+               "unit": "GB/s"}
+    rec["frac"] = rec["achieved"] / rec["peak"]
+    rec.update(frac_mfma=t_mfma / s, frac_hbm=t_hbm / s, flops=flops, bytes=nbytes, ms=ms)
+    return rec
 
 
 def run_workload(w, steps, warmup, ev, int8=False):
@@ -181,19 +235,51 @@ def run_workload(w, steps, warmup, ev, int8=False):
     return res
 
 
-def decode_record(w, steps, warmup, ev, int8=False):
-    """A decode-sized layer: step time and HBM GB/s on the expert weights it
-    touches (bf16 weights, or INT8 codes plus scales)."""
+def layer_record(w, steps, warmup, ev, int8=False, cpu=None):
+    """One layer shape: graph-replayed step time, per-stage times, the step's
+    position against both rooflines, each grouped GEMM's roofline (the
+    dominant one as "roofline") and, with cpu (cpu_baseline's keyword
+    arguments), the oracle's rate on a bounded sample of the same inputs."""
     rd = run_workload(w, steps, warmup, ev, int8=int8)
-    msd = rd["wall_graph"] * 1e3 / steps
-    gbs = rd["wbytes"] / (msd * 1e-3) / 1e9
-    rec = {"workload": w.name, "T": w.T, "weights": "int8 + fp32 row scales" if int8 else w.dtype,
-           "ms_per_step": msd, "tokens_per_s": w.T / (msd * 1e-3),
+    ms = rd["wall_graph"] * 1e3 / steps
+    sw = stage_work(w, rd["kept_rows"], rd["touched"], int8)
+    st = {k: float(v) for k, v in zip(STAGES, rd["stage_ms"])}
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    if w.dtype == "bf16":
+        # the tail launch (when there is one) is part of the second GEMM
+        kernels = {"gemm1": roofline_of(*sw["gemm1"], st["gemm1"], peak),
+                   "gemm2": roofline_of(*sw["gemm2"], st["gemm2_main"] + st["gemm2_tail"], peak)}
+    else:  # one fp32 FFN kernel covers both GEMMs
+        f = sw["gemm1"][0] + sw["gemm2"][0]
+        b = sw["gemm1"][1] + sw["gemm2"][1]
+        kernels = {"ffn_f32": roofline_of(f, b, st["gemm1"], peak)}
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    rec = {"workload": w.name, "desc": w.desc, "T": w.T, "dtype": w.dtype,
+           "weights": "int8 + fp32 row scales" if int8 else w.dtype,
+           "ms_per_step": ms, "us_per_step": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3),
            "eager_ms_per_step": rd["wall"] * 1e3 / steps,
-           "touched_experts": rd["touched"], "weight_bytes": rd["wbytes"],
-           "hbm_gbs": gbs, "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                                        "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
-           "stage_ms": {k: float(v) for k, v in zip(STAGES, rd["stage_ms"])}}
+           "kept_rows": rd["kept_rows"], "touched_experts": rd["touched"],
+           "weight_bytes": sw["weight_bytes"],
+           "weight_gbs": sw["weight_bytes"] / (ms * 1e-3) / 1e9,
+           "active_tflops": (sw["gemm1"][0] + sw["gemm2"][0]) / (ms * 1e-3) / 1e12,
+           "step_roofline": roofline_of(*sw["step"], ms, peak),
+           "roofline": dict(kernels[dom], kernel=dom), "kernels": kernels, "stage_ms": st}
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu_baseline(w, rd["inp"], **cpu)
+    return rec, rd
+
+
+def decode_record(w, steps, warmup, ev, int8=False, cpu=None):
+    """A decode-sized layer: as layer_record, plus the HBM GB/s of the step on
+    the expert weights it touches (bf16 weights, or INT8 codes plus scales)
+    against the HBM peak."""
+    rec, rd = layer_record(w, steps, warmup, ev, int8=int8, cpu=cpu)
+    gbs = rec["weight_gbs"]
+    rec["hbm_gbs"] = gbs
+    rec["kernel_roofline"] = rec["roofline"]
+    rec["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": gbs / PEAK_HBM_GBS,
+                       "what": "touched expert weights / step time"}
     return rec, rd
 
 
@@ -374,9 +460,20 @@ def router_train_timing(w, inp, steps, warmup, noise_std=0.1, bias_rate=1e-3):
             "noise_bytes": 4.0 * w.T * w.N}
 
 
-def cpu_baseline(w, inp, sample):
-    """The oracle, as it stands, on the first `sample` tokens of the same
-    workload (routing over those tokens, capacity, experts, combine)."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, inp, sample, seeded=False, repeats=1):
+    """The oracle, as it stands, on `sample` tokens of the same workload with
+    the same weights (the first ones, or a seeded random set): routing over
+    those tokens, capacity, experts, combine.  Median of `repeats` runs."""
     import numpy as np
     import torch
 
@@ -399,18 +496,30 @@ def cpu_baseline(w, inp, sample):
     W = {"w_r": f64(inp["w_r"]), "w1": stack(inp["w1"]), "w2": stack(inp["w2"])}
     if inp.get("w3") is not None:
         W["w3"] = stack(inp["w3"])
+    if inp.get("b1") is not None:
+        W["b1"], W["b2"] = f64(inp["b1"]), f64(inp["b2"])
     shared = None
     if inp.get("ws1") is not None:
         shared = {"w1": f64(inp["ws1"]), "w3": f64(inp["ws3"]), "w2": f64(inp["ws2"])}
-    x = f64(inp["x"][:sample])
-    t0 = time.perf_counter()
-    ref.layer_forward(x, W, K=w.K, act=w.act, gate_mode=w.gate, cf=w.cf, alpha=w.aux_alpha,
-                      b_r=f64(inp["b_r"]), b_sel=f64(inp["b_sel"]), shared=shared)
-    dt = time.perf_counter() - t0
+    if seeded:
+        rows = np.sort(np.random.default_rng(0).choice(w.T, size=sample, replace=False))
+        x = f64(inp["x"])[rows]
+        which = f"{sample} of {w.T} tokens drawn with numpy default_rng(0)"
+    else:
+        x = f64(inp["x"][:sample])
+        which = f"first {sample} of {w.T} tokens"
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        ref.layer_forward(x, W, K=w.K, act=w.act, gate_mode=w.gate, cf=w.cf, alpha=w.aux_alpha,
+                          b_r=f64(inp["b_r"]), b_sel=f64(inp["b_sel"]), shared=shared)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    med = f", median of {repeats} runs" if repeats > 1 else ""
     return {"value": sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {sample} of {w.T} tokens of {w.name} (same weights), full layer "
-                      f"in NumPy float64 incl. per-expert bf16->fp64 weight widening; "
-                      f"{dt:.1f} s"}
+            "cpu": cpu_model(), "seconds": dt,
+            "sample": f"{which} of {w.name} (same weights), full layer in NumPy float64 "
+                      f"incl. per-expert bf16->fp64 weight widening{med}; {dt:.3g} s"}
 
 
 def traffic_record(name):
@@ -496,12 +605,30 @@ def main():
         torch.cuda.empty_cache()
     if not a.no_decode:
         wd = WL.DEEPSEEK_DECODE
-        rec, rd = decode_record(wd, a.steps, a.warmup, ev)
+        cpu = None if a.no_cpu_baseline else {"sample": wd.T}
+        rec, rd = decode_record(wd, a.steps, a.warmup, ev, cpu=cpu)
         rec["router_train"] = router_train_timing(wd, rd["inp"], a.steps, a.warmup)
         del rd
         torch.cuda.empty_cache()
         rec["int8"], _ = decode_record(wd, a.steps, a.warmup, ev, int8=True)
         line["decode"] = rec
+        torch.cuda.empty_cache()
+    if not a.no_extra:
+        # the other layer shapes; the oracle's sample for each: every token
+        # where that is seconds of CPU work, else a seeded 512-token set
+        extra = [(WL.SWITCH_TOP1, {"sample": WL.SWITCH_TOP1.T}),
+                 (WL.DEEPSEEK_PREFILL, {"sample": 512, "seeded": True}),
+                 (WL.MIXTRAL_DECODE, {"sample": WL.MIXTRAL_DECODE.T}),
+                 (WL.TINY, {"sample": WL.TINY.T, "repeats": 10})]
+        line["workloads"] = {}
+        for we, cpu in extra:
+            if we.name == w.name:
+                continue
+            rec, rd = layer_record(we, a.steps, a.warmup, ev,
+                                   cpu=None if a.no_cpu_baseline else cpu)
+            del rd
+            torch.cuda.empty_cache()
+            line["workloads"][we.name] = rec
     print(json.dumps(line), flush=True)
 
 
