@@ -12,8 +12,8 @@ Default workload: Mixtral-shaped prefill (T=4096, d=4096, N=8, top-2, SwiGLU
 F=14336, bf16).  Unless --no-decode, the line also carries the decode-shaped
 DeepSeek-V3 layer (T=128, d=7168, N=256, top-8, F=2048 + shared expert)
 measured the same way, as HBM GB/s on the expert weights it touches, and
-again with weight-only INT8 expert weights ("int8", the same for a
-decode-sized main workload).  For each workload the router entry point is
+again with weight-only INT8 and INT4 expert weights ("int8", "int4"; the
+same for every decode-sized workload).  For each workload the router entry point is
 also timed alone, plain and with the training-time variants (noise,
 entropy, bias update): "router_train".  Unless --no-backward, "backward"
 times moe_layer_backward on the main workload (gradients of every input and
@@ -116,28 +116,30 @@ def active_work(w, kept_rows):
     return flops_routed + flops_shared, g1_flops
 
 
-def stage_work(w, kept_rows, touched, int8=False):
+def stage_work(w, kept_rows, touched, quant=None):
     """Algorithmic flops and HBM bytes of each grouped-GEMM launch and of the
-    whole step.  Bytes: every touched expert's weights once (bf16, or one
-    byte per INT8 code plus a 4-byte scale per output row), each kept row's
+    whole step.  Bytes: every touched expert's weights once (bf16; INT8: one
+    byte per code plus a 4-byte scale per output row; INT4: half a byte per
+    code plus a 4-byte scale per 128 inputs of a row), each kept row's
     input read once and its output written once; for the step, the touched
     weights plus x read and y written once (intermediates are not counted)."""
     eb = 2 if w.dtype == "bf16" else 4
-    wb = 1 if int8 else eb
+    wb = {"int8": 1.0, "int4": 0.5}.get(quant, eb)
     m1 = 2 if w.act == "swiglu" else 1
     rows, Fs, T, d, F = kept_rows, w.F_shared, w.T, w.d, w.F
-    sc1 = 4.0 * m1 * F if int8 else 0.0
-    sc2 = 4.0 * d if int8 else 0.0
+
+    def scales(out, inp):  # scale bytes of one [out, inp] matrix
+        return {"int8": 4.0 * out, "int4": 4.0 * out * inp / 128}.get(quant, 0.0)
+
     g1_f = 2.0 * rows * d * F * m1 + (2.0 * T * d * Fs * 2 if Fs else 0.0)
-    g1_b = (touched * (m1 * F * d * wb + sc1) + rows * d * eb + rows * F * eb +
-            ((2 * Fs * d * wb + (8.0 * Fs if int8 else 0.0) + T * d * eb + T * Fs * eb)
-             if Fs else 0.0))
+    g1_b = (touched * m1 * (F * d * wb + scales(F, d)) + rows * d * eb + rows * F * eb +
+            ((2 * (Fs * d * wb + scales(Fs, d)) + T * d * eb + T * Fs * eb) if Fs else 0.0))
     g2_f = 2.0 * rows * d * F + (2.0 * T * d * Fs if Fs else 0.0)
-    g2_b = (touched * (d * F * wb + sc2) + rows * F * eb + rows * d * eb +
-            ((d * Fs * wb + sc2 + T * Fs * eb + T * d * eb) if Fs else 0.0))
+    g2_b = (touched * (d * F * wb + scales(d, F)) + rows * F * eb + rows * d * eb +
+            ((d * Fs * wb + scales(d, Fs) + T * Fs * eb + T * d * eb) if Fs else 0.0))
     step_f = g1_f + g2_f + 2.0 * T * d * w.N   # + the router's fp32 logits
-    wts = touched * ((m1 + 1) * F * d * wb + sc1 + sc2) + (
-        (3 * Fs * d * wb + (4.0 * (2 * Fs + d) if int8 else 0.0)) if Fs else 0.0)
+    wts = touched * ((m1 + 1) * F * d * wb + m1 * scales(F, d) + scales(d, F)) + (
+        (3 * Fs * d * wb + 2 * scales(Fs, d) + scales(d, Fs)) if Fs else 0.0)
     step_b = wts + 2.0 * T * d * eb + 4.0 * w.N * d
     return {"gemm1": (g1_f, g1_b), "gemm2": (g2_f, g2_b), "step": (step_f, step_b),
             "weight_bytes": wts}
@@ -162,7 +164,7 @@ def roofline_of(flops, nbytes, ms, peak_tflops=PEAK_BF16_TFLOPS):
     return rec
 
 
-def run_workload(w, steps, warmup, ev, int8=False):
+def run_workload(w, steps, warmup, ev, quant=None):
     import numpy as np
     import torch
 
@@ -172,10 +174,10 @@ def run_workload(w, steps, warmup, ev, int8=False):
 
     inp = make_inputs(w, device="cuda")
     cfg = api.config_for(w)
-    if int8:
-        # weight-only INT8 expert weights (quantized once, outside the timing)
-        inp = api.quantize_expert_weights(inp)
-        cfg.weight_format = "int8"
+    if quant:
+        # weight-only INT8 / INT4 expert weights (quantized once, outside the timing)
+        inp = api.quantize_expert_weights(inp, quant)
+        cfg.weight_format = quant
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     bufs = api.LayerBuffers(cfg, torch.device("cuda"))
@@ -225,24 +227,20 @@ def run_workload(w, steps, warmup, ev, int8=False):
     cnt = bufs.counters.cpu().numpy()
     kept_rows, touched = int(cnt[0]), int(cnt[3])
     total_flops, g1_flops = active_work(w, kept_rows)
-    mats = 3 if w.act == "swiglu" else 2
-    wbytes = 2.0 * (touched * mats * w.d * w.F + (3 * w.d * w.F_shared if w.F_shared else 0))
-    if int8:  # one byte per weight plus a 4-byte scale per output row
-        wbytes = (touched * (mats * w.d * w.F + 4.0 * (2 * w.F + w.d)) +
-                  (3.0 * w.d * w.F_shared + 4.0 * (2 * w.F_shared + w.d) if w.F_shared else 0.0))
+    wbytes = stage_work(w, kept_rows, touched, quant)["weight_bytes"]
     res = dict(inp=inp, bufs=bufs, wall=wall, wall_graph=wall_graph, stage_ms=stage, kept_rows=kept_rows,
                touched=touched, total_flops=total_flops, g1_flops=g1_flops, wbytes=wbytes)
     return res
 
 
-def layer_record(w, steps, warmup, ev, int8=False, cpu=None):
+def layer_record(w, steps, warmup, ev, quant=None, cpu=None):
     """One layer shape: graph-replayed step time, per-stage times, the step's
     position against both rooflines, each grouped GEMM's roofline (the
     dominant one as "roofline") and, with cpu (cpu_baseline's keyword
     arguments), the oracle's rate on a bounded sample of the same inputs."""
-    rd = run_workload(w, steps, warmup, ev, int8=int8)
+    rd = run_workload(w, steps, warmup, ev, quant=quant)
     ms = rd["wall_graph"] * 1e3 / steps
-    sw = stage_work(w, rd["kept_rows"], rd["touched"], int8)
+    sw = stage_work(w, rd["kept_rows"], rd["touched"], quant)
     st = {k: float(v) for k, v in zip(STAGES, rd["stage_ms"])}
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     if w.dtype == "bf16":
@@ -255,7 +253,8 @@ def layer_record(w, steps, warmup, ev, int8=False, cpu=None):
         kernels = {"ffn_f32": roofline_of(f, b, st["gemm1"], peak)}
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     rec = {"workload": w.name, "desc": w.desc, "T": w.T, "dtype": w.dtype,
-           "weights": "int8 + fp32 row scales" if int8 else w.dtype,
+           "weights": {"int8": "int8 + fp32 row scales",
+                       "int4": "int4 + fp32 scales per 128 inputs"}.get(quant, w.dtype),
            "ms_per_step": ms, "us_per_step": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3),
            "eager_ms_per_step": rd["wall"] * 1e3 / steps,
            "kept_rows": rd["kept_rows"], "touched_experts": rd["touched"],
@@ -269,11 +268,11 @@ def layer_record(w, steps, warmup, ev, int8=False, cpu=None):
     return rec, rd
 
 
-def decode_record(w, steps, warmup, ev, int8=False, cpu=None):
+def decode_record(w, steps, warmup, ev, quant=None, cpu=None):
     """A decode-sized layer: as layer_record, plus the HBM GB/s of the step on
     the expert weights it touches (bf16 weights, or INT8 codes plus scales)
     against the HBM peak."""
-    rec, rd = layer_record(w, steps, warmup, ev, int8=int8, cpu=cpu)
+    rec, rd = layer_record(w, steps, warmup, ev, quant=quant, cpu=cpu)
     gbs = rec["weight_gbs"]
     rec["hbm_gbs"] = gbs
     rec["kernel_roofline"] = rec["roofline"]
@@ -601,7 +600,11 @@ def main():
         torch.cuda.empty_cache()
     if w.T * w.K <= 24 * w.N and w.act == "swiglu" and w.dtype == "bf16":
         # a decode-sized main workload: also its INT8-weight variant
-        line["int8"], _ = decode_record(w, a.steps, a.warmup, ev, int8=True)
+        for q in ("int8", "int4"):
+            if q == "int4" and (w.d % 128 or w.F % 128):
+                continue
+            line[q], _ = decode_record(w, a.steps, a.warmup, ev, quant=q)
+            torch.cuda.empty_cache()
         torch.cuda.empty_cache()
     if not a.no_decode:
         wd = WL.DEEPSEEK_DECODE
@@ -610,7 +613,9 @@ def main():
         rec["router_train"] = router_train_timing(wd, rd["inp"], a.steps, a.warmup)
         del rd
         torch.cuda.empty_cache()
-        rec["int8"], _ = decode_record(wd, a.steps, a.warmup, ev, int8=True)
+        rec["int8"], _ = decode_record(wd, a.steps, a.warmup, ev, quant="int8")
+        torch.cuda.empty_cache()
+        rec["int4"], _ = decode_record(wd, a.steps, a.warmup, ev, quant="int4")
         line["decode"] = rec
         torch.cuda.empty_cache()
     if not a.no_extra:
@@ -628,6 +633,11 @@ def main():
                                    cpu=None if a.no_cpu_baseline else cpu)
             del rd
             torch.cuda.empty_cache()
+            if we.T * we.K <= 24 * we.N and we.act == "swiglu" and we.dtype == "bf16":
+                # decode-sized: also with weight-only INT8 and INT4 expert weights
+                for q in ("int8", "int4"):
+                    rec[q], _ = decode_record(we, a.steps, a.warmup, ev, quant=q)
+                    torch.cuda.empty_cache()
             line["workloads"][we.name] = rec
     print(json.dumps(line), flush=True)
 

@@ -74,10 +74,14 @@ typedef enum {
 
 typedef enum {
   MOE_WEIGHTS_DTYPE = 0,  /* expert weights in cfg->dtype                       */
-  MOE_WEIGHTS_INT8 = 1    /* expert weights as int8 codes q with one fp32 scale
+  MOE_WEIGHTS_INT8 = 1,   /* expert weights as int8 codes q with one fp32 scale
                              per output row s (W = q * s), from
                              moe_quantize_int8; bf16 SwiGLU layers at decode
                              sizes only (T*K/N <= 24), else UNSUPPORTED     */
+  MOE_WEIGHTS_INT4 = 2    /* expert weights as packed 4-bit codes with one fp32
+                             scale per 128 consecutive input columns of a row
+                             (W = q * s), from moe_quantize_int4; as INT8, and
+                             d, F, F_shared multiples of 128               */
 } moe_weight_format_t;
 
 typedef enum {
@@ -150,7 +154,12 @@ typedef struct {
  * With weight_format MOE_WEIGHTS_INT8, w1/w3/w2/ws1/ws3/ws2 hold int8 codes
  * in the same layouts and the *_scale arrays their per-output-row fp32
  * scales: w1_scale, w3_scale [N, F], w2_scale [N, d], ws1_scale,
- * ws3_scale [F_shared], ws2_scale [d] (all required then, else ignored).  */
+ * ws3_scale [F_shared], ws2_scale [d] (all required then, else ignored).
+ * With MOE_WEIGHTS_INT4 they hold moe_quantize_int4's packed codes (half a
+ * byte per weight, rows of in/2 bytes) and the *_scale arrays one fp32 scale
+ * per 128 input columns: w1_scale, w3_scale [N, F, d/128], w2_scale
+ * [N, d, F/128], ws1_scale, ws3_scale [F_shared, d/128], ws2_scale
+ * [d, F_shared/128].                                                      */
 typedef struct {
   const float* w_r;
   const float* b_r;
@@ -357,6 +366,23 @@ moe_status_t moe_layer_forward_noalloc(const moe_config_t* cfg, const moe_weight
  * or cols <= 0; UNSUPPORTED for cols % 64 != 0 or rows*cols >= 2^40.
  * rows == 0 enqueues nothing.                                              */
 moe_status_t moe_quantize_int8(const void* w, int64_t rows, int32_t cols, int8_t* q,
+                               float* scale, void* stream);
+
+/* Weight-only INT4 quantization of a bf16 weight matrix w [rows, cols]
+ * (linear-layer layout [out, in]) for the decode layers (wmrh.cn section
+ * 工程优化方案 names INT4/INT8 quantization of the experts; the pages give no
+ * scheme): one fp32 scale per group of 128 consecutive columns of a row,
+ * s = absmax(group) / 7 and q = rint(w / s) (fp32, correctly rounded
+ * division, ties to even) clamped to [-7, 7]; an all-zero group gets s = 0.
+ * This is the round-to-nearest quantizer that GPTQ (Frantar et al., ICLR
+ * 2023) and AWQ (Lin et al., MLSys 2024) use as their baseline at group size
+ * 128.  q [rows, cols / 2] bytes: each code as u = q + 8 in 4 bits, the codes
+ * of columns 8j .. 8j+7 of a row in one little-endian 32-bit word, column
+ * 8j + 2i in bits 4i .. 4i+3 and column 8j + 2i + 1 in bits 16+4i .. 19+4i.
+ * scale [rows, cols / 128] fp32.  Errors: INVALID_ARG for null pointers,
+ * rows < 0 or cols <= 0; UNSUPPORTED for cols % 128 != 0 or
+ * rows*cols >= 2^40.  rows == 0 enqueues nothing.                        */
+moe_status_t moe_quantize_int4(const void* w, int64_t rows, int32_t cols, uint8_t* q,
                                float* scale, void* stream);
 
 /* ======================================================== backward ===

@@ -13,7 +13,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_GELU_TANH = 0, 1
 MOE_GATE_RENORM_ALL, MOE_GATE_SOFTMAX_TOPK, MOE_GATE_PROB_NO_RENORM = 0, 1, 2
-MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_INT8 = 0, 1
+MOE_WEIGHTS_DTYPE, MOE_WEIGHTS_INT8, MOE_WEIGHTS_INT4 = 0, 1, 2
 MOE_FLAG_NOISE_PHILOX = 1
 MOE_TRACE_EVENTS = 7
 MOE_BWD_TRACE_EVENTS = 10
@@ -24,7 +24,7 @@ EXPORTED = ("moe_status_string", "moe_capacity", "moe_workspace_size",
             "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_quantize_int8",
             "moe_backward_workspace_size", "moe_combine_backward", "moe_router_backward",
             "moe_expert_ffn_backward", "moe_dispatch_backward", "moe_layer_backward",
-            "moe_layer_saves_uv", "moe_layer_forward_noalloc")
+            "moe_layer_saves_uv", "moe_layer_forward_noalloc", "moe_quantize_int4")
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -116,6 +116,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
     lib.moe_quantize_int8.restype = C.c_int
     lib.moe_quantize_int8.argtypes = [P, C.c_int64, C.c_int32, P, P, P]
+    lib.moe_quantize_int4.restype = C.c_int
+    lib.moe_quantize_int4.argtypes = [P, C.c_int64, C.c_int32, P, P, P]
     lib.moe_layer_forward.restype = C.c_int
     lib.moe_layer_forward.argtypes = [cfgp, wp, P, C.POINTER(MoeLayerOut), P, S,
                                       C.POINTER(MoeTrace), P]

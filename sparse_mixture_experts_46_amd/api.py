@@ -36,7 +36,7 @@ class Config:
     # noise_seed); 0.1 is the value of the page's router
     noise_std: float = 0.1
     bias_rate: float = 0.0   # step of the selection-bias update (used with b_sel_out)
-    weight_format: str = "dtype"  # "dtype" or "int8" (see moe_quantize_int8)
+    weight_format: str = "dtype"  # "dtype", "int8" or "int4" (moe_quantize_int8 / _int4)
     # router noise drawn in the kernels (Philox-4x32-10 + Box-Muller): the
     # generator key, or None for no in-kernel noise; noise_offset selects the
     # stream of a call (e.g. the training step)
@@ -55,8 +55,9 @@ class Config:
                            aux_alpha=self.aux_alpha,
                            flags=0 if self.noise_seed is None else L.MOE_FLAG_NOISE_PHILOX,
                            noise_std=self.noise_std, bias_rate=self.bias_rate,
-                           weight_format=(L.MOE_WEIGHTS_INT8 if self.weight_format == "int8"
-                                          else L.MOE_WEIGHTS_DTYPE),
+                           weight_format={"int8": L.MOE_WEIGHTS_INT8,
+                                          "int4": L.MOE_WEIGHTS_INT4}.get(self.weight_format,
+                                                                          L.MOE_WEIGHTS_DTYPE),
                            noise_seed=0 if self.noise_seed is None else self.noise_seed,
                            noise_offset=self.noise_offset)
 
@@ -127,13 +128,29 @@ def moe_quantize_int8(w: torch.Tensor):
     return q, s
 
 
-def quantize_expert_weights(w: dict) -> dict:
+def moe_quantize_int4(w: torch.Tensor):
+    """bf16 weights [..., rows, cols] -> (packed INT4 codes uint8
+    [..., rows, cols / 2], fp32 scales [..., rows, cols / 128])."""
+    if w.dtype != torch.bfloat16:
+        raise ValueError("moe_quantize_int4 takes bf16 weights")
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    q = torch.empty(w.shape[:-1] + (cols // 2,), dtype=torch.uint8, device=w.device)
+    s = torch.empty(w.shape[:-1] + (max(cols // 128, 1),), dtype=torch.float32, device=w.device)
+    L.check(L.load().moe_quantize_int4(_p(w), rows, cols, _p(q), _p(s), _stream()),
+            "moe_quantize_int4")
+    return q, s
+
+
+def quantize_expert_weights(w: dict, fmt: str = "int8") -> dict:
     """A copy of the weight dict with every expert matrix (w1, w3, w2 and the
-    shared ws1, ws3, ws2) replaced by int8 codes plus its *_scale."""
+    shared ws1, ws3, ws2) replaced by its codes ("int8" or "int4") plus its
+    *_scale."""
+    quant = {"int8": moe_quantize_int8, "int4": moe_quantize_int4}[fmt]
     out = dict(w)
     for k in ("w1", "w3", "w2", "ws1", "ws3", "ws2"):
         if w.get(k) is not None:
-            out[k], out[k + "_scale"] = moe_quantize_int8(w[k])
+            out[k], out[k + "_scale"] = quant(w[k])
     return out
 
 

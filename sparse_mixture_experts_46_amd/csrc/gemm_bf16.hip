@@ -67,7 +67,9 @@ hipError_t run_decode(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   const int64_t cap = (int64_t)num_cus() * 16;
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
-  if (a.sc0)
+  if (a.qbits == 4)
+    gemm_decode_q4_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);
+  else if (a.qbits == 8)
     gemm_decode_kernel<DUAL, EPI, true><<<(unsigned)grid, 256, 0, s>>>(a);
   else
     gemm_decode_kernel<DUAL, EPI, false><<<(unsigned)grid, 256, 0, s>>>(a);
@@ -231,8 +233,9 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
     g1.cs_u = g1.c_u + (size_t)rows * p.F;  // shared rows after the routed ones (F_shared == F)
     g1.cs_v = g1.c_v + (size_t)rows * p.F;
   }
-  if (p.int8) {
+  if (p.int8 || p.int4) {
     if (k != K_DECODE) return hipErrorNotSupported;  // checked on the host before
+    g1.qbits = p.int4 ? 4 : 8;
     g1.sc0 = p.w1_scale;
     g1.sc1 = p.w3_scale;
     g1.scs0 = p.ws1_scale;
@@ -270,7 +273,8 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   g2.G = G;
   g2.split_bm = sbm2;
   g2.region = 0;
-  if (p.int8) {
+  if (p.int8 || p.int4) {
+    g2.qbits = p.int4 ? 4 : 8;
     g2.sc0 = p.w2_scale;
     g2.scs0 = p.ws2_scale;
   }

@@ -35,8 +35,11 @@ struct GemmArgs {
   int G;
   int split_bm;             // 0: one launch covers every row; else see main_rows()
   int region;               // 0: main rows of each group, 1: the tail rows
-  // weight-only INT8 (decode kernel only): b0/b1/bs0/bs1 then hold int8
-  // codes and these the per-output-row scales, [n_routed, Nout] / [Nout]
+  // weight-only INT8 / INT4 (decode kernels only): b0/b1/bs0/bs1 then hold
+  // int8 codes or packed INT4 codes and these their scales: INT8 one per
+  // output row, [n_routed, Nout] / [Nout]; INT4 one per 128 K of a row,
+  // [n_routed, Nout, Kdim / 128] / [Nout, Kdim / 128]
+  int qbits;  // 0: weights in bf16, 8: INT8, 4: INT4
   const float* sc0;
   const float* sc1;
   const float* scs0;

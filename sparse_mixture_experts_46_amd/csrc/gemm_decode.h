@@ -192,4 +192,193 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------- INT4 --
+// Weight-only INT4 (Q4): W = q * s with q in [-7, 7] stored as u = q + 8
+// nibbles ([Nout, Kdim / 2] bytes per group of the grouped GEMM; the word
+// layout of quant.hip) and one fp32 scale per 128 consecutive K of a row
+// ([Nout, Kdim / 128]).  The tile, the activation staging and the weight
+// double buffering are those of gemm_decode_kernel; K is walked in 128-wide
+// groups, one scale each:
+//  * lane part p (lane / 16) takes K [32p, 32p + 32) of a group: its 16-byte
+//    load holds the 32 codes, four words of 8; word m feeds MFMA m with the
+//    activations of K [32p + 8m, 32p + 8m + 8) (the same permutation of K on
+//    both operands);
+//  * ((word >> 4i) & 0x000F000F) | 0x43004300 is the bf16 pair (128 + u, 128
+//    + u') of two codes, so a word becomes a bf16 fragment of w' = q + 136 in
+//    7 integer instructions;
+//  * per group the MFMAs give sum x w' and, against a fragment of ones,
+//    S = sum x; the group adds s * (sum x w' - 136 S) = s * sum x q to the
+//    fp32 output (every product is exact, the sums are fp32);
+//  * a stage's codes are half the bytes of an INT8 stage over the same K, so
+//    the weights are fetched two stages ahead (three register sets) to keep
+//    as many bytes in flight; every stage issues the same loads (indices
+//    clamped inside the row), which keeps the wait counts exact.
+__device__ __forceinline__ bf16x8_t q4_word_to_bf16(uint32_t w) {
+  uint4 r;
+  r.x = (w & 0x000F000Fu) | 0x43004300u;
+  r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+  r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+  r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+template <bool DUAL, int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_decode_q4_kernel(GemmArgs p) {
+  constexpr int KC = 512;          // K columns per staged activation chunk
+  constexpr int RB = KC * 2 + 16;  // LDS bytes per staged activation row
+  constexpr int SG = KC / 128;     // 128-wide groups per weight stage (one stage per chunk)
+  __shared__ __attribute__((aligned(16))) char abuf[2][16 * RB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int total = p.tile_base[p.G];
+  const int row = lane & 15, part = lane >> 4;
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                0x3F803F80u, 0x3F803F80u));
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const TileInfo ti = resolve_tile(p, tile, 16, 64);
+    const int64_t Kd = p.Kdim;
+    const int ngrp = (int)(Kd / 128);
+    const int nstage = (ngrp + SG - 1) / SG;
+    const uint32_t row_bytes = (uint32_t)Kd * 2;
+    const char* arow_ptr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int lr = ti.mt * 16 + wave * 4 + i;
+      if (lr >= ti.M) lr = ti.M - 1;
+      int64_t ar;
+      if (ti.shared) ar = ti.row0 + lr;
+      else {
+        const int64_t gr = ti.row0 + lr;
+        ar = p.a_rows ? (int64_t)(p.a_rows[gr] / p.a_div) : gr;
+      }
+      arow_ptr[i] = (const char*)((ti.shared ? p.a_shared : p.a) + ar * p.lda);
+    }
+    int n = ti.nt * 64 + wave * 16 + row;
+    if (n >= ti.Nout) n = ti.Nout - 1;
+    // codes: b_stride weights per routed group, two per byte
+    const int64_t wrow = ((ti.shared ? 0 : (int64_t)ti.g * p.b_stride) + (int64_t)n * Kd) / 2 +
+                         part * 16;
+    const char* pb0 = (const char*)(ti.shared ? (const void*)p.bs0 : (const void*)p.b0) + wrow;
+    const char* pb1 = DUAL ? (const char*)(ti.shared ? (const void*)p.bs1 : (const void*)p.b1) + wrow
+                           : nullptr;
+    const int64_t srow = (ti.shared ? 0 : (int64_t)ti.g * p.Nout * ngrp) + (int64_t)n * ngrp;
+    const float* ps0 = (ti.shared ? p.scs0 : p.sc0) + srow;
+    const float* ps1 = DUAL ? (ti.shared ? p.scs1 : p.sc1) + srow : nullptr;
+
+    auto issue_a = [&](int c, int buf) {
+      uint32_t koff = (uint32_t)c * KC * 2 + (uint32_t)lane * 16;
+      if (koff > row_bytes - 16) koff = row_bytes - 16;  // past K: a valid, unused 16 bytes
+#pragma unroll
+      for (int i = 0; i < 4; ++i) buf_dma16(arow_ptr[i], koff, abuf[buf] + (wave * 4 + i) * RB);
+    };
+    // codes two stages ahead (three sets), scales one stage ahead (two)
+    uint4 b0[3][SG], b1[3][SG];
+    float s0[2][SG], s1[2][SG];
+    // vector loads of one stage's codes (both matrices)
+    constexpr int NBV = SG * (DUAL ? 2 : 1);
+    auto issue_b = [&](int st, int set) {
+#pragma unroll
+      for (int j = 0; j < SG; ++j) {
+        // past the row: a valid group again, loaded and not used
+        const int g = st * SG + j < ngrp ? st * SG + j : ngrp - 1;
+        b0[set][j] = *(const uint4*)(pb0 + (int64_t)g * 64);
+        if (DUAL) b1[set][j] = *(const uint4*)(pb1 + (int64_t)g * 64);
+      }
+    };
+    auto issue_s = [&](int st, int set) {
+#pragma unroll
+      for (int j = 0; j < SG; ++j) {
+        const int g = st * SG + j < ngrp ? st * SG + j : ngrp - 1;
+        s0[set][j] = ps0[g];
+        if (DUAL) s1[set][j] = ps1[g];
+      }
+    };
+
+    f32x4_t out0 = {0.f, 0.f, 0.f, 0.f}, out1 = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int st, int buf, int set, int sset) {
+      const int left = ngrp - st * SG;
+      const char* arow_l = abuf[buf] + row * RB + part * 64;
+#pragma unroll
+      for (int j = 0; j < SG; ++j) {
+        if (j < left) {
+          const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t a0 = zero, a1 = zero, sx = zero;
+          const uint4 c0 = b0[set][j];
+          const uint4 c1 = DUAL ? b1[set][j] : c0;
+          const uint32_t w0[4] = {c0.x, c0.y, c0.z, c0.w};
+          const uint32_t w1[4] = {c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, *(const uint4*)(arow_l + j * 256 + m * 16));
+            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, q4_word_to_bf16(w0[m]), a0, 0, 0, 0);
+            if (DUAL) a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, q4_word_to_bf16(w1[m]), a1, 0, 0, 0);
+            sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, ones, sx, 0, 0, 0);
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            out0[v] += s0[sset][j] * (a0[v] - 136.f * sx[v]);
+            if (DUAL) out1[v] += s1[sset][j] * (a1[v] - 136.f * sx[v]);
+          }
+        }
+      }
+    };
+
+    // issue order: a(0), s(0), c(0), c(1), then per stage st: a(st+1),
+    // s(st+1), c(st+2) (a: activation chunk, s: scales, c: codes), so at the
+    // top of stage st only c(st+1) may still be in flight
+    issue_a(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_s(0, 0);
+    issue_b(0, 0);
+    if (nstage > 1) issue_b(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int st = 0; st < nstage; ++st) {
+      if (st + 1 < nstage) wait_vmcnt<NBV>();
+      else wait_vmcnt<0>();
+      __syncthreads();  // every wave's rows of chunk st; buffer (st+1)&1 free
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 1 < nstage) {
+        issue_a(st + 1, (st + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st & 1) issue_s(st + 1, 0);
+        else issue_s(st + 1, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 2 < nstage) {
+        const int set2 = (st + 2) % 3;
+        if (set2 == 0) issue_b(st + 2, 0);
+        else if (set2 == 1) issue_b(st + 2, 1);
+        else issue_b(st + 2, 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int set = st % 3, sset = st & 1;
+      if (set == 0) {
+        if (sset) compute(st, st & 1, 0, 1); else compute(st, st & 1, 0, 0);
+      } else if (set == 1) {
+        if (sset) compute(st, st & 1, 1, 1); else compute(st, st & 1, 1, 0);
+      } else {
+        if (sset) compute(st, st & 1, 2, 1); else compute(st, st & 1, 2, 0);
+      }
+    }
+    __syncthreads();  // the last buffer is read before the next tile stages into it
+
+    // D layout (16x16): col = lane % 16, row = 4 * (lane / 16) + v
+    const int col = ti.nt * 64 + wave * 16 + (lane & 15);
+    if (col < ti.Nout) {
+      uint16_t* cbase = ti.shared ? p.c_shared : p.c;
+      float bias = 0.f;
+      if (EPI != EPI_SILU_MUL && p.bias && !ti.shared)
+        bias = bf16_to_f32(p.bias[(int64_t)ti.g * p.Nout + col]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = ti.mt * 16 + 4 * part + v;
+        if (r < ti.M) {
+          const float o = DUAL ? silu_f(out0[v]) * out1[v] : epi1<EPI>(out0[v], bias);
+          cbase[(ti.row0 + r) * (int64_t)ti.Nout + col] = f32_to_bf16(o);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace moe

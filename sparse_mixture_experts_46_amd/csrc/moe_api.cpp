@@ -27,10 +27,14 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->flags & ~(uint32_t)MOE_FLAG_NOISE_PHILOX) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->aux_alpha)) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->noise_std) || !std::isfinite(c->bias_rate)) return MOE_ERR_INVALID_ARG;
-  if (c->weight_format != MOE_WEIGHTS_DTYPE && c->weight_format != MOE_WEIGHTS_INT8)
+  if (c->weight_format != MOE_WEIGHTS_DTYPE && c->weight_format != MOE_WEIGHTS_INT8 &&
+      c->weight_format != MOE_WEIGHTS_INT4)
     return MOE_ERR_INVALID_ARG;
-  if (c->weight_format == MOE_WEIGHTS_INT8 &&
+  if (c->weight_format != MOE_WEIGHTS_DTYPE &&
       (c->dtype != MOE_BF16 || c->act != MOE_ACT_SWIGLU || !ffn_int8_supported(c->T, c->K, c->N)))
+    return MOE_ERR_UNSUPPORTED;
+  // INT4 scales cover 128 consecutive K of a row: both GEMMs' K must be whole groups
+  if (c->weight_format == MOE_WEIGHTS_INT4 && (c->d % 128 || c->F % 128 || c->F_shared % 128))
     return MOE_ERR_UNSUPPORTED;
   if (c->N > MOE_MAX_EXPERTS || c->K > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (c->d % 64 || c->F % 64 || c->F_shared % 64) return MOE_ERR_UNSUPPORTED;
@@ -203,7 +207,7 @@ moe_status_t check_weights_ffn(const moe_config_t* c, const moe_weights_t* w) {
   if (c->act == MOE_ACT_SWIGLU && !w->w3) return MOE_ERR_INVALID_ARG;
   if (c->act == MOE_ACT_SWIGLU && (w->b1 || w->b2)) return MOE_ERR_UNSUPPORTED;
   if (c->F_shared > 0 && (!w->ws1 || !w->ws3 || !w->ws2)) return MOE_ERR_INVALID_ARG;
-  if (c->weight_format == MOE_WEIGHTS_INT8) {
+  if (c->weight_format != MOE_WEIGHTS_DTYPE) {
     if (!w->w1_scale || !w->w3_scale || !w->w2_scale) return MOE_ERR_INVALID_ARG;
     if (c->F_shared > 0 && (!w->ws1_scale || !w->ws3_scale || !w->ws2_scale))
       return MOE_ERR_INVALID_ARG;
@@ -215,6 +219,7 @@ void set_weights(FfnProblem& p, const moe_config_t* c, const moe_weights_t* w) {
   p.w1 = w->w1; p.w3 = w->w3; p.w2 = w->w2; p.b1 = w->b1; p.b2 = w->b2;
   p.ws1 = w->ws1; p.ws3 = w->ws3; p.ws2 = w->ws2;
   p.int8 = c->weight_format == MOE_WEIGHTS_INT8;
+  p.int4 = c->weight_format == MOE_WEIGHTS_INT4;
   p.w1_scale = w->w1_scale; p.w3_scale = w->w3_scale; p.w2_scale = w->w2_scale;
   p.ws1_scale = w->ws1_scale; p.ws3_scale = w->ws3_scale; p.ws2_scale = w->ws2_scale;
 }
@@ -462,6 +467,16 @@ moe_status_t moe_quantize_int8(const void* w, int64_t rows, int32_t cols, int8_t
   if (cols % 64) return MOE_ERR_UNSUPPORTED;
   if (rows * (int64_t)cols >= (int64_t(1) << 40)) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_quantize_int8(w, rows, cols, q, scale, (hipStream_t)stream));
+}
+
+moe_status_t moe_quantize_int4(const void* w, int64_t rows, int32_t cols, uint8_t* q, float* scale,
+                               void* stream) {
+  if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!w || !q || !scale) return MOE_ERR_INVALID_ARG;
+  if (cols % 128) return MOE_ERR_UNSUPPORTED;
+  if (rows * (int64_t)cols >= (int64_t(1) << 40)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_quantize_int4(w, rows, cols, q, scale, (hipStream_t)stream));
 }
 
 int32_t moe_layer_saves_uv(const moe_config_t* cfg) {

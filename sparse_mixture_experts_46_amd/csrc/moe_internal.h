@@ -102,12 +102,13 @@ struct FfnProblem {
   // GEMM runs the ping-pong kernel (ffn_saves_uv)
   void* save_u;
   void* save_v;
-  // weight-only INT8 (w1/w3/w2/ws* hold int8 codes): per-output-row scales
-  bool int8;
+  // weight-only INT8 (w1/w3/w2/ws* hold int8 codes, per-output-row scales)
+  // or INT4 (packed codes, one scale per 128 K of a row)
+  bool int8, int4;
   const float *w1_scale, *w3_scale, *w2_scale, *ws1_scale, *ws3_scale, *ws2_scale;
 };
 
-// INT8 weights are supported where the decode kernel runs: at most
+// INT8 / INT4 weights are supported where the decode kernel runs: at most
 // this many routed rows per expert on average.
 bool ffn_int8_supported(int64_t T, int K, int N);
 
@@ -125,6 +126,10 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
 // ----------------------------------------------------------- quantization --
 // w bf16 [rows, cols] -> q int8 [rows, cols], scale fp32 [rows]; cols % 8 == 0
 hipError_t launch_quantize_int8(const void* w, int64_t rows, int cols, int8_t* q, float* scale,
+                                hipStream_t stream);
+// w bf16 [rows, cols] -> q [rows, cols / 2] packed INT4 codes, scale fp32
+// [rows, cols / 128]; cols % 128 == 0
+hipError_t launch_quantize_int4(const void* w, int64_t rows, int cols, uint8_t* q, float* scale,
                                 hipStream_t stream);
 
 // --------------------------------------------------------------- combine --

@@ -211,8 +211,9 @@ def test_zero_tokens_is_a_noop(lib):
 
 
 def test_int8_config_rules(lib):
-    """INT8 expert weights: bf16 SwiGLU layers at decode sizes only; the
-    scales are required; unknown formats are argument errors."""
+    """INT8 / INT4 expert weights: bf16 SwiGLU layers at decode sizes only
+    (INT4 also with d and F multiples of 128); the scales are required;
+    unknown formats are argument errors."""
     dec = cfg_of(WL.MIXTRAL_DECODE, weight_format="int8")
     assert dec.weight_format == L.MOE_WEIGHTS_INT8
     assert ws_size(lib, dec)[0] == L.MOE_OK
@@ -221,8 +222,14 @@ def test_int8_config_rules(lib):
         L.MOE_ERR_UNSUPPORTED  # 1024 rows per expert: not a decode size
     assert ws_size(lib, cfg_of(WL.TINY, weight_format="int8"))[0] == \
         L.MOE_ERR_UNSUPPORTED  # fp32 GELU layer
+    for w in (WL.MIXTRAL_DECODE, WL.DEEPSEEK_DECODE):
+        assert ws_size(lib, cfg_of(w, weight_format="int4"))[0] == L.MOE_OK
+    assert ws_size(lib, cfg_of(WL.MIXTRAL_PREFILL, weight_format="int4"))[0] == \
+        L.MOE_ERR_UNSUPPORTED
+    assert ws_size(lib, cfg_of(WL.MIXTRAL_DECODE, weight_format="int4", d=4096 + 64))[0] == \
+        L.MOE_ERR_UNSUPPORTED  # d not a multiple of 128
     bad = cfg_of(WL.MIXTRAL_DECODE)
-    bad.weight_format = 2
+    bad.weight_format = 3
     assert ws_size(lib, bad)[0] == L.MOE_ERR_INVALID_ARG
     fake = C.c_void_p(0x1000)
     w = L.MoeWeights(w_r=0x1000, w1=0x1000, w3=0x1000, w2=0x1000)  # scales missing
@@ -233,6 +240,9 @@ def test_int8_config_rules(lib):
 def test_quantize_rejects_before_launch(lib):
     P = C.c_void_p
     fake = P(0x1000)
+    assert lib.moe_quantize_int4(fake, 4, 192, fake, fake, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_int4(None, 4, 256, fake, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_int4(fake, 0, 256, fake, fake, None) == L.MOE_OK
     assert lib.moe_quantize_int8(fake, -1, 64, fake, fake, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_quantize_int8(fake, 4, 0, fake, fake, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_quantize_int8(None, 4, 64, fake, fake, None) == L.MOE_ERR_INVALID_ARG

@@ -162,3 +162,122 @@ def test_layer_int8_full_size(w):
     inp = make_inputs(w, device=DEV)
     bufs = run_int8_layer(w, inp)
     check_int8_layer(w, inp, bufs)
+
+
+# ------------------------------------------------------------------ INT4 ---
+
+class OracleInt4Stack:
+    """The oracle's own INT4 quantization of a bf16 expert stack, one expert
+    at a time (never the GPU's codes)."""
+
+    def __init__(self, t):
+        self.bits = bf16_bits(t)
+        self.shape = self.bits.shape
+
+    def __getitem__(self, e):
+        q, s = ref.quantize_int4_groups(ref.bf16_bits_to_f64(self.bits[e]))
+        return ref.dequantize_int4_groups(q, s)
+
+    def __len__(self):
+        return self.shape[0]
+
+
+def oracle_int4(w, inp, idx=None):
+    W = {"w_r": f64(inp["w_r"]), "w1": OracleInt4Stack(inp["w1"]),
+         "w3": OracleInt4Stack(inp["w3"]), "w2": OracleInt4Stack(inp["w2"])}
+    shared = None
+    if inp.get("ws1") is not None:
+        def deq(t):
+            return ref.dequantize_int4_groups(*ref.quantize_int4_groups(f64(t)))
+        shared = {"w1": deq(inp["ws1"]), "w3": deq(inp["ws3"]), "w2": deq(inp["ws2"])}
+    return ref.layer_forward(f64(inp["x"]), W, K=w.K, act=w.act, gate_mode=w.gate, cf=w.cf,
+                             alpha=w.aux_alpha, b_r=f64(inp["b_r"]), b_sel=f64(inp["b_sel"]),
+                             shared=shared, idx=idx)
+
+
+@pytest.mark.parametrize("rows,cols,scale", [(37, 128, 1.0), (300, 512, 0.02),
+                                             (64, 7168, 3.0), (2, 14336, 1e-3)])
+def test_quantize_int4_bit_exact(rows, cols, scale):
+    say("quantize int4", rows, cols)
+    g = torch.Generator().manual_seed(rows * 11 + cols)
+    w = (torch.randn((rows, cols), generator=g) * scale).to(torch.bfloat16)
+    if rows > 3:
+        w[1] = 0.0                        # zero row: every group zero
+        w[2, :128] = 0.0
+        w[2, 5] = -0.75                   # a group with one non-zero entry
+        w[3, :] = torch.tensor(0.5, dtype=torch.bfloat16)  # constant row
+    q, s = api.moe_quantize_int4(w.to(DEV))
+    torch.cuda.synchronize()
+    qo, so = ref.quantize_int4_groups(f64(w))
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(q.cpu().numpy(), ref.pack_int4(qo))
+
+
+def run_int4_layer(w, inp):
+    cfg = api.config_for(w)
+    cfg.weight_format = "int4"
+    winp = api.quantize_expert_weights(inp, "int4")
+    bufs = api.moe_layer_forward(cfg, winp, inp["x"])
+    torch.cuda.synchronize()
+    return bufs
+
+
+def check_int4_layer(w, inp, bufs):
+    idx = bufs.idx.cpu().numpy().astype(np.int64)
+    own = ref.layer_forward(f64(inp["x"]), {"w_r": f64(inp["w_r"])}, K=w.K, act=w.act,
+                            gate_mode=w.gate, cf=w.cf, b_r=f64(inp["b_r"]),
+                            b_sel=f64(inp["b_sel"]), experts_needed=False)
+    far = own.margin > NEAR_TIE
+    assert np.array_equal(idx[far], own.idx[far]), "top-K indices"
+    nd = int(np.any(idx[~far] != own.idx[~far], axis=1).sum())
+    report_near_ties(w.name + " (int4)", int((~far).sum()), nd, len(far))
+    o = oracle_int4(w, inp, idx=idx)
+    assert np.array_equal(bufs.offset.cpu().numpy(), o.asg.offset)
+    y = bufs.y.double().cpu().numpy()
+    e = rel_err(y, o.y)
+    say(w.name, f"int4 y rel err {e:.3e} over {w.T} tokens")
+    assert e <= TOL_BF16, (w.name, e)
+
+
+INT4_CASES = [
+    WL.scaled(WL.MIXTRAL_DECODE, d=512, F=768, name="int4_mixtral_small"),
+    WL.scaled(WL.DEEPSEEK_DECODE, d=256, F=384, F_shared=384, name="int4_deepseek_small"),
+    # K = 640 and 384: the last activation chunk holds fewer than 4 groups
+    WL.Workload(name="int4_ragged_t40_n16_k3", T=40, d=640, N=16, K=3, F=384, seed=33),
+    WL.Workload(name="int4_cap_t64_n32_k2", T=64, d=128, N=32, K=2, F=256, seed=34, cf=1.0),
+]
+
+
+@pytest.mark.parametrize("w", INT4_CASES, ids=lambda w: w.name)
+def test_layer_int4(w):
+    say("layer int4", w.name)
+    cpu = make_inputs(w, device="cpu")
+    inp = {k: (None if v is None else v.to(DEV)) for k, v in cpu.items()}
+    check_int4_layer(w, inp, run_int4_layer(w, inp))
+
+
+def test_int4_close_to_bf16():
+    """The INT4 layer stays near the bf16 layer it was quantized from.  With 7
+    levels per side the step is absmax / 7 (absmax of 128 normal weights is
+    about 2.6 sigma), so each weight carries a uniform error of about 0.11
+    sigma RMS; through the two GEMMs the largest output error is about 0.2
+    max|y| on these normal weights: the bound is 0.3."""
+    w = WL.scaled(WL.MIXTRAL_DECODE, d=512, F=768)
+    say("int4 vs bf16", w.name)
+    cpu = make_inputs(w, device="cpu")
+    inp = {k: (None if v is None else v.to(DEV)) for k, v in cpu.items()}
+    b = api.moe_layer_forward(api.config_for(w), inp, inp["x"])
+    torch.cuda.synchronize()
+    y16 = b.y.double().cpu().numpy()
+    y4 = run_int4_layer(w, inp).y.double().cpu().numpy()
+    assert rel_err(y4, y16) < 0.3, rel_err(y4, y16)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("w", [WL.MIXTRAL_DECODE, WL.DEEPSEEK_DECODE], ids=lambda w: w.name)
+def test_layer_int4_full_size(w):
+    """The full decode workloads with INT4 expert weights, as the benchmark
+    runs them: every token against the oracle."""
+    say("layer int4 full", w.name)
+    inp = make_inputs(w, device=DEV)
+    check_int4_layer(w, inp, run_int4_layer(w, inp))
