@@ -251,6 +251,8 @@ def layer_record(w, steps, warmup, ev, quant=None, cpu=None):
         f = sw["gemm1"][0] + sw["gemm2"][0]
         b = sw["gemm1"][1] + sw["gemm2"][1]
         kernels = {"ffn_f32": roofline_of(f, b, st["gemm1"], peak)}
+    for k in kernels:
+        kernels[k]["traffic"] = traffic_of(w.name, quant or "bf16", k)
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     rec = {"workload": w.name, "desc": w.desc, "T": w.T, "dtype": w.dtype,
            "weights": {"int8": "int8 + fp32 row scales",
@@ -269,16 +271,13 @@ def layer_record(w, steps, warmup, ev, quant=None, cpu=None):
 
 
 def decode_record(w, steps, warmup, ev, quant=None, cpu=None):
-    """A decode-sized layer: as layer_record, plus the HBM GB/s of the step on
-    the expert weights it touches (bf16 weights, or INT8 codes plus scales)
-    against the HBM peak."""
+    """A decode-sized layer: as layer_record, plus the HBM GB/s of the whole
+    step on the expert weights it touches (bf16 weights, or INT8 / INT4
+    codes plus scales) against the HBM peak; "roofline" stays the dominant
+    kernel's."""
     rec, rd = layer_record(w, steps, warmup, ev, quant=quant, cpu=cpu)
-    gbs = rec["weight_gbs"]
-    rec["hbm_gbs"] = gbs
-    rec["kernel_roofline"] = rec["roofline"]
-    rec["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                       "frac": gbs / PEAK_HBM_GBS,
-                       "what": "touched expert weights / step time"}
+    rec["hbm_gbs"] = rec["weight_gbs"]
+    rec["hbm_frac"] = rec["weight_gbs"] / PEAK_HBM_GBS
     return rec, rd
 
 
@@ -521,17 +520,26 @@ def cpu_baseline(w, inp, sample, seeded=False, repeats=1):
                       f"incl. per-expert bf16->fp64 weight widening{med}; {dt:.3g} s"}
 
 
-def traffic_record(name):
-    """HBM bytes per launch of the first grouped GEMM from the committed
-    rocprofv3 counter runs, or None when the kernel source changed since."""
-    p = os.path.join(ROOT, "profiles", f"traffic_gemm1_{name}.json")
+def counter_record(name, weights, stage):
+    """The committed rocprofv3 counter summary of one grouped-GEMM stage
+    ("gemm1" / "gemm2") of a workload with bf16, INT8 or INT4 weights, or
+    None when there is none or the GEMM source changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", f"counters_{name}.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
     from sparse_mixture_experts_46_amd.profsum import gemm_source_sha256
     if rec.get("gemm_source_sha256") != gemm_source_sha256():
         return None
-    return rec.get("bytes_per_launch")
+    return rec["stages"].get(f"{weights}:{stage}")
+
+
+def traffic_of(name, weights, stage):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, probe-scaled) or None."""
+    c = counter_record(name, weights, stage)
+    if not c or c.get("fetch_bytes") is None or c.get("write_bytes") is None:
+        return None
+    return c["fetch_bytes"] + c["write_bytes"]
 
 
 def main():
@@ -559,7 +567,7 @@ def main():
     tok_s = w.T / (ms / 1e3)
     g1_ms = float(r["stage_ms"][2])
     g1_tflops = r["g1_flops"] / (g1_ms * 1e-3) / 1e12
-    traffic = traffic_record(w.name)
+    traffic = traffic_of(w.name, "bf16", "gemm1")
     line = {
         "metric": METRIC,
         "value": tok_s,

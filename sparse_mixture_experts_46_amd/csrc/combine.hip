@@ -15,35 +15,46 @@
 namespace moe {
 namespace {
 
-// bf16: each thread owns 8 consecutive columns (16 bytes).
+// bf16: each thread owns 8 consecutive columns (16 bytes) of one token at a
+// time; the workgroup's threads cover the row (blockDim.x divides d / 8 where
+// it can).  The up to KB expert rows of a token are all loaded before any is
+// added, so every thread has KB loads in flight; the sum still runs in slot
+// order.
+template <int KB>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(
     const uint16_t* __restrict__ y_perm, const int32_t* __restrict__ pair_row,
     const float* __restrict__ gate, const uint16_t* __restrict__ y_shared,
     uint16_t* __restrict__ y, int64_t T, int d, int K) {
   const int chunks = d / 8;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-    int32_t rows[kMaxTopK];
-    float gs[kMaxTopK];
-    for (int k = 0; k < K; ++k) {
-      rows[k] = pair_row[t * K + k];
-      gs[k] = gate[t * K + k];
+    int32_t rows[KB];
+    float gs[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      rows[k] = k < K ? pair_row[t * K + k] : -1;
+      gs[k] = k < K ? gate[t * K + k] : 0.f;
     }
-    for (int c = threadIdx.x; c < chunks; c += 256) {
+    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+      uint4 v[KB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+        if (rows[k] >= 0) v[k] = *(const uint4*)(y_perm + (int64_t)rows[k] * d + c * 8);
+      uint4 vs = make_uint4(0u, 0u, 0u, 0u);
+      if (y_shared) vs = *(const uint4*)(y_shared + t * d + c * 8);
       float acc[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-      for (int k = 0; k < K; ++k) {
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
         if (rows[k] < 0) continue;
-        const uint4 v = *(const uint4*)(y_perm + (int64_t)rows[k] * d + c * 8);
         float f[8];
-        unpack_bf16x8(v, f);
+        unpack_bf16x8(v[k], f);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = fmaf(gs[k], f[j], acc[j]);
       }
       if (y_shared) {
-        const uint4 v = *(const uint4*)(y_shared + t * d + c * 8);
         float f[8];
-        unpack_bf16x8(v, f);
+        unpack_bf16x8(vs, f);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] += f[j];
       }
@@ -96,10 +107,18 @@ hipError_t launch_combine(const void* y_perm, const int32_t* pair_row,
                           hipStream_t stream) {
   int64_t grid = T < 8192 ? T : 8192;
   if (grid < 1) grid = 1;
-  if (bf16)
-    combine_bf16_kernel<<<(unsigned)grid, 256, 0, stream>>>(
-        (const uint16_t*)y_perm, pair_row, gate, (const uint16_t*)y_shared, (uint16_t*)y, T, d, K);
-  else
+  if (bf16) {
+    const int chunks = d / 8;
+    const int nt = chunks % 256 == 0 ? 256 : (chunks % 128 == 0 ? 128 : (chunks <= 64 ? 64 : 256));
+    const uint16_t* yp = (const uint16_t*)y_perm;
+    const uint16_t* ys = (const uint16_t*)y_shared;
+    if (K <= 2)
+      combine_bf16_kernel<2><<<(unsigned)grid, nt, 0, stream>>>(yp, pair_row, gate, ys, (uint16_t*)y, T, d, K);
+    else if (K <= 8)
+      combine_bf16_kernel<8><<<(unsigned)grid, nt, 0, stream>>>(yp, pair_row, gate, ys, (uint16_t*)y, T, d, K);
+    else
+      combine_bf16_kernel<kMaxTopK><<<(unsigned)grid, nt, 0, stream>>>(yp, pair_row, gate, ys, (uint16_t*)y, T, d, K);
+  } else
     combine_f32_kernel<<<(unsigned)grid, 256, 0, stream>>>(
         (const float*)y_perm, pair_row, gate, (const float*)y_shared, (float*)y, T, d, K);
   return hipGetLastError();

@@ -193,8 +193,10 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   specs.s[0] = {bm1, bno1, p.F, p.F_shared, 0, 0};
   specs.s[1] = {bm2, bno2, p.d, p.d, sbm2, 0};
   specs.s[2] = {tbm, tbno, p.d, p.d, sbm2, 1};
+  // walk counters after the three tables: 8 for each ping-pong launch
+  int32_t* ctr = p.tile_base + 3 * (p.N + 2);
   tile_setup_kernel<<<1, 1024, 0, stream>>>(p.offset, p.N, srows, specs, split2 ? 3 : 2,
-                                            p.tile_base);
+                                            p.tile_base, ctr, kWalkCounters);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
@@ -224,6 +226,7 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   g1.c = h;
   g1.c_shared = h_shared;
   g1.tile_base = base[0];
+  g1.walk_ctr = ctr;
   g1.G = G;
   g1.split_bm = 0;
   g1.region = 0;
@@ -270,6 +273,7 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   g2.c = (uint16_t*)p.y_perm;
   g2.c_shared = (uint16_t*)p.y_shared;
   g2.tile_base = base[1];
+  g2.walk_ctr = ctr + 8;
   g2.G = G;
   g2.split_bm = sbm2;
   g2.region = 0;
@@ -285,6 +289,7 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
   if (split2) {
     GemmArgs t2 = g2;
     t2.tile_base = base[2];
+    t2.walk_ctr = nullptr;  // the tail's tile kernel walks in the fixed order
     t2.region = 1;
     // a tail is shorter than half a main tile
     const int64_t tt2 = (int64_t)G * ((sbm2 / 2 + tbm - 1) / tbm) * ((p.d + tbno - 1) / tbno);

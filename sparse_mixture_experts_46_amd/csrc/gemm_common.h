@@ -44,6 +44,9 @@ struct GemmArgs {
   const float* sc1;
   const float* scs0;
   const float* scs1;
+  // nullable (ping-pong kernel only, with a grid that is a multiple of 8): 8
+  // zeroed counters, one per XCD, for the dynamic tile order
+  int32_t* walk_ctr;
   // nullable (SwiGLU first GEMM, ping-pong kernel only): also store the
   // gate and up products A W1^T and A W3^T, routed [rows, Nout] / shared
   uint16_t* c_u;
@@ -103,6 +106,38 @@ __device__ __forceinline__ TileWalk tile_walk(int total) {
   return w;
 }
 
+// Dynamic order (kernels given 8 zeroed counters): the tile table is cut
+// into 8 contiguous ranges of equal tile count, range x for XCD x.  A
+// workgroup's first tile is the (bid >> 3)-th of its XCD's range; after
+// that it takes the next untaken tile of that range from the XCD's counter,
+// so the workgroups of one XCD always hold neighbouring tiles (the same
+// expert's rows and weight columns, sharing the XCD's L2) however long each
+// tile took.  A workgroup whose range is used up takes tiles from the next
+// XCDs' ranges in turn; -1 when every range is used up.  Which workgroup
+// computes a tile does not change the tile's result.
+struct DynWalk {
+  int x, nb8, probe, total;
+};
+__device__ __forceinline__ int dyn_lo(int total, int x) { return (int)(((int64_t)total * x) >> 3); }
+__device__ __forceinline__ int dyn_first(DynWalk& w, int total) {
+  w.x = blockIdx.x & 7;
+  w.nb8 = gridDim.x >> 3;
+  w.probe = 0;
+  w.total = total;
+  const int t = dyn_lo(total, w.x) + (int)(blockIdx.x >> 3);
+  return t < dyn_lo(total, w.x + 1) ? t : -2;  // -2: ask the counters
+}
+// One thread of the workgroup calls this.
+__device__ __forceinline__ int dyn_next(DynWalk& w, int32_t* ctr) {
+  while (w.probe < 8) {
+    const int y = (w.x + w.probe) & 7;
+    const int t = dyn_lo(w.total, y) + w.nb8 + atomicAdd(&ctr[y], 1);
+    if (t < dyn_lo(w.total, y + 1)) return t;
+    ++w.probe;
+  }
+  return -1;
+}
+
 // Resolve tile -> (group, first row, rows, output columns, A/B/C pointers).
 struct TileInfo {
   int g, M, Nout, mt, nt;
@@ -141,11 +176,13 @@ struct TileSpecs {
 };
 
 // base[k][g] = sum_{g' < g} tiles of group g' under spec k (k < nspec);
-// tables are (n_routed + 2) apart.  One block of 1024 threads.
+// tables are (n_routed + 2) apart.  Also zeroes nctr walk counters at ctr.
+// One block of 1024 threads.
 static __global__ __launch_bounds__(1024) void tile_setup_kernel(
     const int32_t* __restrict__ offset, int n_routed, int64_t shared_rows, TileSpecs specs,
-    int nspec, int32_t* __restrict__ base) {
+    int nspec, int32_t* __restrict__ base, int32_t* __restrict__ ctr = nullptr, int nctr = 0) {
   __shared__ int32_t cnt[4][1040];
+  if ((int)threadIdx.x < nctr) ctr[threadIdx.x] = 0;
   const int G = n_routed + (shared_rows > 0 ? 1 : 0);
   for (int g = threadIdx.x; g < G; g += 1024) {
     const int M = g < n_routed ? (int)(offset[g + 1] - offset[g]) : (int)shared_rows;

@@ -26,9 +26,11 @@
 //    and DB >= 3 every overwritten slot was last read before the previous
 //    barrier, and the weights get three sub-steps of lead.  Past the end of
 //    K the last block is re-loaded (drained before the epilogue).
-//  * Persistent: one workgroup per CU walks the device-side tile table in a
-//    fixed order; each XCD walks its own contiguous range of tiles (same
-//    expert, neighbouring column tiles) that shares its L2.
+//  * Persistent: one workgroup per CU walks the device-side tile table; each
+//    XCD works through its own contiguous range of tiles (same expert,
+//    neighbouring column tiles) that shares its L2, in a fixed order or,
+//    given walk counters, handing out the range's tiles one at a time so
+//    that the XCD's workgroups stay on neighbouring tiles.
 //  * SwiGLU (DUAL): the B tile holds BN/2 gate rows and the same BN/2 up
 //    rows; silu(gate) * up is formed in registers.
 #pragma once
@@ -37,24 +39,9 @@
 
 #include "gemm_common.h"
 #include "gemm_tile.h"
+#include "lds_dma.h"
 
 namespace moe {
-
-// 16-byte-per-lane global -> LDS copy through a raw buffer resource.
-__device__ __forceinline__ void buf_dma16(const void* base, uint32_t voff, void* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  // base is wave-uniform: saying so keeps the descriptor in SGPRs (else every
-  // load becomes a loop over the lanes' descriptors)
-  const uint64_t b = (uint64_t)base;
-  const uint64_t ub = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0, -1, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, 0, 0, 0);
-#endif
-}
-
-// Physical chunk of logical 16-byte chunk c in tile row r (an involution).
-__device__ __forceinline__ int pp_swz(int r) { return (r >> 2) & 3; }
 
 template <int BM, int BN, int WM, int WN, int DA, int DB, bool DUAL, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
@@ -109,7 +96,20 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
     bsw[j] = pp_swz(r);
   }
 
-  for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
+  // dynamic order: thread 0 takes the next tile from the counters and hands
+  // it over in the first LDS word, which is free between tiles (no DMA in
+  // flight, no fragment reads)
+  const bool dyn = p.walk_ctr != nullptr && (gridDim.x & 7) == 0;
+  DynWalk dw;
+  volatile int* bcast = (volatile int*)smem;
+  for (int tile = dyn ? dyn_first(dw, total) : walk.tile;;) {
+    if (dyn && tile == -2) {
+      if (tid == 0) *bcast = dyn_next(dw, p.walk_ctr);
+      __syncthreads();
+      tile = *bcast;
+      __syncthreads();  // read by every wave before the DMA reuses the word
+    }
+    if (dyn ? tile < 0 : tile >= walk.end) break;
     const TileInfo ti = resolve_tile(p, tile, BM, BNo);
     const int64_t Kd = p.Kdim;
     const char* abase = (const char*)(ti.shared ? p.a_shared : p.a);
@@ -283,6 +283,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
     constexpr bool kHalfOk = (FM % 2 == 0) && (LA % 2 == 0);
     if (kHalfOk && ti.M - ti.mt * BM <= BM / 2) run(std::true_type{});
     else run(std::false_type{});
+    tile = dyn ? -2 : tile + walk.step;
   }
 }
 

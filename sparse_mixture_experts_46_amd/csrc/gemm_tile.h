@@ -21,22 +21,9 @@
 #pragma once
 
 #include "gemm_common.h"
+#include "lds_dma.h"
 
 namespace moe {
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
-
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)l, 16, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) with expcnt/lgkmcnt left unconstrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 template <int CH, int SWZ>
 __device__ __forceinline__ int swz(int row) {

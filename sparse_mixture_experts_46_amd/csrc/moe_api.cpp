@@ -59,7 +59,7 @@ size_t elem_bytes(const moe_config_t* c) { return c->dtype == MOE_BF16 ? 2 : 4; 
 
 // ---- workspace layouts -----------------------------------------------------
 struct RouterWs {
-  size_t split, logits, part_p, part_cnt, part_z, part_fp, total;
+  size_t split, logits, part_p, part_cnt, part_z, part_fp, planes, total;
 };
 RouterWs router_ws(const moe_config_t* c) {
   RouterWs w;
@@ -73,6 +73,7 @@ RouterWs router_ws(const moe_config_t* c) {
   w.part_cnt = o; o = align_up(o + (size_t)nb * c->N * 4);
   w.part_z = o; o = align_up(o + (size_t)nb * 3 * 4);
   w.part_fp = o; o = align_up(o + (size_t)((c->N + 63) / 64) * 4);
+  w.planes = o; o = align_up(o + router_planes_bytes(c->T, c->d, c->N, c->dtype == MOE_BF16));
   w.total = o;
   return w;
 }
@@ -97,7 +98,7 @@ struct FfnWs {
 FfnWs ffn_ws(const moe_config_t* c) {
   FfnWs w;
   size_t o = 0;
-  w.tile_base = o; o = align_up(o + (size_t)3 * (c->N + 2) * 4);
+  w.tile_base = o; o = align_up(o + ((size_t)3 * (c->N + 2) + kWalkCounters) * 4);
   w.h = o; o = align_up(o + ffn_workspace_bytes(c->T, c->d, c->N, c->K, c->F, c->F_shared,
                                                 c->dtype == MOE_BF16));
   w.total = o;
@@ -238,8 +239,9 @@ moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void
   float* entropy = st ? st->entropy : nullptr;
   float* b_out = st ? st->b_sel_out : nullptr;
   if (router_small_path(c->T, c->N)) {
-    hipError_t e = launch_router_logits(x, bf16, w->w_r, w->b_r, at<float>(ws, L.split), lg, c->T,
-                                        c->d, c->N, s, /*reduce_splits=*/false);
+    hipError_t e = launch_router_logits(x, bf16, w->w_r, w->b_r, at<uint16_t>(ws, L.planes),
+                                        at<float>(ws, L.split), lg, c->T, c->d, c->N, s,
+                                        /*reduce_splits=*/false);
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = launch_router_small(at<float>(ws, L.split), router_num_splits(c->T, c->d, c->N, bf16),
                             w->b_r, router_noise(c, w), w->b_sel, lg, idx, gate, c->T, c->N,
@@ -247,8 +249,8 @@ moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void
                             c->bias_rate, s);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
-  hipError_t e = launch_router_logits(x, bf16, w->w_r, w->b_r, at<float>(ws, L.split), lg, c->T,
-                                      c->d, c->N, s);
+  hipError_t e = launch_router_logits(x, bf16, w->w_r, w->b_r, at<uint16_t>(ws, L.planes),
+                                      at<float>(ws, L.split), lg, c->T, c->d, c->N, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_router_topk(lg, router_noise(c, w), w->b_sel, idx, gate, at<float>(ws, L.part_p),
                          at<int32_t>(ws, L.part_cnt), at<float>(ws, L.part_z), c->T, c->N, c->K,

@@ -25,12 +25,19 @@ int64_t router_num_blocks(int64_t T);
 // K splits of the logits GEMM for this shape (partials [splits, T, N]).
 int router_num_splits(int64_t T, int d, int N, bool x_bf16);
 
+// Whether the logits run as a bf16 GEMM against the exact three-part split
+// of W_r (bf16 x, d a multiple of 64), and the bytes of that split's planes
+// [3][N][d] bf16 (0 otherwise).
+bool router_gemm_path(int64_t T, int d, int N, bool x_bf16);
+size_t router_planes_bytes(int64_t T, int d, int N, bool x_bf16);
+
 // logits = x W_r^T + b_r.  With several K splits the partial products go to
 // part [splits, T, N] and (reduce_splits) a reduction writes logits; with one
-// split the logits are written directly (part unused).
+// split the logits are written directly (part unused).  planes: scratch of
+// router_planes_bytes (nullable when that is 0).
 hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, const float* b_r,
-                                float* part, float* logits, int64_t T, int d, int N,
-                                hipStream_t stream, bool reduce_splits = true);
+                                uint16_t* planes, float* part, float* logits, int64_t T, int d,
+                                int N, hipStream_t stream, bool reduce_splits = true);
 
 // Selection, gates and per-block partial statistics on logits + noise.std *
 // (the noise draws), when noise_on(noise):
@@ -66,6 +73,7 @@ hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
 
 // -------------------------------------------------------------- dispatch --
 constexpr int kDispatchTokens = 256;  // tokens per dispatch block
+constexpr int kWalkCounters = 16;     // tile-walk counters of the two grouped GEMMs (8 each)
 int64_t dispatch_num_blocks(int64_t T);
 
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int N, int K,
@@ -96,7 +104,7 @@ struct FfnProblem {
   void* h;          // [(T*K + T_shared), max(F, F_shared)] intermediate
   void* y_perm;     // [T*K, d]
   void* y_shared;   // [T, d]
-  int32_t* tile_base;  // [3 * (N + 2)] scratch: three tile tables
+  int32_t* tile_base;  // [3 * (N + 2) + kWalkCounters] scratch: three tile tables, walk counters
   // nullable, SwiGLU: also store gate(x) = A W1^T and up(x) = A W3^T
   // ([T*K + T_shared, F], shared rows after the routed ones) when the first
   // GEMM runs the ping-pong kernel (ffn_saves_uv)

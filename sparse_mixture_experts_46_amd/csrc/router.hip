@@ -12,6 +12,10 @@
 //     choice), 运行示例 (softmax, top-K on probabilities, divide by their sum).
 //   wmrh.cn explainer ("MoE 的核心思想"): 公式表达重点 (renormalised gates),
 //     Router Z-Loss (penalty on the squares of the router logits).
+#include <type_traits>
+
+#include "host_device.h"
+#include "lds_dma.h"
 #include "moe_common.h"
 #include "moe_internal.h"
 #include "rng.h"
@@ -253,6 +257,206 @@ __global__ __launch_bounds__(256) void router_logits_bf16x3_kernel(
         if (t < T) out[t * N + col] = acc[i][v] + bias;
       }
   }
+}
+
+// ---------------------------------------------- router GEMM, LDS DMA ----
+// The same exact three-part split, done once per call into planes
+// [3][N][d] bf16 (hi, mid, lo), so the logits become a plain bf16 GEMM of x
+// [T, d] against 3N weight rows that the ping-pong scheme of the expert
+// GEMMs can stream:
+//  * 256 tokens x 64 experts per workgroup; its B tile holds the 64 experts'
+//    rows of each plane (192 rows).  8 waves, 64 tokens x 32 experts each:
+//    two token fragments and one fragment per plane, one accumulator per
+//    plane and token fragment; the planes are added in the epilogue.
+//  * Global -> LDS with buffer_load ... lds in 64-wide K blocks (8 rows x
+//    128 bytes per wave instruction), rings of 2 A and 3 B blocks (136 KB),
+//    16-byte chunks swizzled by pp_swz; every 32-wide K sub-step a wave reads
+//    its fragments (memory phase) and runs its 12 MFMAs (compute phase), the
+//    second group of four waves one phase behind the first, so each SIMD
+//    has one wave on the matrix pipe while the other reads LDS.
+//  * blockIdx.z takes an even share of the K blocks; with several shares
+//    each writes fp32 partials [z, T, N] (reduced by
+//    router_split_reduce_kernel), with one the logits plus bias.
+//  * A tile of at most 128 tokens loads and multiplies only its first half.
+constexpr int RG_BM = 256, RG_BE = 64;
+
+__global__ __launch_bounds__(256) void router_split_planes_kernel(
+    const float* __restrict__ w, int64_t n, uint16_t* __restrict__ planes) {
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n;
+       i += (int64_t)gridDim.x * 1024) {
+    const float4 v = *(const float4*)(w + i);
+    uint16_t h0, h1, h2, h3, m0, m1, m2, m3, l0, l1, l2, l3;
+    split3_bf16(v.x, h0, m0, l0);
+    split3_bf16(v.y, h1, m1, l1);
+    split3_bf16(v.z, h2, m2, l2);
+    split3_bf16(v.w, h3, m3, l3);
+    *(uint2*)(planes + i) = make_uint2(pack2(h0, h1), pack2(h2, h3));
+    *(uint2*)(planes + n + i) = make_uint2(pack2(m0, m1), pack2(m2, m3));
+    *(uint2*)(planes + 2 * n + i) = make_uint2(pack2(l0, l1), pack2(l2, l3));
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void router_logits_pp_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
+    const float* __restrict__ b_r, float* __restrict__ out, int64_t T, int d, int N) {
+  constexpr int BM = RG_BM, BE = RG_BE, BN = 3 * BE, WM = 4, WN = 2, NW = 8, DA = 2, DB = 3;
+  constexpr int FM = BM / (WM * 32);                     // token fragments per wave
+  constexpr int LA = BM / (NW * 8), LB = BN / (NW * 8);  // DMA instructions per wave per block
+  constexpr int ASLOT = BM * 128, BSLOT = BN * 128;
+  static_assert(BE % 8 == 0 && WN * 32 == BE, "a DMA instruction's 8 rows are in one plane");
+  extern __shared__ uint4 smem[];
+  char* abuf = (char*)smem;
+  char* bbuf = abuf + DA * ASLOT;
+  const uint4* abuf4 = (const uint4*)abuf;
+  const uint4* bbuf4 = (const uint4*)bbuf;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wm = wave / WN, wn = wave % WN;
+  const int dh = lane >> 5, drow = (lane & 31) >> 2, dch = lane & 3, khalf = lane >> 5;
+  const int64_t t0 = (int64_t)blockIdx.x * BM;
+  const int e0 = blockIdx.y * BE;
+  const int nkb = d / 64;
+  const int kb0 = (int)(((int64_t)blockIdx.z * nkb) / gridDim.z);
+  const int nk = (int)(((int64_t)(blockIdx.z + 1) * nkb) / gridDim.z) - kb0;  // >= 1
+  const int Mt = (int)(T - t0 < BM ? T - t0 : BM);
+
+  int aidx[FM], asw[FM], bidx[3], bsw[3];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = i * (32 * WM) + wm * 32 + (lane & 31);
+    aidx[i] = (r >> 3) * 64 + (r & 7) * 4;
+    asw[i] = pp_swz(r);
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int r = q * BE + wn * 32 + (lane & 31);
+    bidx[q] = (r >> 3) * 64 + (r & 7) * 4;
+    bsw[q] = pp_swz(r);
+  }
+  uint32_t aoff[LA], boff[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int r = (i * NW + wave) * 8 + drow;
+    const int lr = r < Mt ? r : Mt - 1;
+    aoff[i] = (uint32_t)(((t0 + lr) * d + dh * 32 + (dch ^ pp_swz(r)) * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int r = (i * NW + wave) * 8 + drow;
+    const int e = e0 + r % BE < N ? e0 + r % BE : N - 1;
+    boff[i] = (uint32_t)((((int64_t)(r / BE) * N + e) * d + dh * 32 + (dch ^ pp_swz(r)) * 8) * 2);
+  }
+
+  auto run = [&](auto half_c) {
+    constexpr bool HALF = decltype(half_c)::value;
+    constexpr int FMA = HALF ? FM / 2 : FM;
+    constexpr int LAA = HALF ? LA / 2 : LA;
+    auto issue_a = [&](int blk, int slot) {
+      const uint32_t kb = (uint32_t)(kb0 + (blk < nk ? blk : nk - 1)) * 128u;
+      char* st = abuf + slot * ASLOT;
+#pragma unroll
+      for (int i = 0; i < LAA; ++i) buf_dma16(x, aoff[i] + kb, st + (i * NW + wave) * 1024);
+    };
+    auto issue_b = [&](int blk, int slot) {
+      const uint32_t kb = (uint32_t)(kb0 + (blk < nk ? blk : nk - 1)) * 128u;
+      char* st = bbuf + slot * BSLOT;
+#pragma unroll
+      for (int i = 0; i < LB; ++i) buf_dma16(planes, boff[i] + kb, st + (i * NW + wave) * 1024);
+    };
+    f32x16_t acc[3][FMA];
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int i = 0; i < FMA; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[q][i][v] = 0.f;
+    bf16x8_t fa[2][FMA], fb[2][3];
+    auto read_fragments = [&](int sa, int sb, int h) {
+      const uint4* sA = abuf4 + sa * (ASLOT / 16) + h * 32;
+      const uint4* sB = bbuf4 + sb * (BSLOT / 16) + h * 32;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int ch = ks * 2 + khalf;
+#pragma unroll
+        for (int i = 0; i < FMA; ++i) fa[ks][i] = __builtin_bit_cast(bf16x8_t, sA[aidx[i] + (ch ^ asw[i])]);
+#pragma unroll
+        for (int q = 0; q < 3; ++q) fb[ks][q] = __builtin_bit_cast(bf16x8_t, sB[bidx[q] + (ch ^ bsw[q])]);
+      }
+    };
+    auto finish_m_then_compute = [&]() {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+#pragma unroll
+          for (int i = 0; i < FMA; ++i)
+            acc[q][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][q], fa[ks][i], acc[q][i], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    issue_b(0, 0);
+    issue_a(0, 0);
+    issue_b(1, 1);
+    wait_vmcnt<LB>();
+    __syncthreads();
+    if (grp == 1) __builtin_amdgcn_s_barrier();  // the second group runs one phase behind
+    int sa = 0, sb = 0;
+    for (int j = 0; j < nk; ++j) {
+      const int sa1 = sa + 1 == DA ? 0 : sa + 1;
+      const int sb1 = sb + 1 == DB ? 0 : sb + 1;
+      const int sb2 = sb1 + 1 == DB ? 0 : sb1 + 1;
+      read_fragments(sa, sb, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_a(j + 1, sa1);
+      finish_m_then_compute();
+      read_fragments(sa, sb, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_b(j + 2, sb2);
+      wait_vmcnt<LB>();  // this wave's shares of A(j+1) and B(j+1) landed
+      finish_m_then_compute();
+      sa = sa1;
+      sb = sb1;
+    }
+    if (grp == 0) __builtin_amdgcn_s_barrier();
+    wait_vmcnt<0>();
+
+    // 4 consecutive experts per lane and register quad
+    const bool direct = gridDim.z == 1;
+    float* o = out + (direct ? 0 : (int64_t)blockIdx.z * T * N);
+#pragma unroll
+    for (int i = 0; i < FMA; ++i) {
+      const int lr = i * (32 * WM) + wm * 32 + (lane & 31);
+      if (lr >= Mt) continue;
+      float* orow = o + (t0 + lr) * N;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int e = e0 + wn * 32 + 8 * qd + 4 * khalf;
+        float r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int v = 4 * qd + u;
+          r[u] = acc[0][i][v] + acc[1][i][v] + acc[2][i][v];
+          if (direct && b_r && e + u < N) r[u] += b_r[e + u];
+        }
+        if ((N & 3) == 0 && e + 3 < N) {
+          *(float4*)(orow + e) = make_float4(r[0], r[1], r[2], r[3]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (e + u < N) orow[e + u] = r[u];
+        }
+      }
+    }
+  };
+  if (Mt <= BM / 2) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // logits[t, e] = sum_{z = 0, 1, ...} part[z, t, e] + b_r[e] (fixed order).
@@ -639,7 +843,26 @@ int router_tile_m(int64_t T, bool x_bf16) {
   return (x_bf16 && T >= 1024) ? 128 : 64;
 }
 
+bool router_gemm_path(int64_t T, int d, int N, bool x_bf16) {
+  // From 1024 tokens on: below that, writing and re-reading the planes costs
+  // more than the register-staged kernel's fp32 weight reads.  32-bit byte
+  // offsets into x and into the planes.
+  return x_bf16 && T >= 1024 && d % 64 == 0 && (int64_t)2 * T * d < (int64_t(1) << 32) &&
+         (int64_t)6 * N * d < (int64_t(1) << 32);
+}
+
+size_t router_planes_bytes(int64_t T, int d, int N, bool x_bf16) {
+  return router_gemm_path(T, d, N, x_bf16) ? (size_t)6 * N * d : 0;
+}
+
 int router_num_splits(int64_t T, int d, int N, bool x_bf16) {
+  if (router_gemm_path(T, d, N, x_bf16)) {
+    // >= 256 workgroups (one per CU), each at least one 64-wide K block
+    const int64_t tiles = ((T + RG_BM - 1) / RG_BM) * ((N + RG_BE - 1) / RG_BE);
+    int64_t s = (256 + tiles - 1) / tiles;
+    const int64_t max_s = d / 64 < 64 ? d / 64 : 64;
+    return (int)(s < 1 ? 1 : (s > max_s ? max_s : s));
+  }
   // aim for >= 512 workgroups, with at least 128 K elements per split
   const int tm = router_tile_m(T, x_bf16);
   const int64_t tiles = ((T + tm - 1) / tm) * ((N + RT_N - 1) / RT_N);
@@ -652,10 +875,33 @@ int router_num_splits(int64_t T, int d, int N, bool x_bf16) {
 }
 
 hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, const float* b_r,
-                                float* part, float* logits, int64_t T, int d, int N,
-                                hipStream_t stream, bool reduce_splits) {
+                                uint16_t* planes, float* part, float* logits, int64_t T, int d,
+                                int N, hipStream_t stream, bool reduce_splits) {
   static_assert(RB_N == RT_N, "both logit kernels tile experts alike");
   const int ns = router_num_splits(T, d, N, x_bf16);
+  if (router_gemm_path(T, d, N, x_bf16)) {
+    if (!planes) return hipErrorInvalidValue;
+    const int64_t n = (int64_t)N * d;
+    int64_t sb = (n / 4 + 255) / 256;
+    if (sb > 2048) sb = 2048;
+    router_split_planes_kernel<<<(unsigned)sb, 256, 0, stream>>>(w_r, n, planes);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int smem = 2 * RG_BM * 128 + 3 * (3 * RG_BE) * 128;
+    static std::atomic<uint64_t> lds_set{0};
+    e = set_dynamic_lds_once((const void*)router_logits_pp_kernel, smem, lds_set);
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)((T + RG_BM - 1) / RG_BM), (unsigned)((N + RG_BE - 1) / RG_BE),
+              (unsigned)ns);
+    router_logits_pp_kernel<<<grid, 512, smem, stream>>>((const uint16_t*)x, planes, b_r,
+                                                         ns == 1 ? logits : part, T, d, N);
+    e = hipGetLastError();
+    if (e != hipSuccess || ns == 1 || !reduce_splits) return e;
+    int64_t blocks = (T * (int64_t)N + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    router_split_reduce_kernel<<<(unsigned)blocks, 256, 0, stream>>>(part, ns, b_r, logits, T, N);
+    return hipGetLastError();
+  }
   const int tm = router_tile_m(T, x_bf16);
   dim3 grid((unsigned)((T + tm - 1) / tm), (unsigned)((N + RT_N - 1) / RT_N), (unsigned)ns);
   float* out = ns == 1 ? logits : part;

@@ -99,6 +99,15 @@ ROUTER_CASES = [
     # 128-token logit tiles (T >= 1024) with a ragged last token tile and a
     # ragged expert tile
     WL.Workload(name="t1100_n40", T=1100, d=320, N=40, K=3, F=64, seed=14),
+    # the bf16 GEMM path (from 1024 tokens): an odd expert count (element
+    # stores), a router bias added by the kernel (one K split, d = 64) and by
+    # the reduction (several splits), ragged last token tiles of 176 and 20
+    # tokens (half height), and many splits over three expert tiles
+    WL.Workload(name="n30_bias_1split", T=1200, d=64, N=30, K=2, F=64, seed=15,
+                router_bias="uniform", init="uniform"),
+    WL.Workload(name="n37_bias_splits", T=1300, d=256, N=37, K=5, F=64, seed=16,
+                router_bias="uniform", init="uniform"),
+    WL.Workload(name="t1024_n160_splits", T=1024, d=1024, N=160, K=6, F=64, seed=17),
 ]
 
 
@@ -113,10 +122,12 @@ def test_router(w):
     compare_routing(w, o_own, g, w.name, o)
 
 
-def test_router_exact_ties_lower_index():
+@pytest.mark.parametrize("T", [200, 1100])
+def test_router_exact_ties_lower_index(T):
     """Duplicate router rows give bit-identical logits on both sides; the
-    lower expert index must win on the GPU exactly as in the oracle."""
-    w = WL.Workload(name="ties", T=200, d=128, N=16, K=3, F=64, seed=13)
+    lower expert index must win on the GPU exactly as in the oracle (200
+    tokens: the register-staged logits kernel; 1100: the GEMM path)."""
+    w = WL.Workload(name="ties", T=T, d=128, N=16, K=3, F=64, seed=13)
     say("router ties")
     inp = gpu_inputs(w)
     wr = inp["w_r"].clone()
