@@ -59,20 +59,22 @@ hipError_t run_pingpong(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Decode sizes: one workgroup per 16-row x 64-column tile (the tile table is
-// built with those dims), up to 16 workgroups per CU; bf16 or INT8 weights.
+// Decode sizes: one workgroup per 16-row x 16 kDecodeWaves-column tile (the
+// tile table is built with those dims), up to 64 waves' worth of workgroups
+// per CU; bf16, INT8 or INT4 weights.
 template <bool DUAL, int EPI>
 hipError_t run_decode(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   int64_t grid = max_tiles;
-  const int64_t cap = (int64_t)num_cus() * 16;
+  const int64_t cap = (int64_t)num_cus() * (64 / kDecodeWaves);
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
+  constexpr int nt = 64 * kDecodeWaves;
   if (a.qbits == 4)
-    gemm_decode_q4_kernel<DUAL, EPI><<<(unsigned)grid, 256, 0, s>>>(a);
+    gemm_decode_q4_kernel<DUAL, EPI><<<(unsigned)grid, nt, 0, s>>>(a);
   else if (a.qbits == 8)
-    gemm_decode_kernel<DUAL, EPI, true><<<(unsigned)grid, 256, 0, s>>>(a);
+    gemm_decode_kernel<DUAL, EPI, true><<<(unsigned)grid, nt, 0, s>>>(a);
   else
-    gemm_decode_kernel<DUAL, EPI, false><<<(unsigned)grid, 256, 0, s>>>(a);
+    gemm_decode_kernel<DUAL, EPI, false><<<(unsigned)grid, nt, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -95,7 +97,7 @@ Kind pick_kind(double rows_per_expert) {
 // (BM, BN) per kind; BNo = BN/2 for the dual (SwiGLU gate/up) GEMM.
 void kind_dims(Kind k, bool dual, int* bm, int* bno) {
   switch (k) {
-    case K_DECODE: *bm = 16; *bno = 64; return;
+    case K_DECODE: *bm = 16; *bno = 16 * kDecodeWaves; return;
     case K_SMALL:  *bm = 64; *bno = dual ? 128 : 256; return;
     case K_MID:    *bm = 128; *bno = dual ? 128 : 256; return;
     case K_TAIL:   *bm = 32; *bno = dual ? 32 : 64; return;

@@ -7,8 +7,8 @@
 // (v_mfma_f32_16x16x32_bf16) accumulate x * q in fp32 and the epilogue
 // multiplies by s.
 //
-//  * A block owns one 16-row tile and 64 output columns; each of its 4 waves
-//    computes 16 of those columns.
+//  * A block owns one 16-row tile and 16 kDecodeWaves output columns; each
+//    of its waves computes 16 of those columns.
 //  * The block's 16 activation rows are staged in LDS 512 K-columns at a
 //    time by DMA (buffer_load ... lds, one 1 KB row per instruction, rows
 //    16 bytes apart so the fragment reads of 16 rows hit 16 distinct bank
@@ -32,6 +32,9 @@
 
 namespace moe {
 
+// Waves per decode workgroup; a tile is 16 rows x 16 kDecodeWaves columns.
+constexpr int kDecodeWaves = 4;
+
 // int8 codes (|q| <= 127) to bf16, exactly: 8 codes packed in two words.
 __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
   bf16x8_t r;
@@ -46,7 +49,8 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
 }
 
 template <bool DUAL, int EPI, bool Q8>
-__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(GemmArgs p) {
+  constexpr int NWV = kDecodeWaves, RPW = 16 / NWV, BNC = 16 * NWV;
   constexpr int KC = 512;          // K columns per staged activation chunk
   constexpr int RB = KC * 2 + 16;  // LDS bytes per staged activation row
   constexpr int BPB = Q8 ? 1 : 2;  // 16-byte weight loads per lane per 64-wide block
@@ -59,16 +63,16 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
   const int total = p.tile_base[p.G];
   const int row = lane & 15, part = lane >> 4;
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const TileInfo ti = resolve_tile(p, tile, 16, 64);
+    const TileInfo ti = resolve_tile(p, tile, 16, BNC);
     const int64_t Kd = p.Kdim;
     const int nblk = (int)(Kd / 64);               // 64-wide blocks in K
     const int nstage = (nblk + SB - 1) / SB;
     const uint32_t row_bytes = (uint32_t)Kd * 2;
-    // wave w stages activation rows 4w .. 4w+3 of the tile
-    const char* arow_ptr[4];
+    // wave w stages activation rows RPW w .. RPW w + RPW - 1 of the tile
+    const char* arow_ptr[RPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int lr = ti.mt * 16 + wave * 4 + i;
+    for (int i = 0; i < RPW; ++i) {
+      int lr = ti.mt * 16 + wave * RPW + i;
       if (lr >= ti.M) lr = ti.M - 1;
       int64_t ar;
       if (ti.shared) ar = ti.row0 + lr;
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
       }
       arow_ptr[i] = (const char*)((ti.shared ? p.a_shared : p.a) + ar * p.lda);
     }
-    int n = ti.nt * 64 + wave * 16 + row;
+    int n = ti.nt * BNC + wave * 16 + row;
     if (n >= ti.Nout) n = ti.Nout - 1;
     const int64_t wrow = ((ti.shared ? 0 : (int64_t)ti.g * p.b_stride) + (int64_t)n * Kd + part * 16) * ESZ;
     const char* pb0 = (const char*)(ti.shared ? (const void*)p.bs0 : (const void*)p.b0) + wrow;
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
       uint32_t koff = (uint32_t)c * KC * 2 + (uint32_t)lane * 16;
       if (koff > row_bytes - 16) koff = row_bytes - 16;  // past K: a valid, unused 16 bytes
 #pragma unroll
-      for (int i = 0; i < 4; ++i) buf_dma16(arow_ptr[i], koff, abuf[buf] + (wave * 4 + i) * RB);
+      for (int i = 0; i < RPW; ++i) buf_dma16(arow_ptr[i], koff, abuf[buf] + (wave * RPW + i) * RB);
     };
     uint4 b0[2][SB * BPB], b1[2][SB * BPB];
     auto issue_b = [&](int st, int set) {
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
       }
     };
 
-    constexpr int NA = 4;  // activation DMA instructions per wave per chunk
+    constexpr int NA = RPW;  // activation DMA instructions per wave per chunk
     issue_a(0, 0);
     issue_b(0, 0);
     for (int st = 0; st < nstage; ++st) {
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
     __syncthreads();  // the last buffer is read before the next tile stages into it
 
     // D layout (16x16): col = lane % 16, row = 4 * (lane / 16) + v
-    const int col = ti.nt * 64 + wave * 16 + (lane & 15);
+    const int col = ti.nt * BNC + wave * 16 + (lane & 15);
     if (col < ti.Nout) {
       uint16_t* cbase = ti.shared ? p.c_shared : p.c;
       float s0 = 1.f, s1 = 1.f;  // bf16 weights carry no scales
@@ -223,7 +227,8 @@ __device__ __forceinline__ bf16x8_t q4_word_to_bf16(uint32_t w) {
 }
 
 template <bool DUAL, int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_decode_q4_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_decode_q4_kernel(GemmArgs p) {
+  constexpr int NWV = kDecodeWaves, RPW = 16 / NWV, BNC = 16 * NWV;
   constexpr int KC = 512;          // K columns per staged activation chunk
   constexpr int RB = KC * 2 + 16;  // LDS bytes per staged activation row
   constexpr int SG = KC / 128;     // 128-wide groups per weight stage (one stage per chunk)
@@ -235,15 +240,15 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_q4_kernel(GemmArgs p) {
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
                                                                 0x3F803F80u, 0x3F803F80u));
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const TileInfo ti = resolve_tile(p, tile, 16, 64);
+    const TileInfo ti = resolve_tile(p, tile, 16, BNC);
     const int64_t Kd = p.Kdim;
     const int ngrp = (int)(Kd / 128);
     const int nstage = (ngrp + SG - 1) / SG;
     const uint32_t row_bytes = (uint32_t)Kd * 2;
-    const char* arow_ptr[4];
+    const char* arow_ptr[RPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int lr = ti.mt * 16 + wave * 4 + i;
+    for (int i = 0; i < RPW; ++i) {
+      int lr = ti.mt * 16 + wave * RPW + i;
       if (lr >= ti.M) lr = ti.M - 1;
       int64_t ar;
       if (ti.shared) ar = ti.row0 + lr;
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_q4_kernel(GemmArgs p) {
       }
       arow_ptr[i] = (const char*)((ti.shared ? p.a_shared : p.a) + ar * p.lda);
     }
-    int n = ti.nt * 64 + wave * 16 + row;
+    int n = ti.nt * BNC + wave * 16 + row;
     if (n >= ti.Nout) n = ti.Nout - 1;
     // codes: b_stride weights per routed group, two per byte
     const int64_t wrow = ((ti.shared ? 0 : (int64_t)ti.g * p.b_stride) + (int64_t)n * Kd) / 2 +
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_q4_kernel(GemmArgs p) {
       uint32_t koff = (uint32_t)c * KC * 2 + (uint32_t)lane * 16;
       if (koff > row_bytes - 16) koff = row_bytes - 16;  // past K: a valid, unused 16 bytes
 #pragma unroll
-      for (int i = 0; i < 4; ++i) buf_dma16(arow_ptr[i], koff, abuf[buf] + (wave * 4 + i) * RB);
+      for (int i = 0; i < RPW; ++i) buf_dma16(arow_ptr[i], koff, abuf[buf] + (wave * RPW + i) * RB);
     };
     // codes two stages ahead (three sets), scales one stage ahead (two)
     uint4 b0[3][SG], b1[3][SG];
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void gemm_decode_q4_kernel(GemmArgs p) {
     __syncthreads();  // the last buffer is read before the next tile stages into it
 
     // D layout (16x16): col = lane % 16, row = 4 * (lane / 16) + v
-    const int col = ti.nt * 64 + wave * 16 + (lane & 15);
+    const int col = ti.nt * BNC + wave * 16 + (lane & 15);
     if (col < ti.Nout) {
       uint16_t* cbase = ti.shared ? p.c_shared : p.c;
       float bias = 0.f;

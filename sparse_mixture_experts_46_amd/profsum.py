@@ -22,6 +22,7 @@ import argparse
 import bisect
 import csv
 import glob
+import gzip
 import hashlib
 import json
 import os
@@ -71,14 +72,18 @@ def stage_of(kernel: str):
 
 
 def one(pattern):
+    """The first file matching pattern, or pattern + ".gz", opened as text."""
     f = glob.glob(pattern, recursive=True)
-    if not f:
-        raise FileNotFoundError(pattern)
-    return f[0]
+    if f:
+        return open(f[0])
+    f = glob.glob(pattern + ".gz", recursive=True)
+    if f:
+        return gzip.open(f[0], "rt")
+    raise FileNotFoundError(pattern)
 
 
 def stats_table(trace_dir):
-    rows = list(csv.DictReader(open(one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
+    rows = list(csv.DictReader(one(os.path.join(trace_dir, "**", "*kernel_stats.csv"))))
     out = []
     for r in rows:
         out.append((short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
@@ -102,7 +107,7 @@ def sectioned(rows, value):
 
 
 def trace_durations(trace_dir):
-    rows = list(csv.DictReader(open(one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))))
+    rows = list(csv.DictReader(one(os.path.join(trace_dir, "**", "*kernel_trace.csv"))))
     return sectioned(rows, lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
 
 
@@ -110,7 +115,7 @@ def pmc_values(pmc_dirs):
     """({counter: {(kernel, section): [value per launch]}}, {counter: probe value})."""
     vals, probe = {}, {}
     for d in pmc_dirs:
-        rows = list(csv.DictReader(open(one(os.path.join(d, "**", "*counter_collection.csv")))))
+        rows = list(csv.DictReader(one(os.path.join(d, "**", "*counter_collection.csv"))))
         for c in sorted({r["Counter_Name"] for r in rows}):
             rc = [r for r in rows if r["Counter_Name"] == c]
             p = [float(r["Counter_Value"]) for r in rc if short(r["Kernel_Name"]) == PROBE]
@@ -215,6 +220,21 @@ def main():
                                           "fetch_bytes": fb, "write_bytes": wb,
                                           "clock_ghz": clk, "mfma_busy": util,
                                           "executed_flops": xfl}
+    known = {"FETCH_SIZE", "WRITE_SIZE", "GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES",
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CYCLES"}
+    other = sorted(c for c in vals if c not in known)
+    if other:
+        lines += ["", "## Other counters (average per launch, summed over the chip)", "",
+                  "| part | kernel | " + " | ".join(other) + " |",
+                  "|---|---|" + "---|" * len(other)]
+        for ks in keys:
+            if not any(vals[c].get(ks) for c in other):
+                continue
+            cells = []
+            for c in other:
+                v = vals[c].get(ks)
+                cells.append(f"{sum(v) / len(v):.4g}" if v else "")
+            lines.append(f"| {secname(ks[1])} | `{ks[0]}` | " + " | ".join(cells) + " |")
     open(os.path.join(a.out, f"kernels_{a.workload}.md"), "w").write("\n".join(lines) + "\n")
     if rec["stages"]:
         json.dump(rec, open(os.path.join(a.out, f"counters_{a.workload}.json"), "w"), indent=1)
