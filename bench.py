@@ -233,6 +233,26 @@ def run_workload(w, steps, warmup, ev, quant=None):
     return res
 
 
+def kernel_rooflines(w, rd, quant=None):
+    """Each grouped GEMM's roofline from a run_workload result (the tail
+    launch, when there is one, counted with the second GEMM; an fp32 layer's
+    one FFN kernel covers both GEMMs), with its counter-measured traffic
+    where profiles/ holds it, and the dominant one's name."""
+    sw = stage_work(w, rd["kept_rows"], rd["touched"], quant)
+    st = {k: float(v) for k, v in zip(STAGES, rd["stage_ms"])}
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    if w.dtype == "bf16":
+        kernels = {"gemm1": roofline_of(*sw["gemm1"], st["gemm1"], peak),
+                   "gemm2": roofline_of(*sw["gemm2"], st["gemm2_main"] + st["gemm2_tail"], peak)}
+    else:
+        f = sw["gemm1"][0] + sw["gemm2"][0]
+        b = sw["gemm1"][1] + sw["gemm2"][1]
+        kernels = {"ffn_f32": roofline_of(f, b, st["gemm1"], peak)}
+    for k in kernels:
+        kernels[k]["traffic"] = traffic_of(w.name, quant or "bf16", k)
+    return kernels, max(kernels, key=lambda k: kernels[k]["ms"]), sw, st, peak
+
+
 def layer_record(w, steps, warmup, ev, quant=None, cpu=None):
     """One layer shape: graph-replayed step time, per-stage times, the step's
     position against both rooflines, each grouped GEMM's roofline (the
@@ -240,20 +260,7 @@ def layer_record(w, steps, warmup, ev, quant=None, cpu=None):
     arguments), the oracle's rate on a bounded sample of the same inputs."""
     rd = run_workload(w, steps, warmup, ev, quant=quant)
     ms = rd["wall_graph"] * 1e3 / steps
-    sw = stage_work(w, rd["kept_rows"], rd["touched"], quant)
-    st = {k: float(v) for k, v in zip(STAGES, rd["stage_ms"])}
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    if w.dtype == "bf16":
-        # the tail launch (when there is one) is part of the second GEMM
-        kernels = {"gemm1": roofline_of(*sw["gemm1"], st["gemm1"], peak),
-                   "gemm2": roofline_of(*sw["gemm2"], st["gemm2_main"] + st["gemm2_tail"], peak)}
-    else:  # one fp32 FFN kernel covers both GEMMs
-        f = sw["gemm1"][0] + sw["gemm2"][0]
-        b = sw["gemm1"][1] + sw["gemm2"][1]
-        kernels = {"ffn_f32": roofline_of(f, b, st["gemm1"], peak)}
-    for k in kernels:
-        kernels[k]["traffic"] = traffic_of(w.name, quant or "bf16", k)
-    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    kernels, dom, sw, st, peak = kernel_rooflines(w, rd, quant)
     rec = {"workload": w.name, "desc": w.desc, "T": w.T, "dtype": w.dtype,
            "weights": {"int8": "int8 + fp32 row scales",
                        "int4": "int4 + fp32 scales per 128 inputs"}.get(quant, w.dtype),
@@ -523,15 +530,16 @@ def cpu_baseline(w, inp, sample, seeded=False, repeats=1):
 def counter_record(name, weights, stage):
     """The committed rocprofv3 counter summary of one grouped-GEMM stage
     ("gemm1" / "gemm2") of a workload with bf16, INT8 or INT4 weights, or
-    None when there is none or the GEMM source changed since it was taken."""
+    None when there is none or its kernel's sources changed since it was
+    taken."""
     p = os.path.join(ROOT, "profiles", f"counters_{name}.json")
     if not os.path.exists(p):
         return None
-    rec = json.load(open(p))
-    from sparse_mixture_experts_46_amd.profsum import gemm_source_sha256
-    if rec.get("gemm_source_sha256") != gemm_source_sha256():
+    st = json.load(open(p))["stages"].get(f"{weights}:{stage}")
+    from sparse_mixture_experts_46_amd.profsum import family_of, source_sha256
+    if not st or st.get("source_sha256") != source_sha256(family_of(st["kernel"])):
         return None
-    return rec["stages"].get(f"{weights}:{stage}")
+    return st
 
 
 def traffic_of(name, weights, stage):
@@ -565,9 +573,12 @@ def main():
     ms = r["wall_graph"] * 1e3 / a.steps  # graph-launched steps
     ms_eager = r["wall"] * 1e3 / a.steps
     tok_s = w.T / (ms / 1e3)
-    g1_ms = float(r["stage_ms"][2])
-    g1_tflops = r["g1_flops"] / (g1_ms * 1e-3) / 1e12
-    traffic = traffic_of(w.name, "bf16", "gemm1")
+    kernels, dom, _sw, _st, _peak = kernel_rooflines(w, r)
+    names = {"gemm1": "grouped GEMM 1 (gate/up + SiLU*mul)" if w.act == "swiglu"
+             else "grouped GEMM 1 (+ GELU)", "gemm2": "grouped GEMM 2 (down projection)",
+             "ffn_f32": "fp32 expert FFN (both GEMMs)"}
+    rf = dict(kernels[dom], kernel=names[dom], avg_ms=kernels[dom]["ms"],
+              flops_per_launch=kernels[dom]["flops"], bytes_per_launch=kernels[dom]["bytes"])
     line = {
         "metric": METRIC,
         "value": tok_s,
@@ -586,10 +597,8 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "K": w.K, "F": w.F,
                    "F_shared": w.F_shared, "act": w.act, "capacity_factor": w.cf,
                    "router": "fp32", "desc": w.desc},
-        "roofline": {"bound": "mfma", "kernel": "grouped GEMM 1 (gate/up + SiLU*mul)",
-                     "achieved": g1_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": g1_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "avg_ms": g1_ms, "flops_per_launch": r["g1_flops"]},
+        "roofline": rf,
+        "kernels": kernels,
         "active_tflops": r["total_flops"] / (ms * 1e-3) / 1e12,
         "active_frac_of_bf16_peak": r["total_flops"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "weight_gbs": r["wbytes"] / (ms * 1e-3) / 1e9,

@@ -14,7 +14,8 @@
 Writes <out>/kernels_<workload>.md (trace statistics, counters per kernel) and
 <out>/counters_<workload>.json: per grouped-GEMM stage ("bf16:gemm1",
 "int8:gemm2", ...) of the first section, the launches, the trace's average
-duration and the counters per launch, tied to the SHA-256 of the GEMM sources.
+duration and the counters per launch, each tied to the SHA-256 of the sources
+of its kernel family (the prefill DMA kernels, or the decode kernels).
 """
 from __future__ import annotations
 
@@ -29,16 +30,25 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-GEMM_SRCS = ["gemm_bf16.hip", "gemm_common.h", "gemm_pingpong.h", "gemm_tile.h", "gemm_decode.h"]
+# the sources each family of grouped-GEMM kernels is built from (its
+# counter figures go stale when any of them changes)
+FAMILY_SRCS = {
+    "prefill": ["gemm_bf16.hip", "gemm_common.h", "gemm_pingpong.h", "gemm_tile.h", "lds_dma.h"],
+    "decode": ["gemm_bf16.hip", "gemm_common.h", "gemm_decode.h", "lds_dma.h"],
+}
 PROBE = "torch neg (copy probe)"
 N_SIMD = 256 * 4  # MI355X: 256 compute units of 4 SIMDs
+N_XCD = 8         # GRBM_GUI_ACTIVE is summed over the 8 XCDs
 
 
-def gemm_source_sha256() -> str:
-    """SHA-256 over the grouped-GEMM sources (counter figures go stale when
-    any of them changes)."""
+def family_of(kernel: str) -> str:
+    return "decode" if "gemm_decode" in kernel else "prefill"
+
+
+def source_sha256(family: str) -> str:
+    """SHA-256 over the sources of one kernel family."""
     h = hashlib.sha256()
-    for f in GEMM_SRCS:
+    for f in FAMILY_SRCS[family]:
         h.update(open(os.path.join(PKG, "csrc", f), "rb").read())
     return h.hexdigest()
 
@@ -169,8 +179,7 @@ def main():
                   "| stage | ms |", "|---|---|"]
         lines += [f"| {k} | {v:.4f} |" for k, v in bench["stage_ms"].items()]
 
-    rec = {"workload": a.workload, "gemm_source_sha256": gemm_source_sha256(),
-           "cmd": a.cmd.strip(), "stages": {}}
+    rec = {"workload": a.workload, "cmd": a.cmd.strip(), "stages": {}}
     vals, probe = pmc_values(a.pmc) if a.pmc else ({}, {})
     probe_bytes = a.probe_mib * (1 << 20)
     scale = {c: probe_bytes / (probe[c] * 1024.0) for c in ("FETCH_SIZE", "WRITE_SIZE")
@@ -183,8 +192,9 @@ def main():
                       + "; ".join(f"{c} read {probe[c]:.0f} KiB (bytes = KiB x 1024 x "
                                   f"{scale[c]:.3f})" for c in scale) + ".", ""]
         if "GRBM_GUI_ACTIVE" in vals:
-            lines += ["clock = GRBM_GUI_ACTIVE / trace duration; MFMA busy = "
-                      "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs); executed "
+            lines += ["clock = GRBM_GUI_ACTIVE / 8 XCDs / trace duration (for launches of a few "
+                      "us it includes the dispatch around the kernel); MFMA busy = "
+                      "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); executed "
                       "flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.", ""]
         lines += ["| part | kernel | launches | avg us | fetch MB | write MB | clock GHz | "
                   "MFMA busy | executed TFLOP |", "|---|---|---|---|---|---|---|---|---|"]
@@ -201,8 +211,8 @@ def main():
             wb = w * 1024 * scale["WRITE_SIZE"] if w is not None and "WRITE_SIZE" in scale else None
             gui, busy = avg("GRBM_GUI_ACTIVE", ks), avg("SQ_VALU_MFMA_BUSY_CYCLES", ks)
             mops = avg("SQ_INSTS_VALU_MFMA_MOPS_BF16", ks)
-            clk = gui / (us * 1e3) if gui else None
-            util = busy / (gui * N_SIMD) if gui and busy is not None else None
+            clk = gui / N_XCD / (us * 1e3) if gui else None
+            util = busy / (gui / N_XCD * N_SIMD) if gui and busy is not None else None
             xfl = mops * 512 if mops is not None else None
 
             def fmt(x, p):
@@ -216,7 +226,8 @@ def main():
                 key = f"{st[0]}:{st[1]}"
                 prev = rec["stages"].get(key)
                 if prev is None or prev["avg_us"] * prev["launches"] < us * len(dur[ks]):
-                    rec["stages"][key] = {"kernel": k, "launches": len(dur[ks]), "avg_us": us,
+                    rec["stages"][key] = {"kernel": k, "source_sha256": source_sha256(family_of(k)),
+                                          "launches": len(dur[ks]), "avg_us": us,
                                           "fetch_bytes": fb, "write_bytes": wb,
                                           "clock_ghz": clk, "mfma_busy": util,
                                           "executed_flops": xfl}
