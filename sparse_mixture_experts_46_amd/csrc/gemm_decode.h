@@ -209,7 +209,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(GemmArgs
 //    both operands);
 //  * ((word >> 4i) & 0x000F000F) | 0x43004300 is the bf16 pair (128 + u, 128
 //    + u') of two codes, so a word becomes a bf16 fragment of w' = q + 136 in
-//    7 integer instructions;
+//    7 integer instructions (3 shifts and 4 v_and_or_b32);
 //  * per group the MFMAs give sum x w' and, against a fragment of ones,
 //    S = sum x; the group adds s * (sum x w' - 136 S) = s * sum x q to the
 //    fp32 output (every product is exact, the sums are fp32);
@@ -217,12 +217,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(GemmArgs
 //    the weights are fetched two stages ahead (three register sets) to keep
 //    as many bytes in flight; every stage issues the same loads (indices
 //    clamped inside the row), which keeps the wait counts exact.
-__device__ __forceinline__ bf16x8_t q4_word_to_bf16(uint32_t w) {
+// magic = 0x43004300 in a register the compiler cannot fold: (x & mask) |
+// magic then selects one v_and_or_b32 with the mask in an SGPR (a gfx9 VOP3
+// instruction takes at most one SGPR or literal, so with both constants
+// literal it is split into v_and_b32 and v_or_b32).
+__device__ __forceinline__ uint32_t q4_magic() {
+  uint32_t m;
+  asm("v_mov_b32 %0, 0x43004300" : "=v"(m));
+  return m;
+}
+__device__ __forceinline__ bf16x8_t q4_word_to_bf16(uint32_t w, uint32_t magic) {
   uint4 r;
-  r.x = (w & 0x000F000Fu) | 0x43004300u;
-  r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  r.x = (w & 0x000F000Fu) | magic;
+  r.y = ((w >> 4) & 0x000F000Fu) | magic;
+  r.z = ((w >> 8) & 0x000F000Fu) | magic;
+  r.w = ((w >> 12) & 0x000F000Fu) | magic;
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
@@ -239,6 +248,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_deco
   const int row = lane & 15, part = lane >> 4;
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
                                                                 0x3F803F80u, 0x3F803F80u));
+  const uint32_t magic = q4_magic();
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const TileInfo ti = resolve_tile(p, tile, 16, BNC);
     const int64_t Kd = p.Kdim;
@@ -315,8 +325,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_deco
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, *(const uint4*)(arow_l + j * 256 + m * 16));
-            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, q4_word_to_bf16(w0[m]), a0, 0, 0, 0);
-            if (DUAL) a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, q4_word_to_bf16(w1[m]), a1, 0, 0, 0);
+            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, q4_word_to_bf16(w0[m], magic), a0, 0, 0, 0);
+            if (DUAL) a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, q4_word_to_bf16(w1[m], magic), a1, 0, 0, 0);
             sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, ones, sx, 0, 0, 0);
           }
 #pragma unroll
@@ -356,6 +366,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_deco
         else issue_b(st + 2, 2);
       }
       __builtin_amdgcn_sched_barrier(0);
+      // (a copy of the stage without the per-group tests, for full stages,
+      // measured slower: the second GEMM's kernel lost a wave per SIMD)
       const int set = st % 3, sset = st & 1;
       if (set == 0) {
         if (sset) compute(st, st & 1, 0, 1); else compute(st, st & 1, 0, 0);
