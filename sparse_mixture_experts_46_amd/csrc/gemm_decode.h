@@ -16,7 +16,7 @@
 //    once from LDS instead of each wave loading them from L2.
 //  * Each wave streams only its 16 weight rows into registers (per lane and
 //    64-wide K block: 16 bytes of int8 codes, or 32 bytes of bf16) in stages
-//    of 8 blocks (int8) or 4 blocks (bf16), double-buffered, so the next
+//    of 4 blocks (8 for INT8 with one weight matrix), double-buffered, so the next
 //    stage's weights are in flight while the current one is multiplied.
 //    Each stage's weights are issued before the next activation chunk, so
 //    waiting for them does not wait for that chunk.
@@ -54,7 +54,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(GemmArgs
   constexpr int KC = 512;          // K columns per staged activation chunk
   constexpr int RB = KC * 2 + 16;  // LDS bytes per staged activation row
   constexpr int BPB = Q8 ? 1 : 2;  // 16-byte weight loads per lane per 64-wide block
-  constexpr int SB = Q8 ? 8 : 4;   // 64-wide blocks per weight stage
+  // 64-wide blocks per weight stage: INT8 with one weight matrix takes 8,
+  // with two (gate and up) 4 (measured: 8-block stages held the dual INT8
+  // kernel to one sync-and-wait per activation chunk, 1.58 ms against 1.44
+  // on the DeepSeek-shaped decode; the single-matrix kernel is 3 % faster
+  // with 8)
+  constexpr int SB = (Q8 && !DUAL) ? 8 : 4;
   constexpr int SPC = (KC / 64) / SB;  // weight stages per activation chunk
   constexpr int ESZ = Q8 ? 1 : 2;  // weight element bytes
   __shared__ __attribute__((aligned(16))) char abuf[2][16 * RB];
