@@ -249,10 +249,16 @@ moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void
                             c->bias_rate, s);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
+  // the K-split partials are added by the top-K kernel from 1024 tokens on,
+  // else by a reduction of their own
+  const int ns = router_num_splits(c->T, c->d, c->N, bf16);
+  const bool fused = router_topk_adds_splits(c->T, ns);
   hipError_t e = launch_router_logits(x, bf16, w->w_r, w->b_r, at<uint16_t>(ws, L.planes),
-                                      at<float>(ws, L.split), lg, c->T, c->d, c->N, s);
+                                      at<float>(ws, L.split), lg, c->T, c->d, c->N, s,
+                                      /*reduce_splits=*/!fused);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_router_topk(lg, router_noise(c, w), w->b_sel, idx, gate, at<float>(ws, L.part_p),
+  e = launch_router_topk(lg, at<float>(ws, L.split), fused ? ns : 1,
+                         w->b_r, router_noise(c, w), w->b_sel, idx, gate, at<float>(ws, L.part_p),
                          at<int32_t>(ws, L.part_cnt), at<float>(ws, L.part_z), c->T, c->N, c->K,
                          c->gate, s);
   if (e != hipSuccess) return MOE_ERR_HIP;

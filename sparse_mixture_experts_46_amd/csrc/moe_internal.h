@@ -32,22 +32,31 @@ bool router_gemm_path(int64_t T, int d, int N, bool x_bf16);
 size_t router_planes_bytes(int64_t T, int d, int N, bool x_bf16);
 
 // logits = x W_r^T + b_r.  With several K splits the partial products go to
-// part [splits, T, N] and (reduce_splits) a reduction writes logits; with one
-// split the logits are written directly (part unused).  planes: scratch of
-// router_planes_bytes (nullable when that is 0).
+// part [splits, T, N] and (reduce_splits) a reduction writes logits;
+// otherwise a top-K kernel adds them.  With one split the logits are written
+// directly (part unused).  planes: scratch of router_planes_bytes (nullable
+// when that is 0).
 hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, const float* b_r,
                                 uint16_t* planes, float* part, float* logits, int64_t T, int d,
-                                int N, hipStream_t stream, bool reduce_splits = true);
+                                int N, hipStream_t stream, bool reduce_splits);
+
+// Whether router_topk_kernel adds the K splits itself (from 1024 tokens:
+// with fewer, one wave per token adding many splits is latency-bound, and
+// the separate reduction spreads them wider).
+bool router_topk_adds_splits(int64_t T, int nsplit);
 
 // Selection, gates and per-block partial statistics on logits + noise.std *
 // (the noise draws), when noise_on(noise):
 //   part_p [nblk, N] fp32, part_cnt [nblk, N] int32,
 //   part_z [nblk, 3] fp32 (sum of squared logits, of squared log-sum-exp, of
 //   routing entropy)
-hipError_t launch_router_topk(const float* logits, const RouterNoise& noise,
-                              const float* b_sel, int32_t* idx, float* gate, float* part_p,
-                              int32_t* part_cnt, float* part_z, int64_t T, int N, int K,
-                              int gate_mode, hipStream_t stream);
+// With nsplit > 1 the logits are first reduced from the K-split partials
+// part (launch_router_logits without its reduction) plus b_r and written to
+// logits; with nsplit == 1 logits holds them already.
+hipError_t launch_router_topk(float* logits, const float* part, int nsplit, const float* b_r,
+                              const RouterNoise& noise, const float* b_sel, int32_t* idx,
+                              float* gate, float* part_p, int32_t* part_cnt, float* part_z,
+                              int64_t T, int N, int K, int gate_mode, hipStream_t stream);
 
 // Small batches (router_small_path): one workgroup reduces the logit splits
 // (part from launch_router_logits without its reduction; nsplit =

@@ -275,8 +275,8 @@ __global__ __launch_bounds__(256) void router_logits_bf16x3_kernel(
 //    second group of four waves one phase behind the first, so each SIMD
 //    has one wave on the matrix pipe while the other reads LDS.
 //  * blockIdx.z takes an even share of the K blocks; with several shares
-//    each writes fp32 partials [z, T, N] (reduced by
-//    router_split_reduce_kernel), with one the logits plus bias.
+//    each writes fp32 partials [z, T, N] (added in split order by the top-K
+//    kernel or router_split_reduce_kernel), with one the logits plus bias.
 //  * A tile of at most 128 tokens loads and multiplies only its first half.
 constexpr int RG_BM = 256, RG_BE = 64;
 
@@ -459,7 +459,9 @@ __global__ __launch_bounds__(512, 1) void router_logits_pp_kernel(
   else run(std::false_type{});
 }
 
-// logits[t, e] = sum_{z = 0, 1, ...} part[z, t, e] + b_r[e] (fixed order).
+
+// logits[t, e] = sum_{z = 0, 1, ...} part[z, t, e] + b_r[e] (fixed order): the
+// batches whose top-K kernel does not add the splits itself.
 __global__ __launch_bounds__(256) void router_split_reduce_kernel(
     const float* __restrict__ part, int nsplit, const float* __restrict__ b_r,
     float* __restrict__ logits, int64_t T, int N) {
@@ -482,6 +484,51 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave reductions through DPP (no LDS round trip): within each row of 16
+// lanes, quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror and row_mirror
+// leave every lane with its row's result; row_bcast15 (into rows 1 and 3)
+// and row_bcast31 (into rows 2 and 3) then carry rows 0-2 into row 3, and
+// lane 63 is read into every lane.  The order of combination is fixed, so
+// a sum is deterministic.  Lanes a broadcast step leaves out combine the
+// identity.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ uint32_t dpp_src(uint32_t v, uint32_t ident) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, RMASK, 0xF, false);
+}
+#define MOE_DPP_REDUCE(V, IDENT, OP)                                   \
+  do {                                                                 \
+    V = OP(V, (dpp_src<0xB1, 0xF>(V, IDENT)));                          \
+    V = OP(V, (dpp_src<0x4E, 0xF>(V, IDENT)));                          \
+    V = OP(V, (dpp_src<0x141, 0xF>(V, IDENT)));                         \
+    V = OP(V, (dpp_src<0x140, 0xF>(V, IDENT)));                         \
+    V = OP(V, (dpp_src<0x142, 0xA>(V, IDENT)));                         \
+    V = OP(V, (dpp_src<0x143, 0xC>(V, IDENT)));                         \
+    V = (uint32_t)__builtin_amdgcn_readlane((int)V, 63);               \
+  } while (0)
+
+__device__ __forceinline__ uint32_t umax_op(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t fmax_op(uint32_t a, uint32_t b) {
+  return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+}
+__device__ __forceinline__ uint32_t fadd_op(uint32_t a, uint32_t b) {
+  return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+}
+__device__ __forceinline__ uint32_t wave_umax_dpp(uint32_t v) {
+  MOE_DPP_REDUCE(v, 0u, umax_op);
+  return v;
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  uint32_t v = __float_as_uint(x);
+  MOE_DPP_REDUCE(v, 0xff800000u, fmax_op);  // identity -inf
+  return __uint_as_float(v);
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  uint32_t v = __float_as_uint(x);
+  MOE_DPP_REDUCE(v, 0u, fadd_op);
+  return __uint_as_float(v);
+}
+#undef MOE_DPP_REDUCE
+
 // One token's softmax statistics, top-K selection and gates, computed by
 // one wave: lane l holds the logits of experts l, l + 64, ... in l[].  Adds
 // the token's probabilities to pacc, its sum of squared logits to zsum and
@@ -497,7 +544,7 @@ __device__ __forceinline__ void topk_one_token(const float (&l)[NJ], const float
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) m = fmaxf(m, l[j]);
-  m = wave_max(m);
+  m = wave_max_dpp(m);
   float ssum = 0.f, sq = 0.f, gap = 0.f;
   float ex[NJ];
 #pragma unroll
@@ -508,9 +555,9 @@ __device__ __forceinline__ void topk_one_token(const float (&l)[NJ], const float
     sq += (e < N) ? l[j] * l[j] : 0.f;
     gap += (ex[j] > 0.f) ? ex[j] * (m - l[j]) : 0.f;
   }
-  ssum = wave_sum(ssum);
-  sq = wave_sum(sq);
-  gap = wave_sum(gap);
+  ssum = wave_sum_dpp(ssum);
+  sq = wave_sum_dpp(sq);
+  gap = wave_sum_dpp(gap);
   const float inv = 1.0f / ssum;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) pacc[j] += ex[j] * inv;
@@ -537,13 +584,17 @@ __device__ __forceinline__ void topk_one_token(const float (&l)[NJ], const float
         best = key > best ? key : best;
       }
     }
-    best = wave_max_u64(best);
-    const int ew = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+    // the 64-bit maximum as two 32-bit ones: the largest key, then the
+    // largest ~index among the lanes holding it (= the lowest index)
+    const uint32_t khi = (uint32_t)(best >> 32);
+    const uint32_t kmax = wave_umax_dpp(khi);
+    const uint32_t ilo = wave_umax_dpp(khi == kmax ? (uint32_t)(best & 0xffffffffull) : 0u);
+    const int ew = __builtin_amdgcn_readfirstlane((int)(0xffffffffu - ilo));
     const int jw = ew >> 6;
     float cand = 0.f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) cand = (j == jw) ? l[j] : cand;
-    const float lw = __shfl(cand, ew & 63, MOE_WAVE);
+    const float lw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cand), ew & 63));
     if (lane == (ew & 63)) taken |= 1u << jw;
     if (lane == r) { my_l = lw; my_e = ew; }
     lmax_sel = fmaxf(lmax_sel, lw);
@@ -555,7 +606,7 @@ __device__ __forceinline__ void topk_one_token(const float (&l)[NJ], const float
     g = expf(my_l - m) * inv;
   } else {  // renormalised over the chosen K (both forms are equal)
     float ek = (lane < K) ? expf(my_l - lmax_sel) : 0.f;
-    float den = wave_sum(ek);
+    float den = wave_sum_dpp(ek);
     g = ek / den;
   }
   if (lane < K) {
@@ -564,9 +615,13 @@ __device__ __forceinline__ void topk_one_token(const float (&l)[NJ], const float
   }
 }
 
+// With nsplit > 1 the logits are first formed from the K-split partials
+// part [nsplit, T, N] (added in split order, then b_r) and written to
+// logits; with one split they are read from logits.
 template <int NJ>
 __global__ __launch_bounds__(256) void router_topk_kernel(
-    const float* __restrict__ logits, RouterNoise noise,
+    float* __restrict__ logits, const float* __restrict__ part, int nsplit,
+    const float* __restrict__ b_r, RouterNoise noise,
     const float* __restrict__ b_sel, int32_t* __restrict__ idx, float* __restrict__ gate,
     float* __restrict__ part_p, int32_t* __restrict__ part_cnt,
     float* __restrict__ part_z, int64_t T, int N, int K, int gate_mode,
@@ -595,11 +650,24 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     const int64_t t = tb0 + (int64_t)wave * per_wave + i;
     if (t >= T) break;
     float l[NJ];
+    const int64_t n = T * (int64_t)N;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       int e = lane + 64 * j;
-      l[j] = (e < N) ? logits[t * N + e] : -INFINITY;
-      if (noise_on(noise) && e < N) l[j] += noise.std * noise_draw(noise, t * N + e);
+      if (e < N) {
+        const int64_t i = t * N + e;
+        if (nsplit > 1) {
+          float acc = part[i];
+          for (int z = 1; z < nsplit; ++z) acc += part[(int64_t)z * n + i];
+          l[j] = acc + (b_r ? b_r[e] : 0.f);
+          logits[i] = l[j];
+        } else {
+          l[j] = logits[i];
+        }
+        if (noise_on(noise)) l[j] += noise.std * noise_draw(noise, i);
+      } else {
+        l[j] = -INFINITY;
+      }
     }
     topk_one_token<NJ>(l, bsel, lane, N, K, gate_mode, pacc, zsum, lsum, hsum, idx + t * K,
                        gate + t * K, scnt);
@@ -728,7 +796,7 @@ __global__ __launch_bounds__(1024) void router_stats_final_kernel(
 
 // ------------------------------------------------------- small batches ----
 // Everything after the logit GEMM in one workgroup of 16 waves, for small T:
-// the sum of the logit splits (same order as router_split_reduce_kernel),
+// the sum of the logit splits (in split order, as router_split_reduce_kernel),
 // top-K and gates (topk_one_token), and the statistics.  Wave w takes tokens
 // w, w + 16, ...; the per-expert probability sums and the z terms are then
 // added over the waves in wave order, f_e * p_e over experts in expert
@@ -874,6 +942,8 @@ int router_num_splits(int64_t T, int d, int N, bool x_bf16) {
   return (int)s;
 }
 
+bool router_topk_adds_splits(int64_t T, int nsplit) { return nsplit > 1 && T >= 1024; }
+
 hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, const float* b_r,
                                 uint16_t* planes, float* part, float* logits, int64_t T, int d,
                                 int N, hipStream_t stream, bool reduce_splits) {
@@ -895,43 +965,37 @@ hipError_t launch_router_logits(const void* x, bool x_bf16, const float* w_r, co
               (unsigned)ns);
     router_logits_pp_kernel<<<grid, 512, smem, stream>>>((const uint16_t*)x, planes, b_r,
                                                          ns == 1 ? logits : part, T, d, N);
-    e = hipGetLastError();
-    if (e != hipSuccess || ns == 1 || !reduce_splits) return e;
-    int64_t blocks = (T * (int64_t)N + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    router_split_reduce_kernel<<<(unsigned)blocks, 256, 0, stream>>>(part, ns, b_r, logits, T, N);
-    return hipGetLastError();
+  } else {
+    const int tm = router_tile_m(T, x_bf16);
+    dim3 grid((unsigned)((T + tm - 1) / tm), (unsigned)((N + RT_N - 1) / RT_N), (unsigned)ns);
+    float* out = ns == 1 ? logits : part;
+    const uint16_t* xb = (const uint16_t*)x;
+    if (x_bf16 && tm == 128)
+      router_logits_bf16x3_kernel<2, 64><<<grid, 256, 0, stream>>>(xb, w_r, b_r, out, T, d, N);
+    else if (x_bf16)
+      router_logits_bf16x3_kernel<1, 64><<<grid, 256, 0, stream>>>(xb, w_r, b_r, out, T, d, N);
+    else
+      router_logits_kernel<<<grid, 256, 0, stream>>>((const float*)x, w_r, b_r, out, T, d, N);
   }
-  const int tm = router_tile_m(T, x_bf16);
-  dim3 grid((unsigned)((T + tm - 1) / tm), (unsigned)((N + RT_N - 1) / RT_N), (unsigned)ns);
-  float* out = ns == 1 ? logits : part;
-  const uint16_t* xb = (const uint16_t*)x;
-  if (x_bf16 && tm == 128)
-    router_logits_bf16x3_kernel<2, 64><<<grid, 256, 0, stream>>>(xb, w_r, b_r, out, T, d, N);
-  else if (x_bf16)
-    router_logits_bf16x3_kernel<1, 64><<<grid, 256, 0, stream>>>(xb, w_r, b_r, out, T, d, N);
-  else
-    router_logits_kernel<<<grid, 256, 0, stream>>>((const float*)x, w_r, b_r, out, T, d, N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1 || !reduce_splits) return e;
-  int64_t n = T * (int64_t)N;
-  int64_t blocks = (n + 255) / 256;
+  int64_t blocks = (T * (int64_t)N + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   router_split_reduce_kernel<<<(unsigned)blocks, 256, 0, stream>>>(part, ns, b_r, logits, T, N);
   return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const float* logits, const RouterNoise& noise,
-                              const float* b_sel, int32_t* idx, float* gate, float* part_p,
-                              int32_t* part_cnt, float* part_z, int64_t T, int N, int K,
-                              int gate_mode, hipStream_t stream) {
+hipError_t launch_router_topk(float* logits, const float* part, int nsplit, const float* b_r,
+                              const RouterNoise& noise, const float* b_sel, int32_t* idx,
+                              float* gate, float* part_p, int32_t* part_cnt, float* part_z,
+                              int64_t T, int N, int K, int gate_mode, hipStream_t stream) {
   const int tpb = router_tokens_per_block(T);
   const unsigned nblk = (unsigned)((T + tpb - 1) / tpb);
   const size_t smem = (size_t)4 * N * sizeof(float) + (size_t)N * sizeof(int32_t) + 12 * sizeof(float);
   const int nj = (N + 63) / 64;
 #define MOE_TOPK_CASE(NJV)                                                              \
   case NJV:                                                                             \
-    router_topk_kernel<NJV><<<nblk, 256, smem, stream>>>(logits, noise, b_sel,             \
+    router_topk_kernel<NJV><<<nblk, 256, smem, stream>>>(logits, part, nsplit, b_r, noise, b_sel, \
         idx, gate, part_p, part_cnt, part_z, T, N, K, gate_mode, tpb);                 \
     break;
   switch (nj) {
