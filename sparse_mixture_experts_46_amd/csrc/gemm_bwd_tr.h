@@ -22,10 +22,11 @@
 //    (a group's last row tile, a weight gradient's ragged K) read as zeros.
 //  * 8 waves of 128 x 64 outputs (v_mfma_f32_32x32x16_bf16, weight fragment
 //    first); waves 0-3 issue the A tile's DMA, waves 4-7 the B tile's.
-//  * Each wave reads the fragments of the next 16-wide K slice while the
-//    MFMAs of the current one run; the stage's one barrier sits before its
-//    last slice's MFMAs, so the next stage's first fragments are read under
-//    them too.
+//  * Ping-pong, as the forward's DMA kernel: waves 0-3 (tile rows 0-127)
+//    and waves 4-7 (rows 128-255) put one wave on each SIMD; per 32-wide K
+//    sub-step a wave reads its fragments (memory phase), then runs its 16
+//    MFMAs (compute phase), and the second group runs one barrier behind,
+//    so on every SIMD one wave computes while the other reads LDS.
 //  * Epilogues: a weight gradient's bf16 tile and dh's activation backward
 //    go through LDS (free after the K loop's last barrier), so global memory
 //    sees whole rows of 128-byte lines; the other epilogues store 4 columns
@@ -221,39 +222,56 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_tr_kernel(BwdArgs p, int tota
       for (int j = 0; j < FN; ++j)
         xb[j] = B_STRIDED ? frag_t(SB, bn[j], ks) : frag_c(SB, bn[j], ks * 2 + khalf);
     };
-    bf16x8_t fa[FM], fb[FN];
+    // Ping-pong over 32-wide K sub-steps, as the forward's DMA kernel:
+    // group 0 (waves 0-3: tile rows 0-127, the A operand's DMA) and group 1
+    // (waves 4-7: rows 128-255, B's DMA) put one wave on each SIMD.  A
+    // sub-step is a memory phase (read the sub-step's fragments; in a
+    // block's first sub-step also issue this wave's share of the next
+    // block's DMA; in its second wait for that share) and a compute phase
+    // (the MFMAs), each closed by a barrier.  Group 1 starts one barrier
+    // late, so on every SIMD one wave computes while the other moves data.
+    // Block kt+1 goes into the slot of block kt-1, whose last reads (group
+    // 1's memory phase of kt-1's second sub-step) ended before the barrier
+    // that precedes the issue.  Every wave passes the same number of
+    // barriers: 1 + 4 nk + 1.
+    const int grp = wave >> 2;
+    bf16x8_t fa[2][FM], fb[2][FN];
     if (nk > 0) issue(0, 0);
     wait_vmcnt<0>();
     __syncthreads();
-    if (nk > 0) read_frags(0, 0, fa, fb);
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+    if (grp == 1) __builtin_amdgcn_s_barrier();
+    auto finish_m_then_compute = [&]() {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        // the next slice's fragments are read while this slice's MFMAs run
-        bf16x8_t na[FM], nb[FN];
-        if (ks + 1 < BK / 16) {
-          read_frags(kt & 1, ks + 1, na, nb);
-        } else {
-          // stage kt + 1 landed for every wave, and every wave holds stage
-          // kt's last fragments in registers before the stage is refilled
-          // (the barrier alone does not wait for the LDS reads to return)
-          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-          wait_vmcnt<0>();
-          __syncthreads();
-          if (kt + 1 < nk) read_frags((kt + 1) & 1, 0, na, nb);
-        }
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int i = 0; i < FM; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[j][i], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[i] = na[i];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[j] = nb[j];
-      }
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[h][j], fa[h][i], acc[j][i], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      // sub-step 0: K 0..31 of block kt; this wave's DMA share of block kt+1
+      read_frags(cur, 0, fa[0], fb[0]);
+      read_frags(cur, 1, fa[1], fb[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
+      finish_m_then_compute();
+      // sub-step 1: K 32..63; this wave's share of block kt+1 landed
+      read_frags(cur, 2, fa[0], fb[0]);
+      read_frags(cur, 3, fa[1], fb[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<0>();
+      finish_m_then_compute();
     }
+    if (grp == 0) __builtin_amdgcn_s_barrier();  // realign the groups
 
     // ---- epilogue (as gemm_bwd_kernel); split K: parts 1.. write c2's planes
     BwdArgs pe = p;
