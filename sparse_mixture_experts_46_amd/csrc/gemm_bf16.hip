@@ -61,13 +61,14 @@ hipError_t run_pingpong(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
 
 // Decode sizes: one workgroup per 16-row x 16 kDecodeWaves-column tile (the
 // tile table is built with those dims), up to 64 waves' worth of workgroups
-// per CU; bf16, INT8 or INT4 weights.
+// per CU, a multiple of 8 (see decode_walk); bf16, INT8 or INT4 weights.
 template <bool DUAL, int EPI>
 hipError_t run_decode(const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
   int64_t grid = max_tiles;
   const int64_t cap = (int64_t)num_cus() * (64 / kDecodeWaves);
   if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
+  grid = (grid + 7) / 8 * 8;
+  if (grid < 8) grid = 8;
   constexpr int nt = 64 * kDecodeWaves;
   if (a.qbits == 4)
     gemm_decode_q4_kernel<DUAL, EPI><<<(unsigned)grid, nt, 0, s>>>(a);

@@ -35,6 +35,22 @@ namespace moe {
 // Waves per decode workgroup; a tile is 16 rows x 16 kDecodeWaves columns.
 constexpr int kDecodeWaves = 4;
 
+// Tile order.  With at most one tile per workgroup (a grid that is a multiple
+// of 8 and larger than the table) each XCD takes a contiguous eighth of the
+// table, so the weight rows one XCD streams are neighbours.  Measured with 8
+// experts, d = 4096, F = 14336 and 16 tokens (1792 tiles in the first GEMM):
+// 0.320 ms on every run, against 0.32-0.37 ms in dispatch order.  With several
+// tiles per workgroup the dispatch order (tile = block, then += grid) measured
+// as fast or faster.
+__device__ __forceinline__ TileWalk decode_walk(int total) {
+  if ((gridDim.x & 7) == 0 && total < (int)gridDim.x) return tile_walk(total);
+  TileWalk w;
+  w.tile = blockIdx.x;
+  w.step = gridDim.x;
+  w.end = total;
+  return w;
+}
+
 // int8 codes (|q| <= 127) to bf16, exactly: 8 codes packed in two words.
 __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
   bf16x8_t r;
@@ -49,7 +65,7 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
 }
 
 template <bool DUAL, int EPI, bool Q8>
-__global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * kDecodeWaves, DUAL ? 8 / kDecodeWaves : 16 / kDecodeWaves) void gemm_decode_kernel(GemmArgs p) {
   constexpr int NWV = kDecodeWaves, RPW = 16 / NWV, BNC = 16 * NWV;
   constexpr int KC = 512;          // K columns per staged activation chunk
   constexpr int RB = KC * 2 + 16;  // LDS bytes per staged activation row
@@ -67,7 +83,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(GemmArgs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int total = p.tile_base[p.G];
   const int row = lane & 15, part = lane >> 4;
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  for (TileWalk tw = decode_walk(total); tw.tile < tw.end; tw.tile += tw.step) {
+    const int tile = tw.tile;
     const TileInfo ti = resolve_tile(p, tile, 16, BNC);
     const int64_t Kd = p.Kdim;
     const int nblk = (int)(Kd / 64);               // 64-wide blocks in K
@@ -93,6 +110,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(GemmArgs
     const char* pb0 = (const char*)(ti.shared ? (const void*)p.bs0 : (const void*)p.b0) + wrow;
     const char* pb1 = DUAL ? (const char*)(ti.shared ? (const void*)p.bs1 : (const void*)p.b1) + wrow
                            : nullptr;
+    // the INT8 scales and the bias of the lane's output column n (clamped:
+    // the epilogue skips columns past Nout), loaded before the K loop so that
+    // their latency hides under it
+    float s0 = 1.f, s1 = 1.f, bias = 0.f;  // bf16 weights carry no scales
+    if (Q8) {
+      const int64_t si = ti.shared ? n : (int64_t)ti.g * p.Nout + n;
+      s0 = (ti.shared ? p.scs0 : p.sc0)[si];
+      if (DUAL) s1 = (ti.shared ? p.scs1 : p.sc1)[si];
+    }
+    if (EPI != EPI_SILU_MUL && p.bias && !ti.shared)
+      bias = bf16_to_f32(p.bias[(int64_t)ti.g * p.Nout + n]);
 
     auto issue_a = [&](int c, int buf) {
       uint32_t koff = (uint32_t)c * KC * 2 + (uint32_t)lane * 16;
@@ -179,15 +207,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(GemmArgs
     const int col = ti.nt * BNC + wave * 16 + (lane & 15);
     if (col < ti.Nout) {
       uint16_t* cbase = ti.shared ? p.c_shared : p.c;
-      float s0 = 1.f, s1 = 1.f;  // bf16 weights carry no scales
-      if (Q8) {
-        const int64_t si = ti.shared ? col : (int64_t)ti.g * p.Nout + col;
-        s0 = (ti.shared ? p.scs0 : p.sc0)[si];
-        if (DUAL) s1 = (ti.shared ? p.scs1 : p.sc1)[si];
-      }
-      float bias = 0.f;
-      if (EPI != EPI_SILU_MUL && p.bias && !ti.shared)
-        bias = bf16_to_f32(p.bias[(int64_t)ti.g * p.Nout + col]);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = ti.mt * 16 + 4 * part + v;
@@ -246,7 +265,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_deco
   constexpr int KC = 512;          // K columns per staged activation chunk
   constexpr int RB = KC * 2 + 16;  // LDS bytes per staged activation row
   constexpr int SG = KC / 128;     // 128-wide groups per weight stage (one stage per chunk)
+  static_assert(SG == 4, "a stage's scales of 16 rows are one 4-byte DMA per lane");
   __shared__ __attribute__((aligned(16))) char abuf[2][16 * RB];
+  // per wave, three stages of scales: [stage set][matrix][16 rows][SG groups]
+  __shared__ __attribute__((aligned(16))) float sbuf[NWV][3][DUAL ? 2 : 1][16 * SG];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int total = p.tile_base[p.G];
@@ -254,7 +276,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_deco
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
                                                                 0x3F803F80u, 0x3F803F80u));
   const uint32_t magic = q4_magic();
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  for (TileWalk tw = decode_walk(total); tw.tile < tw.end; tw.tile += tw.step) {
+    const int tile = tw.tile;
     const TileInfo ti = resolve_tile(p, tile, 16, BNC);
     const int64_t Kd = p.Kdim;
     const int ngrp = (int)(Kd / 128);
@@ -281,7 +304,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_deco
     const char* pb0 = (const char*)(ti.shared ? (const void*)p.bs0 : (const void*)p.b0) + wrow;
     const char* pb1 = DUAL ? (const char*)(ti.shared ? (const void*)p.bs1 : (const void*)p.b1) + wrow
                            : nullptr;
-    const int64_t srow = (ti.shared ? 0 : (int64_t)ti.g * p.Nout * ngrp) + (int64_t)n * ngrp;
+    // the bias of the lane's output column n, loaded before the K loop
+    float bias = 0.f;
+    if (EPI != EPI_SILU_MUL && p.bias && !ti.shared)
+      bias = bf16_to_f32(p.bias[(int64_t)ti.g * p.Nout + n]);
+    // scales: lane l fetches group l % 4 of a stage for row l / 4 of the
+    // wave's 16 output rows
+    int nd = ti.nt * BNC + wave * 16 + (lane >> 2);
+    if (nd >= ti.Nout) nd = ti.Nout - 1;
+    const int64_t srow = (ti.shared ? 0 : (int64_t)ti.g * p.Nout * ngrp) + (int64_t)nd * ngrp;
     const float* ps0 = (ti.shared ? p.scs0 : p.sc0) + srow;
     const float* ps1 = DUAL ? (ti.shared ? p.scs1 : p.sc1) + srow : nullptr;
 
@@ -291,11 +322,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_deco
 #pragma unroll
       for (int i = 0; i < RPW; ++i) buf_dma16(arow_ptr[i], koff, abuf[buf] + (wave * RPW + i) * RB);
     };
-    // codes two stages ahead (three sets), scales one stage ahead (two)
+    // codes two stages ahead (three register sets), scales as far ahead (three
+    // LDS sets of the wave), the activation chunk one stage ahead (two LDS
+    // buffers).  Scales come from HBM like the codes: fetched one stage ahead
+    // into registers, their latency showed (d = 7168, 256 experts, 128 tokens:
+    // first GEMM 1.21 ms, 0.88 ms with no scale loads at all).
     uint4 b0[3][SG], b1[3][SG];
-    float s0[2][SG], s1[2][SG];
-    // vector loads of one stage's codes (both matrices)
+    // vector loads of one stage's codes (both matrices) and of its scales
     constexpr int NBV = SG * (DUAL ? 2 : 1);
+    constexpr int NS = DUAL ? 2 : 1;
     auto issue_b = [&](int st, int set) {
 #pragma unroll
       for (int j = 0; j < SG; ++j) {
@@ -306,16 +341,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_deco
       }
     };
     auto issue_s = [&](int st, int set) {
-#pragma unroll
-      for (int j = 0; j < SG; ++j) {
-        const int g = st * SG + j < ngrp ? st * SG + j : ngrp - 1;
-        s0[set][j] = ps0[g];
-        if (DUAL) s1[set][j] = ps1[g];
-      }
+      int g = st * SG + (lane & 3);
+      if (g >= ngrp) g = ngrp - 1;  // past the row: loaded and not used
+      lds_dma4(ps0 + g, &sbuf[wave][set][0][0]);
+      if (DUAL) lds_dma4(ps1 + g, &sbuf[wave][set][DUAL ? 1 : 0][0]);
     };
 
     f32x4_t out0 = {0.f, 0.f, 0.f, 0.f}, out1 = {0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int st, int buf, int set, int sset) {
+    auto compute = [&](int st, int buf, int set) {
       const int left = ngrp - st * SG;
       const char* arow_l = abuf[buf] + row * RB + part * 64;
 #pragma unroll
@@ -323,6 +356,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_deco
         if (j < left) {
           const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
           f32x4_t a0 = zero, a1 = zero, sx = zero;
+          const float sc0 = sbuf[wave][set][0][row * SG + j];
+          const float sc1 = DUAL ? sbuf[wave][set][DUAL ? 1 : 0][row * SG + j] : 0.f;
           const uint4 c0 = b0[set][j];
           const uint4 c1 = DUAL ? b1[set][j] : c0;
           const uint32_t w0[4] = {c0.x, c0.y, c0.z, c0.w};
@@ -336,50 +371,55 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_deco
           }
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            out0[v] += s0[sset][j] * (a0[v] - 136.f * sx[v]);
-            if (DUAL) out1[v] += s1[sset][j] * (a1[v] - 136.f * sx[v]);
+            out0[v] += sc0 * (a0[v] - 136.f * sx[v]);
+            if (DUAL) out1[v] += sc1 * (a1[v] - 136.f * sx[v]);
           }
         }
       }
     };
 
-    // issue order: a(0), s(0), c(0), c(1), then per stage st: a(st+1),
-    // s(st+1), c(st+2) (a: activation chunk, s: scales, c: codes), so at the
-    // top of stage st only c(st+1) may still be in flight
-    issue_a(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_s(0, 0);
-    issue_b(0, 0);
-    if (nstage > 1) issue_b(1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int st = 0; st < nstage; ++st) {
-      if (st + 1 < nstage) wait_vmcnt<NBV>();
-      else wait_vmcnt<0>();
-      __syncthreads();  // every wave's rows of chunk st; buffer (st+1)&1 free
+    // Issue order: a(0), s(0), c(0), s(1), c(1), then per stage st: a(st+1),
+    // s(st+2), c(st+2) (a: activation chunk, s: scales, c: codes), so at the
+    // top of stage st only s(st+1) and c(st+1) may still be in flight.  Every
+    // stage issues the same loads (indices clamped inside the row), which
+    // keeps the wait counts exact.
+    {
+      issue_a(0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (st + 1 < nstage) {
-        issue_a(st + 1, (st + 1) & 1);
+      issue_s(0, 0);
+      issue_b(0, 0);
+      if (nstage > 1) {
+        issue_s(1, 1);
+        issue_b(1, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      for (int st = 0; st < nstage; ++st) {
+        if (st + 1 < nstage) wait_vmcnt<NS + NBV>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // every wave's rows of chunk st; buffer (st+1)&1 free
         __builtin_amdgcn_sched_barrier(0);
-        if (st & 1) issue_s(st + 1, 0);
-        else issue_s(st + 1, 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (st + 2 < nstage) {
-        const int set2 = (st + 2) % 3;
-        if (set2 == 0) issue_b(st + 2, 0);
-        else if (set2 == 1) issue_b(st + 2, 1);
-        else issue_b(st + 2, 2);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // (a copy of the stage without the per-group tests, for full stages,
-      // measured slower: the second GEMM's kernel lost a wave per SIMD)
-      const int set = st % 3, sset = st & 1;
-      if (set == 0) {
-        if (sset) compute(st, st & 1, 0, 1); else compute(st, st & 1, 0, 0);
-      } else if (set == 1) {
-        if (sset) compute(st, st & 1, 1, 1); else compute(st, st & 1, 1, 0);
-      } else {
-        if (sset) compute(st, st & 1, 2, 1); else compute(st, st & 1, 2, 0);
+        if (st + 1 < nstage) issue_a(st + 1, (st + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 2 < nstage) {
+          const int set2 = (st + 2) % 3;
+          if (set2 == 0) {
+            issue_s(st + 2, 0);
+            issue_b(st + 2, 0);
+          } else if (set2 == 1) {
+            issue_s(st + 2, 1);
+            issue_b(st + 2, 1);
+          } else {
+            issue_s(st + 2, 2);
+            issue_b(st + 2, 2);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // (a copy of the stage without the per-group tests, for full stages,
+        // measured slower: the second GEMM's kernel lost a wave per SIMD)
+        const int set = st % 3;
+        if (set == 0) compute(st, st & 1, 0);
+        else if (set == 1) compute(st, st & 1, 1);
+        else compute(st, st & 1, 2);
       }
     }
     __syncthreads();  // the last buffer is read before the next tile stages into it
@@ -388,9 +428,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 8 / kDecodeWaves) void gemm_deco
     const int col = ti.nt * BNC + wave * 16 + (lane & 15);
     if (col < ti.Nout) {
       uint16_t* cbase = ti.shared ? p.c_shared : p.c;
-      float bias = 0.f;
-      if (EPI != EPI_SILU_MUL && p.bias && !ti.shared)
-        bias = bf16_to_f32(p.bias[(int64_t)ti.g * p.Nout + col]);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = ti.mt * 16 + 4 * part + v;

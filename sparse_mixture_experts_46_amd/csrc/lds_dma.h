@@ -14,6 +14,12 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)l, 16, 0, 0);
 }
 
+// 4 bytes per lane, global address per lane: lane l's word lands at byte 4 l
+// of the wave's LDS block.
+__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)l, 4, 0, 0);
+}
+
 // 16-byte-per-lane global -> LDS copy through a raw buffer resource: a
 // wave-uniform base plus a 32-bit byte offset per lane.
 __device__ __forceinline__ void buf_dma16(const void* base, uint32_t voff, void* lds) {
