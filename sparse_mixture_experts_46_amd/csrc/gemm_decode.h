@@ -238,9 +238,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves, DUAL ? 8 / kDecodeWaves : 16 / k
 //    S = sum x; the group adds s * (sum x w' - 136 S) = s * sum x q to the
 //    fp32 output (every product is exact, the sums are fp32);
 //  * a stage's codes are half the bytes of an INT8 stage over the same K, so
-//    the weights are fetched two stages ahead (three register sets) to keep
-//    as many bytes in flight; every stage issues the same loads (indices
-//    clamped inside the row), which keeps the wait counts exact.
+//    the codes are fetched two stages ahead (three register sets) to keep
+//    as many bytes in flight, and the stage's scales as far ahead, by LDS
+//    DMA into three per-wave LDS sets (one 4-byte DMA per lane and matrix);
+//    every stage issues the same loads (indices clamped inside the row),
+//    which keeps the wait counts exact.
 // magic = 0x43004300 in a register the compiler cannot fold: (x & mask) |
 // magic then selects one v_and_or_b32 with the mask in an SGPR (a gfx9 VOP3
 // instruction takes at most one SGPR or literal, so with both constants
