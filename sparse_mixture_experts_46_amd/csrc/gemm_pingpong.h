@@ -139,12 +139,17 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
       boff[i] = (uint32_t)(((int64_t)n * Kd + dh * 32 + (dch ^ pp_swz(r)) * 8) * 2);
     }
     const int nk = (int)(Kd / 64);
-    // The tile body, for a full tile or (HALF) a last tile of at most BM / 2
-    // rows: then only the first half of the A loads and of the fragments run.
-    auto run = [&](auto half_c) {
-      constexpr bool HALF = decltype(half_c)::value;
-      constexpr int FMA = HALF ? FM / 2 : FM;  // A fragments computed
-      constexpr int LAA = HALF ? LA / 2 : LA;  // A loads issued per block
+    // The tile body (MODE 0) for a full tile; (MODE 1) for a last tile of at
+    // most BM / 2 rows, where only the first half of the A loads and of the
+    // fragments run; (MODE 2) for a last tile of at most BM / 4 rows, where a
+    // quarter of the A loads run and only the first group's waves, which hold
+    // the tile's first BM / 4 rows in their first fragment, read fragments
+    // and compute (the second group keeps every barrier).
+    auto run = [&](auto mode_c) {
+      constexpr int MODE = decltype(mode_c)::value;
+      constexpr int FMA = MODE == 0 ? FM : FM / 2;                  // A fragments computed
+      constexpr int LAA = MODE == 0 ? LA : MODE == 1 ? LA / 2 : LA / 4;  // A loads per block
+      const bool idle = MODE == 2 && grp == 1;
       auto issue_a = [&](int blk, int slot) {
         const uint32_t kb = (uint32_t)(blk < nk ? blk : nk - 1) * 128u;
         char* st = abuf + slot * ASLOT;
@@ -171,6 +176,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
 
       bf16x8_t fa[2][FMA], fb[2][FN];
       auto read_fragments = [&](int sa, int sb, int h) {
+        if (idle) return;
         const uint4* sA = abuf4 + sa * (ASLOT / 16) + h * 32;
         const uint4* sB = bbuf4 + sb * (BSLOT / 16) + h * 32;
 #pragma unroll
@@ -189,13 +195,15 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
+        if (!idle) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+          for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int i = 0; i < FMA; ++i)
-              acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[j][i], 0, 0, 0);
+              for (int i = 0; i < FMA; ++i)
+                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[j][i], 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
@@ -279,10 +287,15 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
         }
       }
     };
-    // half-height mode needs an even split of the A loads and fragments
+    // half-height mode needs an even split of the A loads and fragments;
+    // quarter-height mode also needs the first group's waves (0-3) to hold
+    // exactly the tile's first BM / 4 rows in their first fragment
     constexpr bool kHalfOk = (FM % 2 == 0) && (LA % 2 == 0);
-    if (kHalfOk && ti.M - ti.mt * BM <= BM / 2) run(std::true_type{});
-    else run(std::false_type{});
+    constexpr bool kQuarterOk = kHalfOk && (LA % 4 == 0) && (BM * WN == 512);
+    const int left = ti.M - ti.mt * BM;
+    if (kQuarterOk && left <= BM / 4) run(std::integral_constant<int, 2>{});
+    else if (kHalfOk && left <= BM / 2) run(std::integral_constant<int, 1>{});
+    else run(std::integral_constant<int, 0>{});
     tile = dyn ? -2 : tile + walk.step;
   }
 }
