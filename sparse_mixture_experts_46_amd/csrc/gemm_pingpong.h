@@ -144,12 +144,16 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
     // fragments run; (MODE 2) for a last tile of at most BM / 4 rows, where a
     // quarter of the A loads run and only the first group's waves, which hold
     // the tile's first BM / 4 rows in their first fragment, read fragments
-    // and compute (the second group keeps every barrier).
+    // and compute (the second group keeps every barrier); (MODE 3) for a last
+    // tile of at most 3 BM / 4 rows, where three quarters of the A loads run
+    // and the second group skips its second fragment (the last BM / 4 rows).
     auto run = [&](auto mode_c) {
       constexpr int MODE = decltype(mode_c)::value;
-      constexpr int FMA = MODE == 0 ? FM : FM / 2;                  // A fragments computed
-      constexpr int LAA = MODE == 0 ? LA : MODE == 1 ? LA / 2 : LA / 4;  // A loads per block
+      constexpr int FMA = (MODE == 1 || MODE == 2) ? FM / 2 : FM;  // A fragments computed
+      constexpr int LAA = MODE == 0 ? LA : MODE == 1 ? LA / 2 : MODE == 2 ? LA / 4 : 3 * LA / 4;
       const bool idle = MODE == 2 && grp == 1;
+      // wave-uniform: whether this wave computes A fragment i
+      auto frag_on = [&](int i) { return MODE != 3 || grp == 0 || i == 0; };
       auto issue_a = [&](int blk, int slot) {
         const uint32_t kb = (uint32_t)(blk < nk ? blk : nk - 1) * 128u;
         char* st = abuf + slot * ASLOT;
@@ -183,7 +187,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
         for (int ks = 0; ks < 2; ++ks) {
           const int ch = ks * 2 + khalf;
 #pragma unroll
-          for (int i = 0; i < FMA; ++i) fa[ks][i] = __builtin_bit_cast(bf16x8_t, sA[aidx[i] + (ch ^ asw[i])]);
+          for (int i = 0; i < FMA; ++i)
+            if (frag_on(i)) fa[ks][i] = __builtin_bit_cast(bf16x8_t, sA[aidx[i] + (ch ^ asw[i])]);
 #pragma unroll
           for (int j = 0; j < FN; ++j) fb[ks][j] = __builtin_bit_cast(bf16x8_t, sB[bidx[j] + (ch ^ bsw[j])]);
         }
@@ -202,7 +207,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
             for (int j = 0; j < FN; ++j)
 #pragma unroll
               for (int i = 0; i < FMA; ++i)
-                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[j][i], 0, 0, 0);
+                if (frag_on(i))
+                  acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[j][i], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
@@ -292,9 +298,13 @@ __global__ __launch_bounds__(512, 1) void gemm_pingpong_kernel(GemmArgs p) {
     // exactly the tile's first BM / 4 rows in their first fragment
     constexpr bool kHalfOk = (FM % 2 == 0) && (LA % 2 == 0);
     constexpr bool kQuarterOk = kHalfOk && (LA % 4 == 0) && (BM * WN == 512);
+    // three-quarter mode: with two fragments, the second group's second one
+    // holds exactly the tile's last BM / 4 rows
+    constexpr bool kThreeQOk = kQuarterOk && (FM == 2);
     const int left = ti.M - ti.mt * BM;
     if (kQuarterOk && left <= BM / 4) run(std::integral_constant<int, 2>{});
     else if (kHalfOk && left <= BM / 2) run(std::integral_constant<int, 1>{});
+    else if (kThreeQOk && left <= 3 * BM / 4) run(std::integral_constant<int, 3>{});
     else run(std::integral_constant<int, 0>{});
     tile = dyn ? -2 : tile + walk.step;
   }
