@@ -16,10 +16,10 @@ namespace moe {
 namespace {
 
 // bf16: each thread owns 8 consecutive columns (16 bytes) of one token at a
-// time; the workgroup's threads cover the row (blockDim.x divides d / 8 where
-// it can).  The up to KB expert rows of a token are all loaded before any is
-// added, so every thread has KB loads in flight; the sum still runs in slot
-// order.
+// time; the gridDim.y workgroups of a token cover its row (blockDim.x divides
+// d / 8 where it can).  The up to KB expert rows of a token are all loaded
+// before any is added, so every thread has KB loads in flight; the sum still
+// runs in slot order.
 template <int KB>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(
     const uint16_t* __restrict__ y_perm, const int32_t* __restrict__ pair_row,
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
       rows[k] = k < K ? pair_row[t * K + k] : -1;
       gs[k] = k < K ? gate[t * K + k] : 0.f;
     }
-    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+    for (int c = blockIdx.y * blockDim.x + threadIdx.x; c < chunks; c += gridDim.y * blockDim.x) {
       uint4 v[KB];
 #pragma unroll
       for (int k = 0; k < KB; ++k)
@@ -109,15 +109,24 @@ hipError_t launch_combine(const void* y_perm, const int32_t* pair_row,
   if (grid < 1) grid = 1;
   if (bf16) {
     const int chunks = d / 8;
-    const int nt = chunks % 256 == 0 ? 256 : (chunks % 128 == 0 ? 128 : (chunks <= 64 ? 64 : 256));
+    int nt = chunks % 256 == 0 ? 256 : (chunks % 128 == 0 ? 128 : (chunks <= 64 ? 64 : 256));
+    // Decode-sized batches: too few tokens to fill the GPU one workgroup per
+    // token, so a token's row is cut over workgroups of 64 threads, one
+    // 16-byte chunk each.
+    int cs = 1;
+    if (T < 1024) {
+      nt = 64;
+      cs = (chunks + 63) / 64;
+    }
+    const dim3 g((unsigned)grid, (unsigned)cs);
     const uint16_t* yp = (const uint16_t*)y_perm;
     const uint16_t* ys = (const uint16_t*)y_shared;
     if (K <= 2)
-      combine_bf16_kernel<2><<<(unsigned)grid, nt, 0, stream>>>(yp, pair_row, gate, ys, (uint16_t*)y, T, d, K);
+      combine_bf16_kernel<2><<<g, nt, 0, stream>>>(yp, pair_row, gate, ys, (uint16_t*)y, T, d, K);
     else if (K <= 8)
-      combine_bf16_kernel<8><<<(unsigned)grid, nt, 0, stream>>>(yp, pair_row, gate, ys, (uint16_t*)y, T, d, K);
+      combine_bf16_kernel<8><<<g, nt, 0, stream>>>(yp, pair_row, gate, ys, (uint16_t*)y, T, d, K);
     else
-      combine_bf16_kernel<kMaxTopK><<<(unsigned)grid, nt, 0, stream>>>(yp, pair_row, gate, ys, (uint16_t*)y, T, d, K);
+      combine_bf16_kernel<kMaxTopK><<<g, nt, 0, stream>>>(yp, pair_row, gate, ys, (uint16_t*)y, T, d, K);
   } else
     combine_f32_kernel<<<(unsigned)grid, 256, 0, stream>>>(
         (const float*)y_perm, pair_row, gate, (const float*)y_shared, (float*)y, T, d, K);

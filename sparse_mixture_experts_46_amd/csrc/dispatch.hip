@@ -24,35 +24,42 @@ namespace {
 constexpr int DT = kDispatchTokens;   // tokens per block
 constexpr int DW = DT / 32;           // 32-bit words per expert bitmap
 
-// Fills the block's bitmap; returns in bad[] per pair whether the id is out
-// of range or repeats an earlier slot of the same token.
-__device__ __forceinline__ void build_bitmap(const int32_t* __restrict__ idx,
-                                             int64_t T, int N, int K,
-                                             uint32_t* bm, int64_t t,
-                                             int local, int nthreads) {
+// A token's K expert ids, loaded once (independent loads, not one dependent
+// load per comparison), and the mask of its slots whose id is out of range
+// or repeats an earlier slot's id.
+struct TokenIds {
+  int32_t e[kMaxTopK];
+  uint32_t bad;
+};
+__device__ __forceinline__ TokenIds load_token(const int32_t* __restrict__ idx, int64_t t, int N,
+                                               int K) {
+  TokenIds r;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) r.e[k] = k < K ? idx[t * K + k] : -1;
+  r.bad = 0u;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    bool bad = r.e[k] < 0 || r.e[k] >= N;
+#pragma unroll
+    for (int k2 = 0; k2 < k; ++k2) bad = bad || r.e[k2] == r.e[k];
+    if (k < K && bad) r.bad |= 1u << k;
+  }
+  return r;
+}
+
+// Fills the block's bitmap from the tokens' ids (tk of token t, valid if
+// t < T).
+__device__ __forceinline__ void build_bitmap(const TokenIds& tk, int64_t T, int N, int K,
+                                             uint32_t* bm, int64_t t, int local, int nthreads) {
   for (int i = threadIdx.x; i < N * DW; i += nthreads) bm[i] = 0u;
   __syncthreads();
   if (t < T) {
-    for (int k = 0; k < K; ++k) {
-      int e = idx[t * K + k];
-      bool bad = (e < 0) || (e >= N);
-      for (int k2 = 0; k2 < k && !bad; ++k2) bad = (idx[t * K + k2] == e);
-      if (!bad) atomicOr(&bm[e * DW + (local >> 5)], 1u << (local & 31));
-    }
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k)
+      if (k < K && !((tk.bad >> k) & 1u))
+        atomicOr(&bm[tk.e[k] * DW + (local >> 5)], 1u << (local & 31));
   }
   __syncthreads();
-}
-
-// Slots of token t whose id is out of range or repeats an earlier slot.
-__device__ __forceinline__ int count_bad(const int32_t* __restrict__ idx, int64_t t, int N, int K) {
-  int nb = 0;
-  for (int k = 0; k < K; ++k) {
-    int e = idx[t * K + k];
-    bool bad = (e < 0) || (e >= N);
-    for (int k2 = 0; k2 < k && !bad; ++k2) bad = (idx[t * K + k2] == e);
-    nb += bad ? 1 : 0;
-  }
-  return nb;
 }
 
 __global__ __launch_bounds__(DT) void dispatch_hist_kernel(
@@ -63,9 +70,10 @@ __global__ __launch_bounds__(DT) void dispatch_hist_kernel(
   const int local = threadIdx.x;
   const int64_t t = (int64_t)blockIdx.x * DT + local;
   if (local == 0) nbad = 0;
-  build_bitmap(idx, T, N, K, bm, t, local, DT);
+  const TokenIds tk = t < T ? load_token(idx, t, N, K) : TokenIds{};
+  build_bitmap(tk, T, N, K, bm, t, local, DT);
   if (t < T) {
-    const int mybad = count_bad(idx, t, N, K);
+    const int mybad = __popc(tk.bad);
     if (mybad) atomicAdd(&nbad, mybad);  // integer: order-independent
   }
   for (int e = local; e < N; e += DT) {
@@ -103,12 +111,16 @@ __device__ __forceinline__ int32_t scan_kept(const int32_t* skept, int32_t* scan
   return total;
 }
 
+// Experts with at least one kept row, counted by a block of 1024 threads
+// (N <= 1024: one expert per thread); every thread gets the count.
+__device__ __forceinline__ int count_touched(const int32_t* skept, int N) {
+  const int tid = threadIdx.x;
+  return __syncthreads_count(tid < N && skept[tid] > 0);
+}
+
 // counters = {kept rows, dropped pairs, bad ids, touched experts}
 __device__ __forceinline__ void write_counters(int32_t* __restrict__ counters, int32_t total,
-                                               int64_t T, int K, int64_t bad,
-                                               const int32_t* skept, int N) {
-  int touched = 0;
-  for (int e = 0; e < N; ++e) touched += skept[e] > 0 ? 1 : 0;
+                                               int64_t T, int K, int64_t bad, int touched) {
   counters[0] = total;
   counters[1] = (int32_t)(T * K - total);
   counters[2] = (int32_t)bad;
@@ -138,17 +150,18 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
   }
   __syncthreads();
   const int32_t total = scan_kept(skept, scan, N, offset, nullptr);
+  const int touched = count_touched(skept, N);
   if (tid == 0 && counters) {
     int64_t bad = 0;
     for (int64_t b = 0; b < nblk; ++b) bad += blk_bad[b];
-    write_counters(counters, total, T, K, bad, skept, N);
+    write_counters(counters, total, T, K, bad, touched);
   }
 }
 
 // Rows of token t's slots: rank among the tokens that chose the expert =
 // base[e] (earlier blocks; 0 if base is null) + the bits of this block's
 // bitmap below the token; kept iff rank < cap, at row off[e] + rank.
-__device__ __forceinline__ void assign_token(const int32_t* __restrict__ idx, int64_t t,
+__device__ __forceinline__ void assign_token(const TokenIds& tk, int64_t t,
                                              int local, int N, int K, int64_t cap,
                                              const uint32_t* bm, const int32_t* base,
                                              const int32_t* off, int32_t* __restrict__ pair_row,
@@ -156,11 +169,12 @@ __device__ __forceinline__ void assign_token(const int32_t* __restrict__ idx, in
                                              uint8_t* __restrict__ dropped) {
   const int w = local >> 5;
   const uint32_t below = (1u << (local & 31)) - 1u;
-  for (int k = 0; k < K; ++k) {
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (k >= K) continue;
     const int64_t pr = t * K + k;
-    int e = idx[pr];
-    bool bad = (e < 0) || (e >= N);
-    for (int k2 = 0; k2 < k && !bad; ++k2) bad = (idx[t * K + k2] == e);
+    const int e = tk.e[k];
+    const bool bad = (tk.bad >> k) & 1u;
     int32_t row = -1;
     if (!bad) {
       int r = 0;
@@ -185,9 +199,10 @@ __global__ __launch_bounds__(DT) void dispatch_assign_kernel(
   extern __shared__ uint32_t bm[];
   const int local = threadIdx.x;
   const int64_t t = (int64_t)blockIdx.x * DT + local;
-  build_bitmap(idx, T, N, K, bm, t, local, DT);
+  const TokenIds tk = t < T ? load_token(idx, t, N, K) : TokenIds{};
+  build_bitmap(tk, T, N, K, bm, t, local, DT);
   if (t >= T) return;
-  assign_token(idx, t, local, N, K, cap, bm, blk_base + (int64_t)blockIdx.x * N, offset, pair_row,
+  assign_token(tk, t, local, N, K, cap, bm, blk_base + (int64_t)blockIdx.x * N, offset, pair_row,
                row_pair, dropped);
 }
 
@@ -208,9 +223,10 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
   const int local = threadIdx.x;
   const int64_t t = local < DT ? (int64_t)local : T;  // threads past DT: no token
   if (local == 0) nbad = 0;
-  build_bitmap(idx, T, N, K, bm, t, local, 1024);
+  const TokenIds tk = t < T ? load_token(idx, t, N, K) : TokenIds{};
+  build_bitmap(tk, T, N, K, bm, t, local, 1024);
   if (t < T) {
-    const int mybad = count_bad(idx, t, N, K);
+    const int mybad = __popc(tk.bad);
     if (mybad) atomicAdd(&nbad, mybad);  // integer: order-independent
   }
   for (int e = local; e < N; e += 1024) {
@@ -223,8 +239,9 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
   }
   __syncthreads();
   const int32_t total = scan_kept(skept, scan, N, offset, soff);
-  if (local == 0 && counters) write_counters(counters, total, T, K, nbad, skept, N);
-  if (t < T) assign_token(idx, t, local, N, K, cap, bm, nullptr, soff, pair_row, row_pair, dropped);
+  const int touched = count_touched(skept, N);
+  if (local == 0 && counters) write_counters(counters, total, T, K, nbad, touched);
+  if (t < T) assign_token(tk, t, local, N, K, cap, bm, nullptr, soff, pair_row, row_pair, dropped);
 }
 
 // x_perm[r] = x[row_pair[r] / K] for r < offset[N]; 16-byte chunks.
