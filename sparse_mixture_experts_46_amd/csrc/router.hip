@@ -466,9 +466,18 @@ __global__ __launch_bounds__(256) void router_split_reduce_kernel(
     const float* __restrict__ part, int nsplit, const float* __restrict__ b_r,
     float* __restrict__ logits, int64_t T, int N) {
   const int64_t n = T * (int64_t)N;
+  constexpr int ZB = 16;  // partials loaded together before they are added
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     float acc = part[i];
-    for (int z = 1; z < nsplit; ++z) acc += part[(int64_t)z * n + i];
+    int z = 1;
+    for (; z + ZB <= nsplit; z += ZB) {
+      float v[ZB];
+#pragma unroll
+      for (int u = 0; u < ZB; ++u) v[u] = part[(int64_t)(z + u) * n + i];
+#pragma unroll
+      for (int u = 0; u < ZB; ++u) acc += v[u];
+    }
+    for (; z < nsplit; ++z) acc += part[(int64_t)z * n + i];
     logits[i] = acc + (b_r ? b_r[i % N] : 0.f);
   }
 }
