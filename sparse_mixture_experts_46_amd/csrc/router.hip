@@ -460,26 +460,39 @@ __global__ __launch_bounds__(512, 1) void router_logits_pp_kernel(
 }
 
 
+// part[0][i] + part[1][i] + ... + part[nsplit - 1][i] (planes n apart), added
+// in split order.  With ZB > 1 the partials are loaded ZB at a time before
+// they are added, so a thread has ZB loads in flight instead of one after
+// another (the small batches, whose many splits made this latency-bound);
+// with few splits (the top-K kernel's large batches) the plain loop is
+// cheaper.
+template <int ZB>
+__device__ __forceinline__ float sum_splits(const float* __restrict__ part, int nsplit, int64_t n,
+                                            int64_t i) {
+  float acc = part[i];
+  if (ZB == 1) {
+    for (int z = 1; z < nsplit; ++z) acc += part[(int64_t)z * n + i];
+    return acc;
+  }
+  for (int z = 1; z < nsplit; z += ZB) {
+    float v[ZB];
+#pragma unroll
+    for (int u = 0; u < ZB; ++u) v[u] = z + u < nsplit ? part[(int64_t)(z + u) * n + i] : 0.f;
+#pragma unroll
+    for (int u = 0; u < ZB; ++u)
+      if (z + u < nsplit) acc += v[u];
+  }
+  return acc;
+}
+
 // logits[t, e] = sum_{z = 0, 1, ...} part[z, t, e] + b_r[e] (fixed order): the
 // batches whose top-K kernel does not add the splits itself.
 __global__ __launch_bounds__(256) void router_split_reduce_kernel(
     const float* __restrict__ part, int nsplit, const float* __restrict__ b_r,
     float* __restrict__ logits, int64_t T, int N) {
   const int64_t n = T * (int64_t)N;
-  constexpr int ZB = 16;  // partials loaded together before they are added
-  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    float acc = part[i];
-    int z = 1;
-    for (; z + ZB <= nsplit; z += ZB) {
-      float v[ZB];
-#pragma unroll
-      for (int u = 0; u < ZB; ++u) v[u] = part[(int64_t)(z + u) * n + i];
-#pragma unroll
-      for (int u = 0; u < ZB; ++u) acc += v[u];
-    }
-    for (; z < nsplit; ++z) acc += part[(int64_t)z * n + i];
-    logits[i] = acc + (b_r ? b_r[i % N] : 0.f);
-  }
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    logits[i] = sum_splits<16>(part, nsplit, n, i) + (b_r ? b_r[i % N] : 0.f);
 }
 
 // --------------------------------------------------------------- top-K ----
@@ -666,9 +679,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
       if (e < N) {
         const int64_t i = t * N + e;
         if (nsplit > 1) {
-          float acc = part[i];
-          for (int z = 1; z < nsplit; ++z) acc += part[(int64_t)z * n + i];
-          l[j] = acc + (b_r ? b_r[e] : 0.f);
+          l[j] = sum_splits<1>(part, nsplit, n, i) + (b_r ? b_r[e] : 0.f);
           logits[i] = l[j];
         } else {
           l[j] = logits[i];
@@ -844,9 +855,7 @@ __global__ __launch_bounds__(1024) void router_small_kernel(
       if (e < N) {
         const int64_t i = t * N + e;
         if (nsplit > 1) {
-          float acc = part[i];
-          for (int z = 1; z < nsplit; ++z) acc += part[(int64_t)z * n + i];
-          l[j] = acc + (b_r ? b_r[e] : 0.f);
+          l[j] = sum_splits<16>(part, nsplit, n, i) + (b_r ? b_r[e] : 0.f);
           logits[i] = l[j];
         } else {
           l[j] = logits[i];
