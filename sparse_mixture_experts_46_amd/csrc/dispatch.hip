@@ -15,6 +15,7 @@
 // expert.  The in-block rank of a pair is the popcount of the expert's bits
 // below its token; the rank across blocks adds an exclusive scan of the
 // per-block counts.  Everything is integer and deterministic.
+#include "gemm_common.h"  // build_tile_tables
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     const int32_t* __restrict__ blk_count, const int32_t* __restrict__ blk_bad,
     int64_t nblk, int64_t T, int N, int K, int64_t cap,
     int32_t* __restrict__ blk_base, int32_t* __restrict__ kept_out,
-    int32_t* __restrict__ offset, int32_t* __restrict__ counters) {
+    int32_t* __restrict__ offset, int32_t* __restrict__ counters, TilePlan plan) {
   __shared__ int32_t skept[kMaxExperts];
   __shared__ int32_t scan[1024];
   const int tid = threadIdx.x;
@@ -156,6 +157,9 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     for (int64_t b = 0; b < nblk; ++b) bad += blk_bad[b];
     write_counters(counters, total, T, K, bad, touched);
   }
+  if (plan.nspec > 0)  // the expert FFN's tile tables, from the kept counts
+    build_tile_tables([&](int g) { return skept[g]; }, plan.n_routed, plan.shared_rows, plan.specs,
+                      plan.nspec, plan.base, plan.ctr, plan.nctr);
 }
 
 // Rows of token t's slots: rank among the tokens that chose the expert =
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, int64_t T, int N, int K, int64_t cap,
     int32_t* __restrict__ kept_out, int32_t* __restrict__ offset,
     int32_t* __restrict__ counters, int32_t* __restrict__ pair_row,
-    int32_t* __restrict__ row_pair, uint8_t* __restrict__ dropped) {
+    int32_t* __restrict__ row_pair, uint8_t* __restrict__ dropped, TilePlan plan) {
   extern __shared__ uint32_t bm[];
   __shared__ int32_t skept[kMaxExperts];
   __shared__ int32_t soff[kMaxExperts];
@@ -242,6 +246,9 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
   const int touched = count_touched(skept, N);
   if (local == 0 && counters) write_counters(counters, total, T, K, nbad, touched);
   if (t < T) assign_token(tk, t, local, N, K, cap, bm, nullptr, soff, pair_row, row_pair, dropped);
+  if (plan.nspec > 0)  // the expert FFN's tile tables, from the kept counts
+    build_tile_tables([&](int g) { return skept[g]; }, plan.n_routed, plan.shared_rows, plan.specs,
+                      plan.nspec, plan.base, plan.ctr, plan.nctr);
 }
 
 // x_perm[r] = x[row_pair[r] / K] for r < offset[N]; 16-byte chunks.
@@ -267,20 +274,26 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int N, int K,
                            int32_t* blk_base, int32_t* blk_bad,
                            int32_t* kept, int32_t* offset, int32_t* pair_row,
                            int32_t* row_pair, uint8_t* dropped,
-                           int32_t* counters, hipStream_t stream) {
+                           int32_t* counters, hipStream_t stream, const TilePlan* plan) {
   const int64_t nblk = dispatch_num_blocks(T);
   const size_t smem = (size_t)N * DW * sizeof(uint32_t);
   const int64_t cap = capacity < 0 ? T : capacity;
+  TilePlan tp = {};
+  if (plan) {
+    // the tables' groups are the dispatch's experts
+    if (plan->n_routed != N || plan->nspec < 0 || plan->nspec > 4) return hipErrorInvalidValue;
+    tp = *plan;
+  }
   if (nblk == 1) {
     dispatch_small_kernel<<<1, 1024, smem, stream>>>(idx, T, N, K, cap, kept, offset, counters,
-                                                     pair_row, row_pair, dropped);
+                                                     pair_row, row_pair, dropped, tp);
     return hipGetLastError();
   }
   dispatch_hist_kernel<<<(unsigned)nblk, DT, smem, stream>>>(idx, T, N, K, blk_count, blk_bad);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   dispatch_scan_kernel<<<1, 1024, 0, stream>>>(blk_count, blk_bad, nblk, T, N, K, cap,
-                                               blk_base, kept, offset, counters);
+                                               blk_base, kept, offset, counters, tp);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   dispatch_assign_kernel<<<(unsigned)nblk, DT, smem, stream>>>(

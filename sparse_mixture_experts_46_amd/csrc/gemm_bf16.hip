@@ -155,7 +155,65 @@ size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared, 
   return (h + 255) / 256 * 256;
 }
 
-hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipEvent_t* ev) {
+namespace {
+
+// The tilings of one bf16 expert-FFN launch.
+struct FfnShape {
+  bool swiglu, split2;
+  Kind k, tk;
+  int64_t rows, srows;
+  int G;
+  int bm1, bno1, bm2, bno2, tbm, tbno, sbm2;
+};
+
+FfnShape ffn_shape(const FfnProblem& p) {
+  FfnShape f;
+  f.swiglu = (p.act == 0);
+  f.rows = p.T * p.K;
+  f.srows = p.F_shared > 0 ? p.T : 0;
+  f.G = p.N + (f.srows > 0 ? 1 : 0);
+  const double rpe = (double)f.rows / (double)p.N;
+  f.k = pick_kind(rpe);
+  // With the largest tiles and many rows per expert (> 640) the second GEMM
+  // has only d / 256 column tiles per row tile, so a partial last row tile
+  // per expert can add a whole round of workgroups.  There each group's rows
+  // are split: the main launch covers whole 256-row tiles (the last one at
+  // least half full) and a tail launch of small tiles the remainder (< 128
+  // rows).  With fewer rows per expert most experts would have a tail, each
+  // streaming that expert's weights a second time.  The first GEMM, with its
+  // many column tiles, always runs in one launch: a tail launch would stream
+  // the touched experts' gate/up weights a second time, which costs more
+  // than the partial tiles it saves.
+  f.split2 = (f.k == K_BIG) && rpe > 640.0;
+  kind_dims(f.k, f.swiglu, &f.bm1, &f.bno1);
+  kind_dims(f.k, false, &f.bm2, &f.bno2);
+  f.tk = (p.F % 128 == 0) ? K_TAIL : K_TAIL64;  // K of GEMM 2 is F
+  kind_dims(f.tk, false, &f.tbm, &f.tbno);
+  f.sbm2 = f.split2 ? f.bm2 : 0;
+  return f;
+}
+
+}  // namespace
+
+bool plan_expert_ffn_tiles(const FfnProblem& p, TilePlan* plan) {
+  if (!p.bf16) return false;
+  const FfnShape f = ffn_shape(p);
+  *plan = {};
+  plan->specs.s[0] = {f.bm1, f.bno1, p.F, p.F_shared, 0, 0};
+  plan->specs.s[1] = {f.bm2, f.bno2, p.d, p.d, f.sbm2, 0};
+  plan->specs.s[2] = {f.tbm, f.tbno, p.d, p.d, f.sbm2, 1};
+  plan->nspec = f.split2 ? 3 : 2;
+  plan->n_routed = p.N;
+  plan->shared_rows = f.srows;
+  plan->base = p.tile_base;
+  // walk counters after the three tables: 8 for each ping-pong launch
+  plan->ctr = p.tile_base + 3 * (p.N + 2);
+  plan->nctr = kWalkCounters;
+  return true;
+}
+
+hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipEvent_t* ev,
+                             bool tables_ready) {
   auto mark = [&](int i) -> hipError_t {
     return (ev && ev[i]) ? hipEventRecord(ev[i], stream) : hipSuccess;
   };
@@ -167,41 +225,24 @@ hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipE
       if ((err = mark(i)) != hipSuccess) return err;
     return hipSuccess;
   }
-  const bool swiglu = (p.act == 0);
-  const int64_t rows = p.T * p.K;
-  const int64_t srows = p.F_shared > 0 ? p.T : 0;
-  const int G = p.N + (srows > 0 ? 1 : 0);
-  const double rpe = (double)rows / (double)p.N;
-  const Kind k = pick_kind(rpe);
-  // With the largest tiles and many rows per expert (> 640) the second GEMM
-  // has only d / 256 column tiles per row tile, so a partial last row tile
-  // per expert can add a whole round of workgroups.  There each group's rows
-  // are split: the main launch covers whole 256-row tiles (the last one at
-  // least half full) and a tail launch of small tiles the remainder (< 128
-  // rows).  With fewer rows per expert most experts would have a tail, each
-  // streaming that expert's weights a second time.  The first GEMM, with its
-  // many column tiles, always runs in one launch: a tail launch would stream
-  // the touched experts' gate/up weights a second time, which costs more
-  // than the partial tiles it saves.
-  const bool split2 = (k == K_BIG) && rpe > 640.0;
-  int bm1, bno1, bm2, bno2, tbm, tbno;
-  kind_dims(k, swiglu, &bm1, &bno1);
-  kind_dims(k, false, &bm2, &bno2);
-  const Kind tk = (p.F % 128 == 0) ? K_TAIL : K_TAIL64;  // K of GEMM 2 is F
-  kind_dims(tk, false, &tbm, &tbno);
-  const int sbm2 = split2 ? bm2 : 0;
+  const FfnShape f = ffn_shape(p);
+  const bool swiglu = f.swiglu, split2 = f.split2;
+  const Kind k = f.k, tk = f.tk;
+  const int64_t rows = f.rows, srows = f.srows;
+  const int G = f.G;
+  const int bm1 = f.bm1, bno1 = f.bno1, bm2 = f.bm2, bno2 = f.bno2, tbm = f.tbm, tbno = f.tbno;
+  const int sbm2 = f.sbm2;
   int32_t* base[3];
   for (int i = 0; i < 3; ++i) base[i] = p.tile_base + i * (p.N + 2);
-  TileSpecs specs = {};
-  specs.s[0] = {bm1, bno1, p.F, p.F_shared, 0, 0};
-  specs.s[1] = {bm2, bno2, p.d, p.d, sbm2, 0};
-  specs.s[2] = {tbm, tbno, p.d, p.d, sbm2, 1};
-  // walk counters after the three tables: 8 for each ping-pong launch
   int32_t* ctr = p.tile_base + 3 * (p.N + 2);
-  tile_setup_kernel<<<1, 1024, 0, stream>>>(p.offset, p.N, srows, specs, split2 ? 3 : 2,
-                                            p.tile_base, ctr, kWalkCounters);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (!tables_ready) {
+    TilePlan plan;
+    plan_expert_ffn_tiles(p, &plan);
+    tile_setup_kernel<<<1, 1024, 0, stream>>>(p.offset, p.N, srows, plan.specs, plan.nspec,
+                                              plan.base, plan.ctr, plan.nctr);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
 
   const int Fm = p.F > p.F_shared ? p.F : p.F_shared;
   uint16_t* h = (uint16_t*)p.h;

@@ -8,6 +8,7 @@
 #pragma once
 
 #include "moe_common.h"
+#include "moe_internal.h"  // TileSpecs
 
 namespace moe {
 
@@ -165,27 +166,20 @@ __device__ __forceinline__ TileInfo resolve_tile(const GemmArgs& p, int tile, in
 }
 
 // ------------------------------------------------------------ tile setup --
-// One tiling of the groups: tile height bm, bno output columns per tile,
-// output widths of the routed / shared groups, and the row region.
-struct TileSpec {
-  int bm, bno, nout, nout_s, split_bm, region;
-};
-
-struct TileSpecs {
-  TileSpec s[4];
-};
-
-// base[k][g] = sum_{g' < g} tiles of group g' under spec k (k < nspec);
-// tables are (n_routed + 2) apart.  Also zeroes nctr walk counters at ctr.
-// One block of 1024 threads.
-static __global__ __launch_bounds__(1024) void tile_setup_kernel(
-    const int32_t* __restrict__ offset, int n_routed, int64_t shared_rows, TileSpecs specs,
-    int nspec, int32_t* __restrict__ base, int32_t* __restrict__ ctr = nullptr, int nctr = 0) {
+// base[k][g] = sum_{g' < g} tiles of group g' under spec k (k < nspec); tables
+// are (n_routed + 2) apart, and base[k][G] is the total.  Also zeroes nctr
+// walk counters at ctr.  Called by every thread of one block of 1024
+// threads; rows(g) gives the rows of group g (the shared group is n_routed).
+template <class Rows>
+__device__ __forceinline__ void build_tile_tables(Rows rows, int n_routed, int64_t shared_rows,
+                                                  const TileSpecs& specs, int nspec,
+                                                  int32_t* __restrict__ base,
+                                                  int32_t* __restrict__ ctr, int nctr) {
   __shared__ int32_t cnt[4][1040];
   if ((int)threadIdx.x < nctr) ctr[threadIdx.x] = 0;
   const int G = n_routed + (shared_rows > 0 ? 1 : 0);
   for (int g = threadIdx.x; g < G; g += 1024) {
-    const int M = g < n_routed ? (int)(offset[g + 1] - offset[g]) : (int)shared_rows;
+    const int M = g < n_routed ? rows(g) : (int)shared_rows;
     for (int k = 0; k < nspec; ++k) {
       const TileSpec& sp = specs.s[k];
       int first, count;
@@ -195,7 +189,7 @@ static __global__ __launch_bounds__(1024) void tile_setup_kernel(
     }
   }
   __syncthreads();
-  if (threadIdx.x < nspec) {  // G <= 1025: a short serial scan per table
+  if ((int)threadIdx.x < nspec) {  // G <= 1025: a short serial scan per table
     const int k = threadIdx.x;
     int32_t* b = base + (int64_t)k * (n_routed + 2);
     int32_t r = 0;
@@ -205,6 +199,15 @@ static __global__ __launch_bounds__(1024) void tile_setup_kernel(
     }
     b[G] = r;
   }
+}
+
+// The tables from the dispatch offsets (the FFN's own launch).  One block
+// of 1024 threads.
+static __global__ __launch_bounds__(1024) void tile_setup_kernel(
+    const int32_t* __restrict__ offset, int n_routed, int64_t shared_rows, TileSpecs specs,
+    int nspec, int32_t* __restrict__ base, int32_t* __restrict__ ctr = nullptr, int nctr = 0) {
+  build_tile_tables([&](int g) { return (int)(offset[g + 1] - offset[g]); }, n_routed,
+                    shared_rows, specs, nspec, base, ctr, nctr);
 }
 
 }  // namespace moe

@@ -272,12 +272,14 @@ moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void
   return MOE_OK;
 }
 
+// plan (nullable): the expert FFN's tile tables, built at the dispatch's end
 moe_status_t do_dispatch(const moe_config_t* c, const int32_t* idx, const moe_dispatch_t* o,
-                         void* ws, hipStream_t s) {
+                         void* ws, hipStream_t s, const TilePlan* plan = nullptr) {
   const DispatchWs L = dispatch_ws(c);
   hipError_t e = launch_dispatch(idx, c->T, c->N, c->K, c->capacity, at<int32_t>(ws, L.blk_count),
                                  at<int32_t>(ws, L.blk_base), at<int32_t>(ws, L.blk_bad), o->kept,
-                                 o->offset, o->pair_row, o->row_pair, o->dropped, o->counters, s);
+                                 o->offset, o->pair_row, o->row_pair, o->dropped, o->counters, s,
+                                 plan);
   return hip_status(e);
 }
 
@@ -439,10 +441,6 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   if ((st = mark(0)) != MOE_OK) return st;
   st = do_router(cfg, w, x, idx, gate, out->logits, &out->stats, at<void>(ws, L.router), s);
   if (st != MOE_OK) return st;
-  if ((st = mark(1)) != MOE_OK) return st;
-  st = do_dispatch(cfg, idx, &d, at<void>(ws, L.dispatch), s);
-  if (st != MOE_OK) return st;
-
   const FfnWs FL = ffn_ws(cfg);
   unsigned char* fws = at<unsigned char>(ws, L.ffn);
   FfnProblem p = {};
@@ -457,10 +455,18 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   p.y_shared = cfg->F_shared > 0 ? at<void>(ws, L.y_shared) : nullptr;
   p.h = fws + FL.h;
   p.tile_base = (int32_t*)(fws + FL.tile_base);
+  // the dispatch builds the FFN's tile tables at its end (one launch fewer)
+  TilePlan plan;
+  const bool planned = plan_expert_ffn_tiles(p, &plan);
+
+  if ((st = mark(1)) != MOE_OK) return st;
+  st = do_dispatch(cfg, idx, &d, at<void>(ws, L.dispatch), s, planned ? &plan : nullptr);
+  if (st != MOE_OK) return st;
+
   hipEvent_t fev[4] = {};
   if (trace)
     for (int i = 0; i < 4; ++i) fev[i] = (hipEvent_t)trace->ev[2 + i];
-  if (launch_expert_ffn(p, s, fev) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_expert_ffn(p, s, fev, planned) != hipSuccess) return MOE_ERR_HIP;
   if (launch_combine(p.y_perm, d.pair_row, gate, p.y_shared, out->y, cfg->T, cfg->d, cfg->K,
                      p.bf16, s) != hipSuccess)
     return MOE_ERR_HIP;

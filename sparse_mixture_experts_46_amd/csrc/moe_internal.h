@@ -80,17 +80,45 @@ hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
                                const float* b_sel, float* b_sel_out, float bias_rate,
                                hipStream_t stream);
 
+// ----------------------------------------------------------- tile tables --
+// One tiling of the expert groups: tile height bm, bno output columns per
+// tile, output widths of the routed / shared groups, and the row region (see
+// main_rows in gemm_common.h).
+struct TileSpec {
+  int bm, bno, nout, nout_s, split_bm, region;
+};
+
+struct TileSpecs {
+  TileSpec s[4];
+};
+
+// The tile tables of one expert-FFN launch: nspec tilings (0: none), tables
+// (n_routed + 2) apart from base, and nctr walk counters at ctr to zero.
+// The dispatch kernels build them at their end when given one, which saves
+// the FFN its own table launch.
+struct TilePlan {
+  TileSpecs specs;
+  int nspec;
+  int n_routed;
+  int64_t shared_rows;
+  int32_t* base;
+  int32_t* ctr;
+  int nctr;
+};
+
 // -------------------------------------------------------------- dispatch --
 constexpr int kDispatchTokens = 256;  // tokens per dispatch block
 constexpr int kWalkCounters = 16;     // tile-walk counters of the two grouped GEMMs (8 each)
 int64_t dispatch_num_blocks(int64_t T);
 
+// plan (nullable): tile tables to build from the kept counts (see TilePlan)
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int N, int K,
                            int64_t capacity, int32_t* blk_count,
                            int32_t* blk_base, int32_t* blk_bad,
                            int32_t* kept, int32_t* offset, int32_t* pair_row,
                            int32_t* row_pair, uint8_t* dropped,
-                           int32_t* counters, hipStream_t stream);
+                           int32_t* counters, hipStream_t stream,
+                           const TilePlan* plan = nullptr);
 
 hipError_t launch_permute(const void* x, int elem_bytes, const int32_t* row_pair,
                           const int32_t* offset, int N, int K, int d,
@@ -135,10 +163,16 @@ bool ffn_saves_uv(int64_t T, int K, int N, int act, bool bf16);
 
 size_t ffn_workspace_bytes(int64_t T, int d, int N, int K, int F, int F_shared,
                            bool bf16);
+// The tile tables launch_expert_ffn(p) uses; false when it uses none (fp32
+// layers).
+bool plan_expert_ffn_tiles(const FfnProblem& p, TilePlan* plan);
+
 // ev (nullable, else 4 nullable events): recorded before the first grouped
 // GEMM, after it, after the main launch of the second grouped GEMM and after
-// its tail launch.
-hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipEvent_t* ev);
+// its tail launch.  tables_ready: the tables of plan_expert_ffn_tiles(p) were
+// built on the stream already (by the dispatch), so they are not built again.
+hipError_t launch_expert_ffn(const FfnProblem& p, hipStream_t stream, const hipEvent_t* ev,
+                             bool tables_ready = false);
 
 // ----------------------------------------------------------- quantization --
 // w bf16 [rows, cols] -> q int8 [rows, cols], scale fp32 [rows]; cols % 8 == 0
