@@ -339,6 +339,13 @@ LAYER_SMALL = [
     WL.scaled(WL.DEEPSEEK_PREFILL, T=300, d=256, F=128, F_shared=128, N=64, name="deepseek_small"),
     WL.scaled(WL.DEEPSEEK_DECODE, T=20, d=256, F=128, F_shared=128, N=64, name="deepseek_decode_small"),
     WL.scaled(WL.MIXTRAL_DECODE, T=16, d=256, F=512, name="mixtral_decode_small"),
+    # the most experts the library takes, plus a shared group (1025 groups):
+    # the dispatch builds the FFN's tile tables in its one-block kernel (96
+    # tokens) and in its scan kernel (600 tokens, three dispatch blocks)
+    WL.scaled(WL.DEEPSEEK_DECODE, T=96, d=64, F=64, F_shared=64, N=1024, K=4,
+              name="n1024_shared_one_block"),
+    WL.scaled(WL.DEEPSEEK_PREFILL, T=600, d=64, F=64, F_shared=64, N=1024, K=4,
+              name="n1024_shared_scan"),
 ]
 
 
