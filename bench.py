@@ -475,10 +475,11 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w, inp, sample, seeded=False, repeats=1):
+def cpu_baseline(w, inp, sample, seeded=False, repeats=1, single_core=False):
     """The oracle, as it stands, on `sample` tokens of the same workload with
     the same weights (the first ones, or a seeded random set): routing over
-    those tokens, capacity, experts, combine.  Median of `repeats` runs."""
+    those tokens, capacity, experts, combine.  Median of `repeats` runs; with
+    single_core, the same again with the BLAS library held to one thread."""
     import numpy as np
     import torch
 
@@ -513,18 +514,32 @@ def cpu_baseline(w, inp, sample, seeded=False, repeats=1):
     else:
         x = f64(inp["x"][:sample])
         which = f"first {sample} of {w.T} tokens"
-    times = []
-    for _ in range(repeats):
-        t0 = time.perf_counter()
-        ref.layer_forward(x, W, K=w.K, act=w.act, gate_mode=w.gate, cf=w.cf, alpha=w.aux_alpha,
-                          b_r=f64(inp["b_r"]), b_sel=f64(inp["b_sel"]), shared=shared)
-        times.append(time.perf_counter() - t0)
-    dt = float(np.median(times))
+    def timed():
+        times = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            ref.layer_forward(x, W, K=w.K, act=w.act, gate_mode=w.gate, cf=w.cf,
+                              alpha=w.aux_alpha, b_r=f64(inp["b_r"]), b_sel=f64(inp["b_sel"]),
+                              shared=shared)
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times))
+
+    dt = timed()
     med = f", median of {repeats} runs" if repeats > 1 else ""
-    return {"value": sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "cpu": cpu_model(), "seconds": dt,
-            "sample": f"{which} of {w.name} (same weights), full layer in NumPy float64 "
-                      f"incl. per-expert bf16->fp64 weight widening{med}; {dt:.3g} s"}
+    rec = {"value": sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "cpu": cpu_model(), "seconds": dt,
+           "sample": f"{which} of {w.name} (same weights), full layer in NumPy float64 "
+                     f"incl. per-expert bf16->fp64 weight widening{med}; {dt:.3g} s"}
+    if single_core:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1, user_api="blas"):
+                dt1 = timed()
+            rec["single_core"] = {"value": sample / dt1, "unit": "tokens/s", "cores": 1,
+                                  "seconds": dt1}
+        except Exception as e:  # threadpoolctl missing or unable to limit
+            rec["single_core"] = {"error": repr(e)}
+    return rec
 
 
 def counter_record(name, weights, stage):
@@ -638,10 +653,10 @@ def main():
     if not a.no_extra:
         # the other layer shapes; the oracle's sample for each: every token
         # where that is seconds of CPU work, else a seeded 512-token set
-        extra = [(WL.SWITCH_TOP1, {"sample": WL.SWITCH_TOP1.T}),
+        extra = [(WL.SWITCH_TOP1, {"sample": WL.SWITCH_TOP1.T, "single_core": True}),
                  (WL.DEEPSEEK_PREFILL, {"sample": 512, "seeded": True}),
                  (WL.MIXTRAL_DECODE, {"sample": WL.MIXTRAL_DECODE.T}),
-                 (WL.TINY, {"sample": WL.TINY.T, "repeats": 10})]
+                 (WL.TINY, {"sample": WL.TINY.T, "repeats": 10, "single_core": True})]
         line["workloads"] = {}
         for we, cpu in extra:
             if we.name == w.name:
