@@ -238,6 +238,21 @@ moe_status_t do_router(const moe_config_t* c, const moe_weights_t* w, const void
   float* loss = st ? st->loss : nullptr;
   float* entropy = st ? st->entropy : nullptr;
   float* b_out = st ? st->b_sel_out : nullptr;
+  if (router_fused_path(c->T, c->N, bf16)) {
+    hipError_t e = launch_router_fused(x, w->w_r, w->b_r, router_noise(c, w), w->b_sel, lg, idx,
+                                       gate, at<float>(ws, L.part_p), at<int32_t>(ws, L.part_cnt),
+                                       at<float>(ws, L.part_z), c->T, c->d, c->N, c->K, c->gate,
+                                       s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (count || f || p || loss || entropy || b_out) {
+      e = launch_router_stats(at<float>(ws, L.part_p), at<int32_t>(ws, L.part_cnt),
+                              at<float>(ws, L.part_z), at<float>(ws, L.part_fp),
+                              router_num_blocks(c->T), c->T, c->N, c->K, c->aux_alpha, count, f,
+                              p, loss, entropy, w->b_sel, b_out, c->bias_rate, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+  }
   if (router_small_path(c->T, c->N)) {
     hipError_t e = launch_router_logits(x, bf16, w->w_r, w->b_r, at<uint16_t>(ws, L.planes),
                                         at<float>(ws, L.split), lg, c->T, c->d, c->N, s,

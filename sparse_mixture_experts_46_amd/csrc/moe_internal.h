@@ -58,6 +58,17 @@ hipError_t launch_router_topk(float* logits, const float* part, int nsplit, cons
                               float* gate, float* part_p, int32_t* part_cnt, float* part_z,
                               int64_t T, int N, int K, int gate_mode, hipStream_t stream);
 
+// Few experts with bf16 x above kRouterSmallT tokens (router_fused_path:
+// N <= 16): logits, top-K, gates and the per-block partials (as
+// launch_router_topk) in one kernel, without K splits or planes;
+// launch_router_stats follows.
+bool router_fused_path(int64_t T, int N, bool x_bf16);
+hipError_t launch_router_fused(const void* x, const float* w_r, const float* b_r,
+                               const RouterNoise& noise, const float* b_sel, float* logits,
+                               int32_t* idx, float* gate, float* part_p, int32_t* part_cnt,
+                               float* part_z, int64_t T, int d, int N, int K, int gate_mode,
+                               hipStream_t stream);
+
 // Small batches (router_small_path): one workgroup reduces the logit splits
 // (part from launch_router_logits without its reduction; nsplit =
 // router_num_splits), selects, gates and writes the statistics.  Null

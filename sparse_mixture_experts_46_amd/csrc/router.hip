@@ -727,11 +727,50 @@ __device__ __forceinline__ float bias_step(const float* b_sel, int e, int64_t co
 // (c = t / 64) in increasing j; the first 64 threads add the 16 chunk sums
 // in order and write count, f and p; thread 0 adds the block's f_e * p_e in
 // expert order into part_fp[b].  Every sum runs in a fixed order.
+// Loss terms: aux = alpha * N * aux_sum (aux_sum: the part_fp values added in
+// block order); z and z_lse from the per-token-block partials (strided sums,
+// then a fixed tree).  Called by every thread of a block of 1024.
+__device__ __forceinline__ void stats_final_body(float aux_sum, const float* __restrict__ part_z,
+                                                 int64_t nblk, int64_t T, int N, float alpha,
+                                                 float* __restrict__ loss,
+                                                 float* __restrict__ entropy) {
+  __shared__ float rz[1024], rl[1024], rh[1024];
+  const int tid = threadIdx.x;
+  float z = 0.f, zl = 0.f, h = 0.f;
+  for (int64_t b = tid; b < nblk; b += 1024) {
+    z += part_z[3 * b];
+    zl += part_z[3 * b + 1];
+    h += part_z[3 * b + 2];
+  }
+  rz[tid] = z;
+  rl[tid] = zl;
+  rh[tid] = h;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (tid < o) {
+      rz[tid] += rz[tid + o];
+      rl[tid] += rl[tid + o];
+      rh[tid] += rh[tid + o];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const float invT = 1.0f / (float)T;
+    if (loss) {
+      loss[0] = alpha * (float)N * aux_sum;
+      loss[1] = rz[0] * invT;
+      loss[2] = rl[0] * invT;
+    }
+    if (entropy) entropy[0] = rh[0] * invT;
+  }
+}
+
 __global__ __launch_bounds__(1024) void router_stats_expert_kernel(
     const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt, int64_t nblk,
     int64_t T, int N, int K, int32_t* __restrict__ count, float* __restrict__ f,
     float* __restrict__ p, float* __restrict__ part_fp, const float* b_sel, float* b_out,
-    float bias_rate) {
+    float bias_rate, const float* __restrict__ part_z, float alpha, float* __restrict__ loss,
+    float* __restrict__ entropy) {
   __shared__ float sp[1024];
   __shared__ int64_t sc[1024];
   __shared__ float red[64];
@@ -740,7 +779,24 @@ __global__ __launch_bounds__(1024) void router_stats_expert_kernel(
   float s = 0.f;
   int64_t cnt = 0;
   if (e < N) {
-    for (int64_t j = c; j < nblk; j += 16) {
+    // eight partials loaded before they are added (in the same order): one
+    // dependent load per partial made this latency-bound
+    int64_t j = c;
+    for (; j + 16 * 7 < nblk; j += 16 * 8) {
+      float v[8];
+      int32_t q[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        v[u] = part_p[(j + 16 * u) * N + e];
+        q[u] = part_cnt[(j + 16 * u) * N + e];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s += v[u];
+        cnt += q[u];
+      }
+    }
+    for (; j < nblk; j += 16) {
       s += part_p[j * N + e];
       cnt += part_cnt[j * N + e];
     }
@@ -768,51 +824,165 @@ __global__ __launch_bounds__(1024) void router_stats_expert_kernel(
     red[tid] = fp;
   }
   __syncthreads();
+  __shared__ float fp_sum;
   if (tid == 0) {
     float acc = 0.f;
     for (int i = 0; i < 64; ++i) acc += red[i];
     part_fp[blockIdx.x] = acc;
+    fp_sum = acc;
+  }
+  if (gridDim.x == 1 && (loss || entropy)) {
+    // one block holds every expert: the loss terms here, without a launch
+    __syncthreads();
+    stats_final_body(0.f + fp_sum, part_z, nblk, T, N, alpha, loss, entropy);
   }
 }
 
-// Loss terms: aux = alpha * N * (sum of part_fp in block order); z and z_lse
-// from the per-token-block partials (strided sums, then a fixed tree).
+// The loss terms of more than 64 experts (several expert blocks).
 __global__ __launch_bounds__(1024) void router_stats_final_kernel(
     const float* __restrict__ part_fp, int nfp, const float* __restrict__ part_z, int64_t nblk,
     int64_t T, int N, float alpha, float* __restrict__ loss, float* __restrict__ entropy) {
-  __shared__ float rz[1024], rl[1024], rh[1024];
-  const int tid = threadIdx.x;
-  float z = 0.f, zl = 0.f, h = 0.f;
-  for (int64_t b = tid; b < nblk; b += 1024) {
-    z += part_z[3 * b];
-    zl += part_z[3 * b + 1];
-    h += part_z[3 * b + 2];
-  }
-  rz[tid] = z;
-  rl[tid] = zl;
-  rh[tid] = h;
-  __syncthreads();
-  for (int o = 512; o > 0; o >>= 1) {
-    if (tid < o) {
-      rz[tid] += rz[tid + o];
-      rl[tid] += rl[tid + o];
-      rh[tid] += rh[tid + o];
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    const float invT = 1.0f / (float)T;
-    if (loss) {
-      float aux = 0.f;
-      for (int i = 0; i < nfp; ++i) aux += part_fp[i];
-      loss[0] = alpha * (float)N * aux;
-      loss[1] = rz[0] * invT;
-      loss[2] = rl[0] * invT;
-    }
-    if (entropy) entropy[0] = rh[0] * invT;
-  }
+  float aux = 0.f;
+  for (int i = 0; i < nfp; ++i) aux += part_fp[i];
+  stats_final_body(aux, part_z, nblk, T, N, alpha, loss, entropy);
 }
 
+
+// ------------------------------------------------- few experts, fused ----
+// N <= 16 with bf16 x: the logits, softmax, top-K, gates and the block's
+// partial statistics in one kernel.  The logit GEMM is then 2 T d N flops,
+// too few to fill matrix-core tiles, so it runs as fp32 FMAs (each product
+// of a bf16 x and an fp32 weight is exact inside the fma; the sums are
+// fp32), with x read once.
+//  * A block takes tpb tokens in groups of G = 64 / NE (NE = 8 or 16, >= N).
+//    Its NW waves split d: wave w, lane l take the 8 columns from
+//    8 (l + 64 (w + NW i)), i = 0, 1, ..., and keep one partial per (token,
+//    expert) of the group, 64 per lane, each summed in column order.
+//  * A butterfly over the lanes (strides 32, 16, ..., 1; at stride s a lane
+//    keeps the upper half of its values when its bit s is set, else the
+//    lower half, and adds the partner's copy of that half) leaves lane L
+//    with the wave's partial for token L / NE, expert L % NE.  The logit is
+//    the wave partials added in wave order, then + b_r.
+//  * Then one wave per token as in the top-K kernel (topk_one_token), and
+//    the block's partial sums in the same layout, for router_stats.
+// (A one-block form for T <= 64, statistics included, measured no faster
+// than the split logits kernel and the small-batch kernel there: 18.6 us
+// against 19.4 on the Mixtral-shaped decode; latency-bound on one CU.)
+template <int NE, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void router_fused_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ b_r,
+    RouterNoise noise, const float* __restrict__ b_sel, float* __restrict__ logits,
+    int32_t* __restrict__ idx, float* __restrict__ gate, float* __restrict__ part_p,
+    int32_t* __restrict__ part_cnt, float* __restrict__ part_z, int64_t T, int d, int N, int K,
+    int gate_mode, int tpb) {
+  static_assert(NE == 8 || NE == 16, "8 or 16 expert slots");
+  constexpr int G = 64 / NE;
+  __shared__ float red[NW][64];
+  __shared__ float sp[NW][16];
+  __shared__ int32_t scnt[16];
+  __shared__ float sz[NW][3];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < 16) scnt[tid] = 0;
+  __syncthreads();
+
+  float pacc[1] = {0.f}, bsel[1];
+  bsel[0] = (b_sel && lane < N) ? b_sel[lane] : 0.f;
+  float zsum = 0.f, lsum = 0.f, hsum = 0.f;
+  const int64_t tb0 = (int64_t)blockIdx.x * tpb;
+  const int64_t tend = tb0 + tpb < T ? tb0 + tpb : T;
+  for (int64_t t0 = tb0; t0 < tend; t0 += G) {
+    float acc[64];
+#pragma unroll
+    for (int v = 0; v < 64; ++v) acc[v] = 0.f;
+    for (int k = 8 * (lane + 64 * wave); k < d; k += 8 * 64 * NW) {
+      // every load of the pass issued before the first fma, with the token
+      // and expert indices clamped in range instead of tested, so that one
+      // memory latency covers them all; the slots past tend or N then hold
+      // duplicates that are never read
+      uint4 xr[G];  // 8 bf16 of each token of the group
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int64_t tt = t0 + g < tend ? t0 + g : tend - 1;
+        xr[g] = *(const uint4*)(x + tt * d + k);
+      }
+      float4 wa[NE], wb[NE];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int ee = e < N ? e : N - 1;
+        wa[e] = *(const float4*)(w_r + (int64_t)ee * d + k);
+        wb[e] = *(const float4*)(w_r + (int64_t)ee * d + k + 4);
+      }
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float a = acc[g * NE + e];
+          a = fmaf(__uint_as_float(xr[g].x << 16), wa[e].x, a);
+          a = fmaf(__uint_as_float(xr[g].x & 0xffff0000u), wa[e].y, a);
+          a = fmaf(__uint_as_float(xr[g].y << 16), wa[e].z, a);
+          a = fmaf(__uint_as_float(xr[g].y & 0xffff0000u), wa[e].w, a);
+          a = fmaf(__uint_as_float(xr[g].z << 16), wb[e].x, a);
+          a = fmaf(__uint_as_float(xr[g].z & 0xffff0000u), wb[e].y, a);
+          a = fmaf(__uint_as_float(xr[g].w << 16), wb[e].z, a);
+          a = fmaf(__uint_as_float(xr[g].w & 0xffff0000u), wb[e].w, a);
+          acc[g * NE + e] = a;
+        }
+      }
+    }
+    // butterfly: 64 values per lane -> one (token, expert) partial per lane
+#pragma unroll
+    for (int st = 0; st < 6; ++st) {
+      const int s = 32 >> st;  // stride, and half the values still held
+      const bool up = (lane & s) != 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i < s) {
+          const float send = up ? acc[i] : acc[i + s];
+          const float keep = up ? acc[i + s] : acc[i];
+          acc[i] = keep + __shfl_xor(send, s);
+        }
+      }
+    }
+    red[wave][lane] = acc[0];
+    __syncthreads();
+    for (int g = wave; g < G; g += NW) {
+      const int64_t t = t0 + g;
+      if (t >= tend) break;
+      float l[1];
+      if (lane < N) {
+        float v = red[0][g * NE + lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[w][g * NE + lane];
+        v += b_r ? b_r[lane] : 0.f;
+        logits[t * N + lane] = v;
+        if (noise_on(noise)) v += noise.std * noise_draw(noise, t * N + lane);
+        l[0] = v;
+      } else {
+        l[0] = -INFINITY;
+      }
+      topk_one_token<1>(l, bsel, lane, N, K, gate_mode, pacc, zsum, lsum, hsum, idx + t * K,
+                        gate + t * K, scnt);
+    }
+    __syncthreads();  // red is read before the next group writes it
+  }
+  if (lane < N) sp[wave][lane] = pacc[0];
+  if (lane == 0) { sz[wave][0] = zsum; sz[wave][1] = lsum; sz[wave][2] = hsum; }
+  __syncthreads();
+  if (tid < N) {
+    float v = sp[0][tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += sp[w][tid];
+    part_p[(int64_t)blockIdx.x * N + tid] = v;
+    part_cnt[(int64_t)blockIdx.x * N + tid] = scnt[tid];
+  }
+  if (tid < 3) {
+    float v = sz[0][tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += sz[w][tid];
+    part_z[blockIdx.x * 3 + tid] = v;
+  }
+}
 
 // ------------------------------------------------------- small batches ----
 // Everything after the logit GEMM in one workgroup of 16 waves, for small T:
@@ -929,12 +1099,16 @@ int router_tile_m(int64_t T, bool x_bf16) {
   return (x_bf16 && T >= 1024) ? 128 : 64;
 }
 
+bool router_fused_path(int64_t T, int N, bool x_bf16) {
+  return x_bf16 && N <= 16 && T > kRouterSmallT;
+}
+
 bool router_gemm_path(int64_t T, int d, int N, bool x_bf16) {
   // From 1024 tokens on: below that, writing and re-reading the planes costs
   // more than the register-staged kernel's fp32 weight reads.  32-bit byte
   // offsets into x and into the planes.
-  return x_bf16 && T >= 1024 && d % 64 == 0 && (int64_t)2 * T * d < (int64_t(1) << 32) &&
-         (int64_t)6 * N * d < (int64_t(1) << 32);
+  return x_bf16 && !router_fused_path(T, N, x_bf16) && T >= 1024 && d % 64 == 0 &&
+         (int64_t)2 * T * d < (int64_t(1) << 32) && (int64_t)6 * N * d < (int64_t(1) << 32);
 }
 
 size_t router_planes_bytes(int64_t T, int d, int N, bool x_bf16) {
@@ -942,6 +1116,7 @@ size_t router_planes_bytes(int64_t T, int d, int N, bool x_bf16) {
 }
 
 int router_num_splits(int64_t T, int d, int N, bool x_bf16) {
+  if (router_fused_path(T, N, x_bf16)) return 1;
   if (router_gemm_path(T, d, N, x_bf16)) {
     // >= 256 workgroups (one per CU), each at least one 64-wide K block
     const int64_t tiles = ((T + RG_BM - 1) / RG_BM) * ((N + RG_BE - 1) / RG_BE);
@@ -1036,11 +1211,24 @@ hipError_t launch_router_stats(const float* part_p, const int32_t* part_cnt,
   const int nfp = (N + 63) / 64;
   router_stats_expert_kernel<<<nfp, 1024, 0, stream>>>(part_p, part_cnt, nblk, T, N, K, count,
                                                        f, p, part_fp, b_sel, b_sel_out,
-                                                       bias_rate);
+                                                       bias_rate, part_z, alpha, loss, entropy);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || (!loss && !entropy)) return e;
+  if (e != hipSuccess || (!loss && !entropy) || nfp == 1) return e;
   router_stats_final_kernel<<<1, 1024, 0, stream>>>(part_fp, nfp, part_z, nblk, T, N, alpha, loss,
                                                     entropy);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_fused(const void* x, const float* w_r, const float* b_r,
+                               const RouterNoise& noise, const float* b_sel, float* logits,
+                               int32_t* idx, float* gate, float* part_p, int32_t* part_cnt,
+                               float* part_z, int64_t T, int d, int N, int K, int gate_mode,
+                               hipStream_t stream) {
+  const int tpb = router_tokens_per_block(T);
+  const unsigned nblk = (unsigned)((T + tpb - 1) / tpb);
+  auto kern = N <= 8 ? router_fused_kernel<8, 4> : router_fused_kernel<16, 4>;
+  kern<<<nblk, 256, 0, stream>>>((const uint16_t*)x, w_r, b_r, noise, b_sel, logits, idx, gate,
+                                 part_p, part_cnt, part_z, T, d, N, K, gate_mode, tpb);
   return hipGetLastError();
 }
 
