@@ -679,7 +679,11 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
       if (e < N) {
         const int64_t i = t * N + e;
         if (nsplit > 1) {
-          l[j] = sum_splits<1>(part, nsplit, n, i) + (b_r ? b_r[e] : 0.f);
+          // many splits (few expert tiles, e.g. 64 experts: 8 splits): eight
+          // partials in flight at a time; two: the plain loop, which measured
+          // faster there
+          l[j] = (nsplit > 2 ? sum_splits<8>(part, nsplit, n, i) : sum_splits<1>(part, nsplit, n, i)) +
+                 (b_r ? b_r[e] : 0.f);
           logits[i] = l[j];
         } else {
           l[j] = logits[i];
