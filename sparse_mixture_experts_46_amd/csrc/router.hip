@@ -853,8 +853,8 @@ __global__ __launch_bounds__(1024) void router_stats_final_kernel(
 
 
 // ------------------------------------------------- few experts, fused ----
-// N <= 16 with bf16 x: the logits, softmax, top-K, gates and the block's
-// partial statistics in one kernel.  The logit GEMM is then 2 T d N flops,
+// N <= 16 with bf16 x, more than 64 tokens: the logits, softmax, top-K,
+// gates and the block's partial statistics in one kernel.  The logit GEMM is then 2 T d N flops,
 // too few to fill matrix-core tiles, so it runs as fp32 FMAs (each product
 // of a bf16 x and an fp32 weight is exact inside the fma; the sums are
 // fp32), with x read once.
