@@ -62,7 +62,14 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 }
 
 // silu(u) = u / (1 + exp(-u)); gelu_tanh(u) = 0.5 u (1 + tanh(sqrt(2/pi)(u + 0.044715 u^3))).
-__device__ __forceinline__ float silu_f(float u) { return u / (1.0f + __expf(-u)); }
+// silu divides by one hardware reciprocal (v_rcp_f32, within 1 ulp) and a
+// multiply instead of the correctly rounded division, whose expansion is
+// about ten instructions per element of the SwiGLU epilogues; the results go
+// to bf16 (or carry an fp32 error of a few ulp).  1 + exp(-u) >= 1, and its
+// infinity (u below about -88) gives a reciprocal of 0 and silu = -0.
+__device__ __forceinline__ float silu_f(float u) {
+  return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u));
+}
 
 __device__ __forceinline__ float gelu_tanh_f(float u) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
