@@ -71,10 +71,14 @@ __device__ __forceinline__ float silu_f(float u) {
   return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u));
 }
 
+// gelu_tanh through 0.5 (1 + tanh(z)) = 1 / (1 + exp(-2 z)): one exp and one
+// hardware reciprocal, as silu, instead of tanhf (the bf16 epilogues and the
+// backward's recompute of h; the fp32 layer keeps tanhf).  A large negative
+// argument gives exp = inf, a reciprocal of 0 and gelu = -0.
 __device__ __forceinline__ float gelu_tanh_f(float u) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  float inner = c * (u + 0.044715f * u * u * u);
-  return 0.5f * u * (1.0f + tanhf(inner));
+  const float inner = c * (u + 0.044715f * u * u * u);
+  return u * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * inner));
 }
 
 // Find the group g with base[g] <= v < base[g+1] (base is non-decreasing,
