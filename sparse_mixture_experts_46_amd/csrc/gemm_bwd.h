@@ -89,15 +89,19 @@ struct BwdArgs {
   const void* cin2_shared;
 };
 
+// The sigmoids of both derivatives through one exp and the hardware
+// reciprocal (v_rcp_f32, within 1 ulp), as the forward's silu and gelu,
+// instead of a correctly rounded division or tanhf: with s = sigmoid(2 z),
+// tanh z = 2 s - 1, 1 + tanh z = 2 s and 1 - tanh^2 z = 4 s (1 - s).
 __device__ __forceinline__ float silu_grad_f(float u) {
-  const float s = 1.0f / (1.0f + __expf(-u));
+  const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-u));
   return s * (1.0f + u * (1.0f - s));
 }
 
 __device__ __forceinline__ float gelu_tanh_grad_f(float u) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  const float th = tanhf(c * (u + 0.044715f * u * u * u));
-  return 0.5f * (1.0f + th) + 0.5f * u * (1.0f - th * th) * c * (1.0f + 3.0f * 0.044715f * u * u);
+  const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * c * (u + 0.044715f * u * u * u)));
+  return s + 2.0f * u * s * (1.0f - s) * c * (1.0f + 3.0f * 0.044715f * u * u);
 }
 
 // Tile of a grouped problem.

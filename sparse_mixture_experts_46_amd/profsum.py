@@ -33,8 +33,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # the sources each family of grouped-GEMM kernels is built from (its
 # counter figures go stale when any of them changes)
 FAMILY_SRCS = {
-    "prefill": ["gemm_bf16.hip", "gemm_common.h", "gemm_pingpong.h", "gemm_tile.h", "lds_dma.h"],
-    "decode": ["gemm_bf16.hip", "gemm_common.h", "gemm_decode.h", "lds_dma.h"],
+    "prefill": ["gemm_bf16.hip", "gemm_common.h", "gemm_pingpong.h", "gemm_tile.h", "lds_dma.h",
+                "moe_common.h"],
+    "decode": ["gemm_bf16.hip", "gemm_common.h", "gemm_decode.h", "lds_dma.h", "moe_common.h"],
 }
 PROBE = "torch neg (copy probe)"
 N_SIMD = 256 * 4  # MI355X: 256 compute units of 4 SIMDs
