@@ -139,8 +139,21 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
   __shared__ int32_t scan[1024];
   const int tid = threadIdx.x;
   for (int e = tid; e < N; e += 1024) {
+    // eight block counts loaded before they are scanned: one dependent load
+    // per block made this latency-bound
     int32_t run = 0;
-    for (int64_t b = 0; b < nblk; ++b) {
+    int64_t b = 0;
+    for (; b + 8 <= nblk; b += 8) {
+      int32_t c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = blk_count[(b + u) * N + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        blk_base[(b + u) * N + e] = run;
+        run += c[u];
+      }
+    }
+    for (; b < nblk; ++b) {
       int32_t c = blk_count[b * N + e];
       blk_base[b * N + e] = run;
       run += c;
@@ -152,10 +165,18 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
   __syncthreads();
   const int32_t total = scan_kept(skept, scan, N, offset, nullptr);
   const int touched = count_touched(skept, N);
-  if (tid == 0 && counters) {
+  if (counters) {  // bad ids: per-thread strided sums, then thread 0 adds them
     int64_t bad = 0;
-    for (int64_t b = 0; b < nblk; ++b) bad += blk_bad[b];
-    write_counters(counters, total, T, K, bad, touched);
+    for (int64_t b = tid; b < nblk; b += 1024) bad += blk_bad[b];
+    scan[tid] = (int32_t)bad;  // scan[] is free again after scan_kept
+    __syncthreads();
+    if (tid == 0) {
+      int64_t all = 0;
+      const int nt = nblk < 1024 ? (int)nblk : 1024;
+      for (int i = 0; i < nt; ++i) all += scan[i];
+      write_counters(counters, total, T, K, all, touched);
+    }
+    __syncthreads();
   }
   if (plan.nspec > 0)  // the expert FFN's tile tables, from the kept counts
     build_tile_tables([&](int g) { return skept[g]; }, plan.n_routed, plan.shared_rows, plan.specs,
